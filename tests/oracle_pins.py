@@ -1,0 +1,377 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes an ``oracle.oracle.Oracle`` and raises
+AssertionError when the oracle disagrees with what the pages and the
+mathematics fix: hand-worked blocks (``tests/golden``), exhaustive
+enumerations of the bit fields, closed-form identities, an independent
+bit-gathering evaluator with exact rational arithmetic on tiny shapes, and
+library routines (numpy's f16 conversion and float64 matmul).
+
+The same functions run against deliberately broken copies of the oracle in
+``test_oracle_mutants.py`` to show that a plausible mistake anywhere in it
+fails at least one pin.
+
+Sources:
+  trueno-gpu 0.4.11, src/kernels/quantize/fused.rs --
+    FusedRmsNormQ4KGemvKernel::build_ptx PHASE 1-2 (RMSNorm) and PHASE 3
+    (Q4_K super-block layout, 6-bit scale/min extraction, 64-value chunks).
+  inferencelayer 0.2.13, src/bin/kernel_lab.rs --
+    GEMV_F16S WGSL (Q4_0 nibble order, d*(q-8)); moe_lab / MOE_PURE_READ
+    (expert-stacked rows, per-(token, slot) selection).
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+
+from bit_block_quantized_dequant_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+# --------------------------------------------------------------------------
+# Test-local encoders, written as the inverse of the page's extraction rule
+# (they exist only here, to build hand-made blocks).
+# --------------------------------------------------------------------------
+def pack_scale_min(sc, m):
+    """Pack 8 six-bit scales and 8 six-bit mins (last axis) into the 12 Q4_K
+    bytes (last axis)."""
+    sc = np.asarray(sc, dtype=np.int64)
+    m = np.asarray(m, dtype=np.int64)
+    S = np.zeros(sc.shape[:-1] + (12,), dtype=np.int64)
+    for j in range(4):
+        S[..., j] = (sc[..., j] & 63) | ((sc[..., j + 4] >> 4) << 6)
+        S[..., j + 4] = (m[..., j] & 63) | ((m[..., j + 4] >> 4) << 6)
+        S[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    return S.astype(np.uint8)
+
+
+def f16_bytes(v):
+    return np.frombuffer(np.float16(v).tobytes(), dtype=np.uint8)
+
+
+def q4k_block(d, dmin, sc, m, qs):
+    return np.concatenate([f16_bytes(d), f16_bytes(dmin), pack_scale_min(sc, m),
+                           np.asarray(qs, dtype=np.uint8)]).astype(np.uint8)
+
+
+def q4_0_block(d, qs):
+    return np.concatenate([f16_bytes(d), np.asarray(qs, dtype=np.uint8)]).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Independent evaluator: gathers every field bit by bit from the raw bytes
+# and works in exact rational arithmetic.  It never calls the oracle.
+# --------------------------------------------------------------------------
+def _bits(buf, bit_off, nbits):
+    v = 0
+    for i in range(nbits):
+        b = bit_off + i
+        v |= ((int(buf[b >> 3]) >> (b & 7)) & 1) << i
+    return v
+
+
+def _half(buf, byte_off):
+    return Fraction(struct.unpack("<e", bytes(buf[byte_off:byte_off + 2]))[0])
+
+
+# Source bit (inside the 12 scale bytes) of every bit of scale/min j.
+def _q4k_field_bits(j):
+    if j < 4:
+        sc = [8 * j + i for i in range(6)]
+        mn = [8 * (j + 4) + i for i in range(6)]
+    else:
+        sc = [8 * (j + 4) + i for i in range(4)] + [8 * (j - 4) + 6, 8 * (j - 4) + 7]
+        mn = [8 * (j + 4) + 4 + i for i in range(4)] + [8 * j + 6, 8 * j + 7]
+    return sc, mn
+
+
+def _gather(buf, base_bit, srcs):
+    return sum(_bits(buf, base_bit + s, 1) << i for i, s in enumerate(srcs))
+
+
+def brute_weight_q4_0(row, e):
+    b, j = divmod(e, 32)
+    q = _bits(row, 8 * (18 * b + 2 + j % 16) + 4 * (j // 16), 4)
+    return _half(row, 18 * b) * (q - 8)
+
+
+def brute_weight_q4k(row, e):
+    s, t = divmod(e, 256)
+    base = 144 * s
+    q = _bits(row, 8 * (base + 16 + 32 * (t // 64) + t % 32) + 4 * ((t % 64) // 32), 4)
+    scb, mnb = _q4k_field_bits(t // 32)
+    sc = _gather(row, 8 * (base + 4), scb)
+    mn = _gather(row, 8 * (base + 4), mnb)
+    return _half(row, base) * sc * q - _half(row, base + 2) * mn
+
+
+def _to_f32(fr):
+    # the exact value has at most 50 significant bits, so float() is exact
+    return np.float32(float(fr))
+
+
+# --------------------------------------------------------------------------
+# Pins
+# --------------------------------------------------------------------------
+def pin_f16_decode(o):
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    got = np.array([o.f16_to_f32(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN positions differ"
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32)), "f16 decode"
+
+
+def pin_q4_0_golden(o):
+    g = load_golden("q4_0_worked_block.txt")
+    blk = np.frombuffer(bytes.fromhex(g["block_hex"]), dtype=np.uint8)
+    want = np.array([float(v) for v in g["dequant"].split()], dtype=np.float32)
+    got = o.dequant_q4_0(blk, 1, 32)[0]
+    assert np.array_equal(got, want), (got, want)
+    y1, _ = o.q4_0_gemv(blk, np.ones((1, 32), np.float32), 1, 32)
+    yk, _ = o.q4_0_gemv(blk, np.arange(32, dtype=np.float32)[None], 1, 32)
+    assert y1[0, 0] == float(g["y_x_ones"]) and yk[0, 0] == float(g["y_x_index"])
+
+
+def pin_q4k_golden(o):
+    g = load_golden("q4k_worked_superblock.txt")
+    hdr = np.frombuffer(bytes.fromhex(g["header_hex"]), dtype=np.uint8)
+    blk = np.concatenate([hdr, np.full(128, int(g["qs_byte"], 16), np.uint8)])
+    sc = [int(v) for v in g["sc"].split()]
+    mn = [int(v) for v in g["m"].split()]
+    for j in range(8):
+        assert o.q4k_scale_min(hdr[4:16], j) == (sc[j], mn[j]), j
+    assert np.array_equal(pack_scale_min(sc, mn), hdr[4:16])
+    vals = [float(v) for v in g["subblock_values"].split()]
+    want = np.repeat(np.array(vals, np.float32), 32)
+    got = o.dequant_q4k(blk, 1, 256)[0]
+    assert np.array_equal(got, want)
+    y, _ = o.q4k_gemv(blk, np.ones((1, 256), np.float32), 1, 256)
+    assert y[0, 0] == float(g["y_x_ones"])
+
+
+def pin_q4k_scale_roundtrip(o):
+    """Exhaustive: every (scale, min) pair in every sub-block slot decodes to
+    itself.  d = dmin = 1; element 0 of every sub-block has q = 0 (reads -m)
+    and element 1 has q = 1 (reads sc - m)."""
+    rng = synth.make_rng(7)
+    s_all, m_all = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    n = 64 * 64
+    qs = np.zeros(128, np.uint8)
+    for c in range(4):
+        qs[32 * c + 1] = 0x11  # element 64c+1 (low) and 64c+33 (high) get q = 1
+    for j in range(8):
+        sc = rng.integers(0, 64, (n, 8))
+        mn = rng.integers(0, 64, (n, 8))
+        sc[:, j] = s_all.reshape(-1)
+        mn[:, j] = m_all.reshape(-1)
+        w = np.zeros((n, 144), np.uint8)
+        w[:, 0:2] = f16_bytes(1.0)
+        w[:, 2:4] = f16_bytes(1.0)
+        w[:, 4:16] = pack_scale_min(sc, mn)
+        w[:, 16:] = qs
+        deq = o.dequant_q4k(w, n, 256).reshape(n, 8, 32)
+        assert np.array_equal(-deq[:, :, 0], mn.astype(np.float32)), j
+        assert np.array_equal(deq[:, :, 1] - deq[:, :, 0], sc.astype(np.float32)), j
+
+
+def pin_element_order(o):
+    """Exhaustive one-hot nibbles: exactly one output moves, at the place the
+    layout gives (Q4_K: byte b of qs is element 64*(b//32) + b%32, +32 for
+    the high nibble; Q4_0: byte j is element j, +16 for the high nibble)."""
+    hdr_sc = [1] * 8
+    hdr_m = [0] * 8
+    blocks, where = [], []
+    for b in range(128):
+        for h in range(2):
+            qs = np.zeros(128, np.uint8)
+            qs[b] = 15 << (4 * h)
+            blocks.append(q4k_block(1.0, 0.0, hdr_sc, hdr_m, qs))
+            where.append(64 * (b // 32) + b % 32 + 32 * h)
+    deq = o.dequant_q4k(np.stack(blocks), len(blocks), 256)
+    for i, pos in enumerate(where):
+        nz = np.flatnonzero(deq[i])
+        assert list(nz) == [pos] and deq[i, pos] == 15.0, (i, nz, pos)
+    blocks, where = [], []
+    for j in range(16):
+        for h in range(2):
+            qs = np.full(16, 0x88, np.uint8)  # q = 8 everywhere -> weight 0
+            qs[j] = (0x8 << 4) | 0xF if h == 0 else (0xF << 4) | 0x8
+            blocks.append(q4_0_block(1.0, qs))
+            where.append(j + 16 * h)
+    deq = o.dequant_q4_0(np.stack(blocks), len(blocks), 32)
+    for i, pos in enumerate(where):
+        nz = np.flatnonzero(deq[i])
+        assert list(nz) == [pos] and deq[i, pos] == 7.0, (i, nz, pos)
+
+
+def pin_identities(o):
+    """All-equal nibbles c: Q4_0 gives sum_b d_b (c-8) X_b; Q4_K gives
+    sum_j (d sc_j c - dmin m_j) X_j (X = block or sub-block sums of x).
+    q = 0 isolates the mins; d = dmin = 0 gives exactly 0."""
+    rng = synth.make_rng(11)
+    K = 512
+    x = synth.activations(rng, 2, K)
+    for c in (0, 5, 8, 15):
+        ds = rng.uniform(0.01, 0.1, K // 32).astype(np.float16)
+        row = np.concatenate([q4_0_block(d, np.full(16, c | (c << 4), np.uint8)) for d in ds])
+        y, _ = o.q4_0_gemv(row, x, 1, K)
+        X = x.astype(np.float64).reshape(2, K // 32, 32).sum(-1)
+        want = (X * (ds.astype(np.float64) * (c - 8))).sum(-1)
+        assert np.allclose(y[:, 0], want, rtol=1e-12, atol=1e-12), (c, y, want)
+    for c in (0, 7, 15):
+        blks, terms = [], []
+        for s in range(K // 256):
+            d, dmin = np.float16(rng.uniform(0.005, 0.05)), np.float16(rng.uniform(0.005, 0.05))
+            sc, mn = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+            blks.append(q4k_block(d, dmin, sc, mn, np.full(128, c | (c << 4), np.uint8)))
+            terms.append((float(d) * sc * c - float(dmin) * mn))
+        row = np.concatenate(blks)
+        y, _ = o.q4k_gemv(row, x, 1, K)
+        X = x.astype(np.float64).reshape(2, K // 32, 32).sum(-1)
+        want = (X * np.concatenate(terms)).sum(-1)
+        assert np.allclose(y[:, 0], want, rtol=1e-12, atol=1e-12), (c, y, want)
+    zero = q4k_block(0.0, 0.0, [63] * 8, [63] * 8, np.full(128, 0xFF, np.uint8))
+    y, _ = o.q4k_gemv(zero, x[:, :256], 1, 256)
+    assert np.all(y == 0.0)
+
+
+def pin_gemv_onehot_and_scaling(o):
+    """x = e_k gives y[n] = w[n,k] exactly; x = 0 gives 0; y(2x) = 2 y(x)."""
+    rng = synth.make_rng(13)
+    N, K = 6, 512
+    for fmt in ("q4_0", "q4k"):
+        if fmt == "q4_0":
+            w = synth.q4_0_matrix(rng, N, K)
+            deq, gemv = o.dequant_q4_0(w, N, K), o.q4_0_gemv
+        else:
+            w = synth.q4k_matrix(rng, N, K)
+            deq, gemv = o.dequant_q4k(w, N, K), o.q4k_gemv
+        eye = np.eye(K, dtype=np.float32)[::37]
+        y, _ = gemv(w, eye, N, K)
+        assert np.array_equal(y.astype(np.float32), deq[:, ::37].T), fmt
+        y0, a0 = gemv(w, np.zeros((1, K), np.float32), N, K)
+        assert np.all(y0 == 0) and np.all(a0 == 0)
+        x = synth.activations(rng, 3, K)
+        y1, a1 = gemv(w, x, N, K)
+        y2, a2 = gemv(w, 2 * x, N, K)
+        assert np.array_equal(y2, 2 * y1) and np.array_equal(a2, 2 * a1), fmt
+
+
+def pin_bruteforce(o, seeds=range(6)):
+    """Independent bit-gathering evaluator with exact rationals on tiny shapes:
+    dequant bit-exact, GEMV within double rounding, |w*x| sum likewise."""
+    for seed in seeds:
+        rng = synth.make_rng(100 + seed)
+        K = 256 * (1 + seed % 2)
+        N, M = 2 + seed % 3, 1 + seed % 3
+        x = synth.activations(rng, M, K)
+        for fmt in ("q4_0", "q4k"):
+            if fmt == "q4_0":
+                w = synth.q4_0_matrix(rng, N, K)
+                deq, gemv, bw = o.dequant_q4_0(w, N, K), o.q4_0_gemv, brute_weight_q4_0
+            else:
+                w = synth.q4k_matrix(rng, N, K)
+                deq, gemv, bw = o.dequant_q4k(w, N, K), o.q4k_gemv, brute_weight_q4k
+            y, a = gemv(w, x, N, K)
+            for n in range(N):
+                wf = [_to_f32(bw(w[n], e)) for e in range(K)]
+                assert np.array_equal(np.array(wf, np.float32), deq[n]), (fmt, seed, n)
+                for m in range(M):
+                    exact = sum(Fraction(float(wk)) * Fraction(float(xk))
+                                for wk, xk in zip(wf, x[m]))
+                    aex = sum(abs(Fraction(float(wk)) * Fraction(float(xk)))
+                              for wk, xk in zip(wf, x[m]))
+                    tol = K * 2.0 ** -52 * float(aex)
+                    assert abs(y[m, n] - float(exact)) <= tol, (fmt, seed, n, m)
+                    assert abs(a[m, n] - float(aex)) <= tol, (fmt, seed, n, m)
+
+
+def pin_gemv_vs_numpy(o):
+    """The oracle GEMV equals numpy's float64 matmul of its dequantized rows."""
+    rng = synth.make_rng(17)
+    N, K = 40, 1024
+    x = synth.activations(rng, 4, K)
+    for fmt in ("q4_0", "q4k"):
+        w = synth.q4_0_matrix(rng, N, K) if fmt == "q4_0" else synth.q4k_matrix(rng, N, K)
+        deq = o.dequant_q4_0(w, N, K) if fmt == "q4_0" else o.dequant_q4k(w, N, K)
+        y, a = (o.q4_0_gemv if fmt == "q4_0" else o.q4k_gemv)(w, x, N, K, nthreads=3)
+        ref = x.astype(np.float64) @ deq.astype(np.float64).T
+        aref = np.abs(x.astype(np.float64)) @ np.abs(deq.astype(np.float64)).T
+        assert np.all(np.abs(y - ref) <= 1e-12 * aref), fmt
+        assert np.allclose(a, aref, rtol=1e-12), fmt
+
+
+def pin_rmsnorm(o):
+    """Constant rows with gamma = 1 give c/sqrt(c^2 + eps) (closed form);
+    random rows match the float64 formula to float32 rounding."""
+    eps = 1e-5
+    K = 512
+    for c in (0.75, -3.0, 1e-3, 20.0):
+        xh = o.rmsnorm(np.full((1, K), c, np.float32), np.ones(K, np.float32), eps)
+        want = c / np.sqrt(c * c + eps)
+        assert np.all(np.abs(xh - want) <= 4 * np.spacing(np.float32(abs(want)))), (c, xh[0, 0])
+    rng = synth.make_rng(19)
+    x = synth.activations(rng, 3, K, 2.0)
+    g = synth.gamma(rng, K)
+    xh = o.rmsnorm(x, g, eps)
+    xd = x.astype(np.float64)
+    ref = xd / np.sqrt((xd * xd).mean(-1, keepdims=True) + eps) * g.astype(np.float64)
+    assert np.all(np.abs(xh - ref) <= 1e-6 * np.abs(ref) + 1e-12)
+    y, a, xh2 = o.fused_rmsnorm_q4k_gemv(synth.q4k_matrix(rng, 5, K), x, g, eps, 5, K)
+    assert np.array_equal(xh2, xh)
+
+
+def pin_composites(o):
+    """Gate/up and MoE are the plain GEMV per matrix and per (token, slot);
+    an expert id outside [0, E) yields NaN rows."""
+    rng = synth.make_rng(23)
+    N, K, E, M, top_k = 8, 512, 5, 3, 2
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K)
+    g, u, ag, au = o.gate_up_q4k_gemv(wg, wu, x, N, K)
+    assert np.array_equal(g, o.q4k_gemv(wg, x, N, K)[0])
+    assert np.array_equal(u, o.q4k_gemv(wu, x, N, K)[0])
+    mg, mu = synth.q4_0_matrix(rng, E * N, K), synth.q4_0_matrix(rng, E * N, K)
+    ids = np.array([[4, 0], [2, 4], [1, 7]], np.int32)
+    g, u, ag, au = o.moe_q4_0_gemv(mg, mu, x, ids, E, N, K)
+    rb = synth.q4_0_row_bytes(K)
+    for m in range(M):
+        for s in range(top_k):
+            e = ids[m, s]
+            if e >= E:
+                assert np.all(np.isnan(g[m, s])) and np.all(np.isnan(u[m, s]))
+                continue
+            ge = mg[e * N:(e + 1) * N].reshape(-1)
+            ue = mu[e * N:(e + 1) * N].reshape(-1)
+            assert np.array_equal(g[m, s], o.q4_0_gemv(ge, x[m], N, K)[0][0]), (m, s)
+            assert np.array_equal(u[m, s], o.q4_0_gemv(ue, x[m], N, K)[0][0]), (m, s)
+    assert rb == K // 32 * 18
+
+
+def pin_checksum(o):
+    rng = synth.make_rng(29)
+    w = synth.q4k_matrix(rng, 7, 512)
+    got = o.row_checksum(w, 7, w.shape[1])
+    want = (w.view("<u4").astype(np.uint64).sum(-1) % (1 << 32)).astype(np.uint32)
+    assert np.array_equal(got, want)
+
+
+# fast pins first: the mutant test stops at the first failing pin
+ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_gemv_onehot_and_scaling,
+            pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
+            pin_rmsnorm, pin_composites, pin_f16_decode, pin_bruteforce]
