@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of libq4gemv on one MI355X.
+
+Default run (one JSON line on stdout): the headline workload, the fused
+gate+up Q4_K GEMV at M=1, K=4096, N=14336 per matrix (66,060,288 weight bytes
+per call), timed over --steps calls after --warmup untimed calls.
+
+  value        whole-job effective weight bandwidth: weight bytes of all timed
+               calls / wall time between two device synchronizations (GB/s)
+  roofline     the kernel itself: weight bytes per launch / mean launch
+               duration from HIP events recorded around each launch on the
+               launch stream, against the 8 TB/s HBM3E peak
+  pure_read    the same for the pure-read ceiling kernel (same bytes, same
+               addressing, no arithmetic)
+  cpu_baseline the CPU oracle (plain C, float64) timed on this host's cores on
+               a bounded sample of the same workload
+
+Weights stay resident in HBM; to measure HBM and not the 256 MB Infinity Cache
+every call reads a different copy of the weights, from a rotation of copies
+totalling at least 1 GiB.
+
+  --all REPORT   additionally time every named workload and its ceiling and
+                 write REPORT.json and REPORT.md
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective weight GB/s and % of HBM peak, Q4_K GEMV M=1 K=4096"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--all", metavar="REPORT", default=None,
+                    help="also time every named workload; write REPORT.json / REPORT.md")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound of the CPU-oracle sample (0 skips it)")
+    return ap.parse_args()
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class Rotation:
+    """`ncopies` copies of one packed weight buffer inside one device allocation."""
+
+    def __init__(self, torch, dev, host_bytes, min_total=ROTATE_BYTES):
+        import numpy as np
+        nbytes = int(host_bytes.nbytes)
+        self.nbytes = nbytes
+        self.stride = (nbytes + 4095) // 4096 * 4096
+        self.ncopies = max(2, math.ceil(min_total / self.stride))
+        self.buf = torch.empty(self.ncopies * self.stride, dtype=torch.uint8, device=dev)
+        src = torch.from_numpy(np.ascontiguousarray(host_bytes).reshape(-1)).to(dev)
+        self.buf.view(self.ncopies, self.stride)[:, :nbytes].copy_(
+            src.view(1, nbytes).expand(self.ncopies, nbytes))
+        self.base = self.buf.data_ptr()
+        del src
+
+    def ptr(self, i):
+        return self.base + (i % self.ncopies) * self.stride
+
+
+def time_launches(torch, launch, warmup, steps):
+    """launch(i) enqueues call i.  Returns (wall seconds, per-launch ms list)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        launch(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def stats(durs_ms):
+    s = sorted(durs_ms)
+    n = len(s)
+    return dict(mean_ms=sum(s) / n, median_ms=s[n // 2], min_ms=s[0], max_ms=s[-1],
+                spread=s[-1] / s[0] - 1.0 if s[0] > 0 else None)
+
+
+def check(status, what):
+    if status != 0:
+        import bit_block_quantized_dequant_amd as q4
+        raise RuntimeError("%s failed: %s" % (what, q4.q4_strerror(status)))
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
+# ---------------------------------------------------------------------------
+def setup_workload(torch, dev, index, M):
+    import numpy as np
+
+    import bit_block_quantized_dequant_amd as q4
+    from bit_block_quantized_dequant_amd import synth
+
+    L = q4.lib()
+    d = synth.workload_inputs(index, M=M)
+    N, K = d["N"], d["K"]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    keep = []
+
+    def T(a):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        keep.append(t)
+        return t
+
+    x = T(d["x"])
+    notes = {}
+    rot = None
+    if index in (1, 2):
+        rot = Rotation(torch, dev, d["w"])
+        y = torch.empty(M, N, device=dev)
+        cks = torch.empty(N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+
+        def launch(i):
+            check(L.q4_0_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K, stream),
+                  "q4_0_gemv")
+
+        def ceil_launch(i):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4_0_GEMV, rot.ptr(i), None, None,
+                                 M, 0, 0, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+    elif index == 3:
+        rot = Rotation(torch, dev, d["w"])
+        g = T(d["gamma"])
+        y = torch.empty(M, N, device=dev)
+        cks = torch.empty(N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+
+        def launch(i):
+            check(L.fused_rmsnorm_q4k_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), g.data_ptr(),
+                                           d["eps"], M, N, K, stream), "fused_rmsnorm_q4k_gemv")
+
+        def ceil_launch(i):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4K_GEMV, rot.ptr(i), None, None,
+                                 M, 0, 0, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+    elif index == 4:
+        both = np.concatenate([d["w_gate"].reshape(-1), d["w_up"].reshape(-1)])
+        rot = Rotation(torch, dev, both)
+        half = d["w_gate"].nbytes
+        gate = torch.empty(M, N, device=dev)
+        up = torch.empty(M, N, device=dev)
+        cks = torch.empty(2 * N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+
+        def launch(i):
+            p = rot.ptr(i)
+            check(L.fused_gate_up_q4k_gemv(gate.data_ptr(), up.data_ptr(), p, p + half,
+                                           x.data_ptr(), M, N, K, stream),
+                  "fused_gate_up_q4k_gemv")
+
+        def ceil_launch(i):
+            p = rot.ptr(i)
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_GATE_UP, p, p + half, None, M, 0, 0,
+                                 N, K, stream), "q4_pure_read")
+        keep += [rot, gate, up, cks]
+    elif index == 5:
+        E, top_k = d["E"], d["top_k"]
+        both = np.concatenate([d["w_gate"].reshape(-1), d["w_up"].reshape(-1)])
+        rot = Rotation(torch, dev, both)
+        half = d["w_gate"].nbytes
+        ids = T(d["ids"])
+        gate = torch.empty(M, top_k, N, device=dev)
+        up = torch.empty(M, top_k, N, device=dev)
+        cks = torch.empty(2 * M * top_k * N, dtype=torch.int32, device=dev)
+        uniq = len(set(int(e) for e in d["ids"].reshape(-1)))
+        per_expert = 2 * N * synth.q4_0_row_bytes(K)
+        wbytes = uniq * per_expert
+        notes = dict(unique_experts=uniq, pairs=M * top_k,
+                     pair_counted_bytes=M * top_k * per_expert)
+
+        def launch(i):
+            p = rot.ptr(i)
+            check(L.moe_q4_gemv(gate.data_ptr(), up.data_ptr(), p, p + half, x.data_ptr(),
+                                ids.data_ptr(), M, top_k, E, N, K, stream), "moe_q4_gemv")
+
+        def ceil_launch(i):
+            p = rot.ptr(i)
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_MOE, p, p + half, ids.data_ptr(), M,
+                                 top_k, E, N, K, stream), "q4_pure_read")
+        keep += [rot, gate, up, cks]
+    notes["copies"] = rot.ncopies
+    return wbytes, launch, ceil_launch, notes, keep
+
+
+def measure(torch, dev, index, M, warmup, steps):
+    wbytes, launch, ceil_launch, notes, keep = setup_workload(torch, dev, index, M)
+    wall, durs = time_launches(torch, launch, warmup, steps)
+    cwall, cdurs = time_launches(torch, ceil_launch, warmup, steps)
+    st, cst = stats(durs), stats(cdurs)
+    res = dict(index=index, M=M, weight_bytes=wbytes, wall_s=wall, steps=steps,
+               value_gbs=wbytes * steps / wall / 1e9,
+               kernel=st, kernel_gbs=wbytes / (st["mean_ms"] * 1e-3) / 1e9,
+               kernel_gbs_median=wbytes / (st["median_ms"] * 1e-3) / 1e9,
+               ceiling=cst, ceiling_gbs=wbytes / (cst["mean_ms"] * 1e-3) / 1e9, **notes)
+    res["frac_of_peak"] = res["kernel_gbs"] / HBM_PEAK_GBS
+    res["frac_of_ceiling"] = res["kernel_gbs"] / res["ceiling_gbs"]
+    del keep
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(seconds):
+    """The oracle's gate+up GEMV of the headline workload, timed on the host."""
+    from bit_block_quantized_dequant_amd import synth
+    from oracle import oracle
+
+    o = oracle.default()
+    d = synth.workload_inputs(4, M=1)
+    N, K = d["N"], d["K"]
+    nt = host_threads()
+    wbytes = d["w_gate"].nbytes + d["w_up"].nbytes
+    o.gate_up_q4k_gemv(d["w_gate"][:64], d["w_up"][:64], d["x"], 64, K, nt)  # warm
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        o.gate_up_q4k_gemv(d["w_gate"], d["w_up"], d["x"], N, K, nt)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or calls >= 1000:
+            break
+    return dict(value=wbytes * calls / el / 1e9, unit="GB/s", cores=nt, kind="oracle",
+                sample="%d full calls of the oracle's gate+up Q4_K GEMV (M=1, K=4096, "
+                       "N=14336x2; float64 accumulation) in %.1f s on %d threads"
+                       % (calls, el, nt))
+
+
+def write_report(path, rows, headline):
+    with open(path + ".json", "w") as f:
+        json.dump(dict(headline=headline, workloads=rows), f, indent=1)
+    names = {1: "q4_0_gemv K=512 N=256", 2: "q4_0_gemv K=4096 N=4096",
+             3: "fused_rmsnorm_q4k_gemv K=3584 N=18944", 4: "fused_gate_up_q4k_gemv K=4096 N=14336x2",
+             5: "moe_q4_gemv E=64 top6 N=1408 K=2048"}
+    lines = ["| workload | M | weight MB | kernel us (median) | GB/s (mean dur) | % of 8 TB/s | "
+             "ceiling GB/s | % of ceiling | spread |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %s | %d | %.2f | %.2f | %.0f | %.1f%% | %.0f | %.1f%% | %.2f |" % (
+            names[r["index"]], r["M"], r["weight_bytes"] / 1e6, r["kernel"]["median_ms"] * 1e3,
+            r["kernel_gbs"], 100 * r["frac_of_peak"], r["ceiling_gbs"],
+            100 * r["frac_of_ceiling"], r["kernel"]["spread"]))
+    with open(path + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_block_quantized_dequant_amd as q4
+
+    q4.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    head = measure(torch, dev, 4, 1, args.warmup, args.steps)
+    print("headline: kernel %.2f us (median %.2f), %.0f GB/s; ceiling %.0f GB/s; wall %.0f GB/s"
+          % (head["kernel"]["mean_ms"] * 1e3, head["kernel"]["median_ms"] * 1e3,
+             head["kernel_gbs"], head["ceiling_gbs"], head["value_gbs"]), file=sys.stderr,
+          flush=True)
+
+    rows = []
+    if args.all:
+        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 4)), (5, (4,))):
+            for M in Ms:
+                r = measure(torch, dev, index, M, args.warmup, args.steps)
+                rows.append(r)
+                print("workload %d M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of ceiling)"
+                      % (index, M, r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
+                         100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"]),
+                      file=sys.stderr, flush=True)
+
+    cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    ms_per_step = head["wall_s"] / head["steps"] * 1e3
+    line = {
+        "metric": METRIC,
+        "value": round(head["value_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fused_gate_up_q4k_gemv Q4_K M=1 K=4096 N=14336x2 "
+                               "(66,060,288 weight bytes per call; %d rotating copies)"
+                               % head["copies"]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["kernel_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["frac_of_peak"], 4),
+            "traffic": None,
+            "kernel_us_mean": round(head["kernel"]["mean_ms"] * 1e3, 3),
+            "kernel_us_median": round(head["kernel"]["median_ms"] * 1e3, 3),
+        },
+        "pure_read": {
+            "achieved": round(head["ceiling_gbs"], 2),
+            "unit": "GB/s",
+            "kernel_frac_of_ceiling": round(head["frac_of_ceiling"], 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    if args.all:
+        write_report(args.all, rows, line)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+"""Python binding of libq4gemv: decode-time GEMV over 4-bit block-quantized
+weights on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every function has the name and argument order of
+the C call in include/q4gemv.h; tensors are torch device tensors (their
+data_ptr() is passed), sizes are ints, and `stream` defaults to torch's
+current stream on the tensors' device.  All arithmetic runs in the HIP
+kernels of libq4gemv.so; there is no other implementation to fall back to,
+and a missing library raises ImportError on first use.
+
+The binding adds guards the C ABI cannot make by itself: every tensor must
+live on a GPU, be contiguous and be at least as large as the call will touch,
+so that a wrong argument raises here instead of reaching a kernel.  A nonzero
+status from the library raises Q4Error.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
+    "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "moe_q4_gemv", "dequant_q4k",
+    "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
+    "Q4_READ_GATE_UP", "Q4_READ_MOE", "LIB_PATH", "q4_0_row_bytes", "q4k_row_bytes",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
+
+Q4_READ_Q4_0_GEMV = 0
+Q4_READ_Q4K_GEMV = 1
+Q4_READ_GATE_UP = 2
+Q4_READ_MOE = 3
+
+STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_BATCH", 4: "Q4_ERR_ALIGN",
+          5: "Q4_ERR_ARG", 6: "Q4_ERR_HIP"}
+
+_LIB = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (call, STATUS.get(status, status),
+                                                 q4_strerror(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libq4gemv.so (raises ImportError if it was never built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libq4gemv.so is not built at %s; build it with "
+                              "`python -m bit_block_quantized_dequant_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.q4_strerror.argtypes = [ctypes.c_int]
+        L.q4_strerror.restype = ctypes.c_char_p
+        L.q4_version.argtypes = []
+        L.q4_version.restype = ctypes.c_int
+        sigs = {
+            "q4_0_gemv": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "q4k_gemv": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "fused_rmsnorm_q4k_gemv": [_vp, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _i64,
+                                       _vp],
+            "fused_gate_up_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "moe_q4_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
+            "dequant_q4k": [_vp, _vp, _i64, _i64, _vp],
+            "dequant_q4_0": [_vp, _vp, _i64, _i64, _vp],
+            "q4_pure_read": [_vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                             _vp],
+        }
+        for name, args in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def q4_version() -> int:
+    return int(lib().q4_version())
+
+
+def q4_strerror(status: int) -> str:
+    return lib().q4_strerror(int(status)).decode()
+
+
+def q4_0_row_bytes(K: int) -> int:
+    return K // 32 * 18
+
+
+def q4k_row_bytes(K: int) -> int:
+    return K // 256 * 144
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(t, name, min_bytes=None, device=None):
+    """Device pointer of tensor `t` (None passes NULL), after the guards."""
+    if t is None:
+        return None, device
+    if isinstance(t, int):  # a raw device address, passed through unchecked
+        return t, device
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, other arguments on %s" % (name, t.device, device))
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError("%s holds %d bytes, the call needs %d" %
+                         (name, t.numel() * t.element_size(), min_bytes))
+    return t.data_ptr(), t.device
+
+
+def _stream(stream, device):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ok(status, call):
+    if status != 0:
+        raise Q4Error(status, call)
+
+
+def _sz(v, per):
+    # bytes a call touches for a size that may be invalid (the library refuses those)
+    return max(0, int(v)) * per
+
+
+# --------------------------------------------------------------------------
+# calls (names and argument order of include/q4gemv.h)
+# --------------------------------------------------------------------------
+def q4_0_gemv(y, w, x, M, N, K, stream=None):
+    """y[M,N] = x[M,K] . W^T, W Q4_0 [N rows]."""
+    py, dev = _ptr(y, "y", _sz(M * N, 4))
+    pw, dev = _ptr(w, "w", _sz(N, q4_0_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    _ok(lib().q4_0_gemv(py, pw, px, M, N, K, _stream(stream, dev)), "q4_0_gemv")
+
+
+def q4k_gemv(y, w, x, M, N, K, stream=None):
+    """y[M,N] = x[M,K] . W^T, W Q4_K [N rows]."""
+    py, dev = _ptr(y, "y", _sz(M * N, 4))
+    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    _ok(lib().q4k_gemv(py, pw, px, M, N, K, _stream(stream, dev)), "q4k_gemv")
+
+
+def fused_rmsnorm_q4k_gemv(y, w, x, gamma, eps, M, N, K, stream=None):
+    """y = RMSNorm(x; gamma, eps) . W^T, W Q4_K."""
+    py, dev = _ptr(y, "y", _sz(M * N, 4))
+    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    pg, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    _ok(lib().fused_rmsnorm_q4k_gemv(py, pw, px, pg, float(eps), M, N, K, _stream(stream, dev)),
+        "fused_rmsnorm_q4k_gemv")
+
+
+def fused_gate_up_q4k_gemv(gate, up, w_gate, w_up, x, M, N, K, stream=None):
+    """gate = x . Wg^T, up = x . Wu^T (Q4_K), one staging of x."""
+    pg, dev = _ptr(gate, "gate", _sz(M * N, 4))
+    pu, dev = _ptr(up, "up", _sz(M * N, 4), dev)
+    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
+    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    _ok(lib().fused_gate_up_q4k_gemv(pg, pu, pwg, pwu, px, M, N, K, _stream(stream, dev)),
+        "fused_gate_up_q4k_gemv")
+
+
+def moe_q4_gemv(gate, up, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
+    """gate/up[M, top_k, N] of the selected Q4_0 experts (expert-stacked rows)."""
+    pg, dev = _ptr(gate, "gate", _sz(M * top_k * N, 4))
+    pu, dev = _ptr(up, "up", _sz(M * top_k * N, 4), dev)
+    pwg, dev = _ptr(w_gate, "w_gate", _sz(E * N, q4_0_row_bytes(K)), dev)
+    pwu, dev = _ptr(w_up, "w_up", _sz(E * N, q4_0_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4), dev)
+    _ok(lib().moe_q4_gemv(pg, pu, pwg, pwu, px, pi, M, top_k, E, N, K, _stream(stream, dev)),
+        "moe_q4_gemv")
+
+
+def dequant_q4k(out, w, N, K, stream=None):
+    """out[N,K] fp32 = the Q4_K weights, bit-exact."""
+    po, dev = _ptr(out, "out", _sz(N * K, 4))
+    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
+    _ok(lib().dequant_q4k(po, pw, N, K, _stream(stream, dev)), "dequant_q4k")
+
+
+def dequant_q4_0(out, w, N, K, stream=None):
+    """out[N,K] fp32 = the Q4_0 weights, bit-exact."""
+    po, dev = _ptr(out, "out", _sz(N * K, 4))
+    pw, dev = _ptr(w, "w", _sz(N, q4_0_row_bytes(K)), dev)
+    _ok(lib().dequant_q4_0(po, pw, N, K, _stream(stream, dev)), "dequant_q4_0")
+
+
+def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=None):
+    """Read the weight bytes of the named call with its addressing; write row checksums."""
+    if kernel_id == Q4_READ_MOE:
+        rows, nmat, rb = E * N, 2, q4_0_row_bytes(K)
+        ncks = 2 * M * top_k * N
+    else:
+        nmat = 2 if kernel_id == Q4_READ_GATE_UP else 1
+        rb = q4_0_row_bytes(K) if kernel_id == Q4_READ_Q4_0_GEMV else q4k_row_bytes(K)
+        rows, ncks = N, nmat * N
+    pc, dev = _ptr(checksum, "checksum", _sz(ncks, 4))
+    p0, dev = _ptr(w0, "w0", _sz(rows, rb), dev)
+    p1, dev = _ptr(w1, "w1", _sz(rows, rb) if nmat == 2 else None, dev)
+    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4) if kernel_id == Q4_READ_MOE else None, dev)
+    _ok(lib().q4_pure_read(pc, int(kernel_id), p0, p1, pi, M, top_k, E, N, K,
+                           _stream(stream, dev)), "q4_pure_read")

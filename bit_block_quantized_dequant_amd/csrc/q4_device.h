@@ -1,0 +1,273 @@
+// q4_device.h -- device-side building blocks of libq4gemv (gfx950, wave64).
+//
+// Block formats (little-endian):
+//   Q4_0: 18 bytes per 32 weights: f16 d, then 16 bytes whose low nibble j is
+//         element j and high nibble element j+16; w = d*(q-8)
+//         (inferencelayer 0.2.13, src/bin/kernel_lab.rs, GEMV_F16S WGSL).
+//   Q4_K: 144 bytes per 256 weights: f16 d, f16 dmin, 12 bytes of packed 6-bit
+//         scales/mins, 128 nibble bytes in 64-element chunks (32 low nibbles,
+//         then 32 high nibbles); w = d*sc*q - dmin*m
+//         (trueno-gpu 0.4.11, src/kernels/quantize/fused.rs,
+//          FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3).
+//
+// The unit of work of one lane is 64 consecutive weights of one row:
+//   Q4_K: chunk g of super-block s (unit u = 4s + g): its 32 nibble bytes
+//         hold sub-block 2g in the low nibbles and 2g+1 in the high nibbles;
+//         the 16-byte super-block header is loaded beside them.
+//   Q4_0: the block pair (2u, 2u+1): 36 bytes, 9 dword-aligned words.
+//
+// Arithmetic trick (exact): a nibble q masked into the low bits of a 16-bit
+// half is the f16 subnormal q * 2^-24, and a nibble masked in place in the
+// high half of a byte is 16q * 2^-24.  v_fma_mix_f32 converts such a half to
+// fp32 exactly inside the fused multiply-add, so one instruction does
+// convert + multiply + accumulate.  The activations are staged pre-scaled by
+// 2^24 (elements met as low nibbles) or 2^20 (high nibbles), which makes
+// every product exactly q * x.  The 6-bit Q4_K scales and mins are used the
+// same way (value sc * 2^-24), so Q4_K row sums come out scaled by 2^-24 and
+// are multiplied by 2^24 once at the end; powers of two are exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+constexpr int kWave = 64;
+constexpr int kFmtQ4_0 = 0;
+constexpr int kFmtQ4K = 1;
+
+constexpr int kUnitElems = 64;      // weights per lane unit
+constexpr int kQ4KBytes = 144;      // Q4_K super-block
+constexpr int kQ4_0PairBytes = 36;  // two Q4_0 blocks
+constexpr int kUnitWords = 12;      // registers per loaded unit (Q4_0 uses 9)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load from a 4-byte aligned address (Q4_0 pairs sit at a
+// 36-byte stride, so only dword alignment is guaranteed).
+__device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
+    const uint32_t* q = (const uint32_t*)__builtin_assume_aligned(p, 4);
+    u32x4 v;
+    __builtin_memcpy(&v, q, 16);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
+    return *(const uint32_t*)__builtin_assume_aligned(p, 4);
+}
+
+// The low / high 16-bit half of a word taken as f16 and widened exactly.
+__device__ __forceinline__ float h_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float h_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// ---------------------------------------------------------------------------
+// Unit loads.  `row` points at the first byte of the weight row.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, uint32_t (&r)[kUnitWords]) {
+    if constexpr (FMT == kFmtQ4K) {
+        const uint8_t* sb = row + (u >> 2) * kQ4KBytes;
+        const uint8_t* qs = sb + 16 + 32 * (u & 3);
+        u32x4 h = ldg16(sb);
+        u32x4 a = ldg16(qs);
+        u32x4 b = ldg16(qs + 16);
+        r[0] = h.x; r[1] = h.y; r[2] = h.z; r[3] = h.w;
+        r[4] = a.x; r[5] = a.y; r[6] = a.z; r[7] = a.w;
+        r[8] = b.x; r[9] = b.y; r[10] = b.z; r[11] = b.w;
+    } else {
+        const uint8_t* p = row + u * kQ4_0PairBytes;
+        u32x4 a = ldg16(p);
+        u32x4 b = ldg16(p + 16);
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        r[8] = ldg4(p + 32);
+        r[9] = r[10] = r[11] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K scale/min pairs of the two sub-blocks (2g, 2g+1) a lane works on, as
+// two f16-subnormal halves (value v * 2^-24) each.  Header words: h1 = S[0..3],
+// h2 = S[4..7], h3 = S[8..11].
+//   sub-blocks 0-3: sc = S[j] & 63, m = S[j+4] & 63
+//   sub-blocks 4-7: sc = (S[j+4] & 15) | (S[j-4] >> 6) << 4,
+//                   m  = (S[j+4] >> 4) | (S[j]   >> 6) << 4
+// `sel` = 0x0C000C00 | 2g | (2g+1) << 16 picks bytes 2g, 2g+1 out of the
+// eight bytes {high-group word, low-group word} into the two halves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t q4k_sel(int g) {
+    return 0x0C000C00u | (uint32_t)(2 * g) | ((uint32_t)(2 * g + 1) << 16);
+}
+
+__device__ __forceinline__ void q4k_scale_pairs(uint32_t h1, uint32_t h2, uint32_t h3,
+                                                uint32_t sel, uint32_t& scp, uint32_t& mp) {
+    const uint32_t lo4 = 0x0F0F0F0Fu;
+    // sub-blocks 4-7: low nibble from S[8..11], bits 4-5 from the top of S[0..7]
+    uint32_t sc_hi = (lo4 & h3) | (~lo4 & (h1 >> 2));
+    uint32_t m_hi = (lo4 & (h3 >> 4)) | (~lo4 & (h2 >> 2));
+    scp = __builtin_amdgcn_perm(sc_hi, h1, sel) & 0x003F003Fu;
+    mp = __builtin_amdgcn_perm(m_hi, h2, sel) & 0x003F003Fu;
+}
+
+// ---------------------------------------------------------------------------
+// Nibble dot products.  One word q of nibble bytes b0..b3 feeds
+//   lo: low nibbles  of b0,b1,b2,b3 against xa = x[e], x[e+1], x[e+2], x[e+3]
+//   hi: high nibbles of b0,b1,b2,b3 against xb (the elements they encode).
+// xa / xb are staged pre-scaled (2^24 / 2^20), so each product is q * x.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void nib_dot(uint32_t q, const float4& xa, const float4& xb,
+                                        float& slo, float& shi) {
+    const uint32_t t0 = q & 0x000F000Fu;  // low nibbles of b0, b2
+    const uint32_t t1 = q & 0x00F000F0u;  // high nibbles of b0, b2 (times 16)
+    const uint32_t q8 = q >> 8;
+    const uint32_t t2 = q8 & 0x000F000Fu;  // low nibbles of b1, b3
+    const uint32_t t3 = q8 & 0x00F000F0u;  // high nibbles of b1, b3 (times 16)
+    slo = __builtin_fmaf(h_lo(t0), xa.x, slo);
+    shi = __builtin_fmaf(h_lo(t1), xb.x, shi);
+    slo = __builtin_fmaf(h_hi(t0), xa.z, slo);
+    shi = __builtin_fmaf(h_hi(t1), xb.z, shi);
+    slo = __builtin_fmaf(h_lo(t2), xa.y, slo);
+    shi = __builtin_fmaf(h_lo(t3), xb.y, shi);
+    slo = __builtin_fmaf(h_hi(t2), xa.w, slo);
+    shi = __builtin_fmaf(h_hi(t3), xb.w, shi);
+}
+
+// LDS layout of the staged activations: per token row, K/4 float4 chunks;
+// unit u's 16 chunks are stored XOR-swizzled (chunk c at u*16 + (c ^ (u&15)))
+// so that 16 lanes reading the same logical chunk of 16 consecutive units hit
+// 16 different bank groups.
+__device__ __forceinline__ int xchunk(int u, int c) { return u * 16 + (c ^ (u & 15)); }
+
+// Is element e (within its row) met as a high nibble?  Q4_K: elements 32..63
+// of each 64-element chunk; Q4_0: elements 16..31 of each 32-element block.
+template <int FMT>
+__device__ __forceinline__ bool elem_is_high(int e) {
+    return FMT == kFmtQ4K ? (e & 32) != 0 : (e & 16) != 0;
+}
+
+// ---------------------------------------------------------------------------
+// One unit of NR rows against M token rows of staged activations.  Every
+// activation chunk is read from LDS once and used for all NR rows.
+//   xl  : LDS chunks of token 0 (token m at xl + m * kq)
+//   xs  : LDS per-32-run sums of token 0, as float2 per unit (token m at
+//         xs + m * (K/64)); Q4_K: plain sums X; Q4_0: -8 * X.
+// acc[r][m] accumulates row r's dot product with token m (Q4_K: scaled by
+// 2^-24).  For M > 1 a scheduling fence after each nibble word keeps the
+// compiler from hoisting all 16*M chunk reads at once (register pressure).
+// ---------------------------------------------------------------------------
+template <int FMT, int M, int NR>
+__device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], int u,
+                                         uint32_t sel, const float4* __restrict__ xl, int kq,
+                                         const float2* __restrict__ xs, int k64,
+                                         float (&acc)[NR][M]) {
+    const float4* xu = xl + u * 16;
+    const int sw = u & 15;
+    if constexpr (FMT == kFmtQ4K) {
+        float s0[NR][M], s1[NR][M];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) { s0[r][m] = 0.f; s1[r][m] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float4 xa = xu[m * kq + (i ^ sw)];
+                const float4 xb = xu[m * kq + ((8 + i) ^ sw)];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) nib_dot(w[r][4 + i], xa, xb, s0[r][m], s1[r][m]);
+            }
+            if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint32_t scp, mp;
+            q4k_scale_pairs(w[r][1], w[r][2], w[r][3], sel, scp, mp);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float2 X = xs[m * k64 + u];
+                float t = __builtin_fmaf(h_lo(scp), s0[r][m], 0.0f);
+                t = __builtin_fmaf(h_hi(scp), s1[r][m], t);
+                float v = __builtin_fmaf(h_lo(mp), X.x, 0.0f);
+                v = __builtin_fmaf(h_hi(mp), X.y, v);
+                acc[r][m] = __builtin_fmaf(h_lo(w[r][0]), t, acc[r][m]);
+                acc[r][m] = __builtin_fmaf(-h_hi(w[r][0]), v, acc[r][m]);
+            }
+        }
+    } else {
+        // block A = bytes 0..17 (d in w0.lo, nibbles shifted by two bytes),
+        // block B = bytes 18..35 (d in w4.hi, nibbles in w5..w8)
+        uint32_t qa[NR][4];
+        float a0[NR][M], a1[NR][M], b0[NR][M], b1[NR][M];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            qa[r][0] = __builtin_amdgcn_alignbit(w[r][1], w[r][0], 16);
+            qa[r][1] = __builtin_amdgcn_alignbit(w[r][2], w[r][1], 16);
+            qa[r][2] = __builtin_amdgcn_alignbit(w[r][3], w[r][2], 16);
+            qa[r][3] = __builtin_amdgcn_alignbit(w[r][4], w[r][3], 16);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float2 X8 = xs[m * k64 + u];  // (-8 * X_A, -8 * X_B)
+                a0[r][m] = X8.x; a1[r][m] = 0.f;
+                b0[r][m] = X8.y; b1[r][m] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float4 xal = xu[m * kq + (i ^ sw)];
+                const float4 xah = xu[m * kq + ((4 + i) ^ sw)];
+                const float4 xbl = xu[m * kq + ((8 + i) ^ sw)];
+                const float4 xbh = xu[m * kq + ((12 + i) ^ sw)];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    nib_dot(qa[r][i], xal, xah, a0[r][m], a1[r][m]);
+                    nib_dot(w[r][5 + i], xbl, xbh, b0[r][m], b1[r][m]);
+                }
+            }
+            if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                acc[r][m] = __builtin_fmaf(h_lo(w[r][0]), a0[r][m] + a1[r][m], acc[r][m]);
+                acc[r][m] = __builtin_fmaf(h_hi(w[r][4]), b0[r][m] + b1[r][m], acc[r][m]);
+            }
+    }
+}
+
+// Sum of the words a pure-read pass attributes to this unit: every Q4_0
+// word; for Q4_K the nibble words, plus the header once per super-block
+// (by the lane holding chunk 0).
+template <int FMT>
+__device__ __forceinline__ uint32_t unit_checksum(const uint32_t (&w)[kUnitWords], int u) {
+    uint32_t s = 0;
+    if constexpr (FMT == kFmtQ4K) {
+#pragma unroll
+        for (int i = 4; i < 12; ++i) s += w[i];
+        if ((u & 3) == 0) s += w[0] + w[1] + w[2] + w[3];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) s += w[i];
+    }
+    return s;
+}
+
+// Butterfly sum over aligned groups of `width` lanes (power of two <= 64);
+// every lane of a group ends with the group's total.
+__device__ __forceinline__ float group_sum(float v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, kWave);
+    return v;
+}
+
+}  // namespace q4

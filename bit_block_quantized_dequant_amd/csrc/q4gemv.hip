@@ -1,0 +1,345 @@
+// q4gemv.hip -- host side of libq4gemv: argument validation, launch planning
+// and the extern "C" entry points declared in include/q4gemv.h.
+//
+// Validation runs before any HIP call, so every refusal path is testable on
+// a machine without a GPU.  Launches go through hipLaunchKernel on the
+// caller's stream; the library allocates nothing and keeps no per-call state
+// (only a per-device cache of the compute-unit count and of which kernels
+// have had their LDS limit raised).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "q4_kernels.h"
+#include "q4gemv.h"
+
+using namespace q4;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// ---------------------------------------------------------------------------
+// Validation (pure host code)
+// ---------------------------------------------------------------------------
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_dims(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > 8) return Q4_ERR_BATCH;
+    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (M * K > Q4_MAX_MK) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+    int cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int device_cus(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return Q4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev[dev].cus == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return Q4_ERR_HIP;
+        g_dev[dev].cus = cus;
+    }
+    *out = g_dev[dev].cus;
+    return Q4_OK;
+}
+
+// Optional tuning override of the resident workgroups per CU (read once).
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+int pow2ceil(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// LDS bytes of a GEMV workgroup: M rows of K floats plus K/32 run sums each.
+size_t gemv_lds_bytes(int M, int K, bool pure) {
+    if (pure) return 0;
+    return (size_t)M * K * 4 + (size_t)M * (K / 32) * 4;
+}
+
+// Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
+// the static shared state), capped at 2 (16 waves of 512-thread groups).
+int wg_per_cu(size_t lds) {
+    const size_t cap = 160 * 1024 - 2048;
+    int by_lds = lds == 0 ? 2 : (int)(cap / lds);
+    int w = by_lds < 2 ? by_lds : 2;
+    static const int override_wg = env_int("Q4GEMV_WG_PER_CU", 0);
+    if (override_wg > 0 && override_wg < w) w = override_wg;
+    return w < 1 ? 1 : w;
+}
+
+// Raise a kernel's dynamic-LDS limit to the full 160 KB once per device.
+int allow_big_lds(const void* kern, std::atomic<int>* done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
+    if (done[dev].load(std::memory_order_acquire)) return Q4_OK;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - 2048);
+    if (e != hipSuccess) return Q4_ERR_HIP;
+    done[dev].store(1, std::memory_order_release);
+    return Q4_OK;
+}
+
+template <typename Kern>
+int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
+           std::atomic<int>* big_lds_done) {
+    if (lds > 64 * 1024) {
+        int st = allow_big_lds((const void*)kern, big_lds_done);
+        if (st) return st;
+    }
+    void* args[] = {(void*)&p};
+    hipError_t e = hipLaunchKernel((const void*)kern, dim3(blocks), dim3(kBlock), args, lds,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+// Fill the work-split fields of p for a call with `rows` rows per matrix
+// and RR rows per lane; returns the number of workgroups.
+int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
+         int cus) {
+    p.K = K;
+    p.upr = K / kUnitElems;
+    p.lg = p.upr >= kWave ? kWave : pow2ceil(p.upr);
+    p.upl = (p.upr + p.lg - 1) / p.lg;
+    p.rgw = kWave / p.lg;
+    const int nrg = (rows + RR - 1) / RR;
+    long long tasks;
+    if (moe) {
+        p.nrg = (nrg + p.rgw - 1) / p.rgw * p.rgw;
+        p.ntasks = 0;
+        tasks = (long long)npairs_max * (p.nrg / p.rgw);
+    } else {
+        p.nrg = nrg;
+        p.ntasks = (nrg + p.rgw - 1) / p.rgw;
+        tasks = p.ntasks;
+    }
+    const int wpb = kBlock / kWave;
+    const long long target = (long long)cus * wg_per_cu(gemv_lds_bytes(M, K, pure)) * wpb;
+    const long long per = (tasks + target - 1) / target;          // tasks per wave
+    const long long waves = per > 0 ? (tasks + per - 1) / per : 1;  // balanced
+    int blocks = (int)((waves + wpb - 1) / wpb);
+    if (blocks < 1) blocks = 1;
+    p.nwaves = blocks * wpb;
+    return blocks;
+}
+
+// Row-pair count per lane: two rows of a single matrix, or one row of each
+// of two matrices, so every lane streams two rows per step.
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
+    constexpr int RR = NMAT == 1 ? 2 : 1;
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    // a pure-read pass takes the launch shape of the call it mirrors
+    const int blocks = plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus);
+    const size_t lds = gemv_lds_bytes(M, p.K, PURE);
+    return launch(gemv_kernel<FMT, M, NMAT, RR, MODE, PURE>, p, blocks, lds, stream,
+                  big_lds_done);
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE>
+int run(GemvParams& p, int M, int npairs_max, void* stream) {
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st) return st;
+    switch (M) {
+        case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);
+        case 2: return run_m<FMT, NMAT, MODE, PURE, 2>(p, cus, npairs_max, stream);
+        case 3: return run_m<FMT, NMAT, MODE, PURE, 3>(p, cus, npairs_max, stream);
+        case 4: return run_m<FMT, NMAT, MODE, PURE, 4>(p, cus, npairs_max, stream);
+        case 5: return run_m<FMT, NMAT, MODE, PURE, 5>(p, cus, npairs_max, stream);
+        case 6: return run_m<FMT, NMAT, MODE, PURE, 6>(p, cus, npairs_max, stream);
+        case 7: return run_m<FMT, NMAT, MODE, PURE, 7>(p, cus, npairs_max, stream);
+        case 8: return run_m<FMT, NMAT, MODE, PURE, 8>(p, cus, npairs_max, stream);
+    }
+    return Q4_ERR_BATCH;
+}
+
+GemvParams base_params(const void* w0, const void* w1, float* y0, float* y1, const float* x,
+                       int64_t N, int64_t K, int fmt) {
+    GemvParams p = {};
+    p.w0 = (const uint8_t*)w0;
+    p.w1 = (const uint8_t*)w1;
+    p.y0 = y0;
+    p.y1 = y1;
+    p.x = x;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.row_bytes = fmt == kFmtQ4K ? (K / 256) * kQ4KBytes : (K / 32) * 18;
+    return p;
+}
+
+int check_moe(int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K) {
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (E < 1 || E >= (1 << 20) || top_k < 1 || top_k > E || M * top_k > kMaxPairs)
+        return Q4_ERR_SHAPE;
+    if (E * N > INT32_MAX) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_strerror(int status) {
+    switch (status) {
+        case Q4_OK: return "ok";
+        case Q4_ERR_NULL: return "a required pointer is NULL";
+        case Q4_ERR_SHAPE: return "N, K, E, top_k or M*K outside the supported limits";
+        case Q4_ERR_BATCH: return "batch M outside [1, 8]";
+        case Q4_ERR_ALIGN: return "pointer not aligned (weights and x: 16 bytes; others: 4)";
+        case Q4_ERR_ARG: return "invalid argument";
+        case Q4_ERR_HIP: return "the HIP runtime refused the launch";
+    }
+    return "unknown status";
+}
+
+int q4_version(void) { return 1; }
+
+int q4_0_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
+              void* stream) {
+    if (!y || !w || !x) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w, w, y, y, x, N, K, kFmtQ4_0);
+    return run<kFmtQ4_0, 1, kModeDense, false>(p, (int)M, 0, stream);
+}
+
+int q4k_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
+             void* stream) {
+    if (!y || !w || !x) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w, w, y, y, x, N, K, kFmtQ4K);
+    return run<kFmtQ4K, 1, kModeDense, false>(p, (int)M, 0, stream);
+}
+
+int fused_rmsnorm_q4k_gemv(float* y, const void* w, const float* x, const float* gamma,
+                           float eps, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!y || !w || !x || !gamma) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return Q4_ERR_ARG;
+    GemvParams p = base_params(w, w, y, y, x, N, K, kFmtQ4K);
+    p.gamma = gamma;
+    p.eps = eps;
+    return run<kFmtQ4K, 1, kModeNorm, false>(p, (int)M, 0, stream);
+}
+
+int fused_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate, const void* w_up,
+                           const float* x, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!gate || !up || !w_gate || !w_up || !x) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gate, 4) ||
+        !aligned(up, 4))
+        return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w_gate, w_up, gate, up, x, N, K, kFmtQ4K);
+    return run<kFmtQ4K, 2, kModeDense, false>(p, (int)M, 0, stream);
+}
+
+int moe_q4_gemv(float* gate, float* up, const void* w_gate, const void* w_up, const float* x,
+                const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
+                void* stream) {
+    if (!gate || !up || !w_gate || !w_up || !x || !ids) return Q4_ERR_NULL;
+    int st = check_moe(M, top_k, E, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gate, 4) ||
+        !aligned(up, 4) || !aligned(ids, 4))
+        return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w_gate, w_up, gate, up, x, N, K, kFmtQ4_0);
+    p.ids = ids;
+    p.top_k = (int)top_k;
+    p.E = (int)E;
+    const int umax = (int)(M * top_k < E ? M * top_k : E);
+    return run<kFmtQ4_0, 2, kModeMoe, false>(p, (int)M, umax, stream);
+}
+
+int dequant_q4k(float* out, const void* w, int64_t N, int64_t K, void* stream) {
+    if (!out || !w) return Q4_ERR_NULL;
+    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+    const long long upr = K / kUnitElems;
+    const long long nunits = (long long)N * upr;
+    const long long blocks = (nunits + 255) / 256;
+    if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
+    hipLaunchKernelGGL(dequant_kernel<kFmtQ4K>, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr,
+                       (long long)(K / 256) * kQ4KBytes);
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream) {
+    if (!out || !w) return Q4_ERR_NULL;
+    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+    const long long upr = K / kUnitElems;
+    const long long nunits = (long long)N * upr;
+    const long long blocks = (nunits + 255) / 256;
+    if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
+    hipLaunchKernelGGL(dequant_kernel<kFmtQ4_0>, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr,
+                       (long long)(K / 32) * 18);
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
+                 const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
+                 void* stream) {
+    if (kernel_id < Q4_READ_Q4_0_GEMV || kernel_id > Q4_READ_MOE) return Q4_ERR_ARG;
+    if (!checksum || !w0) return Q4_ERR_NULL;
+    if ((kernel_id == Q4_READ_GATE_UP || kernel_id == Q4_READ_MOE) && !w1) return Q4_ERR_NULL;
+    if (kernel_id == Q4_READ_MOE && !ids) return Q4_ERR_NULL;
+    int st = kernel_id == Q4_READ_MOE ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w0, 16) || (w1 && !aligned(w1, 16)) || !aligned(checksum, 4) ||
+        (ids && !aligned(ids, 4)))
+        return Q4_ERR_ALIGN;
+    const int fmt = (kernel_id == Q4_READ_Q4_0_GEMV || kernel_id == Q4_READ_MOE) ? kFmtQ4_0
+                                                                                 : kFmtQ4K;
+    GemvParams p = base_params(w0, w1 ? w1 : w0, nullptr, nullptr, nullptr, N, K, fmt);
+    p.cks = checksum;
+    switch (kernel_id) {
+        case Q4_READ_Q4_0_GEMV: return run<kFmtQ4_0, 1, kModeDense, true>(p, (int)M, 0, stream);
+        case Q4_READ_Q4K_GEMV: return run<kFmtQ4K, 1, kModeDense, true>(p, (int)M, 0, stream);
+        case Q4_READ_GATE_UP: return run<kFmtQ4K, 2, kModeDense, true>(p, (int)M, 0, stream);
+        case Q4_READ_MOE: {
+            p.ids = ids;
+            p.top_k = (int)top_k;
+            p.E = (int)E;
+            const int umax = (int)(M * top_k < E ? M * top_k : E);
+            return run<kFmtQ4_0, 2, kModeMoe, true>(p, (int)M, umax, stream);
+        }
+    }
+    return Q4_ERR_ARG;
+}
+
+}  // extern "C"

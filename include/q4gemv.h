@@ -1,0 +1,182 @@
+/*
+ * q4gemv.h -- C ABI of libq4gemv: decode-time GEMV over 4-bit
+ * block-quantized weights on AMD Instinct MI355X (gfx950).
+ *
+ * Weight formats (little-endian, rows contiguous, row n of a matrix starts at
+ * byte n * row_bytes):
+ *
+ *   Q4_0, 18 bytes per block of 32 weights, row_bytes = K/32 * 18:
+ *     +0  f16 d
+ *     +2  16 bytes of nibbles: the low nibble of byte j is element j, the
+ *         high nibble is element j+16; weight = d * (q - 8).
+ *     (inferencelayer 0.2.13, src/bin/kernel_lab.rs, GEMV_F16S WGSL:
+ *      q4_lo / q4_hi and the per-block scale.)
+ *
+ *   Q4_K, 144 bytes per super-block of 256 weights, row_bytes = K/256 * 144:
+ *     +0  f16 d, +2 f16 dmin, +4 twelve bytes S packing eight 6-bit scales
+ *     and eight 6-bit mins, +16 128 bytes of nibbles.  Sub-block j (32
+ *     weights) has scale sc_j and min m_j: for j < 4, sc_j = S[j] & 63 and
+ *     m_j = S[j+4] & 63; for j >= 4, sc_j = (S[j+4] & 15) | (S[j-4] >> 6) << 4
+ *     and m_j = (S[j+4] >> 4) | (S[j] >> 6) << 4.  Element t of the
+ *     super-block is in byte 32*(t/64) + t%32 of the nibbles, low nibble when
+ *     t%64 < 32, high nibble otherwise; weight = d*sc_j*q - dmin*m_j with
+ *     j = t/32.
+ *     (trueno-gpu 0.4.11, src/kernels/quantize/fused.rs,
+ *      FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3.)
+ *
+ * Activations x / X are fp32 [M, K] row-major; outputs are fp32 [M, N]
+ * row-major (for the expert call, [M, top_k, N]).  GEMV means
+ * y[m, n] = sum_k w[n, k] * x[m, k], evaluated in fp32 with fp32
+ * accumulation; each output is within 1e-4 * sum_k |w[n,k] * x[m,k]| of the
+ * exact value for finite inputs with |x| < 2^100.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
+ *     stated otherwise.  The caller owns every buffer; the library never
+ *     allocates, frees or keeps a pointer, and keeps no per-call state.
+ *   - Inputs are read-only; outputs are fully overwritten (never
+ *     accumulated into) and must not alias any input.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     null stream).  Results are valid once work queued later on the same
+ *     stream can observe them.
+ *   - Arguments are validated on the host before any HIP call; on a
+ *     validation error nothing is launched and a status > 0 is returned.
+ *     Q4_ERR_HIP means the launch itself failed; kernel faults surface, as
+ *     usual for HIP, on a later synchronization.
+ *   - Limits: 1 <= M <= 8 (Q4_ERR_BATCH); K > 0, K % 256 == 0,
+ *     M * K <= Q4_MAX_MK, 1 <= N < 2^31 (Q4_ERR_SHAPE).  Weight and x
+ *     pointers 16-byte aligned, all other pointers 4-byte aligned
+ *     (Q4_ERR_ALIGN).  Values out of range are refused, never clamped.
+ *   - The library is re-entrant; calls on different streams may overlap.
+ */
+#ifndef Q4GEMV_H
+#define Q4GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,   /* a required pointer is NULL */
+    Q4_ERR_SHAPE = 2,  /* N, K, E, top_k or M*K outside the documented limits */
+    Q4_ERR_BATCH = 3,  /* M outside [1, 8] */
+    Q4_ERR_ALIGN = 4,  /* a pointer is not aligned as documented */
+    Q4_ERR_ARG = 5,    /* another argument is invalid (eps, kernel id) */
+    Q4_ERR_HIP = 6     /* the HIP runtime refused the launch */
+};
+
+/* Largest M * K accepted: the activations of one call are staged whole in
+ * the 160 KB LDS of a compute unit. */
+#define Q4_MAX_MK 32768
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* q4_strerror(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int q4_version(void);
+
+/*
+ * y[M, N] = X[M, K] . W^T with W in Q4_0 (N rows).  The weights are read
+ * once for all M rows of X.
+ * (inferencelayer 0.2.13, src/bin/kernel_lab.rs: GEMV_F16S, several
+ *  activation columns per weight read.)
+ */
+int q4_0_gemv(float* y, const void* w, const float* x,
+              int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * y[M, N] = X[M, K] . W^T with W in Q4_K (N rows), weights read once for all M.
+ * (trueno-gpu 0.4.11, fused.rs, FusedRmsNormQ4KGemvKernel PHASE 3.)
+ */
+int q4k_gemv(float* y, const void* w, const float* x,
+             int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * RMSNorm of every row of X, then Q4_K GEMV of the normalized rows:
+ *   r_m = 1 / sqrt(sum_k x[m,k]^2 / K + eps),  xhat[m,k] = (x[m,k] * r_m) * gamma[k],
+ *   y[m, n] = sum_k w[n,k] * xhat[m,k].
+ * The normalization is fp32 and never leaves the chip.  gamma: fp32 [K].
+ * eps must be finite and >= 0 (Q4_ERR_ARG).
+ * (trueno-gpu 0.4.11, fused.rs, FusedRmsNormQ4KGemvKernel, PHASE 1 to 3.)
+ */
+int fused_rmsnorm_q4k_gemv(float* y, const void* w, const float* x, const float* gamma,
+                           float eps, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * gate[M, N] = X . Wg^T and up[M, N] = X . Wu^T, both Q4_K with N rows, from
+ * one staging of X.  gate and up must not overlap.
+ * (trueno-gpu 0.4.11, fused.rs, FusedGateUpQ4KGemvKernel.)
+ */
+int fused_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate, const void* w_up,
+                           const float* x, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Expert-selected gate/up GEMV over Q4_0 experts.  w_gate and w_up each hold
+ * E expert matrices of N rows, stacked: expert e's row r is global row
+ * e*N + r.  ids: int32 [M, top_k], the experts chosen for each token.  For
+ * token m and slot s with e = ids[m, s]:
+ *   gate[m, s, r] = sum_k Wg[e*N + r, k] * x[m, k]   (likewise up),
+ * gate and up being fp32 [M, top_k, N].  Only the selected experts' rows
+ * are read, each selected expert once per call however many tokens chose it.
+ * Precondition 0 <= ids < E (the ids live on the device, so they cannot be
+ * checked without a synchronization): an id outside it reads nothing and
+ * yields NaN in that (token, slot)'s rows.  Limits: 1 <= E < 2^20,
+ * 1 <= top_k <= E, M * top_k <= 64, E * N < 2^31 (Q4_ERR_SHAPE).
+ * (inferencelayer 0.2.13, src/bin/kernel_lab.rs: moe_lab and MOE_PURE_READ.)
+ */
+int moe_q4_gemv(float* gate, float* up, const void* w_gate, const void* w_up,
+                const float* x, const int32_t* ids, int64_t M, int64_t top_k, int64_t E,
+                int64_t N, int64_t K, void* stream);
+
+/*
+ * Dequantize N rows of Q4_K to fp32 out[N, K], bit-exact: every weight is
+ * the correctly rounded fp32 value of d*sc*q - dmin*m.
+ * (trueno-gpu 0.4.11, fused.rs, FusedRmsNormQ4KGemvKernel PHASE 3.)
+ */
+int dequant_q4k(float* out, const void* w, int64_t N, int64_t K, void* stream);
+
+/*
+ * Dequantize N rows of Q4_0 to fp32 out[N, K], bit-exact (d*(q-8) is exact).
+ * (inferencelayer 0.2.13, kernel_lab.rs, GEMV_F16S: q4_lo / q4_hi.)
+ */
+int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream);
+
+/*
+ * Pure-read bandwidth ceiling: reads exactly the weight bytes that the named
+ * GEMV call reads, with the same addressing, work split and launch shape,
+ * but does no unpack, no arithmetic on x and never reads x.  To prove every
+ * byte was read it writes, for every weight row it visited, the sum of that
+ * row's little-endian 32-bit words modulo 2^32.
+ * (inferencelayer 0.2.13, kernel_lab.rs: MOE_PURE_READ and the pure_read
+ *  variant of the dense lab, whose ratio to the real kernel separates an
+ *  access-pattern limit from an arithmetic limit.)
+ *
+ *   kernel_id           reads                               checksum layout (uint32)
+ *   Q4_READ_Q4_0_GEMV   w0: Q4_0 [N, K]                     [N]
+ *   Q4_READ_Q4K_GEMV    w0: Q4_K [N, K]                     [N]
+ *   Q4_READ_GATE_UP     w0, w1: Q4_K [N, K] each            [2, N]  (w0 rows, then w1)
+ *   Q4_READ_MOE         w0, w1: Q4_0 experts as moe_q4_gemv [2, M, top_k, N]
+ *
+ * M selects the launch shape of the mirrored call (and, for Q4_READ_MOE,
+ * the number of tokens); ids, top_k and E are used by Q4_READ_MOE only
+ * (pass NULL / 0 otherwise).  For an expert id outside [0, E) the checksum
+ * rows are 0xFFFFFFFF.  Unknown kernel_id: Q4_ERR_ARG.
+ */
+enum {
+    Q4_READ_Q4_0_GEMV = 0,
+    Q4_READ_Q4K_GEMV = 1,
+    Q4_READ_GATE_UP = 2,
+    Q4_READ_MOE = 3
+};
+int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
+                 const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4GEMV_H */

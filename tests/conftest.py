@@ -16,3 +16,13 @@ def pytest_configure(config):
 def orc():
     from oracle import oracle
     return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def q4lib():
+    """The built libq4gemv.so (compiled first only if it was never built)."""
+    import bit_block_quantized_dequant_amd as q4
+    if not os.path.exists(q4.LIB_PATH):
+        from bit_block_quantized_dequant_amd import build
+        build.build()
+    return q4.lib()

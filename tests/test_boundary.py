@@ -1,0 +1,158 @@
+"""The C-ABI boundary on the CPU: libq4gemv.so loads, exports every call that
+include/q4gemv.h declares, and refuses invalid arguments with the documented
+status before any HIP call (so none of these tests needs a GPU; no call here
+has a fully valid argument list, so nothing is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_block_quantized_dequant_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4gemv.h")
+
+OK, NULL, SHAPE, BATCH, ALIGN, ARG, HIP = range(7)
+# fake, never dereferenced addresses: aligned and misaligned
+A = 0x7F0000000000
+MIS = A + 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ["q4_0_gemv", "q4k_gemv", "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv",
+              "moe_q4_gemv", "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
+              "q4_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(q4lib):
+    for n in declared_functions():
+        assert hasattr(q4lib, n), "libq4gemv.so does not export %s" % n
+
+
+def test_exports_are_c_symbols(q4lib):
+    # no C++ mangling on the ABI
+    out = os.popen("nm -D --defined-only %s" % q4.LIB_PATH).read()
+    for n in declared_functions():
+        assert re.search(r"\bT %s$" % n, out, flags=re.M), n
+
+
+def test_version_and_strerror(q4lib):
+    assert q4.q4_version() == 1
+    for s in range(7):
+        assert q4.q4_strerror(s) and q4.q4_strerror(s) != "unknown status"
+    assert q4.q4_strerror(99) == "unknown status"
+
+
+def L():
+    return q4.lib()
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, A, A, 1, 16, 256, None), NULL),
+    ((A, None, A, 1, 16, 256, None), NULL),
+    ((A, A, None, 1, 16, 256, None), NULL),
+    ((A, A, A, 0, 16, 256, None), BATCH),
+    ((A, A, A, 9, 16, 256, None), BATCH),
+    ((A, A, A, -1, 16, 256, None), BATCH),
+    ((A, A, A, 1, 0, 256, None), SHAPE),
+    ((A, A, A, 1, 2 ** 31, 256, None), SHAPE),
+    ((A, A, A, 1, 16, 0, None), SHAPE),
+    ((A, A, A, 1, 16, 288, None), SHAPE),
+    ((A, A, A, 1, 16, -256, None), SHAPE),
+    ((A, A, A, 2, 16, 32768, None), SHAPE),  # M*K over the LDS limit
+    ((A, MIS, A, 1, 16, 256, None), ALIGN),
+    ((A, A + 4, A, 1, 16, 256, None), ALIGN),
+    ((A, A, A + 8, 1, 16, 256, None), ALIGN),
+    ((A + 1, A, A, 1, 16, 256, None), ALIGN),
+])
+@pytest.mark.parametrize("fn", ["q4_0_gemv", "q4k_gemv"])
+def test_dense_validation(q4lib, fn, args, want):
+    assert getattr(L(), fn)(*args) == want
+
+
+def test_rmsnorm_validation(q4lib):
+    f = L().fused_rmsnorm_q4k_gemv
+    assert f(A, A, A, None, 1e-5, 1, 16, 256, None) == NULL
+    assert f(A, A, A, A + 4, 1e-5, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A, -1.0, 1, 16, 256, None) == ARG
+    assert f(A, A, A, A, float("nan"), 1, 16, 256, None) == ARG
+    assert f(A, A, A, A, float("inf"), 1, 16, 256, None) == ARG
+    assert f(A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
+
+
+def test_gate_up_validation(q4lib):
+    f = L().fused_gate_up_q4k_gemv
+    assert f(A, None, A, A, A, 1, 16, 256, None) == NULL
+    assert f(A, A, A, None, A, 1, 16, 256, None) == NULL
+    assert f(A, A, A, A + 4, A, 1, 16, 256, None) == ALIGN
+    assert f(A, A + 2, A, A, A, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A, A, 1, 16, 100, None) == SHAPE
+
+
+@pytest.mark.parametrize("M,top_k,E,N,K,want", [
+    (4, 0, 64, 1408, 2048, SHAPE),
+    (4, 65, 64, 1408, 2048, SHAPE),
+    (4, 6, 0, 1408, 2048, SHAPE),
+    (4, 6, 2 ** 20, 1408, 2048, SHAPE),
+    (8, 9, 64, 16, 256, SHAPE),         # 72 (token, slot) pairs > 64
+    (4, 6, 64, 2 ** 26, 256, SHAPE),    # E * N >= 2^31
+    (9, 6, 64, 1408, 2048, BATCH),
+    (4, 6, 64, 1408, 2000, SHAPE),
+])
+def test_moe_validation(q4lib, M, top_k, E, N, K, want):
+    assert L().moe_q4_gemv(A, A, A, A, A, A, M, top_k, E, N, K, None) == want
+
+
+def test_moe_null_and_align(q4lib):
+    f = L().moe_q4_gemv
+    assert f(A, A, A, A, A, None, 4, 6, 64, 1408, 2048, None) == NULL
+    assert f(A, A, A, A, A, A + 2, 4, 6, 64, 1408, 2048, None) == ALIGN
+
+
+def test_dequant_validation(q4lib):
+    for f in (L().dequant_q4k, L().dequant_q4_0):
+        assert f(None, A, 4, 256, None) == NULL
+        assert f(A, None, 4, 256, None) == NULL
+        assert f(A, A, 0, 256, None) == SHAPE
+        assert f(A, A, 4, 100, None) == SHAPE
+        assert f(A + 4, A, 4, 256, None) == ALIGN
+        assert f(A, A + 4, 4, 256, None) == ALIGN
+
+
+def test_pure_read_validation(q4lib):
+    f = L().q4_pure_read
+    assert f(A, 9, A, A, None, 1, 0, 0, 16, 256, None) == ARG
+    assert f(A, -1, A, A, None, 1, 0, 0, 16, 256, None) == ARG
+    assert f(None, 0, A, None, None, 1, 0, 0, 16, 256, None) == NULL
+    assert f(A, 2, A, None, None, 1, 0, 0, 16, 256, None) == NULL  # gate/up needs w1
+    assert f(A, 3, A, A, None, 4, 6, 64, 16, 256, None) == NULL    # moe needs ids
+    assert f(A, 1, A, None, None, 1, 0, 0, 16, 300, None) == SHAPE
+    assert f(A, 3, A, A, A, 4, 0, 64, 16, 256, None) == SHAPE
+    assert f(A + 1, 0, A, None, None, 1, 0, 0, 16, 256, None) == ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    y = torch.zeros(16)
+    w = torch.zeros(16 * 144, dtype=torch.uint8)
+    x = torch.zeros(256)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q4.q4k_gemv(y, w, x, 1, 16, 256)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q4.dequant_q4k(torch.zeros(16, 256), w, 16, 256)
+
+
+def test_binding_raises_q4error(q4lib):
+    # a NULL output through the binding surfaces as Q4Error(Q4_ERR_NULL)
+    with pytest.raises(q4.Q4Error) as ei:
+        q4._ok(L().q4k_gemv(None, A, A, 1, 16, 256, None), "q4k_gemv")
+    assert ei.value.status == NULL
