@@ -8,8 +8,8 @@ per call), timed over --steps calls after --warmup untimed calls.
   value        whole-job effective weight bandwidth: weight bytes of all timed
                calls / wall time between two device synchronizations (GB/s)
   roofline     the kernel itself: weight bytes per launch / mean launch
-               duration from HIP events recorded around each launch on the
-               launch stream, against the 8 TB/s HBM3E peak
+               duration, from HIP events recorded on the launch stream around
+               batches of back-to-back launches, against the 8 TB/s HBM3E peak
   pure_read    the same for the pure-read ceiling kernel (same bytes, same
                addressing, no arithmetic)
   cpu_baseline the CPU oracle (plain C, float64) timed on this host's cores on
@@ -79,28 +79,36 @@ class Rotation:
         return self.base + (i % self.ncopies) * self.stride
 
 
-def time_launches(torch, launch, warmup, steps):
-    """launch(i) enqueues call i.  Returns (wall seconds, per-launch ms list)."""
+def time_launches(torch, launch, warmup, steps, batches=5):
+    """launch(i) enqueues call i.  The timed launches run back to back on the
+    stream in `batches` groups, each bracketed by its own pair of HIP events;
+    returns (wall seconds of all timed launches between two device
+    synchronizations, per-launch mean ms of each batch)."""
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    per = max(1, steps // batches)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
+          for _ in range(batches)]
+    n = 0
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
-        launch(warmup + i)
-        ev[i][1].record()
+    for b in range(batches):
+        cnt = per if b < batches - 1 else steps - per * (batches - 1)
+        ev[b][0].record()
+        for _ in range(cnt):
+            launch(warmup + n)
+            n += 1
+        ev[b][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    cnts = [per] * (batches - 1) + [steps - per * (batches - 1)]
+    return wall, [a.elapsed_time(b) / c for (a, b), c in zip(ev, cnts)], cnts
 
 
-def stats(durs_ms):
-    s = sorted(durs_ms)
-    n = len(s)
-    return dict(mean_ms=sum(s) / n, median_ms=s[n // 2], min_ms=s[0], max_ms=s[-1],
+def stats(batch_ms, cnts):
+    s = sorted(batch_ms)
+    mean = sum(m * c for m, c in zip(batch_ms, cnts)) / sum(cnts)
+    return dict(mean_ms=mean, median_ms=s[len(s) // 2], min_ms=s[0], max_ms=s[-1],
                 spread=s[-1] / s[0] - 1.0 if s[0] > 0 else None)
 
 
@@ -213,9 +221,9 @@ def setup_workload(torch, dev, index, M):
 
 def measure(torch, dev, index, M, warmup, steps):
     wbytes, launch, ceil_launch, notes, keep = setup_workload(torch, dev, index, M)
-    wall, durs = time_launches(torch, launch, warmup, steps)
-    cwall, cdurs = time_launches(torch, ceil_launch, warmup, steps)
-    st, cst = stats(durs), stats(cdurs)
+    wall, durs, cnts = time_launches(torch, launch, warmup, steps)
+    cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps)
+    st, cst = stats(durs, cnts), stats(cdurs, ccnts)
     res = dict(index=index, M=M, weight_bytes=wbytes, wall_s=wall, steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
                kernel=st, kernel_gbs=wbytes / (st["mean_ms"] * 1e-3) / 1e9,

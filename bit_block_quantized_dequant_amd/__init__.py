@@ -23,7 +23,9 @@ __all__ = [
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "LIB_PATH", "q4_0_row_bytes", "q4k_row_bytes",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
+# Q4GEMV_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("Q4GEMV_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
 
 Q4_READ_Q4_0_GEMV = 0
 Q4_READ_Q4K_GEMV = 1

@@ -45,11 +45,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte global load from a 4-byte aligned address (Q4_0 pairs sit at a
 // 36-byte stride, so only dword alignment is guaranteed).
+#ifndef Q4_NT_LOADS
+#define Q4_NT_LOADS 0
+#endif
 __device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
+#if Q4_NT_LOADS
+    typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+    const u32x4a4 t = __builtin_nontemporal_load((const u32x4a4*)__builtin_assume_aligned(p, 4));
+    return u32x4{t.x, t.y, t.z, t.w};
+#else
     const uint32_t* q = (const uint32_t*)__builtin_assume_aligned(p, 4);
     u32x4 v;
     __builtin_memcpy(&v, q, 16);
     return v;
+#endif
 }
 
 __device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
@@ -65,28 +74,33 @@ __device__ __forceinline__ float h_hi(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Unit loads.  `row` points at the first byte of the weight row.
+// Unit loads.  Q4_K: `p` is the super-block, g the 32-byte nibble chunk (the
+// 16-byte header is loaded beside it); Q4_0: `p` is the block pair.
 // ---------------------------------------------------------------------------
 template <int FMT>
-__device__ __forceinline__ void load_unit(const uint8_t* row, int u, uint32_t (&r)[kUnitWords]) {
+__device__ __forceinline__ void load_unit(const uint8_t* p, int g, uint32_t (&r)[kUnitWords]) {
     if constexpr (FMT == kFmtQ4K) {
-        const uint8_t* sb = row + (u >> 2) * kQ4KBytes;
-        const uint8_t* qs = sb + 16 + 32 * (u & 3);
-        u32x4 h = ldg16(sb);
+        const uint8_t* qs = p + 16 + 32 * g;
+        u32x4 h = ldg16(p);
         u32x4 a = ldg16(qs);
         u32x4 b = ldg16(qs + 16);
         r[0] = h.x; r[1] = h.y; r[2] = h.z; r[3] = h.w;
         r[4] = a.x; r[5] = a.y; r[6] = a.z; r[7] = a.w;
         r[8] = b.x; r[9] = b.y; r[10] = b.z; r[11] = b.w;
     } else {
-        const uint8_t* p = row + u * kQ4_0PairBytes;
+        (void)g;
         u32x4 a = ldg16(p);
         u32x4 b = ldg16(p + 16);
         r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
         r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
         r[8] = ldg4(p + 32);
-        r[9] = r[10] = r[11] = 0u;
     }
+}
+
+// Unit u of a row: the super-block (Q4_K) or block pair (Q4_0) it lives in.
+template <int FMT>
+__device__ __forceinline__ const uint8_t* unit_ptr(const uint8_t* row, int u) {
+    return FMT == kFmtQ4K ? row + (u >> 2) * kQ4KBytes : row + u * kQ4_0PairBytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -156,14 +170,15 @@ __device__ __forceinline__ bool elem_is_high(int e) {
 //   xs  : LDS per-32-run sums of token 0, as float2 per unit (token m at
 //         xs + m * (K/64)); Q4_K: plain sums X; Q4_0: -8 * X.
 // acc[r][m] accumulates row r's dot product with token m (Q4_K: scaled by
-// 2^-24).  For M > 1 a scheduling fence after each nibble word keeps the
+// 2^-24); with act == false the accumulators are left as they were (a lane
+// past the end of its row computes on a clamped duplicate and drops it).  For M > 1 a scheduling fence after each nibble word keeps the
 // compiler from hoisting all 16*M chunk reads at once (register pressure).
 // ---------------------------------------------------------------------------
 template <int FMT, int M, int NR>
 __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], int u,
                                          uint32_t sel, const float4* __restrict__ xl, int kq,
                                          const float2* __restrict__ xs, int k64,
-                                         float (&acc)[NR][M]) {
+                                         float (&acc)[NR][M], bool act = true) {
     const float4* xu = xl + u * 16;
     const int sw = u & 15;
     if constexpr (FMT == kFmtQ4K) {
@@ -194,8 +209,9 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
                 t = __builtin_fmaf(h_hi(scp), s1[r][m], t);
                 float v = __builtin_fmaf(h_lo(mp), X.x, 0.0f);
                 v = __builtin_fmaf(h_hi(mp), X.y, v);
-                acc[r][m] = __builtin_fmaf(h_lo(w[r][0]), t, acc[r][m]);
-                acc[r][m] = __builtin_fmaf(-h_hi(w[r][0]), v, acc[r][m]);
+                float a = __builtin_fmaf(h_lo(w[r][0]), t, acc[r][m]);
+                a = __builtin_fmaf(-h_hi(w[r][0]), v, a);
+                acc[r][m] = act ? a : acc[r][m];
             }
         }
     } else {
@@ -216,18 +232,21 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
                 b0[r][m] = X8.y; b1[r][m] = 0.f;
             }
         }
+        // nibble word i: block A (words 0-3, chunks i and 4+i) or block B
+        // (words 4-7, chunks 8+i' and 12+i')
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
+            const int ca = i < 4 ? i : 4 + i;  // low-nibble chunk; high = ca + 4
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const float4 xal = xu[m * kq + (i ^ sw)];
-                const float4 xah = xu[m * kq + ((4 + i) ^ sw)];
-                const float4 xbl = xu[m * kq + ((8 + i) ^ sw)];
-                const float4 xbh = xu[m * kq + ((12 + i) ^ sw)];
+                const float4 xlo = xu[m * kq + (ca ^ sw)];
+                const float4 xhi = xu[m * kq + ((ca + 4) ^ sw)];
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
-                    nib_dot(qa[r][i], xal, xah, a0[r][m], a1[r][m]);
-                    nib_dot(w[r][5 + i], xbl, xbh, b0[r][m], b1[r][m]);
+                    if (i < 4)
+                        nib_dot(qa[r][i], xlo, xhi, a0[r][m], a1[r][m]);
+                    else
+                        nib_dot(w[r][1 + i], xlo, xhi, b0[r][m], b1[r][m]);
                 }
             }
             if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
@@ -236,8 +255,9 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
         for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                acc[r][m] = __builtin_fmaf(h_lo(w[r][0]), a0[r][m] + a1[r][m], acc[r][m]);
-                acc[r][m] = __builtin_fmaf(h_hi(w[r][4]), b0[r][m] + b1[r][m], acc[r][m]);
+                float a = __builtin_fmaf(h_lo(w[r][0]), a0[r][m] + a1[r][m], acc[r][m]);
+                a = __builtin_fmaf(h_hi(w[r][4]), b0[r][m] + b1[r][m], a);
+                acc[r][m] = act ? a : acc[r][m];
             }
     }
 }
@@ -259,14 +279,37 @@ __device__ __forceinline__ uint32_t unit_checksum(const uint32_t (&w)[kUnitWords
     return s;
 }
 
-// Butterfly sum over aligned groups of `width` lanes (power of two <= 64);
-// every lane of a group ends with the group's total.
-__device__ __forceinline__ float group_sum(float v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+// Sum over aligned groups of `width` lanes (power of two, 4 <= width <= 64)
+// with DPP lane moves: xor 1 and 2 (quad_perm), 4 (row_half_mirror) and 8
+// (row_mirror) leave every lane of a 16-lane row with the row's sum;
+// row_bcast:15 then adds row 0's total into row 1 (and row 2's into row 3)
+// and row_bcast:31 adds lanes 0-31's total into rows 2 and 3.  The group's
+// total is exact in its LAST lane (li == width - 1) for every width; other
+// lanes may hold partial sums.  The addition order is fixed by the width
+// alone, so equal inputs give bit-equal results in every kernel.
+template <typename T>
+__device__ __forceinline__ T dpp_add(T v, int ctrl_sel) {
+    int iv = __builtin_bit_cast(int, v);
+    int t;
+    switch (ctrl_sel) {
+        case 0: t = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false); break;   // quad xor 1
+        case 1: t = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false); break;   // quad xor 2
+        case 2: t = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xF, 0xF, false); break;  // half mirror
+        case 3: t = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xF, 0xF, false); break;  // mirror
+        case 4: t = __builtin_amdgcn_update_dpp(0, iv, 0x142, 0xA, 0xF, false); break;  // bcast 15
+        default: t = __builtin_amdgcn_update_dpp(0, iv, 0x143, 0xC, 0xF, false); break; // bcast 31
+    }
+    return v + __builtin_bit_cast(T, t);
 }
-__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, kWave);
+
+template <typename T>
+__device__ __forceinline__ T group_total(T v, int width) {
+    v = dpp_add(v, 0);
+    v = dpp_add(v, 1);
+    if (width > 4) v = dpp_add(v, 2);
+    if (width > 8) v = dpp_add(v, 3);
+    if (width > 16) v = dpp_add(v, 4);
+    if (width > 32) v = dpp_add(v, 5);
     return v;
 }
 

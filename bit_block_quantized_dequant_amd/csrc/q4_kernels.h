@@ -23,6 +23,10 @@
 
 #include "q4_device.h"
 
+#ifndef Q4_TASK_ORDER
+#define Q4_TASK_ORDER 1
+#endif
+
 namespace q4 {
 
 constexpr int kBlock = 512;  // threads per workgroup (8 waves)
@@ -68,47 +72,107 @@ struct MoeShared {
 // q4_device.h; xs receives per-32-element sums (times -8 for Q4_0).  For
 // kModeNorm the rows are first RMS-normalized in fp32:
 //   r = 1 / sqrt(sum(x^2) / K + eps),  xhat = (x * r) * gamma.
-template <int FMT, int M, int MODE>
-__device__ __forceinline__ void stage_x(const GemvParams& p, float4* xl, float* xsum,
-                                        float* red) {
-    const int tid = threadIdx.x;
+// Split in two so that the first weight loads can be issued in between: the
+// global loads of the first kXReg chunks per thread go out first (the load
+// counter is in order, so waiting for them later does not wait for the
+// weights); chunks beyond that (M*K > 8192 floats) load in the second half.
+constexpr int kXReg = 4;
+
+struct XStage {
+    float4 x[kXReg];
+    float4 g[kXReg];
+};
+
+template <int MODE>
+__device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage& st) {
     const int kq = p.K >> 2;
+    const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
+    const float4* g4 = (const float4*)p.gamma;
+#pragma unroll
+    for (int k = 0; k < kXReg; ++k) {
+        // unconditional (clamped) loads keep the load-counter waits exact
+        const int i = min((int)threadIdx.x + k * (int)blockDim.x, total - 1);
+        st.x[k] = x4[i];
+        if constexpr (MODE == kModeNorm) st.g[k] = g4[i % kq];
+    }
+}
+
+// One float4 chunk i of the activations: its 32-element run sum (over the 8
+// lanes that hold the run) and its pre-scaled, swizzled LDS copy.  Called by
+// every lane; only lanes with `store` write (the others hold a clamped
+// duplicate chunk and only take part in the lane exchange).
+template <int FMT, int M>
+__device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i, bool store,
+                                            float4* xl, float* xsum) {
+    const int kq = p.K >> 2;
+    const int m = i / kq;
+    const int c = i - m * kq;
+    // 8 consecutive lanes hold one 32-element run
+    float s = (v.x + v.y) + (v.z + v.w);
+    s = dpp_add(s, 0);
+    s = dpp_add(s, 1);
+    s = dpp_add(s, 2);
+    if (store && (c & 7) == 7) xsum[m * (p.K >> 5) + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
+    const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
+    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+    if (store) xl[m * kq + xchunk(c >> 4, c & 15)] = v;
+}
+
+template <int FMT, int M, int MODE>
+__device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage& st, float4* xl,
+                                               float* xsum, float* red) {
+    const int tid = threadIdx.x;
+    const int bs = blockDim.x;
+    const int kq = p.K >> 2;
+    const int total = M * kq;
+    const float4* x4 = (const float4*)p.x;
+    const float4* g4 = (const float4*)p.gamma;
     float rnorm[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) rnorm[m] = 1.0f;
     if constexpr (MODE == kModeNorm) {
-        const int nw = blockDim.x >> 6;
+        const int nw = bs >> 6;
         const int wave = tid >> 6, lane = tid & 63;
+        float ss[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) ss[m] = 0.f;
+        auto acc_sq = [&](float4 v, int i) {
+            const int m = i / kq;
+            float t = 0.f;
+            t = __builtin_fmaf(v.x, v.x, t);
+            t = __builtin_fmaf(v.y, v.y, t);
+            t = __builtin_fmaf(v.z, v.z, t);
+            t = __builtin_fmaf(v.w, v.w, t);
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm)
+                if (m == mm) ss[mm] += t;
+        };
+#pragma unroll
+        for (int k = 0; k < kXReg; ++k) {
+            const int i = tid + k * bs;
+            const float4 v = st.x[k];
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            acc_sq(i < total ? v : z, min(i, total - 1));
+        }
+        for (int i = tid + kXReg * bs; i < total; i += bs) acc_sq(x4[i], i);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float ss = 0.f;
-            for (int c = tid; c < kq; c += blockDim.x) {
-                const float4 v = x4[m * kq + c];
-                ss = __builtin_fmaf(v.x, v.x, ss);
-                ss = __builtin_fmaf(v.y, v.y, ss);
-                ss = __builtin_fmaf(v.z, v.z, ss);
-                ss = __builtin_fmaf(v.w, v.w, ss);
-            }
-            ss = group_sum(ss, kWave);
-            if (lane == 0) red[m * 16 + wave] = ss;
+            const float v = group_total(ss[m], kWave);
+            if (lane == kWave - 1) red[m * 16 + wave] = v;
         }
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float ss = 0.f;
-            for (int i = 0; i < nw; ++i) ss += red[m * 16 + i];
-            const float ms = ss / (float)p.K;
+            float t = 0.f;
+            for (int i = 0; i < nw; ++i) t += red[m * 16 + i];
+            const float ms = t / (float)p.K;
             rnorm[m] = 1.0f / sqrtf(ms + p.eps);
         }
     }
-    const float4* g4 = (const float4*)p.gamma;
-    for (int i = tid; i < M * kq; i += blockDim.x) {
-        const int m = i / kq;
-        const int c = i - m * kq;
-        float4 v = x4[i];
+    auto norm = [&](float4 v, float4 g, int i) {
         if constexpr (MODE == kModeNorm) {
-            const float4 g = g4[c];
+            const int m = i / kq;
             float r = rnorm[0];
 #pragma unroll
             for (int mm = 1; mm < M; ++mm)
@@ -118,15 +182,18 @@ __device__ __forceinline__ void stage_x(const GemvParams& p, float4* xl, float* 
             v.z = (v.z * r) * g.z;
             v.w = (v.w * r) * g.w;
         }
-        // 8 consecutive lanes hold one 32-element run
-        float s = (v.x + v.y) + (v.z + v.w);
-        s += __shfl_xor(s, 1, kWave);
-        s += __shfl_xor(s, 2, kWave);
-        s += __shfl_xor(s, 4, kWave);
-        if ((c & 7) == 0) xsum[m * (p.K >> 5) + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
-        const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
-        v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-        xl[m * kq + xchunk(c >> 4, c & 15)] = v;
+        return v;
+    };
+#pragma unroll
+    for (int k = 0; k < kXReg; ++k) {
+        const int i = tid + k * bs;
+        const int ic = min(i, total - 1);
+        stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum);
+    }
+    for (int i = tid + kXReg * bs; i < total; i += bs) {
+        float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+        if constexpr (MODE == kModeNorm) g = g4[i % kq];
+        stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
     }
 }
 
@@ -172,29 +239,120 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
     }
 }
 
-template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE>
+template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
     __shared__ float red[8 * 16];
 
+    constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int gwave = blockIdx.x * (blockDim.x >> 6) + (tid >> 6);
+    // the wave index is wave-uniform; say so, so that all task bookkeeping
+    // stays in scalar registers and the loops are scalar branches
+    const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (tid >> 6));
     const int kq = p.K >> 2;
     const int k64 = p.K >> 6;
     float4* xl = smem;
     float* xsum = (float*)(smem + M * kq);
 
-    if constexpr (MODE == kModeMoe) moe_dedupe<M>(p, moe);
-    if constexpr (!PURE) stage_x<FMT, M, MODE>(p, xl, xsum, red);
-    __syncthreads();
-
+    // ---- the wave's task range ----
     int ntasks = p.ntasks;
     int tpe = 1;  // tasks per expert (expert call)
     if constexpr (MODE == kModeMoe) {
+        moe_dedupe<M>(p, moe);
+        __syncthreads();
         tpe = p.nrg / p.rgw;
         ntasks = moe.nu * tpe;
+    }
+#if Q4_TASK_ORDER == 1
+    // strided: wave w takes tasks w, w + W, w + 2W, ... so that all waves
+    // sweep one moving window of the weights together
+    const int t0 = gwave;
+    const int t1 = ntasks;
+    const int tstride = p.nwaves;
+#else
+    // contiguous: wave w takes one balanced range of consecutive tasks
+    const int t0 = (int)(((long long)gwave * ntasks) / p.nwaves);
+    const int t1 = (int)(((long long)(gwave + 1) * ntasks) / p.nwaves);
+    const int tstride = 1;
+#endif
+    const int gi = lane / p.lg;       // row group of this lane within a pass
+    const int li = lane - gi * p.lg;  // lane within its row group
+    const uint32_t sel = q4k_sel(li & 3);
+
+    // ---- cursor over (task, unit) steps; advanced without divisions ----
+    struct Cursor {
+        int t, ui, ue, rgt;
+    };
+    auto first_cursor = [&]() {
+        Cursor c;
+        c.t = t0;
+        c.ui = 0;
+        c.ue = MODE == kModeMoe ? t0 / tpe : 0;
+        c.rgt = MODE == kModeMoe ? t0 - c.ue * tpe : t0;
+        return c;
+    };
+    auto next_cursor = [&](Cursor c) {
+        if (++c.ui == p.upl) {
+            c.ui = 0;
+            c.t += tstride;
+            c.rgt += tstride;
+            if (MODE == kModeMoe && c.rgt >= tpe) {
+                c.ue += c.rgt / tpe;
+                c.rgt -= (c.rgt / tpe) * tpe;
+            }
+        }
+        return c;
+    };
+    // first row of this lane's row group
+    auto group_row = [&](const Cursor& c) { return (c.rgt * p.rgw + gi) * RR; };
+    // Loads are unconditional (a branch around them would make the compiler
+    // wait for every outstanding load before each step): lanes past the end of
+    // the row re-read the row's last unit and rows past N re-read row N-1;
+    // those lines are on their way anyway and the results are never used.
+    const int u_last = p.upr - 1;
+    auto unit_off = [&](int u) -> long long {
+        return FMT == kFmtQ4K ? (long long)(u >> 2) * kQ4KBytes : (long long)u * kQ4_0PairBytes;
+    };
+    const long long uoff_lane = unit_off(li);
+    const long long uoff_last = unit_off(u_last);
+    const long long pass_stride = unit_off(p.lg);
+    auto load = [&](const Cursor& c, uint32_t (&dst)[NR][kUnitWords]) {
+        const int u = li + c.ui * p.lg;
+        const bool in_row = u <= u_last;
+        const long long uoff = in_row ? uoff_lane + c.ui * pass_stride : uoff_last;
+        const int g = in_row ? (li & 3) : (u_last & 3);
+        const int r0 = group_row(c);
+        // (an expert index past the dedupe result, possible only for a wave
+        // with no tasks, reads a valid expert instead)
+        long long ubase = 0;
+        if constexpr (MODE == kModeMoe) {
+            const int nu = moe.nu;
+            ubase = nu > 0 ? (long long)moe.uexp[min(c.ue, nu - 1)] * p.N : 0ll;
+        }
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            const int row = min(r0 + r, p.N - 1);
+            const long long off = (ubase + row) * p.row_bytes + uoff;
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt)
+                load_unit<FMT>((mt == 0 ? p.w0 : p.w1) + off, g, dst[mt * RR + r]);
+        }
+    };
+
+    uint32_t bufA[NR][kUnitWords];
+    uint32_t bufB[NR][kUnitWords];
+    Cursor ca = first_cursor();
+    // Activation loads first, then the first weight loads, then the staging
+    // arithmetic: the HBM latency of the first step overlaps the staging.
+    XStage xst;
+    if constexpr (!PURE) stage_x_issue<MODE>(p, M, xst);
+    load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
+    if constexpr (!PURE) stage_x_finish<FMT, M, MODE>(p, xst, xl, xsum, red);
+    __syncthreads();
+
+    if constexpr (MODE == kModeMoe) {
         // rows of pairs with an invalid id: NaN (or an all-ones checksum)
         if (moe.invalid) {
             const int P = M * p.top_k;
@@ -214,73 +372,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
             }
         }
     }
-
-    const int t0 = (int)(((long long)gwave * ntasks) / p.nwaves);
-    const int t1 = (int)(((long long)(gwave + 1) * ntasks) / p.nwaves);
     if (t0 >= t1) return;
-
-    const int gi = lane / p.lg;       // row group of this lane within a pass
-    const int li = lane - gi * p.lg;  // lane within its row group
-    const uint32_t sel = q4k_sel(li & 3);
-    const int nsteps = (t1 - t0) * p.upl;
-
-    // Resolve (task, unit step) -> row base pointers and unit index.
-    struct Where {
-        const uint8_t* row[NMAT][RR];
-        int rowid[RR];  // row index within the matrix (-1: none)
-        int u;
-        bool active;
-        int uexp;  // unique-expert index (expert call)
-    };
-    auto where = [&](int step) {
-        Where wh;
-        const int t = t0 + step / p.upl;
-        const int ui = step - (step / p.upl) * p.upl;
-        wh.u = li + ui * p.lg;
-        int rg;
-        long long rbase = 0;
-        wh.uexp = 0;
-        if constexpr (MODE == kModeMoe) {
-            wh.uexp = t / tpe;
-            rg = (t - wh.uexp * tpe) * p.rgw + gi;
-            rbase = (long long)moe.uexp[wh.uexp] * p.N;
-        } else {
-            rg = t * p.rgw + gi;
-        }
-        bool any = false;
-#pragma unroll
-        for (int r = 0; r < RR; ++r) {
-            const int row = rg * RR + r;
-            const bool ok = row < p.N;
-            wh.rowid[r] = ok ? row : -1;
-            any |= ok;
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                const uint8_t* base = mt == 0 ? p.w0 : p.w1;
-                wh.row[mt][r] = base + (rbase + (ok ? row : 0)) * p.row_bytes;
-            }
-        }
-        wh.active = any && wh.u < p.upr;
-        return wh;
-    };
-
-    // rows of a step, matrix-major: row index q = mt * RR + r
-    constexpr int NR = NMAT * RR;
-    uint32_t cur[NR][kUnitWords];
-    uint32_t nxt[NR][kUnitWords];
-    auto load = [&](const Where& wh, uint32_t (&dst)[NR][kUnitWords]) {
-#pragma unroll
-        for (int r = 0; r < RR; ++r)
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                if (wh.active && wh.rowid[r] >= 0) {
-                    load_unit<FMT>(wh.row[mt][r], wh.u, dst[mt * RR + r]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < kUnitWords; ++i) dst[mt * RR + r][i] = 0u;
-                }
-            }
-    };
 
     float acc[NR][M];
     uint32_t cks[NR];
@@ -291,92 +383,135 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
         for (int m = 0; m < M; ++m) acc[q][m] = 0.f;
     }
 
-    Where wc = where(0);
-    load(wc, cur);
-    for (int s = 0; s < nsteps; ++s) {
-        Where wn = wc;
-        if (s + 1 < nsteps) {
-            wn = where(s + 1);
-            load(wn, nxt);
-        }
-        // ---- compute step s ----
-        if (wc.active) {
-            if constexpr (PURE) {
+    // Compute on the loaded data unconditionally (lanes past the end of the
+    // row hold a clamped valid unit; their result is dropped by a select, not
+    // a branch, so the compiler's load-counter waits stay exact).
+    auto compute = [&](const Cursor& c, const uint32_t (&w)[NR][kUnitWords]) {
+        const int u = li + c.ui * p.lg;
+        const bool act = u <= u_last;
+        const int uc = act ? u : u_last;
+        if constexpr (PURE) {
 #pragma unroll
-                for (int q = 0; q < NR; ++q) cks[q] += unit_checksum<FMT>(cur[q], wc.u);
-            } else if constexpr (MODE == kModeMoe) {
-                // tokens that chose this expert (uniform across the wave)
-                const unsigned int tm = moe.utok[wc.uexp];
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    if ((tm >> m) & 1u) {
-                        float a1[NR][1];
-#pragma unroll
-                        for (int q = 0; q < NR; ++q) a1[q][0] = acc[q][m];
-                        rows_dot<FMT, 1, NR>(cur, wc.u, sel, xl + m * kq, kq,
-                                             (const float2*)xsum + m * k64, k64, a1);
-#pragma unroll
-                        for (int q = 0; q < NR; ++q) acc[q][m] = a1[q][0];
-                    }
-                }
-            } else {
-                rows_dot<FMT, M, NR>(cur, wc.u, sel, xl, kq, (const float2*)xsum, k64, acc);
+            for (int q = 0; q < NR; ++q) {
+                const uint32_t v = unit_checksum<FMT>(w[q], uc);
+                cks[q] += act ? v : 0u;
             }
+        } else if constexpr (MODE == kModeMoe) {
+            // tokens that chose this expert (uniform across the wave)
+            const unsigned int tm = moe.utok[c.ue];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if ((tm >> m) & 1u) {
+                    float a1[NR][1];
+#pragma unroll
+                    for (int q = 0; q < NR; ++q) a1[q][0] = acc[q][m];
+                    rows_dot<FMT, 1, NR>(w, uc, sel, xl + m * kq, kq,
+                                         (const float2*)xsum + m * k64, k64, a1, act);
+#pragma unroll
+                    for (int q = 0; q < NR; ++q) acc[q][m] = a1[q][0];
+                }
+                if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            rows_dot<FMT, M, NR>(w, uc, sel, xl, kq, (const float2*)xsum, k64, acc, act);
         }
-        // ---- end of a task: reduce over the row group and write ----
-        const int ui = s - (s / p.upl) * p.upl;
-        if (ui == p.upl - 1) {
-            const float oscale = FMT == kFmtQ4K ? 0x1p24f : 1.0f;
+        if (c.ui != p.upl - 1) return;
+        // ---- end of a task: reduce over the row group; its last lane writes ----
+        const int r0 = group_row(c);
+        const bool last_lane = li == p.lg - 1;
+        const float oscale = FMT == kFmtQ4K ? 0x1p24f : 1.0f;
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
+        for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-                for (int r = 0; r < RR; ++r) {
-                    const int q = mt * RR + r;
-                    const int row = wc.rowid[r];
-                    if constexpr (PURE) {
-                        const uint32_t v = group_sum_u32(cks[q], p.lg);
-                        cks[q] = 0u;
-                        if (li == 0 && row >= 0) {
+            for (int r = 0; r < RR; ++r) {
+                const int q = mt * RR + r;
+                const int row = r0 + r;
+                const bool wr = last_lane && row < p.N;
+                if constexpr (PURE) {
+                    const uint32_t v = group_total(cks[q], p.lg);
+                    cks[q] = 0u;
+                    if (wr) {
+                        if constexpr (MODE == kModeMoe) {
+                            const long long P = (long long)M * p.top_k;
+                            unsigned long long pm = moe.upairs[c.ue];
+                            while (pm) {
+                                const int pr = __builtin_ctzll(pm);
+                                pm &= pm - 1ull;
+                                p.cks[((long long)mt * P + pr) * p.N + row] = v;
+                            }
+                        } else {
+                            p.cks[(long long)mt * p.N + row] = v;
+                        }
+                    }
+                } else {
+                    float* y = mt == 0 ? p.y0 : p.y1;
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const float v = group_total(acc[q][m], p.lg) * oscale;
+                        acc[q][m] = 0.f;
+                        if (wr) {
                             if constexpr (MODE == kModeMoe) {
-                                const long long P = (long long)M * p.top_k;
-                                unsigned long long pm = moe.upairs[wc.uexp];
+                                unsigned long long pm = moe.upairs[c.ue];
                                 while (pm) {
                                     const int pr = __builtin_ctzll(pm);
                                     pm &= pm - 1ull;
-                                    p.cks[((long long)mt * P + pr) * p.N + row] = v;
+                                    if (pr / p.top_k == m) y[(long long)pr * p.N + row] = v;
                                 }
                             } else {
-                                p.cks[(long long)mt * p.N + row] = v;
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            const float v = group_sum(acc[q][m], p.lg) * oscale;
-                            acc[q][m] = 0.f;
-                            if (li == 0 && row >= 0) {
-                                float* y = mt == 0 ? p.y0 : p.y1;
-                                if constexpr (MODE == kModeMoe) {
-                                    unsigned long long pm = moe.upairs[wc.uexp];
-                                    while (pm) {
-                                        const int pr = __builtin_ctzll(pm);
-                                        pm &= pm - 1ull;
-                                        if (pr / p.top_k == m) y[(long long)pr * p.N + row] = v;
-                                    }
-                                } else {
-                                    y[(long long)m * p.N + row] = v;
-                                }
+                                y[(long long)m * p.N + row] = v;
                             }
                         }
                     }
                 }
+            }
+    };
+
+    // ---- main loop: PF steps of loads in flight ahead of the computed step ----
+    // (a step past the wave's last task reloads the last one, so that every
+    // load is unconditional)
+    if constexpr (PF == 1) {
+        for (;;) {
+            const Cursor cb = next_cursor(ca);
+            const bool hb = cb.t < t1;
+            load(hb ? cb : ca, bufB);
+            __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before computing
+            compute(ca, bufA);
+            if (!hb) break;
+            const Cursor cc = next_cursor(cb);
+            const bool hc = cc.t < t1;
+            load(hc ? cc : cb, bufA);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cb, bufB);
+            if (!hc) break;
+            ca = cc;
         }
-        // ---- rotate the double buffer ----
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-#pragma unroll
-            for (int i = 0; i < kUnitWords; ++i) cur[q][i] = nxt[q][i];
-        wc = wn;
+    } else {
+        uint32_t bufC[NR][kUnitWords];
+        Cursor cb = next_cursor(ca);
+        Cursor lastv = cb.t < t1 ? cb : ca;
+        load(lastv, bufB);
+        for (;;) {
+            const Cursor cc = next_cursor(cb);
+            lastv = cc.t < t1 ? cc : lastv;
+            load(lastv, bufC);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ca, bufA);
+            if (!(cb.t < t1)) break;
+            const Cursor cd = next_cursor(cc);
+            lastv = cd.t < t1 ? cd : lastv;
+            load(lastv, bufA);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cb, bufB);
+            if (!(cc.t < t1)) break;
+            const Cursor ce = next_cursor(cd);
+            lastv = ce.t < t1 ? ce : lastv;
+            load(lastv, bufB);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cc, bufC);
+            if (!(cd.t < t1)) break;
+            ca = cd;
+            cb = ce;
+        }
     }
 }
 
@@ -396,7 +531,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
     const long long n = gid / upr;
     const int u = (int)(gid - n * upr);
     uint32_t r[kUnitWords];
-    load_unit<FMT>(w + n * row_bytes, u, r);
+    load_unit<FMT>(unit_ptr<FMT>(w + n * row_bytes, u), u & 3, r);
     float4* o = (float4*)(out + n * (long long)upr * kUnitElems + (long long)u * kUnitElems);
     if constexpr (FMT == kFmtQ4K) {
         uint32_t scp, mp;

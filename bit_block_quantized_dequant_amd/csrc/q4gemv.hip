@@ -138,25 +138,37 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
         tasks = p.ntasks;
     }
     const int wpb = kBlock / kWave;
-    const long long target = (long long)cus * wg_per_cu(gemv_lds_bytes(M, K, pure)) * wpb;
-    const long long per = (tasks + target - 1) / target;          // tasks per wave
-    const long long waves = per > 0 ? (tasks + per - 1) / per : 1;  // balanced
-    int blocks = (int)((waves + wpb - 1) / wpb);
-    if (blocks < 1) blocks = 1;
+    const int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure));
+    // Every CU gets the same number of workgroups (the per-CU load/issue rate
+    // is shared by its waves); tasks are then split evenly over all waves.
+    static const int bpc_override = env_int("Q4GEMV_BLOCKS_PER_CU", 0);
+    const int bpc = bpc_override > 0 ? bpc_override : wgc;
+    long long blocks_ll = (long long)cus * bpc;
+    const long long need = (tasks + wpb - 1) / wpb;  // no more waves than tasks
+    if (blocks_ll > need) blocks_ll = need;
+    int blocks = (int)(blocks_ll < 1 ? 1 : blocks_ll);
     p.nwaves = blocks * wpb;
     return blocks;
 }
 
-// Row-pair count per lane: two rows of a single matrix, or one row of each
-// of two matrices, so every lane streams two rows per step.
+#ifndef Q4_RR_SINGLE
+#define Q4_RR_SINGLE 2  // rows per lane per step, single-matrix calls
+#endif
+#ifndef Q4_RR_PAIR
+#define Q4_RR_PAIR 1  // rows per lane per step and matrix, two-matrix calls
+#endif
+#ifndef Q4_PREFETCH
+#define Q4_PREFETCH 1  // steps of weight loads in flight ahead of the computed one
+#endif
+
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
 int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
-    constexpr int RR = NMAT == 1 ? 2 : 1;
+    constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
     static std::atomic<int> big_lds_done[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors
     const int blocks = plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus);
     const size_t lds = gemv_lds_bytes(M, p.K, PURE);
-    return launch(gemv_kernel<FMT, M, NMAT, RR, MODE, PURE>, p, blocks, lds, stream,
+    return launch(gemv_kernel<FMT, M, NMAT, RR, MODE, PURE, Q4_PREFETCH>, p, blocks, lds, stream,
                   big_lds_done);
 }
 
