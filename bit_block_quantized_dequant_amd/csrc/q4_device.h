@@ -97,6 +97,29 @@ __device__ __forceinline__ void load_unit(const uint8_t* p, int g, uint32_t (&r)
     }
 }
 
+// Same, as a base plus 32-bit offsets: Q4_K header at base + ho and its
+// 32 nibble bytes at base + qo; Q4_0 pair at base + ho (qo unused).
+template <int FMT>
+__device__ __forceinline__ void load_unit_at(const uint8_t* base, uint32_t ho, uint32_t qo,
+                                             uint32_t (&r)[kUnitWords]) {
+    if constexpr (FMT == kFmtQ4K) {
+        u32x4 h = ldg16(base + ho);
+        u32x4 a = ldg16(base + qo);
+        u32x4 b = ldg16(base + qo + 16);
+        r[0] = h.x; r[1] = h.y; r[2] = h.z; r[3] = h.w;
+        r[4] = a.x; r[5] = a.y; r[6] = a.z; r[7] = a.w;
+        r[8] = b.x; r[9] = b.y; r[10] = b.z; r[11] = b.w;
+    } else {
+        (void)qo;
+        const uint8_t* p = base + ho;
+        u32x4 a = ldg16(p);
+        u32x4 b = ldg16(p + 16);
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        r[8] = ldg4(p + 32);
+    }
+}
+
 // Unit u of a row: the super-block (Q4_K) or block pair (Q4_0) it lives in.
 template <int FMT>
 __device__ __forceinline__ const uint8_t* unit_ptr(const uint8_t* row, int u) {
@@ -150,11 +173,15 @@ __device__ __forceinline__ void nib_dot(uint32_t q, const float4& xa, const floa
     shi = __builtin_fmaf(h_hi(t3), xb.w, shi);
 }
 
-// LDS layout of the staged activations: per token row, K/4 float4 chunks;
-// unit u's 16 chunks are stored XOR-swizzled (chunk c at u*16 + (c ^ (u&15)))
-// so that 16 lanes reading the same logical chunk of 16 consecutive units hit
-// 16 different bank groups.
-__device__ __forceinline__ int xchunk(int u, int c) { return u * 16 + (c ^ (u & 15)); }
+// LDS layout of the staged activations: per token row, unit u's 16 float4
+// chunks at u*17 .. u*17+15 (one chunk of padding per unit).  Lanes reading
+// the same chunk of consecutive units are 272 bytes apart, i.e. 4 banks
+// apart, so 16 of them hit 16 different bank groups; and a chunk's offset
+// from the lane's unit base is a compile-time constant (an immediate in the
+// LDS instruction, no address arithmetic per step).
+constexpr int kUnitChunks = 17;
+__device__ __forceinline__ int xchunk(int u, int c) { return u * kUnitChunks + c; }
+__device__ __forceinline__ int xrow_chunks(int K) { return (K >> 6) * kUnitChunks; }
 
 // Is element e (within its row) met as a high nibble?  Q4_K: elements 32..63
 // of each 64-element chunk; Q4_0: elements 16..31 of each 32-element block.
@@ -166,7 +193,7 @@ __device__ __forceinline__ bool elem_is_high(int e) {
 // ---------------------------------------------------------------------------
 // One unit of NR rows against M token rows of staged activations.  Every
 // activation chunk is read from LDS once and used for all NR rows.
-//   xl  : LDS chunks of token 0 (token m at xl + m * kq)
+//   xl  : LDS chunks of token 0 (token m at xl + m * kq, kq = xrow_chunks(K))
 //   xs  : LDS per-32-run sums of token 0, as float2 per unit (token m at
 //         xs + m * (K/64)); Q4_K: plain sums X; Q4_0: -8 * X.
 // acc[r][m] accumulates row r's dot product with token m (Q4_K: scaled by
@@ -179,8 +206,7 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
                                          uint32_t sel, const float4* __restrict__ xl, int kq,
                                          const float2* __restrict__ xs, int k64,
                                          float (&acc)[NR][M], bool act = true) {
-    const float4* xu = xl + u * 16;
-    const int sw = u & 15;
+    const float4* xu = xl + u * kUnitChunks;
     if constexpr (FMT == kFmtQ4K) {
         float s0[NR][M], s1[NR][M];
 #pragma unroll
@@ -191,8 +217,8 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const float4 xa = xu[m * kq + (i ^ sw)];
-                const float4 xb = xu[m * kq + ((8 + i) ^ sw)];
+                const float4 xa = xu[m * kq + i];
+                const float4 xb = xu[m * kq + 8 + i];
 #pragma unroll
                 for (int r = 0; r < NR; ++r) nib_dot(w[r][4 + i], xa, xb, s0[r][m], s1[r][m]);
             }
@@ -239,8 +265,8 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
             const int ca = i < 4 ? i : 4 + i;  // low-nibble chunk; high = ca + 4
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const float4 xlo = xu[m * kq + (ca ^ sw)];
-                const float4 xhi = xu[m * kq + ((ca + 4) ^ sw)];
+                const float4 xlo = xu[m * kq + ca];
+                const float4 xhi = xu[m * kq + ca + 4];
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
                     if (i < 4)

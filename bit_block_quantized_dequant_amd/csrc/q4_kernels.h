@@ -29,7 +29,10 @@
 
 namespace q4 {
 
-constexpr int kBlock = 512;  // threads per workgroup (8 waves)
+#ifndef Q4_BLOCK
+#define Q4_BLOCK 512
+#endif
+constexpr int kBlock = Q4_BLOCK;  // threads per workgroup
 constexpr int kModeDense = 0;
 constexpr int kModeNorm = 1;
 constexpr int kModeMoe = 2;
@@ -116,7 +119,7 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
     if (store && (c & 7) == 7) xsum[m * (p.K >> 5) + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
     const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
     v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-    if (store) xl[m * kq + xchunk(c >> 4, c & 15)] = v;
+    if (store) xl[m * xrow_chunks(p.K) + xchunk(c >> 4, c & 15)] = v;
 }
 
 template <int FMT, int M, int MODE>
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
     // the wave index is wave-uniform; say so, so that all task bookkeeping
     // stays in scalar registers and the loops are scalar branches
     const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (tid >> 6));
-    const int kq = p.K >> 2;
+    const int kq = xrow_chunks(p.K);  // LDS float4 chunks per token row
     const int k64 = p.K >> 6;
     float4* xl = smem;
     float* xsum = (float*)(smem + M * kq);
@@ -312,18 +315,23 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
     // the row re-read the row's last unit and rows past N re-read row N-1;
     // those lines are on their way anyway and the results are never used.
     const int u_last = p.upr - 1;
-    auto unit_off = [&](int u) -> long long {
-        return FMT == kFmtQ4K ? (long long)(u >> 2) * kQ4KBytes : (long long)u * kQ4_0PairBytes;
+    // Weight addresses: a wave-uniform 64-bit base (matrix, expert, the
+    // task's first row) plus a 32-bit per-lane offset (row inside the task,
+    // unit inside the row), so that the loads take the scalar-base form.
+    auto unit_off = [&](int u) -> uint32_t {
+        return FMT == kFmtQ4K ? (uint32_t)(u >> 2) * kQ4KBytes : (uint32_t)u * kQ4_0PairBytes;
     };
-    const long long uoff_lane = unit_off(li);
-    const long long uoff_last = unit_off(u_last);
-    const long long pass_stride = unit_off(p.lg);
+    const uint32_t uoff_lane = unit_off(li);
+    const uint32_t uoff_last = unit_off(u_last);
+    const uint32_t pass_stride = unit_off(p.lg);
+    const uint32_t rb = (uint32_t)p.row_bytes;
     auto load = [&](const Cursor& c, uint32_t (&dst)[NR][kUnitWords]) {
         const int u = li + c.ui * p.lg;
         const bool in_row = u <= u_last;
-        const long long uoff = in_row ? uoff_lane + c.ui * pass_stride : uoff_last;
+        const uint32_t uoff = in_row ? uoff_lane + c.ui * pass_stride : uoff_last;
         const int g = in_row ? (li & 3) : (u_last & 3);
-        const int r0 = group_row(c);
+        const uint32_t qoff = FMT == kFmtQ4K ? uoff + 16u + 32u * (uint32_t)g : uoff;
+        const int R0 = c.rgt * p.rgw * RR;  // the task's first row (uniform)
         // (an expert index past the dedupe result, possible only for a wave
         // with no tasks, reads a valid expert instead)
         long long ubase = 0;
@@ -331,13 +339,21 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
             const int nu = moe.nu;
             ubase = nu > 0 ? (long long)moe.uexp[min(c.ue, nu - 1)] * p.N : 0ll;
         }
+        // The uniform base row is clamped into [0, N-1] (a wave without tasks,
+        // or a padded row group of the expert call, may start past N); rows
+        // past N then re-read row N-1.
+        const int R0c = max(0, min(R0, p.N - 1));
+        const long long sbase = (ubase + R0c) * p.row_bytes;
+        const int lrow_max = p.N - 1 - R0c;  // >= 0
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            const int row = min(r0 + r, p.N - 1);
-            const long long off = (ubase + row) * p.row_bytes + uoff;
+            const uint32_t lr = (uint32_t)min(gi * RR + r + (R0 - R0c), lrow_max);
+            const uint32_t ro = lr * rb;
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
-                load_unit<FMT>((mt == 0 ? p.w0 : p.w1) + off, g, dst[mt * RR + r]);
+            for (int mt = 0; mt < NMAT; ++mt) {
+                const uint8_t* b = (mt == 0 ? p.w0 : p.w1) + sbase;
+                load_unit_at<FMT>(b, ro + uoff, ro + qoff, dst[mt * RR + r]);
+            }
         }
     };
 

@@ -75,10 +75,11 @@ int pow2ceil(int v) {
     return p;
 }
 
-// LDS bytes of a GEMV workgroup: M rows of K floats plus K/32 run sums each.
+// LDS bytes of a GEMV workgroup: M rows of K floats (17 float4 chunks per
+// 64 elements) plus K/32 run sums each.
 size_t gemv_lds_bytes(int M, int K, bool pure) {
     if (pure) return 0;
-    return (size_t)M * K * 4 + (size_t)M * (K / 32) * 4;
+    return (size_t)M * (K / 64) * 17 * 16 + (size_t)M * (K / 32) * 4;
 }
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less

@@ -1,0 +1,47 @@
+"""CPU proof that the GEMV kernel's weight loads stay in bounds: the host
+model in addr_model.py replays the launch plan, the strided task split, the
+cursors and the address clamping of every lane for each call shape the GPU
+tests use, plus adversarial ones (waves without tasks, padded expert row
+groups, one-row matrices)."""
+import pytest
+
+import addr_model as A
+
+DENSE = [(1, 1, 256), (3, 5, 256), (8, 37, 512), (2, 129, 1024), (5, 1000, 2048),
+         (7, 333, 3584), (1, 4097, 4096), (4, 250, 8192), (1, 77, 32768), (8, 61, 4096),
+         (6, 3, 5120), (1, 256, 512), (1, 4096, 4096), (1, 18944, 3584), (2, 2, 256)]
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q4_0"])
+@pytest.mark.parametrize("M,N,K", DENSE)
+def test_single_matrix_loads_in_bounds(fmt, M, N, K):
+    assert A.check(fmt, M, N, K, RR=2, nmat=1, cus=8) > 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 41, 512), (8, 130, 4096), (2, 9, 8192),
+                                   (1, 14336, 4096)])
+def test_two_matrix_loads_in_bounds(M, N, K):
+    assert A.check("q4k", M, N, K, RR=1, nmat=2, cus=8) > 0
+
+
+@pytest.mark.parametrize("experts,E,N,K,npairs", [([0], 1, 5, 256, 1), ([3, 1], 4, 70, 512, 6),
+                                                  ([15, 0, 7], 16, 33, 1024, 64),
+                                                  ([6, 2, 5], 7, 200, 4096, 6),
+                                                  ([63, 0, 31, 5], 64, 1408, 2048, 24),
+                                                  ([], 4, 16, 256, 8)])
+def test_expert_loads_in_bounds(experts, E, N, K, npairs):
+    A.check("q4_0", 4, N, K, RR=1, nmat=2, moe_experts=experts, E=E, npairs_max=npairs, cus=8)
+
+
+def test_model_catches_the_unclamped_base():
+    # Without the clamp of the uniform base row, a wave with no tasks
+    # (t0 >= ntasks, strided split) starts past N and its 32-bit lane offset
+    # wraps: the model must flag that form of the code.
+    import os
+    src = open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "addr_model.py")).read()
+    unclamped = src.replace("R0c = max(0, min(R0, N - 1))", "R0c = R0")
+    assert unclamped != src
+    ns = {}
+    exec(compile(unclamped, "addr_model_unclamped", "exec"), ns)
+    with pytest.raises(AssertionError):
+        ns["check"]("q4k", 1, 1, 256, 2, 1, cus=8)
