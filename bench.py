@@ -299,7 +299,7 @@ def main():
 
     rows = []
     if args.all:
-        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 4)), (5, (4,))):
+        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 2, 4, 8)), (5, (4,))):
             for M in Ms:
                 r = measure(torch, dev, index, M, args.warmup, args.steps)
                 rows.append(r)

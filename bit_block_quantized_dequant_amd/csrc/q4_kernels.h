@@ -60,6 +60,7 @@ struct GemvParams {
     int nrg;        // row groups per matrix (expert call: padded to a multiple of rgw)
     int ntasks;     // dense calls: total tasks (expert call: computed in the kernel)
     int nwaves;     // waves in the grid
+    int ks;         // batched kernel: waves that split one tile's K range
 };
 
 // Shared state of the expert call after the in-kernel dedupe.

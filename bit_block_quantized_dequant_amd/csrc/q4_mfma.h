@@ -1,0 +1,510 @@
+// q4_mfma.h -- matrix-core GEMV kernel for batched calls (M >= 2 token rows;
+// the library sends it batches of M >= 3).
+//
+// With several token rows the fp32 VALU path runs out of issue slots (one
+// mixed FMA per weight per token), so the dense batched calls run the
+// products on v_mfma_f32_16x16x32_f16 instead:
+//
+//   D[i][j] = sum_k A[i][k] * B[k][j]   (16 x 16 x 32, fp32 accumulate)
+//   lane l holds A[l%16][8(l/16)+t], B[8(l/16)+t][l%16], D[4(l/16)+r][l%16]
+//
+//   * B = weights.  Column j is row j of a 16-row tile, and the 32 k-slots
+//     are the 32 elements of one Q4_0 block or one Q4_K sub-block, which
+//     share one scale.  A nibble masked into a 16-bit half in place is the
+//     exact f16 subnormal q*2^-24 (low nibble) or 16q*2^-24 (high nibble).
+//   * A = activations.  Row i = 2m + h is the high (h = 0) or low (h = 1)
+//     f16 part of token m scaled by 2^e_m, e_m chosen so the token's largest
+//     magnitude lies in [2^14, 2^15); hi + lo keep ~22 bits of every x.
+//     Elements met as high nibbles are staged with a further 2^-4, so every
+//     product is exactly q * x * 2^(e_m - 24).
+//   * Each lane's D values belong to its own weight row j, so the block
+//     scales are applied in the lane that loaded them:
+//       Q4_0 (w = d (q - 8)):        y += d * (D - 8 X)
+//       Q4_K (w = d sc q - dmin m):  y += d * sum_J sc_J D_J - dmin * Dmin,
+//     X being block sums of x; Dmin = sum_J m_J X_J is one more MFMA per
+//     super-block with the sub-block sums as A and the 6-bit mins as B.
+//   (Q4_0 layout: inferencelayer 0.2.13, src/bin/kernel_lab.rs, GEMV_F16S;
+//    Q4_K layout: trueno-gpu 0.4.11, src/kernels/quantize/fused.rs,
+//    FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3.)
+//
+// Fragment order.  The 8 k-slots t of lane group c come from 4 nibble
+// bytes of each of 2 dwords as (byte 0, 2, 1, 3) -- a mask of the dword and
+// a mask of the dword shifted by 8 -- so slot t holds byte slot_byte(t):
+//   Q4_K sub-block J, group c:  bytes 8c..8c+7 of 64-element chunk J/2
+//                               (low nibbles for even J, high for odd J)
+//   Q4_0 block, group c:        bytes 8(c&1)..+7, low nibbles for c < 2
+//                               (elements 8c..), high for c >= 2
+// In both formats the 8 elements of (32-group g, lane group c) are the
+// consecutive elements 8p..8p+7 with p = 4g + c, and the A fragment of that
+// "piece" p sits in LDS at (p * 2M + i) * 16 bytes.
+//
+// Work split.  A tile is 16 rows of one matrix.  A workgroup is 8 waves in
+// groups of KS; each group takes one tile per round and its KS waves split
+// the tile's K range, adding their partial sums through LDS at the end of
+// the round.  Every wave keeps PD steps of weight loads in flight in a
+// register ring, across rounds too; the first PD go out before the
+// activations are staged (once per workgroup, RMS-normalized first for the
+// fused call).
+#pragma once
+
+#include "q4_kernels.h"
+
+namespace q4 {
+
+constexpr int kMBlock = 512;  // threads per workgroup
+constexpr int kMWaves = kMBlock / kWave;
+constexpr int kMaxMK = 32768;  // M * K limit of the library
+constexpr int kMPieces = (kMaxMK / 8 + kMBlock - 1) / kMBlock;  // staging pieces per thread
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
+
+// byte of the 8-byte lane slice that feeds k-slot t
+__host__ __device__ constexpr int slot_byte(int t) {
+    return (t & 4) | ((t & 1) << 1) | ((t >> 1) & 1);
+}
+
+template <int FMT>
+struct MStep {
+    static constexpr int kElems = FMT == kFmtQ4K ? 256 : 128;  // elements per step
+    static constexpr int kBytes = FMT == kFmtQ4K ? 144 : 72;   // bytes per row per step
+};
+
+// LDS map (bytes) for M tokens and K columns.
+struct MLayout {
+    int frag;  // A fragments: (K/8) pieces x 2M rows x 16 bytes
+    int aux;   // Q4_K: Dmin A operand, (K/256) x 4 groups x 2M rows x 2 halves
+               // Q4_0: block sums X, (K/32) blocks x 8 tokens x fp32
+    int exps;  // e_m, 8 ints (padded to 64 bytes)
+    int part;  // partial sums, 2 buffers x 8 waves x 64 lanes x float2
+    int bytes;
+};
+
+__host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
+    MLayout l;
+    l.frag = 0;
+    l.aux = pure ? 0 : (K / 8) * 2 * M * 16;
+    l.exps = l.aux + (pure ? 0 : (fmt == kFmtQ4K ? (K / 256) * 4 * 2 * M * 4 : (K / 32) * 8 * 4));
+    l.part = l.exps + 64;
+    l.bytes = l.part + 2 * kMWaves * 64 * 8;
+    return l;
+}
+
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-126, 127]
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// ---------------------------------------------------------------------------
+// Staging of the activations into A fragments.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ bool piece_is_high(int pp) {
+    return FMT == kFmtQ4K ? ((pp >> 2) & 1) : ((pp >> 1) & 1);
+}
+
+template <int FMT, int M, int MODE>
+__device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLayout& ly,
+                                       float* red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ppt = p.K >> 3;  // pieces per token
+    const int np = M * ppt;
+    float v[kMPieces][8];
+    int um[kMPieces];
+    // unconditional loads of clamped pieces keep the load-counter waits exact
+#pragma unroll
+    for (int k = 0; k < kMPieces; ++k) {
+        const int pc = min(tid + k * kMBlock, np - 1);
+        int m = 0;
+#pragma unroll
+        for (int mm = 1; mm < M; ++mm) m += pc >= mm * ppt;
+        um[k] = m;
+        const float4* src = (const float4*)(p.x + (long long)m * p.K + 8 * (pc - m * ppt));
+        const float4 a = src[0], b = src[1];
+        v[k][0] = a.x; v[k][1] = a.y; v[k][2] = a.z; v[k][3] = a.w;
+        v[k][4] = b.x; v[k][5] = b.y; v[k][6] = b.z; v[k][7] = b.w;
+    }
+    auto valid = [&](int k) { return tid + k * kMBlock < np; };
+
+    // RMSNorm: r_m = 1 / sqrt(sum(x^2) / K + eps), xhat = (x * r_m) * gamma
+    if constexpr (MODE == kModeNorm) {
+        float ss[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) ss[m] = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMPieces; ++k) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = __builtin_fmaf(v[k][e], v[k][e], t);
+            t = valid(k) ? t : 0.f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) ss[m] += um[k] == m ? t : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float t = group_total(ss[m], kWave);
+            if (lane == kWave - 1) red[m * kMWaves + wave] = t;
+        }
+        __syncthreads();
+        float rn[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float t = 0.f;
+            for (int w = 0; w < kMWaves; ++w) t += red[m * kMWaves + w];
+            rn[m] = 1.0f / sqrtf(t / (float)p.K + p.eps);
+        }
+        __syncthreads();  // red is written again below
+#pragma unroll
+        for (int k = 0; k < kMPieces; ++k) {
+            const int pc = min(tid + k * kMBlock, np - 1);
+            const float4* gs = (const float4*)(p.gamma + 8 * (pc - um[k] * ppt));
+            const float4 ga = gs[0], gb = gs[1];
+            const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+            float r = rn[0];
+#pragma unroll
+            for (int m = 1; m < M; ++m) r = um[k] == m ? rn[m] : r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[k][e] = (v[k][e] * r) * g[e];
+        }
+    }
+
+    // e_m: the token's largest magnitude times 2^e_m lies in [2^14, 2^15)
+    {
+        float am[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) am[m] = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMPieces; ++k) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(v[k][e]));
+            t = valid(k) ? t : 0.f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) am[m] = fmaxf(am[m], um[k] == m ? t : 0.f);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float t = am[m];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) t = fmaxf(t, __shfl_xor(t, off, kWave));
+            if (lane == 0) red[m * kMWaves + wave] = t;
+        }
+        __syncthreads();
+        if (tid < M) {
+            float t = 0.f;
+            for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red[tid * kMWaves + w]);
+            const int ex = (int)((__builtin_bit_cast(uint32_t, t) >> 23) & 0xFF) - 127;
+            int e = t > 0.f ? 14 - ex : 0;
+            e = max(-100, min(120, e));
+            ((int*)(lds + ly.exps))[tid] = e;
+        }
+        __syncthreads();
+    }
+    const int* ex = (const int*)(lds + ly.exps);
+
+    // fragments (hi/lo f16 of x 2^e, high-nibble pieces 2^-4 more) and sums
+#pragma unroll
+    for (int k = 0; k < kMPieces; ++k) {
+        const int pc = min(tid + k * kMBlock, np - 1);
+        const int m = um[k];
+        const int pp = pc - m * ppt;
+        const int e = ex[m];
+        const float s = pow2f(e);
+        const float sf = piece_is_high<FMT>(pp) ? s * 0.0625f : s;
+        h8 hi, lo;
+        float part = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float xs = v[k][slot_byte(t)] * sf;
+            const _Float16 h = (_Float16)xs;
+            hi[t] = h;
+            lo[t] = (_Float16)(xs - (float)h);
+            part += v[k][t] * s;
+        }
+        // the 4 pieces of one 32-element group are 4 consecutive threads
+        part = dpp_add(part, 0);
+        part = dpp_add(part, 1);
+        if (valid(k)) {
+            *(h8*)(lds + ly.frag + (pp * 2 * M + 2 * m) * 16) = hi;
+            *(h8*)(lds + ly.frag + (pp * 2 * M + 2 * m + 1) * 16) = lo;
+            if ((pp & 3) == 0) {
+                const int g32 = pp >> 2;  // Q4_0 block / Q4_K sub-block index
+                if constexpr (FMT == kFmtQ4_0) {
+                    ((float*)(lds + ly.aux))[g32 * 8 + m] = part;
+                } else {
+                    // Dmin A operand: group c = J/2 of super-block sb holds
+                    // the sums of sub-blocks 2c (half 0) and 2c+1 (half 1),
+                    // scaled by 2^-5 to stay inside the f16 range
+                    const int sb = g32 >> 3, J = g32 & 7;
+                    const float xs = part * 0.03125f;
+                    const _Float16 h = (_Float16)xs;
+                    const _Float16 l = (_Float16)(xs - (float)h);
+                    _Float16* a = (_Float16*)(lds + ly.aux);
+                    const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
+                    a[base] = h;
+                    a[base + 2] = l;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD>
+__global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) {
+    static_assert(M >= 2 && M <= 8, "batched kernel");
+    using St = MStep<FMT>;
+    extern __shared__ float4 smem4[];
+    char* lds = (char*)smem4;
+    __shared__ float red[8 * kMWaves];
+    const MLayout ly = mlayout(FMT, M, p.K, PURE);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KS = p.ks;              // waves per tile (1, 2, 4 or 8; at most S)
+    const int TG = kMWaves / KS;      // tiles per workgroup and round
+    const int grp = wave / KS, sl = wave - grp * KS;
+    const int jrow = lane & 15;  // tile row of this lane's B column and D values
+    const int c = lane >> 4;     // k group
+    const int S = p.K / St::kElems;
+    const int st0 = sl * S / KS, st1 = (sl + 1) * S / KS;  // st1 > st0 as KS <= S
+    const int tpm = (p.N + 15) >> 4;
+    const int ntiles = NMAT * tpm;
+    const int per_round = gridDim.x * TG;
+    const int nrounds = (ntiles + per_round - 1) / per_round;
+    const uint32_t rb = (uint32_t)p.row_bytes;
+
+    // weight registers of one step (12 dwords in both formats)
+    struct WR {
+        uint32_t v[12];
+    };
+    // Loads past the wave's last step, and those of a group without a tile
+    // in the last round, are not consumed: they go to the group's own
+    // last-round tile with every lane on one address (spread over the chip,
+    // one cache line per instruction) and stay unconditional.
+    auto load = [&](int r, int st, WR& w) {
+        const int rr = min(r, nrounds - 1);
+        const int traw = (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
+        const bool idle = r >= nrounds || traw >= ntiles;  // wave-uniform
+        const int t = min(traw, ntiles - 1);
+        const int mt = NMAT == 2 ? (t >= tpm ? 1 : 0) : 0;
+        const int row0 = (t - mt * tpm) << 4;
+        const uint8_t* base = (mt ? p.w1 : p.w0) + (long long)row0 * p.row_bytes;
+        const uint32_t lr = (uint32_t)min(jrow, p.N - 1 - row0);
+        const uint32_t off = idle ? 0u : lr * rb + (uint32_t)st * St::kBytes;
+        if constexpr (FMT == kFmtQ4K) {
+            const uint32_t co = idle ? 0u : 8u * (uint32_t)c;
+            const u32x4 h = ldg16(base + off);
+            w.v[0] = h.x; w.v[1] = h.y; w.v[2] = h.z; w.v[3] = h.w;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t* q =
+                    (const uint32_t*)__builtin_assume_aligned(base + off + co + 16 + 32 * g, 8);
+                w.v[4 + 2 * g] = q[0];
+                w.v[5 + 2 * g] = q[1];
+            }
+        } else {
+            // per block pair (36 bytes, words 0..8): words 2h..2h+2 hold the
+            // lane's bytes of block A, words 5+2h..6+2h those of block B, and
+            // word 4 (h = 0) or word 0 (h = 1) the scale the others lack
+            const uint32_t h8o = idle ? 0u : 8u * (uint32_t)(c & 1);
+            const uint32_t zo = idle ? 0u : 16u - 2u * h8o;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint8_t* pr = base + off + 36 * k;
+                const uint32_t* a = (const uint32_t*)__builtin_assume_aligned(pr + h8o, 4);
+                const uint32_t* b = (const uint32_t*)__builtin_assume_aligned(pr + 20 + h8o, 4);
+                const uint32_t* z = (const uint32_t*)__builtin_assume_aligned(pr + zo, 4);
+                w.v[6 * k + 0] = a[0]; w.v[6 * k + 1] = a[1]; w.v[6 * k + 2] = a[2];
+                w.v[6 * k + 3] = b[0]; w.v[6 * k + 4] = b[1];
+                w.v[6 * k + 5] = z[0];
+            }
+        }
+    };
+
+    // A fragment of piece pp for this lane (rows i >= 2M repeat row 2M-1)
+    const int i_lane = min(jrow, 2 * M - 1);
+    auto afrag = [&](int pp) { return *(const h8*)(lds + ly.frag + (pp * 2 * M + i_lane) * 16); };
+
+    auto compute = [&](const WR& w, int st, float2& y) {
+        if constexpr (FMT == kFmtQ4K) {
+            const uint32_t h1 = w.v[1], h2 = w.v[2], h3 = w.v[3];
+            const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;
+            const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+            float scf[8];  // (v_cvt_f32_ubyte0..3)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                scf[j] = (float)((sc_lo >> (8 * j)) & 0xFFu);
+                scf[4 + j] = (float)((sc_hi >> (8 * j)) & 0xFFu);
+            }
+            f4 acc = (f4)(0.f);
+            const int pbase = st * 32 + c;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t d0 = w.v[4 + 2 * g], d1 = w.v[5 + 2 * g];
+                const uint32_t d08 = d0 >> 8, d18 = d1 >> 8;
+                const u32x4m blo = {d0 & 0x000F000Fu, d08 & 0x000F000Fu, d1 & 0x000F000Fu,
+                                    d18 & 0x000F000Fu};
+                const u32x4m bhi = {d0 & 0x00F000F0u, d08 & 0x00F000F0u, d1 & 0x00F000F0u,
+                                    d18 & 0x00F000F0u};
+                const f4 Dl = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    afrag(pbase + 8 * g), __builtin_bit_cast(h8, blo), (f4)(0.f), 0, 0, 0);
+                const f4 Dh = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    afrag(pbase + 8 * g + 4), __builtin_bit_cast(h8, bhi), (f4)(0.f), 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[r] = __builtin_fmaf(scf[2 * g], Dl[r], acc[r]);
+                    acc[r] = __builtin_fmaf(scf[2 * g + 1], Dh[r], acc[r]);
+                }
+            }
+            uint32_t scp, mp;
+            q4k_scale_pairs(h1, h2, h3, q4k_sel(c), scp, mp);
+            (void)scp;
+            const uint32_t am =
+                *(const uint32_t*)(lds + ly.aux + ((st * 4 + c) * 2 * M + i_lane) * 4);
+            const u32x4m amin = {am, 0u, 0u, 0u};
+            const u32x4m bmin = {mp, 0u, 0u, 0u};
+            const f4 Dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(h8, amin), __builtin_bit_cast(h8, bmin), (f4)(0.f), 0, 0, 0);
+            const float d = h_lo(w.v[0]), dmin32 = h_hi(w.v[0]) * 32.0f;
+            f4 t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = __builtin_fmaf(-dmin32, Dm[r], d * acc[r]);
+            y.x += t[0] + t[1];
+            y.y += t[2] + t[3];
+        } else {
+            const uint32_t hsel = (uint32_t)(c & 1);
+            const uint32_t mask = c >= 2 ? 0x00F000F0u : 0x000F000Fu;
+            const float* xsum = (const float*)(lds + ly.aux);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t a0 = w.v[6 * k], a1 = w.v[6 * k + 1], a2 = w.v[6 * k + 2];
+                const uint32_t b0 = w.v[6 * k + 3], b1 = w.v[6 * k + 4], z = w.v[6 * k + 5];
+                const uint32_t qa0 = __builtin_amdgcn_alignbit(a1, a0, 16);
+                const uint32_t qa1 = __builtin_amdgcn_alignbit(a2, a1, 16);
+                const float dA = h_lo(hsel ? z : a0);
+                const float dB = h_hi(hsel ? a2 : z);
+                const u32x4m ba = {qa0 & mask, (qa0 >> 8) & mask, qa1 & mask, (qa1 >> 8) & mask};
+                const u32x4m bb = {b0 & mask, (b0 >> 8) & mask, b1 & mask, (b1 >> 8) & mask};
+                const int blk = st * 4 + 2 * k;  // block index of block A in the row
+                const f4 DA = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    afrag(blk * 4 + c), __builtin_bit_cast(h8, ba), (f4)(0.f), 0, 0, 0);
+                const f4 DB = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    afrag(blk * 4 + 4 + c), __builtin_bit_cast(h8, bb), (f4)(0.f), 0, 0, 0);
+                const float2 XA = *(const float2*)(xsum + blk * 8 + 2 * c);
+                const float2 XB = *(const float2*)(xsum + blk * 8 + 8 + 2 * c);
+                // d (D - 8 X 2^-24): X holds sums of x 2^e, D carries 2^(e-24)
+                y.x = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.x, DA[0] + DA[1]), y.x);
+                y.y = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.y, DA[2] + DA[3]), y.y);
+                y.x = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.x, DB[0] + DB[1]), y.x);
+                y.y = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.y, DB[2] + DB[3]), y.y);
+            }
+        }
+    };
+
+    // word checksum of the step's bytes, each word counted by one lane
+    auto checksum = [&](const WR& w) {
+        uint32_t s = 0;
+        if constexpr (FMT == kFmtQ4K) {
+#pragma unroll
+            for (int i = 4; i < 12; ++i) s += w.v[i];
+            if (c == 0) s += w.v[0] + w.v[1] + w.v[2] + w.v[3];
+        } else {
+            // lane group 0: words 0,1 (a), 5,6 (b), 4 (z); group 1: 2,3 (a), 7,8 (b)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                uint32_t t = w.v[6 * k] + w.v[6 * k + 1] + w.v[6 * k + 3] + w.v[6 * k + 4];
+                if (c == 0) t += w.v[6 * k + 5];
+                s += c < 2 ? t : 0u;
+            }
+        }
+        return s;
+    };
+
+    // End of round r: add the KS partial sums of the group's tile and write.
+    auto finish = [&](int r, float2 y, uint32_t cks, int buf) {
+        float2* part = (float2*)(lds + ly.part) + buf * kMWaves * 64;
+        if constexpr (PURE) y.x = __builtin_bit_cast(float, cks);
+        part[wave * 64 + lane] = y;
+        __syncthreads();
+        const int t = (r * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
+        if (sl == 0 && t < ntiles) {
+            const int mt = NMAT == 2 ? (t >= tpm ? 1 : 0) : 0;
+            const int row = ((t - mt * tpm) << 4) + jrow;
+            if constexpr (PURE) {
+                uint32_t tot = cks;
+                for (int k = 1; k < KS; ++k)
+                    tot += __builtin_bit_cast(uint32_t, part[(wave + k) * 64 + lane].x);
+                tot += __shfl_xor(tot, 16, kWave);
+                tot += __shfl_xor(tot, 32, kWave);
+                if (c == 0 && row < p.N) p.cks[(long long)mt * p.N + row] = tot;
+            } else {
+                float2 tot = y;
+                for (int k = 1; k < KS; ++k) {
+                    const float2 o = part[(wave + k) * 64 + lane];
+                    tot.x += o.x;
+                    tot.y += o.y;
+                }
+                const int* ex = (const int*)(lds + ly.exps);
+                float* yo = mt ? p.y1 : p.y0;
+                if (row < p.N) {
+                    if (2 * c < M) yo[(long long)(2 * c) * p.N + row] = tot.x * pow2f(24 - ex[2 * c]);
+                    if (2 * c + 1 < M)
+                        yo[(long long)(2 * c + 1) * p.N + row] = tot.y * pow2f(24 - ex[2 * c + 1]);
+                }
+            }
+        }
+    };
+
+    // Ring of PD steps in flight.  The wave's steps, round after round, are
+    // (r, st0) .. (r, st1 - 1); slot j of the ring is consumed and reloaded
+    // in place, PD steps ahead (past the last round the tile index clamps,
+    // so the loads stay unconditional and the load-counter waits exact).
+    WR w[PD];
+    int lr = 0, ls = st0;
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+        load(lr, ls, w[j]);
+        if (++ls == st1) {
+            ls = st0;
+            ++lr;
+        }
+    }
+    if constexpr (!PURE) mstage<FMT, M, MODE>(p, lds, ly, red);
+    __syncthreads();
+
+    const int n = nrounds * (st1 - st0);
+    int cs = st0, cr = 0, buf = 0;
+    float2 y = make_float2(0.f, 0.f);
+    uint32_t cks = 0;
+    for (int base = 0; base < n; base += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) {
+            const bool act = base + j < n;  // wave-uniform
+            if (act) {
+                if constexpr (PURE) {
+                    cks += checksum(w[j]);
+                } else {
+                    compute(w[j], cs, y);
+                }
+            }
+            load(lr, ls, w[j]);
+            if (++ls == st1) {
+                ls = st0;
+                ++lr;
+            }
+            if (act && ++cs == st1) {
+                cs = st0;
+                finish(cr, y, cks, buf);
+                ++cr;
+                buf ^= 1;
+                y = make_float2(0.f, 0.f);
+                cks = 0;
+            }
+        }
+    }
+}
+
+}  // namespace q4

@@ -16,6 +16,7 @@
 #include <mutex>
 
 #include "q4_kernels.h"
+#include "q4_mfma.h"
 #include "q4gemv.h"
 
 using namespace q4;
@@ -23,6 +24,7 @@ using namespace q4;
 namespace {
 
 constexpr int kMaxDevices = 64;
+static_assert(Q4_MAX_MK == kMaxMK, "staging of the batched kernel is sized for Q4_MAX_MK");
 
 // ---------------------------------------------------------------------------
 // Validation (pure host code)
@@ -107,13 +109,13 @@ int allow_big_lds(const void* kern, std::atomic<int>* done) {
 
 template <typename Kern>
 int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
-           std::atomic<int>* big_lds_done) {
+           std::atomic<int>* big_lds_done, int threads = kBlock) {
     if (lds > 64 * 1024) {
         int st = allow_big_lds((const void*)kern, big_lds_done);
         if (st) return st;
     }
     void* args[] = {(void*)&p};
-    hipError_t e = hipLaunchKernel((const void*)kern, dim3(blocks), dim3(kBlock), args, lds,
+    hipError_t e = hipLaunchKernel((const void*)kern, dim3(blocks), dim3(threads), args, lds,
                                    (hipStream_t)stream);
     return e == hipSuccess ? Q4_OK : Q4_ERR_HIP;
 }
@@ -173,11 +175,83 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
                   big_lds_done);
 }
 
+// Matrix-core kernel: steps of weight loads each wave keeps in flight, and
+// the number of waves per CU the K split aims for.
+#ifndef Q4_MFMA_PD_Q4K
+#define Q4_MFMA_PD_Q4K 4
+#endif
+#ifndef Q4_MFMA_PD_Q4_0
+#define Q4_MFMA_PD_Q4_0 6
+#endif
+#ifndef Q4_MFMA_WAVES_PER_CU
+#define Q4_MFMA_WAVES_PER_CU 8
+#endif
+
+// Waves that split one 16-row tile's K range (1, 2, 4 or 8): the fewest that
+// give every CU its share of waves, at most one per step of the row.  It
+// depends on the matrix shape and the CU count only, so a token's result
+// does not depend on the batch it is computed in.
+int mfma_ks(long long ntiles, int steps, int cus) {
+    static const int forced = env_int("Q4GEMV_MFMA_KS", 0);
+    const long long want = (long long)cus * Q4_MFMA_WAVES_PER_CU;
+    int ks = 1;
+    while (ks < kMWaves && 2 * ks <= steps && ntiles * ks < want) ks *= 2;
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8)
+        ks = forced <= steps ? forced : ks;
+    return ks;
+}
+
+// Batches of at least this many token rows run on the matrix-core kernel
+// (at M = 2 the VALU kernel is still below its issue limit and faster).
+// Q4GEMV_MFMA=0 sends every batch to the VALU kernel (for comparisons; the
+// results differ only by rounding).
+#ifndef Q4_MFMA_MIN_M
+#define Q4_MFMA_MIN_M 3
+#endif
+bool mfma_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_MFMA");
+        return !(s && *s && atoi(s) == 0);
+    }();
+    return on;
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+int run_mfma_m(GemvParams& p, int cus, void* stream) {
+    constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
+    // a pure-read pass takes the launch shape of the call it mirrors
+    const int wgc = wg_per_cu((size_t)mlayout(FMT, M, p.K, false).bytes);
+    const long long ntiles = (long long)NMAT * ((p.N + 15) / 16);
+    p.ks = mfma_ks(ntiles, p.K / (FMT == kFmtQ4K ? 256 : 128), cus);
+    const int TG = kMWaves / p.ks;
+    long long blocks = (long long)cus * wgc;
+    const long long need = (ntiles + TG - 1) / TG;
+    if (blocks > need) blocks = need;
+    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
+                  big_lds_done, kMBlock);
+}
+
 template <int FMT, int NMAT, int MODE, bool PURE>
 int run(GemvParams& p, int M, int npairs_max, void* stream) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st) return st;
+    if constexpr (MODE != kModeMoe) {
+        if (M >= Q4_MFMA_MIN_M && mfma_enabled()) {
+            switch (M) {
+                case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, stream);
+                case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, stream);
+                case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, stream);
+                case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, stream);
+                case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, stream);
+                case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, stream);
+                case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, stream);
+            }
+            return Q4_ERR_BATCH;
+        }
+    }
     switch (M) {
         case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);
         case 2: return run_m<FMT, NMAT, MODE, PURE, 2>(p, cus, npairs_max, stream);

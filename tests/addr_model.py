@@ -112,3 +112,155 @@ def check(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
         n += 1
     return n
+
+
+# ---------------------------------------------------------------------------
+# Matrix-core kernel (batched calls, M >= 2): q4_mfma.h and run_mfma_m().
+# ---------------------------------------------------------------------------
+LDS_CAP = 160 * 1024 - 2048  # dynamic LDS a kernel may ask for
+
+
+def mlayout(fmt, M, K, pure=False):
+    """Byte offsets of the kernel's LDS regions (mlayout() in q4_mfma.h)."""
+    aux = 0 if pure else (K // 8) * 2 * M * 16
+    aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k" else (K // 32) * 8 * 4)
+    exps = aux + aux_bytes
+    part = exps + 64
+    return dict(frag=0, aux=aux, exps=exps, part=part, bytes=part + 2 * 8 * 64 * 8)
+
+
+def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
+    """Waves per tile (mfma_ks() in q4gemv.hip)."""
+    ks = 1
+    while ks < 8 and 2 * ks <= steps and ntiles * ks < cus * waves_per_cu:
+        ks *= 2
+    return ks
+
+
+def mfma_plan(fmt, M, K, N, nmat, cus=256):
+    lds = mlayout(fmt, M, K)["bytes"]
+    wgc = max(1, min(2, LDS_CAP // lds))
+    ntiles = nmat * ((N + 15) // 16)
+    steps = K // (256 if fmt == "q4k" else 128)
+    KS = mfma_ks(ntiles, steps, cus)
+    TG = 8 // KS
+    blocks = min(cus * wgc, (ntiles + TG - 1) // TG)
+    return dict(lds=lds, blocks=blocks, ntiles=ntiles, TG=TG, KS=KS, steps=steps)
+
+
+def mfma_positions(S, KS, nrounds, wave, PD):
+    """(round, step) of every weight load a wave issues: the ring's first PD
+    steps, then one load PD steps ahead for every slot the loop visits."""
+    sl = wave % KS
+    st0, st1 = sl * S // KS, (sl + 1) * S // KS
+    ns = st1 - st0
+    assert ns >= 1
+    n = nrounds * ns
+    visits = -(-n // PD) * PD
+    return [(q // ns, st0 + q % ns) for q in range(visits + PD)]
+
+
+def mfma_loads(fmt, M, N, K, nmat, cus=256):
+    """Yield (matrix, byte offset, nbytes) of every weight load."""
+    pl = mfma_plan(fmt, M, K, N, nmat, cus)
+    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    SB, PD = (144, 4) if fmt == "q4k" else (72, 6)
+    S, KS = pl["steps"], pl["KS"]
+    tpm = (N + 15) // 16
+    ntiles, TG, G = pl["ntiles"], pl["TG"], pl["blocks"]
+    nrounds = (ntiles + G * TG - 1) // (G * TG)
+    for b in range(G):
+        for wave in range(8):
+            grp = wave // KS
+            for (r, st) in mfma_positions(S, KS, nrounds, wave, PD):
+                rr = min(r, nrounds - 1)
+                traw = (rr * G + b) * TG + grp
+                idle = r >= nrounds or traw >= ntiles
+                t = min(traw, ntiles - 1)
+                mt = 1 if (nmat == 2 and t >= tpm) else 0
+                row0 = (t - mt * tpm) * 16
+                base = row0 * rb
+                for lane in range(64):
+                    jrow, c = lane & 15, lane >> 4
+                    lr = min(jrow, N - 1 - row0) & U32
+                    off = 0 if idle else (lr * rb + st * SB) & U32
+                    if fmt == "q4k":
+                        co = 0 if idle else 8 * c
+                        yield mt, base + off, 16
+                        for g in range(4):
+                            yield mt, base + off + co + 16 + 32 * g, 8
+                    else:
+                        h8o = 0 if idle else 8 * (c & 1)
+                        zo = 0 if idle else 16 - 2 * h8o
+                        for k in range(2):
+                            pr = off + 36 * k
+                            yield mt, base + pr + h8o, 12
+                            yield mt, base + pr + 20 + h8o, 8
+                            yield mt, base + pr + zo, 4
+
+
+def mfma_check(fmt, M, N, K, nmat, cus=256):
+    pl = mfma_plan(fmt, M, K, N, nmat, cus)
+    assert pl["lds"] <= LDS_CAP, (fmt, M, K, pl["lds"])
+    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    limit = N * rb
+    n = 0
+    for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus):
+        assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
+        n += 1
+    return n
+
+
+def mfma_lds_check(fmt, M, K):
+    """Every LDS byte the kernel writes while staging or reads while
+    computing lies inside its region, and every fragment and sum a compute
+    step reads was written by the staging."""
+    ly = mlayout(fmt, M, K)
+    ppt = K // 8
+    frag_w, aux_w = set(), set()
+    for m in range(M):
+        for pp in range(ppt):
+            for h in range(2):
+                o = (pp * 2 * M + 2 * m + h) * 16
+                assert ly["frag"] <= o and o + 16 <= ly["aux"]
+                frag_w.add(o)
+            if pp & 3 == 0:
+                g32 = pp >> 2
+                if fmt == "q4_0":
+                    o = ly["aux"] + (g32 * 8 + m) * 4
+                    assert o + 4 <= ly["exps"]
+                    aux_w.add(o)
+                else:
+                    sb, J = g32 >> 3, g32 & 7
+                    half = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1)
+                    for hh in (half, half + 2):
+                        o = ly["aux"] + 2 * hh
+                        assert o + 2 <= ly["exps"]
+                        aux_w.add(o)
+    S = K // (256 if fmt == "q4k" else 128)
+    for st in range(S):
+        for lane in range(64):
+            jrow, c = lane & 15, lane >> 4
+            i = min(jrow, 2 * M - 1)
+            if fmt == "q4k":
+                pps = [st * 32 + 8 * g + c + 4 * hi for g in range(4) for hi in range(2)]
+                o = ly["aux"] + ((st * 4 + c) * 2 * M + i) * 4
+                assert o + 4 <= ly["exps"]
+                assert o in aux_w and o + 2 in aux_w
+            else:
+                pps = []
+                for k in range(2):
+                    blk = st * 4 + 2 * k
+                    pps += [blk * 4 + c, blk * 4 + 4 + c]
+                    for bb in (blk, blk + 1):
+                        o = ly["aux"] + (bb * 8 + 2 * c) * 4
+                        assert o + 8 <= ly["exps"]
+                        # token 2c (and 2c + 1) sums exist when those tokens do
+                        for hm in range(2):
+                            if 2 * c + hm < M:
+                                assert o + 4 * hm in aux_w
+            for pp in pps:
+                o = (pp * 2 * M + i) * 16
+                assert o + 16 <= ly["aux"] and o in frag_w
+    assert ly["part"] + 2 * 8 * 64 * 8 == ly["bytes"]
+    return True

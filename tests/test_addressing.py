@@ -45,3 +45,50 @@ def test_model_catches_the_unclamped_base():
     exec(compile(unclamped, "addr_model_unclamped", "exec"), ns)
     with pytest.raises(AssertionError):
         ns["check"]("q4k", 1, 1, 256, 2, 1, cus=8)
+
+
+# ---------------------------------------------------------------------------
+# matrix-core kernel of the batched calls (M >= 2)
+# ---------------------------------------------------------------------------
+BATCHED = [(M, N, K) for (M, N, K) in DENSE if M >= 2] + [
+    (8, 4096, 4096), (4, 14336, 4096), (2, 16, 16384), (8, 17, 256), (2, 1, 256)]
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q4_0"])
+@pytest.mark.parametrize("M,N,K", BATCHED)
+def test_batched_loads_in_bounds(fmt, M, N, K):
+    # few CUs so that workgroups run several rounds and waves prefetch across
+    # them; many CUs so that the K split and idle tile groups come into play
+    assert A.mfma_check(fmt, M, N, K, nmat=1, cus=4) > 0
+    if N * K <= 4096 * 4096:
+        assert A.mfma_check(fmt, M, N, K, nmat=1, cus=256) > 0
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 41, 512), (8, 130, 4096), (2, 9, 8192), (4, 14336, 4096)])
+def test_batched_two_matrix_loads_in_bounds(M, N, K):
+    assert A.mfma_check("q4k", M, N, K, nmat=2, cus=4) > 0
+    assert A.mfma_check("q4k", M, N, K, nmat=2, cus=256) > 0
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q4_0"])
+@pytest.mark.parametrize("M,K", [(2, 256), (3, 512), (8, 4096), (2, 16384), (4, 8192),
+                                 (7, 3584), (5, 2048)])
+def test_batched_lds_regions(fmt, M, K):
+    assert A.mfma_lds_check(fmt, M, K)
+
+
+def test_batched_lds_fits_every_shape():
+    for fmt in ("q4k", "q4_0"):
+        for M in range(2, 9):
+            for K in range(256, 32768 // M + 1, 256):
+                assert A.mlayout(fmt, M, K)["bytes"] + 256 <= 160 * 1024, (fmt, M, K)
+
+
+def test_batched_ks_choices():
+    # one tile, long rows: all 8 waves split K; short rows cap the split
+    assert A.mfma_ks(1, 32, 256) == 8
+    assert A.mfma_ks(1, 1, 256) == 1
+    assert A.mfma_ks(1, 3, 256) == 2
+    # plenty of tiles: no split
+    assert A.mfma_ks(4096, 16, 256) == 1
+    assert A.mfma_ks(1792, 16, 256) == 2

@@ -6,8 +6,9 @@ Bars:
   * GEMV outputs: |y_gpu - y_ref| <= 1e-4 * sum_k |w[n,k] * x[m,k]| per output
     element, y_ref and the sum from the oracle in float64;
   * pure-read checksums: bit-exact against the oracle's row word sums;
-  * invariants the design promises bit-exactly: a batch equals its rows run
-    one by one, gate/up equal two single-matrix calls, the expert call equals
+  * invariants the design promises bit-exactly: a token row of a batched
+    call does not depend on the other rows or its position, gate/up equal
+    two single-matrix calls, the expert call equals
     per-(token, slot) single calls, y(2x) = 2 y(x), one-hot x gives the
     dequantized column.
 All five named workloads run at full size; smaller shapes cover ragged row
@@ -307,7 +308,10 @@ def test_moe_shapes(dev, orc, M, top_k, E, N, K):
 # ---------------------------------------------------------------------------
 # pure-read ceiling: checksums prove every byte was read
 # ---------------------------------------------------------------------------
-def test_pure_read_checksums(dev, orc):
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_pure_read_checksums(dev, orc, M):
+    """The pure-read pass of each call (VALU addressing at M <= 2, matrix-core
+    addressing at M >= 3) touches every weight word exactly once."""
     import torch
     import bit_block_quantized_dequant_amd as q4
     rng = synth.make_rng(77)
@@ -316,18 +320,18 @@ def test_pure_read_checksums(dev, orc):
     w1 = synth.q4k_matrix(rng, N, K)
     rb = synth.q4k_row_bytes(K)
     c = empty((2 * N,), dev, torch.int32)
-    q4.q4_pure_read(c, q4.Q4_READ_GATE_UP, T(w0, dev), T(w1, dev), None, 1, 0, 0, N, K)
+    q4.q4_pure_read(c, q4.Q4_READ_GATE_UP, T(w0, dev), T(w1, dev), None, M, 0, 0, N, K)
     got = host(c).view(np.uint32)
     want = np.concatenate([orc.row_checksum(w0, N, rb), orc.row_checksum(w1, N, rb)])
     assert np.array_equal(got, want)
     c = empty((N,), dev, torch.int32)
-    q4.q4_pure_read(c, q4.Q4_READ_Q4K_GEMV, T(w0, dev), None, None, 1, 0, 0, N, K)
+    q4.q4_pure_read(c, q4.Q4_READ_Q4K_GEMV, T(w0, dev), None, None, M, 0, 0, N, K)
     assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w0, N, rb))
     N, K = 1000, 2048
     w0 = synth.q4_0_matrix(rng, N, K)
     rb = synth.q4_0_row_bytes(K)
     c = empty((N,), dev, torch.int32)
-    q4.q4_pure_read(c, q4.Q4_READ_Q4_0_GEMV, T(w0, dev), None, None, 4, 0, 0, N, K)
+    q4.q4_pure_read(c, q4.Q4_READ_Q4_0_GEMV, T(w0, dev), None, None, M, 0, 0, N, K)
     assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w0, N, rb))
 
 
@@ -358,7 +362,11 @@ def test_pure_read_moe_checksums(dev, orc):
 # ---------------------------------------------------------------------------
 # bit-exact invariants of the design
 # ---------------------------------------------------------------------------
-def test_batch_equals_single_rows(dev):
+def test_batch_rows_independent_of_batch(dev):
+    """Batches of M >= 3 (matrix-core kernel) compute every token row on its
+    own: the rows of an M=8 batch equal, bit for bit, the same tokens run in
+    smaller batches at other positions.  (M = 1, 2 run the VALU kernel, whose
+    rounding differs; they are held to the oracle bound like every call.)"""
     import bit_block_quantized_dequant_amd as q4
     rng = synth.make_rng(31)
     N, K, M = 777, 4096, 8
@@ -370,10 +378,36 @@ def test_batch_equals_single_rows(dev):
         yb = empty((M, N), dev)
         f(yb, wd, xd, M, N, K)
         yb = host(yb)
-        for m in range(M):
-            y1 = empty((1, N), dev)
-            f(y1, wd, xd[m:m + 1].contiguous(), 1, N, K)
-            assert_bits(host(y1)[0], yb[m], "%s batch row %d vs single" % (fmt, m))
+        for sub in ([7, 0, 2], [3, 5, 1, 6], [6, 2, 4, 0, 1], [1, 2, 3, 4, 5, 6, 7]):
+            ys = empty((len(sub), N), dev)
+            f(ys, wd, T(x[sub], dev), len(sub), N, K)
+            ys = host(ys)
+            for j, m in enumerate(sub):
+                assert_bits(ys[j], yb[m], "%s token %d at row %d of %d vs row %d of 8"
+                            % (fmt, m, j, len(sub), m))
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4k"])
+def test_batched_token_magnitudes(dev, orc, fmt):
+    """Each token of a batch is scaled by its own power of two before its f16
+    split: tokens 1e-30 and 1e30 apart, and an all-zero token, in one batch."""
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(34)
+    N, K, M = 200, 2048, 6
+    w = synth.q4_0_matrix(rng, N, K) if fmt == "q4_0" else synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K)
+    x[0] *= np.float32(1e-30)
+    x[1] *= np.float32(1e30)
+    x[2] = 0.0
+    x[3, ::7] = 0.0
+    x[4] *= np.float32(2.0 ** -60)
+    y = empty((M, N), dev)
+    f = q4.q4_0_gemv if fmt == "q4_0" else q4.q4k_gemv
+    f(y, T(w, dev), T(x, dev), M, N, K)
+    ref, ab = (orc.q4_0_gemv if fmt == "q4_0" else orc.q4k_gemv)(w, x, N, K, NT)
+    y = host(y)
+    assert_bound(y, ref, ab, fmt + " mixed token magnitudes")
+    assert np.all(y[2] == 0.0)
 
 
 def test_gate_up_equals_two_single_calls(dev):
