@@ -9,7 +9,8 @@ per call), timed over --steps calls after --warmup untimed calls.
                calls / wall time between two device synchronizations (GB/s)
   roofline     the kernel itself: weight bytes per launch / mean launch
                duration, from HIP events recorded on the launch stream around
-               batches of back-to-back launches, against the 8 TB/s HBM3E peak
+               replays of HIP graphs of back-to-back launches (no host gaps),
+               against the 8 TB/s HBM3E peak
   pure_read    the same for the pure-read ceiling kernel (same bytes, same
                addressing, no arithmetic)
   cpu_baseline the CPU oracle (plain C, float64) timed on this host's cores on
@@ -21,6 +22,15 @@ totalling at least 1 GiB.
 
   --all REPORT   additionally time every named workload and its ceiling and
                  write REPORT.json and REPORT.md
+  --copy-calibration MIB
+                 only run a plain device-to-device copy of MIB MiB 20 times:
+                 the known-size reference that scales the FETCH_SIZE and
+                 WRITE_SIZE counters of a profiler run into bytes
+
+roofline.traffic is the HBM bytes per launch of the headline kernel measured
+with those counters (FETCH_SIZE + WRITE_SIZE, each scaled by the copy's
+factor); it is read from the counter summary in profiles/ and reported only
+while the kernel sources hash to the value recorded there, else null.
 """
 import argparse
 import json
@@ -34,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective weight GB/s and % of HBM peak, Q4_K GEMV M=1 K=4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_gate_up_q4k_M1_K4096_N14336x2.txt")
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
 
@@ -46,6 +57,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--all", metavar="REPORT", default=None,
                     help="also time every named workload; write REPORT.json / REPORT.md")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB 20 times (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound of the CPU-oracle sample (0 skips it)")
     return ap.parse_args()
@@ -79,29 +92,52 @@ class Rotation:
         return self.base + (i % self.ncopies) * self.stride
 
 
-def time_launches(torch, launch, warmup, steps, batches=5):
-    """launch(i) enqueues call i.  The timed launches run back to back on the
-    stream in `batches` groups, each bracketed by its own pair of HIP events;
-    returns (wall seconds of all timed launches between two device
-    synchronizations, per-launch mean ms of each batch)."""
-    for i in range(warmup):
-        launch(i)
+def time_launches(torch, launch, warmup, steps, outs, batches=5):
+    """launch(i, stream) enqueues call i.  The warmup calls run eagerly; the
+    timed calls are captured as `batches` HIP graphs of back-to-back launches
+    (so host-side launch overhead cannot leave the GPU idle between them),
+    and each graph replay is bracketed by its own pair of HIP events on the
+    replay stream.  Returns (wall seconds of all timed launches between two
+    device synchronizations, per-launch mean ms of each batch, launches per
+    batch).  Afterwards the last graph's outputs (`outs`) are checked to be
+    bit-identical to an eager launch of the same call."""
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            launch(i, s.cuda_stream)
     torch.cuda.synchronize()
     per = max(1, steps // batches)
+    cnts = [per] * (batches - 1) + [steps - per * (batches - 1)]
+    graphs, n = [], warmup
+    for cnt in cnts:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            for k in range(cnt):
+                launch(n + k, s.cuda_stream)
+            g.capture_end()
+        graphs.append(g)
+        n += cnt
+    for g in graphs:  # first replays upload the graphs
+        g.replay()
+    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(batches)]
-    n = 0
     t0 = time.perf_counter()
-    for b in range(batches):
-        cnt = per if b < batches - 1 else steps - per * (batches - 1)
-        ev[b][0].record()
-        for _ in range(cnt):
-            launch(warmup + n)
-            n += 1
-        ev[b][1].record()
+    with torch.cuda.stream(s):
+        for b, g in enumerate(graphs):
+            ev[b][0].record()
+            g.replay()
+            ev[b][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    cnts = [per] * (batches - 1) + [steps - per * (batches - 1)]
+    got = [o.clone() for o in outs]
+    with torch.cuda.stream(s):
+        launch(n - 1, s.cuda_stream)
+    torch.cuda.synchronize()
+    for a, b in zip(got, outs):
+        if not torch.equal(a.view(torch.int32), b.view(torch.int32)):
+            raise RuntimeError("graph replay and eager launch of the same call differ")
     return wall, [a.elapsed_time(b) / c for (a, b), c in zip(ev, cnts)], cnts
 
 
@@ -130,7 +166,6 @@ def setup_workload(torch, dev, index, M):
     L = q4.lib()
     d = synth.workload_inputs(index, M=M)
     N, K = d["N"], d["K"]
-    stream = torch.cuda.current_stream(dev).cuda_stream
     keep = []
 
     def T(a):
@@ -147,14 +182,15 @@ def setup_workload(torch, dev, index, M):
         cks = torch.empty(N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
 
-        def launch(i):
+        def launch(i, stream):
             check(L.q4_0_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K, stream),
                   "q4_0_gemv")
 
-        def ceil_launch(i):
+        def ceil_launch(i, stream):
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4_0_GEMV, rot.ptr(i), None, None,
                                  M, 0, 0, N, K, stream), "q4_pure_read")
         keep += [rot, y, cks]
+        outs, couts = [y], [cks]
     elif index == 3:
         rot = Rotation(torch, dev, d["w"])
         g = T(d["gamma"])
@@ -162,14 +198,15 @@ def setup_workload(torch, dev, index, M):
         cks = torch.empty(N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
 
-        def launch(i):
+        def launch(i, stream):
             check(L.fused_rmsnorm_q4k_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), g.data_ptr(),
                                            d["eps"], M, N, K, stream), "fused_rmsnorm_q4k_gemv")
 
-        def ceil_launch(i):
+        def ceil_launch(i, stream):
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4K_GEMV, rot.ptr(i), None, None,
                                  M, 0, 0, N, K, stream), "q4_pure_read")
         keep += [rot, y, cks]
+        outs, couts = [y], [cks]
     elif index == 4:
         both = np.concatenate([d["w_gate"].reshape(-1), d["w_up"].reshape(-1)])
         rot = Rotation(torch, dev, both)
@@ -179,17 +216,18 @@ def setup_workload(torch, dev, index, M):
         cks = torch.empty(2 * N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
 
-        def launch(i):
+        def launch(i, stream):
             p = rot.ptr(i)
             check(L.fused_gate_up_q4k_gemv(gate.data_ptr(), up.data_ptr(), p, p + half,
                                            x.data_ptr(), M, N, K, stream),
                   "fused_gate_up_q4k_gemv")
 
-        def ceil_launch(i):
+        def ceil_launch(i, stream):
             p = rot.ptr(i)
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_GATE_UP, p, p + half, None, M, 0, 0,
                                  N, K, stream), "q4_pure_read")
         keep += [rot, gate, up, cks]
+        outs, couts = [gate, up], [cks]
     elif index == 5:
         E, top_k = d["E"], d["top_k"]
         both = np.concatenate([d["w_gate"].reshape(-1), d["w_up"].reshape(-1)])
@@ -205,24 +243,25 @@ def setup_workload(torch, dev, index, M):
         notes = dict(unique_experts=uniq, pairs=M * top_k,
                      pair_counted_bytes=M * top_k * per_expert)
 
-        def launch(i):
+        def launch(i, stream):
             p = rot.ptr(i)
             check(L.moe_q4_gemv(gate.data_ptr(), up.data_ptr(), p, p + half, x.data_ptr(),
                                 ids.data_ptr(), M, top_k, E, N, K, stream), "moe_q4_gemv")
 
-        def ceil_launch(i):
+        def ceil_launch(i, stream):
             p = rot.ptr(i)
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_MOE, p, p + half, ids.data_ptr(), M,
                                  top_k, E, N, K, stream), "q4_pure_read")
         keep += [rot, gate, up, cks]
+        outs, couts = [gate, up], [cks]
     notes["copies"] = rot.ncopies
-    return wbytes, launch, ceil_launch, notes, keep
+    return wbytes, launch, ceil_launch, notes, keep, outs, couts
 
 
 def measure(torch, dev, index, M, warmup, steps):
-    wbytes, launch, ceil_launch, notes, keep = setup_workload(torch, dev, index, M)
-    wall, durs, cnts = time_launches(torch, launch, warmup, steps)
-    cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps)
+    wbytes, launch, ceil_launch, notes, keep, outs, couts = setup_workload(torch, dev, index, M)
+    wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
+    cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
     st, cst = stats(durs, cnts), stats(cdurs, ccnts)
     res = dict(index=index, M=M, weight_bytes=wbytes, wall_s=wall, steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
@@ -260,6 +299,51 @@ def cpu_baseline(seconds):
                        % (calls, el, nt))
 
 
+def source_sha256():
+    """Hash of the HIP sources and the C header the library is built from."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "bit_block_quantized_dequant_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".h", ".hip")))
+    files.append(os.path.join(ROOT, "include", "q4gemv.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != source_sha256():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev, mib):
+    """A plain device-to-device copy of known size, run 20 times."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copy calibration: %d launches, %d bytes read and %d bytes written per launch"
+          % (20, n * 4, n * 4), flush=True)
+
+
 def write_report(path, rows, headline):
     with open(path + ".json", "w") as f:
         json.dump(dict(headline=headline, workloads=rows), f, indent=1)
@@ -290,6 +374,9 @@ def main():
     q4.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        copy_calibration(torch, dev, args.copy_calibration)
+        return
 
     head = measure(torch, dev, 4, 1, args.warmup, args.steps)
     print("headline: kernel %.2f us (median %.2f), %.0f GB/s; ceiling %.0f GB/s; wall %.0f GB/s"
@@ -333,7 +420,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["frac_of_peak"], 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "kernel_us_mean": round(head["kernel"]["mean_ms"] * 1e3, 3),
             "kernel_us_median": round(head["kernel"]["median_ms"] * 1e3, 3),
         },

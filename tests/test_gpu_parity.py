@@ -470,3 +470,44 @@ def test_scaling_onehot_zero(dev, orc):
         z = empty((1, N), dev)
         f(z, wd, T(np.zeros((1, K), np.float32), dev), 1, N, K)
         assert np.all(host(z) == 0.0)
+
+
+def test_graph_replay_matches_eager(dev):
+    """The calls can be captured in a HIP graph (no allocation, no memset in
+    the library): every replay, with other eager work and synchronizations
+    between replays, equals the eager call bit for bit."""
+    import torch
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(35)
+    N, K = 1000, 4096
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    w0 = synth.q4_0_matrix(rng, N, K)
+    gam = synth.gamma(rng, K)
+    x = synth.activations(rng, 8, K)
+    wgd, wud, w0d, gd, xd = T(wg, dev), T(wu, dev), T(w0, dev), T(gam, dev), T(x, dev)
+    outs = {k: empty((8, N), dev) for k in ("g1", "u1", "n1", "k4", "q8")}
+
+    def calls(stream):
+        q4.fused_gate_up_q4k_gemv(outs["g1"], outs["u1"], wgd, wud, xd, 1, N, K, stream=stream)
+        q4.fused_rmsnorm_q4k_gemv(outs["n1"], wgd, xd, gd, 1e-5, 3, N, K, stream=stream)
+        q4.q4k_gemv(outs["k4"], wud, xd, 4, N, K, stream=stream)
+        q4.q4_0_gemv(outs["q8"], w0d, xd, 8, N, K, stream=stream)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        calls(s)
+    torch.cuda.synchronize()
+    want = {k: host(v).copy() for k, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        calls(s)
+        g.capture_end()
+    for rep in range(3):
+        for v in outs.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert_bits(host(v), want[k], "graph replay %d, %s" % (rep, k))
