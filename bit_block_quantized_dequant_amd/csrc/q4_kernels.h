@@ -123,7 +123,10 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
     if (store) xl[m * xrow_chunks(p.K) + xchunk(c >> 4, c & 15)] = v;
 }
 
-template <int FMT, int M, int MODE>
+// TAIL: the call may have more than kXReg chunks per thread (M * K > kXReg *
+// 4 * blockDim); kernels that cannot are compiled without the extra loops,
+// whose load waits would otherwise also cover the weight loads in flight.
+template <int FMT, int M, int MODE, bool TAIL>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage& st, float4* xl,
                                                float* xsum, float* red) {
     const int tid = threadIdx.x;
@@ -159,7 +162,8 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
             acc_sq(i < total ? v : z, min(i, total - 1));
         }
-        for (int i = tid + kXReg * bs; i < total; i += bs) acc_sq(x4[i], i);
+        if constexpr (TAIL)
+            for (int i = tid + kXReg * bs; i < total; i += bs) acc_sq(x4[i], i);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float v = group_total(ss[m], kWave);
@@ -194,10 +198,12 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         const int ic = min(i, total - 1);
         stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum);
     }
-    for (int i = tid + kXReg * bs; i < total; i += bs) {
-        float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-        if constexpr (MODE == kModeNorm) g = g4[i % kq];
-        stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
+    if constexpr (TAIL) {
+        for (int i = tid + kXReg * bs; i < total; i += bs) {
+            float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (MODE == kModeNorm) g = g4[i % kq];
+            stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
+        }
     }
 }
 
@@ -243,8 +249,12 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
     }
 }
 
-template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
+// XR: every lane works on one fixed unit of each row (M = 1, K <= 64 units of
+// 64 weights): its 64 activations and two run sums are copied from LDS into
+// registers once, and the main loop reads no LDS at all.
+template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, bool XR, bool TAIL>
+__device__ __forceinline__ void gemv_body(const GemvParams& p) {
+    static_assert(!XR || (M == 1 && MODE != kModeMoe), "register-resident x: M = 1 only");
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
     __shared__ float red[8 * 16];
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
     XStage xst;
     if constexpr (!PURE) stage_x_issue<MODE>(p, M, xst);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
-    if constexpr (!PURE) stage_x_finish<FMT, M, MODE>(p, xst, xl, xsum, red);
+    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL>(p, xst, xl, xsum, red);
     __syncthreads();
 
     if constexpr (MODE == kModeMoe) {
@@ -390,6 +400,16 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
         }
     }
     if (t0 >= t1) return;
+
+    // register-resident activations of this lane's unit (XR)
+    float4 xr[XR ? kUnitChunks - 1 : 1];
+    float2 xsr[1];
+    if constexpr (XR) {
+        const int uc = min(li, p.upr - 1);
+#pragma unroll
+        for (int c = 0; c < kUnitChunks - 1; ++c) xr[c] = xl[xchunk(uc, c)];
+        xsr[0] = ((const float2*)xsum)[uc];
+    }
 
     float acc[NR][M];
     uint32_t cks[NR];
@@ -429,6 +449,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
                 }
                 if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
             }
+        } else if constexpr (XR) {
+            rows_dot<FMT, M, NR>(w, 0, sel, xr, 0, xsr, 0, acc, act);
         } else {
             rows_dot<FMT, M, NR>(w, uc, sel, xl, kq, (const float2*)xsum, k64, acc, act);
         }
@@ -530,6 +552,19 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
             cb = ce;
         }
     }
+}
+
+template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, bool TAIL>
+__global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p) {
+    gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, false, TAIL>(p);
+}
+
+// The register-resident variant must fit 128 VGPRs: two 512-thread
+// workgroups per CU, as for the LDS variant.
+template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_kernel_xr(const GemvParams p) {
+    gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, true, false>(p);
 }
 
 // ---------------------------------------------------------------------------

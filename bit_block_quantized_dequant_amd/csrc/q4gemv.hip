@@ -107,6 +107,20 @@ int allow_big_lds(const void* kern, std::atomic<int>* done) {
     return Q4_OK;
 }
 
+// Workgroups of `kern` that can be resident on one CU at once (registers,
+// LDS and waves), from the runtime's occupancy calculator; cached per device.
+int resident_per_cu(const void* kern, int threads, size_t lds, std::atomic<int>* cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+    int v = cache[dev].load(std::memory_order_acquire);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds) != hipSuccess || n < 1)
+        n = 1;
+    cache[dev].store(n, std::memory_order_release);
+    return n;
+}
+
 template <typename Kern>
 int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
            std::atomic<int>* big_lds_done, int threads = kBlock) {
@@ -121,9 +135,10 @@ int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
 }
 
 // Fill the work-split fields of p for a call with `rows` rows per matrix
-// and RR rows per lane; returns the number of workgroups.
+// and RR rows per lane; returns the number of workgroups (at most `resident`
+// per CU, the kernel's occupancy limit).
 int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
-         int cus) {
+         int cus, int resident) {
     p.K = K;
     p.upr = K / kUnitElems;
     p.lg = p.upr >= kWave ? kWave : pow2ceil(p.upr);
@@ -141,7 +156,8 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
         tasks = p.ntasks;
     }
     const int wpb = kBlock / kWave;
-    const int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure));
+    int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure));
+    if (wgc > resident) wgc = resident;
     // Every CU gets the same number of workgroups (the per-CU load/issue rate
     // is shared by its waves); tasks are then split evenly over all waves.
     static const int bpc_override = env_int("Q4GEMV_BLOCKS_PER_CU", 0);
@@ -164,15 +180,48 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
 #define Q4_PREFETCH 1  // steps of weight loads in flight ahead of the computed one
 #endif
 
-template <int FMT, int NMAT, int MODE, bool PURE, int M>
-int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
+// Q4GEMV_XR=0 keeps the activations in LDS also where they fit in registers
+// (for comparisons).
+bool xr_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_XR");
+        return !(s && *s && atoi(s) == 0);
+    }();
+    return on;
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
+int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
     static std::atomic<int> big_lds_done[kMaxDevices];
+    static std::atomic<int> resident[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors
-    const int blocks = plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus);
+    auto kern = [](bool pure) {
+        if constexpr (XR)
+            return pure ? gemv_kernel_xr<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH>
+                        : gemv_kernel_xr<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH>;
+        else
+            return pure ? gemv_kernel<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, TAIL>
+                        : gemv_kernel<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, TAIL>;
+    };
+    const int res = resident_per_cu((const void*)kern(false), kBlock,
+                                    gemv_lds_bytes(M, p.K, false), resident);
+    const int blocks = plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res);
     const size_t lds = gemv_lds_bytes(M, p.K, PURE);
-    return launch(gemv_kernel<FMT, M, NMAT, RR, MODE, PURE, Q4_PREFETCH>, p, blocks, lds, stream,
-                  big_lds_done);
+    return launch(kern(PURE), p, blocks, lds, stream, big_lds_done);
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
+    if constexpr (M == 1 && MODE != kModeMoe) {
+        // one 64-weight unit per lane per row: K <= 64 * 64 (and then the
+        // activations need no staging loop beyond the first kXReg chunks)
+        if (p.K <= kWave * kUnitElems && xr_enabled())
+            return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
+    }
+    if ((long long)M * p.K > (long long)kXReg * 4 * kBlock)
+        return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
+    return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }
 
 // Matrix-core kernel: steps of weight loads each wave keeps in flight, and
@@ -222,7 +271,18 @@ int run_mfma_m(GemvParams& p, int cus, void* stream) {
     static std::atomic<int> big_lds_done[kMaxDevices];
     const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
     // a pure-read pass takes the launch shape of the call it mirrors
-    const int wgc = wg_per_cu((size_t)mlayout(FMT, M, p.K, false).bytes);
+    static std::atomic<int> resident[kMaxDevices];
+    const size_t call_lds = (size_t)mlayout(FMT, M, p.K, false).bytes;
+    int wgc = wg_per_cu(call_lds);
+    if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
+        static std::atomic<int> big_lds_mirror[kMaxDevices];
+        int st = allow_big_lds((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
+                               big_lds_mirror);
+        if (st) return st;
+    }
+    const int res = resident_per_cu((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
+                                    kMBlock, call_lds, resident);
+    if (wgc > res) wgc = res;
     const long long ntiles = (long long)NMAT * ((p.N + 15) / 16);
     p.ks = mfma_ks(ntiles, p.K / (FMT == kFmtQ4K ? 256 : 128), cus);
     const int TG = kMWaves / p.ks;

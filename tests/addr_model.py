@@ -40,8 +40,9 @@ def unit_off(fmt, u):
 
 
 def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
-    """Yield (matrix, byte offset, nbytes) of every load; moe_experts is the
-    list of unique valid experts the in-kernel dedupe would produce."""
+    """Yield (matrix, byte offset, nbytes) of every load (a superset: each
+    visited cursor in its normal and its idle form); moe_experts is the list
+    of unique valid experts the in-kernel dedupe would produce."""
     moe = moe_experts is not None
     pl = plan(M, K, N, RR, moe, kw.get("npairs_max", 1), **{k: v for k, v in kw.items()
                                                              if k in ("cus", "bpc")})
@@ -101,6 +102,11 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
                             yield mt, sbase + ((ro + uoff) & U32), 16
                             yield mt, sbase + ((ro + uoff) & U32) + 16, 16
                             yield mt, sbase + ((ro + uoff) & U32) + 32, 4
+                        # idle form of the same cursor (loads past the wave's
+                        # last step): every lane reads the task's first bytes
+                        yield mt, sbase, 16
+                        yield mt, sbase + 16, 16
+                        yield mt, sbase + 32, 16 if fmt == "q4k" else 4
 
 
 def check(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
