@@ -20,23 +20,24 @@
 //   * Each lane's D values belong to its own weight row j, so the block
 //     scales are applied in the lane that loaded them:
 //       Q4_0 (w = d (q - 8)):        y += d * (D - 8 X)
-//       Q4_K (w = d sc q - dmin m):  y += d * sum_J sc_J D_J - dmin * Dmin,
-//     X being block sums of x; Dmin = sum_J m_J X_J is one more MFMA per
-//     super-block with the sub-block sums as A and the 6-bit mins as B.
+//       Q4_K (w = d sc q - dmin m):  y += d * D - dmin * Dmin, where the
+//     6-bit sub-block scales are folded into B (an f16 multiply of the
+//     subnormal nibble by sc is exact), so one accumulation runs over all
+//     sub-blocks; X are block sums of x, and Dmin = sum_J m_J X_J is one
+//     more MFMA per super-block with the sub-block sums as A and the 6-bit
+//     mins as B.
 //   (Q4_0 layout: inferencelayer 0.2.13, src/bin/kernel_lab.rs, GEMV_F16S;
 //    Q4_K layout: trueno-gpu 0.4.11, src/kernels/quantize/fused.rs,
 //    FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3.)
 //
 // Fragment order.  The 8 k-slots t of lane group c come from 4 nibble
 // bytes of each of 2 dwords as (byte 0, 2, 1, 3) -- a mask of the dword and
-// a mask of the dword shifted by 8 -- so slot t holds byte slot_byte(t):
-//   Q4_K sub-block J, group c:  bytes 8c..8c+7 of 64-element chunk J/2
-//                               (low nibbles for even J, high for odd J)
-//   Q4_0 block, group c:        bytes 8(c&1)..+7, low nibbles for c < 2
-//                               (elements 8c..), high for c >= 2
-// In both formats the 8 elements of (32-group g, lane group c) are the
-// consecutive elements 8p..8p+7 with p = 4g + c, and the A fragment of that
-// "piece" p sits in LDS at (p * 2M + i) * 16 bytes.
+// a mask of the dword shifted by 8 -- so slot t holds byte slot_byte(t) of
+// an 8-byte slice; the 8 elements are the consecutive elements 8p .. 8p+7
+// of one "piece" p, whose A fragment sits in LDS at (p * 2M + i) * 16 bytes.
+//   Q4_0 block b, group c:  bytes 8(c&1) .. of its nibbles, low nibbles for
+//                           c < 2 (elements 8c ..), high for c >= 2: p = 4b + c
+//   Q4_K: see compute() (a lane's slices come from 16-byte loads).
 //
 // Work split.  A tile is 16 rows of one matrix.  A workgroup is 8 waves in
 // groups of KS; each group takes one tile per round and its KS waves split
@@ -295,16 +296,16 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         const uint32_t lr = (uint32_t)min(jrow, p.N - 1 - row0);
         const uint32_t off = idle ? 0u : lr * rb + (uint32_t)st * St::kBytes;
         if constexpr (FMT == kFmtQ4K) {
-            const uint32_t co = idle ? 0u : 8u * (uint32_t)c;
+            // header, then 16 bytes of each 64-byte half of the nibbles:
+            // lane group c takes bytes 16c .. 16c+15 of half h (chunk 2h +
+            // c/2, bytes 16(c&1) ..)
+            const uint32_t co = idle ? 0u : 16u * (uint32_t)c;
             const u32x4 h = ldg16(base + off);
+            const u32x4 q0 = ldg16(base + off + co + 16);
+            const u32x4 q1 = ldg16(base + off + co + 80);
             w.v[0] = h.x; w.v[1] = h.y; w.v[2] = h.z; w.v[3] = h.w;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t* q =
-                    (const uint32_t*)__builtin_assume_aligned(base + off + co + 16 + 32 * g, 8);
-                w.v[4 + 2 * g] = q[0];
-                w.v[5 + 2 * g] = q[1];
-            }
+            w.v[4] = q0.x; w.v[5] = q0.y; w.v[6] = q0.z; w.v[7] = q0.w;
+            w.v[8] = q1.x; w.v[9] = q1.y; w.v[10] = q1.z; w.v[11] = q1.w;
         } else {
             // per block pair (36 bytes, words 0..8): words 2h..2h+2 hold the
             // lane's bytes of block A, words 5+2h..6+2h those of block B, and
@@ -330,38 +331,61 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     auto compute = [&](const WR& w, int st, float2& y) {
         if constexpr (FMT == kFmtQ4K) {
+            // Lane group c holds, of half h (h = 0, 1), the 16 bytes
+            // 16(c&1) .. of chunk g = 2h + c/2: low nibbles of sub-block
+            // J = 2g, high nibbles of J = 2g + 1.  MFMA (h, n, s) takes the
+            // nibbles n of bytes 8s .. 8s+7 (s = 0, 1): piece
+            // p = 8g + 4n + 2(c&1) + s of the row.  The sub-block scale goes
+            // into B: (q * 2^-24) * sc is the exact subnormal q*sc*2^-24
+            // (q*sc <= 945), and for an in-place high nibble
+            // (16q * 2^-24) * sc is exact too (its A piece carries 2^-4).
             const uint32_t h1 = w.v[1], h2 = w.v[2], h3 = w.v[3];
-            const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;
-            const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
-            float scf[8];  // (v_cvt_f32_ubyte0..3)
+            const uint32_t qq = (uint32_t)(c >> 1);
+            const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;  // sub-blocks 0..3
+            const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);  // 4..7
+            // scales of sub-blocks 2g, 2g + 1 for g = qq (half 0) and 2 + qq
+            // (half 1), each as an f16 pair (sc, sc)
+            uint32_t scp[2][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                scf[j] = (float)((sc_lo >> (8 * j)) & 0xFFu);
-                scf[4 + j] = (float)((sc_hi >> (8 * j)) & 0xFFu);
-            }
-            f4 acc = (f4)(0.f);
-            const int pbase = st * 32 + c;
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint32_t sb = (hh ? sc_hi : sc_lo) >> (16u * qq);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t d0 = w.v[4 + 2 * g], d1 = w.v[5 + 2 * g];
-                const uint32_t d08 = d0 >> 8, d18 = d1 >> 8;
-                const u32x4m blo = {d0 & 0x000F000Fu, d08 & 0x000F000Fu, d1 & 0x000F000Fu,
-                                    d18 & 0x000F000Fu};
-                const u32x4m bhi = {d0 & 0x00F000F0u, d08 & 0x00F000F0u, d1 & 0x00F000F0u,
-                                    d18 & 0x00F000F0u};
-                const f4 Dl = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    afrag(pbase + 8 * g), __builtin_bit_cast(h8, blo), (f4)(0.f), 0, 0, 0);
-                const f4 Dh = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    afrag(pbase + 8 * g + 4), __builtin_bit_cast(h8, bhi), (f4)(0.f), 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc[r] = __builtin_fmaf(scf[2 * g], Dl[r], acc[r]);
-                    acc[r] = __builtin_fmaf(scf[2 * g + 1], Dh[r], acc[r]);
+                for (int n = 0; n < 2; ++n) {
+                    const float f = (float)((sb >> (8 * n)) & 0xFFu);
+                    scp[hh][n] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f, f));
                 }
             }
-            uint32_t scp, mp;
-            q4k_scale_pairs(h1, h2, h3, q4k_sel(c), scp, mp);
-            (void)scp;
+            typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+            auto pmul = [](uint32_t a, uint32_t b) {
+                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, a) *
+                                                        __builtin_bit_cast(h2v, b));
+            };
+            f4 acc0 = (f4)(0.f), acc1 = (f4)(0.f);
+            const int pbase = st * 32 + 8 * (int)qq + 2 * (c & 1);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int sidx = 0; sidx < 2; ++sidx) {
+                    const uint32_t d0 = w.v[4 + 4 * hh + 2 * sidx], d1 = w.v[5 + 4 * hh + 2 * sidx];
+                    const uint32_t d08 = d0 >> 8, d18 = d1 >> 8;
+                    const u32x4m blo = {pmul(d0 & 0x000F000Fu, scp[hh][0]),
+                                        pmul(d08 & 0x000F000Fu, scp[hh][0]),
+                                        pmul(d1 & 0x000F000Fu, scp[hh][0]),
+                                        pmul(d18 & 0x000F000Fu, scp[hh][0])};
+                    const u32x4m bhi = {pmul(d0 & 0x00F000F0u, scp[hh][1]),
+                                        pmul(d08 & 0x00F000F0u, scp[hh][1]),
+                                        pmul(d1 & 0x00F000F0u, scp[hh][1]),
+                                        pmul(d18 & 0x00F000F0u, scp[hh][1])};
+                    const int pp = pbase + 16 * hh + sidx;
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        afrag(pp), __builtin_bit_cast(h8, blo), acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        afrag(pp + 4), __builtin_bit_cast(h8, bhi), acc1, 0, 0, 0);
+                }
+            }
+            uint32_t scq, mp;
+            q4k_scale_pairs(h1, h2, h3, q4k_sel(c), scq, mp);
+            (void)scq;
             const uint32_t am =
                 *(const uint32_t*)(lds + ly.aux + ((st * 4 + c) * 2 * M + i_lane) * 4);
             const u32x4m amin = {am, 0u, 0u, 0u};
@@ -371,7 +395,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             const float d = h_lo(w.v[0]), dmin32 = h_hi(w.v[0]) * 32.0f;
             f4 t;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = __builtin_fmaf(-dmin32, Dm[r], d * acc[r]);
+            for (int r = 0; r < 4; ++r) t[r] = __builtin_fmaf(-dmin32, Dm[r], d * (acc0[r] + acc1[r]));
             y.x += t[0] + t[1];
             y.y += t[2] + t[3];
         } else {

@@ -227,7 +227,7 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
 // Matrix-core kernel: steps of weight loads each wave keeps in flight, and
 // the number of waves per CU the K split aims for.
 #ifndef Q4_MFMA_PD_Q4K
-#define Q4_MFMA_PD_Q4K 4
+#define Q4_MFMA_PD_Q4K 2
 #endif
 #ifndef Q4_MFMA_PD_Q4_0
 #define Q4_MFMA_PD_Q4_0 6

@@ -170,7 +170,7 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
     """Yield (matrix, byte offset, nbytes) of every weight load."""
     pl = mfma_plan(fmt, M, K, N, nmat, cus)
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
-    SB, PD = (144, 4) if fmt == "q4k" else (72, 6)
+    SB, PD = (144, 2) if fmt == "q4k" else (72, 6)
     S, KS = pl["steps"], pl["KS"]
     tpm = (N + 15) // 16
     ntiles, TG, G = pl["ntiles"], pl["TG"], pl["blocks"]
@@ -191,10 +191,10 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
                     lr = min(jrow, N - 1 - row0) & U32
                     off = 0 if idle else (lr * rb + st * SB) & U32
                     if fmt == "q4k":
-                        co = 0 if idle else 8 * c
+                        co = 0 if idle else 16 * c
                         yield mt, base + off, 16
-                        for g in range(4):
-                            yield mt, base + off + co + 16 + 32 * g, 8
+                        yield mt, base + off + co + 16, 16
+                        yield mt, base + off + co + 80, 16
                     else:
                         h8o = 0 if idle else 8 * (c & 1)
                         zo = 0 if idle else 16 - 2 * h8o
@@ -249,7 +249,9 @@ def mfma_lds_check(fmt, M, K):
             jrow, c = lane & 15, lane >> 4
             i = min(jrow, 2 * M - 1)
             if fmt == "q4k":
-                pps = [st * 32 + 8 * g + c + 4 * hi for g in range(4) for hi in range(2)]
+                pb = st * 32 + 8 * (c >> 1) + 2 * (c & 1)
+                pps = [pb + 16 * h + s + 4 * n for h in range(2) for s in range(2)
+                       for n in range(2)]
                 o = ly["aux"] + ((st * 4 + c) * 2 * M + i) * 4
                 assert o + 4 <= ly["exps"]
                 assert o in aux_w and o + 2 in aux_w
