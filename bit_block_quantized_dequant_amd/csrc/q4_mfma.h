@@ -34,7 +34,7 @@
 // bytes of each of 2 dwords as (byte 0, 2, 1, 3) -- a mask of the dword and
 // a mask of the dword shifted by 8 -- so slot t holds byte slot_byte(t) of
 // an 8-byte slice; the 8 elements are the consecutive elements 8p .. 8p+7
-// of one "piece" p, whose A fragment sits in LDS at (p * 2M + i) * 16 bytes.
+// of one "piece" p, whose A fragment for row i sits in LDS slot fslot(i, p).
 //   Q4_0 block b, group c:  bytes 8(c&1) .. of its nibbles, low nibbles for
 //                           c < 2 (elements 8c ..), high for c >= 2: p = 4b + c
 //   Q4_K: see compute() (a lane's slices come from 16-byte loads).
@@ -74,7 +74,7 @@ struct MStep {
 
 // LDS map (bytes) for M tokens and K columns.
 struct MLayout {
-    int frag;  // A fragments: (K/8) pieces x 2M rows x 16 bytes
+    int frag;  // A fragments: 2M rows x (K/8 + 1) pieces x 16 bytes (see fslot)
     int aux;   // Q4_K: Dmin A operand, (K/256) x 4 groups x 2M rows x 2 halves
                // Q4_0: block sums X, (K/32) blocks x 8 tokens x fp32
     int exps;  // e_m, 8 ints (padded to 64 bytes)
@@ -85,12 +85,18 @@ struct MLayout {
 __host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
     MLayout l;
     l.frag = 0;
-    l.aux = pure ? 0 : (K / 8) * 2 * M * 16;
+    l.aux = pure ? 0 : (K / 8 + 1) * 2 * M * 16;
     l.exps = l.aux + (pure ? 0 : (fmt == kFmtQ4K ? (K / 256) * 4 * 2 * M * 4 : (K / 32) * 8 * 4));
     l.part = l.exps + 64;
     l.bytes = l.part + 2 * kMWaves * 64 * 8;
     return l;
 }
+
+// 16-byte slot of the A fragment of piece p, row i: rows of K/8 + 1 slots.
+// The odd row length puts the rows a lane group reads 4 banks apart (all 64
+// banks for 16 rows), and the staging writes consecutive pieces of a row
+// to consecutive slots; both are free of bank conflicts.
+__device__ __forceinline__ int fslot(int K, int i, int p) { return i * ((K >> 3) + 1) + p; }
 
 __device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-126, 127]
     return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
@@ -226,8 +232,8 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         part = dpp_add(part, 0);
         part = dpp_add(part, 1);
         if (valid(k)) {
-            *(h8*)(lds + ly.frag + (pp * 2 * M + 2 * m) * 16) = hi;
-            *(h8*)(lds + ly.frag + (pp * 2 * M + 2 * m + 1) * 16) = lo;
+            *(h8*)(lds + ly.frag + fslot(p.K, 2 * m, pp) * 16) = hi;
+            *(h8*)(lds + ly.frag + fslot(p.K, 2 * m + 1, pp) * 16) = lo;
             if ((pp & 3) == 0) {
                 const int g32 = pp >> 2;  // Q4_0 block / Q4_K sub-block index
                 if constexpr (FMT == kFmtQ4_0) {
@@ -327,7 +333,8 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     // A fragment of piece pp for this lane (rows i >= 2M repeat row 2M-1)
     const int i_lane = min(jrow, 2 * M - 1);
-    auto afrag = [&](int pp) { return *(const h8*)(lds + ly.frag + (pp * 2 * M + i_lane) * 16); };
+    const char* arow = lds + ly.frag + fslot(p.K, i_lane, 0) * 16;
+    auto afrag = [&](int pp) { return *(const h8*)(arow + pp * 16); };
 
     auto compute = [&](const WR& w, int st, float2& y) {
         if constexpr (FMT == kFmtQ4K) {

@@ -230,7 +230,7 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
 #define Q4_MFMA_PD_Q4K 2
 #endif
 #ifndef Q4_MFMA_PD_Q4_0
-#define Q4_MFMA_PD_Q4_0 6
+#define Q4_MFMA_PD_Q4_0 3
 #endif
 #ifndef Q4_MFMA_WAVES_PER_CU
 #define Q4_MFMA_WAVES_PER_CU 8

@@ -128,7 +128,7 @@ LDS_CAP = 160 * 1024 - 2048  # dynamic LDS a kernel may ask for
 
 def mlayout(fmt, M, K, pure=False):
     """Byte offsets of the kernel's LDS regions (mlayout() in q4_mfma.h)."""
-    aux = 0 if pure else (K // 8) * 2 * M * 16
+    aux = 0 if pure else (K // 8 + 1) * 2 * M * 16
     aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k" else (K // 32) * 8 * 4)
     exps = aux + aux_bytes
     part = exps + 64
@@ -170,7 +170,7 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
     """Yield (matrix, byte offset, nbytes) of every weight load."""
     pl = mfma_plan(fmt, M, K, N, nmat, cus)
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
-    SB, PD = (144, 2) if fmt == "q4k" else (72, 6)
+    SB, PD = (144, 2) if fmt == "q4k" else (72, 3)
     S, KS = pl["steps"], pl["KS"]
     tpm = (N + 15) // 16
     ntiles, TG, G = pl["ntiles"], pl["TG"], pl["blocks"]
@@ -227,7 +227,7 @@ def mfma_lds_check(fmt, M, K):
     for m in range(M):
         for pp in range(ppt):
             for h in range(2):
-                o = (pp * 2 * M + 2 * m + h) * 16
+                o = ((2 * m + h) * (K // 8 + 1) + pp) * 16
                 assert ly["frag"] <= o and o + 16 <= ly["aux"]
                 frag_w.add(o)
             if pp & 3 == 0:
@@ -268,7 +268,7 @@ def mfma_lds_check(fmt, M, K):
                             if 2 * c + hm < M:
                                 assert o + 4 * hm in aux_w
             for pp in pps:
-                o = (pp * 2 * M + i) * 16
+                o = (i * (K // 8 + 1) + pp) * 16
                 assert o + 16 <= ly["aux"] and o in frag_w
     assert ly["part"] + 2 * 8 * 64 * 8 == ly["bytes"]
     return True
