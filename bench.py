@@ -12,7 +12,8 @@ per call), timed over --steps calls after --warmup untimed calls.
                replays of HIP graphs of back-to-back launches (no host gaps),
                against the 8 TB/s HBM3E peak
   pure_read    the same for the pure-read ceiling kernel (same bytes, same
-               addressing, no arithmetic)
+               addressing, no arithmetic) and for the reference stream (the
+               same byte count read as contiguous rows)
   cpu_baseline the CPU oracle (plain C, float64) timed on this host's cores on
                a bounded sample of the same workload
 
@@ -157,14 +158,14 @@ def check(status, what):
 # ---------------------------------------------------------------------------
 # workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
 # ---------------------------------------------------------------------------
-def setup_workload(torch, dev, index, M):
+def setup_workload(torch, dev, index, M, distinct=False):
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
     from bit_block_quantized_dequant_amd import synth
 
     L = q4.lib()
-    d = synth.workload_inputs(index, M=M)
+    d = synth.workload_inputs(index, M=M, distinct=distinct)
     N, K = d["N"], d["K"]
     keep = []
 
@@ -255,21 +256,34 @@ def setup_workload(torch, dev, index, M):
         keep += [rot, gate, up, cks]
         outs, couts = [gate, up], [cks]
     notes["copies"] = rot.ncopies
-    return wbytes, launch, ceil_launch, notes, keep, outs, couts
+    # reference stream: the same byte count as contiguous rows of K * 9/16 bytes
+    srb = synth.q4k_row_bytes(K)
+    srows = wbytes // srb
+    scks = torch.empty(srows, dtype=torch.int32, device=dev)
+    keep.append(scks)
+
+    def stream_launch(i, stream):
+        check(L.q4_pure_read(scks.data_ptr(), q4.Q4_READ_STREAM, rot.ptr(i), None, None, 1, 0, 0,
+                             srows, K, stream), "q4_pure_read")
+    return wbytes, launch, ceil_launch, notes, keep, outs, couts, (stream_launch, [scks])
 
 
-def measure(torch, dev, index, M, warmup, steps):
-    wbytes, launch, ceil_launch, notes, keep, outs, couts = setup_workload(torch, dev, index, M)
+def measure(torch, dev, index, M, warmup, steps, distinct=False):
+    (wbytes, launch, ceil_launch, notes, keep, outs, couts,
+     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct)
     wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
     cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
-    st, cst = stats(durs, cnts), stats(cdurs, ccnts)
-    res = dict(index=index, M=M, weight_bytes=wbytes, wall_s=wall, steps=steps,
+    swall, sdurs, scnts = time_launches(torch, stream_launch, warmup, steps, souts)
+    st, cst, sst = stats(durs, cnts), stats(cdurs, ccnts), stats(sdurs, scnts)
+    res = dict(index=index, M=M, distinct=distinct, weight_bytes=wbytes, wall_s=wall, steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
                kernel=st, kernel_gbs=wbytes / (st["mean_ms"] * 1e-3) / 1e9,
                kernel_gbs_median=wbytes / (st["median_ms"] * 1e-3) / 1e9,
-               ceiling=cst, ceiling_gbs=wbytes / (cst["mean_ms"] * 1e-3) / 1e9, **notes)
+               ceiling=cst, ceiling_gbs=wbytes / (cst["mean_ms"] * 1e-3) / 1e9,
+               stream=sst, stream_gbs=wbytes / (sst["mean_ms"] * 1e-3) / 1e9, **notes)
     res["frac_of_peak"] = res["kernel_gbs"] / HBM_PEAK_GBS
     res["frac_of_ceiling"] = res["kernel_gbs"] / res["ceiling_gbs"]
+    res["frac_of_stream"] = res["kernel_gbs"] / res["stream_gbs"]
     del keep
     torch.cuda.empty_cache()
     return res
@@ -293,10 +307,15 @@ def cpu_baseline(seconds):
         el = time.perf_counter() - t0
         if el >= seconds or calls >= 1000:
             break
+    t1 = time.perf_counter()
+    o.gate_up_q4k_gemv(d["w_gate"], d["w_up"], d["x"], N, K, 1)
+    one = time.perf_counter() - t1
     return dict(value=wbytes * calls / el / 1e9, unit="GB/s", cores=nt, kind="oracle",
+                single_thread_value=wbytes / one / 1e9,
                 sample="%d full calls of the oracle's gate+up Q4_K GEMV (M=1, K=4096, "
-                       "N=14336x2; float64 accumulation) in %.1f s on %d threads"
-                       % (calls, el, nt))
+                       "N=14336x2; float64 accumulation) in %.1f s on %d threads; "
+                       "single_thread_value: one full call on 1 thread (%.2f s)"
+                       % (calls, el, nt, one))
 
 
 def source_sha256():
@@ -351,12 +370,19 @@ def write_report(path, rows, headline):
              3: "fused_rmsnorm_q4k_gemv K=3584 N=18944", 4: "fused_gate_up_q4k_gemv K=4096 N=14336x2",
              5: "moe_q4_gemv E=64 top6 N=1408 K=2048"}
     lines = ["| workload | M | weight MB | kernel us (median) | GB/s (mean dur) | % of 8 TB/s | "
-             "ceiling GB/s | % of ceiling | spread |", "|---|---|---|---|---|---|---|---|---|"]
+             "ceiling GB/s | % of ceiling | stream GB/s | % of stream | spread |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append("| %s | %d | %.2f | %.2f | %.0f | %.1f%% | %.0f | %.1f%% | %.2f |" % (
-            names[r["index"]], r["M"], r["weight_bytes"] / 1e6, r["kernel"]["median_ms"] * 1e3,
-            r["kernel_gbs"], 100 * r["frac_of_peak"], r["ceiling_gbs"],
-            100 * r["frac_of_ceiling"], r["kernel"]["spread"]))
+        name = names[r["index"]]
+        if r["index"] == 5:
+            name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
+                                           r["unique_experts"])
+        lines.append("| %s | %d | %.2f | %.2f | %.0f | %.1f%% | %.0f | %.1f%% | %.0f | %.1f%% | "
+                     "%.2f |" % (
+                         name, r["M"], r["weight_bytes"] / 1e6, r["kernel"]["median_ms"] * 1e3,
+                         r["kernel_gbs"], 100 * r["frac_of_peak"], r["ceiling_gbs"],
+                         100 * r["frac_of_ceiling"], r["stream_gbs"], 100 * r["frac_of_stream"],
+                         r["kernel"]["spread"]))
     with open(path + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -386,14 +412,17 @@ def main():
 
     rows = []
     if args.all:
-        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 2, 4, 8)), (5, (4,))):
+        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 2, 4, 8)), (5, (4,)),
+                          (-5, (4,))):
             for M in Ms:
-                r = measure(torch, dev, index, M, args.warmup, args.steps)
+                r = measure(torch, dev, abs(index), M, args.warmup, args.steps, index < 0)
                 rows.append(r)
-                print("workload %d M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of ceiling)"
-                      % (index, M, r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
-                         100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"]),
-                      file=sys.stderr, flush=True)
+                print("workload %d%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
+                      "ceiling, %.1f%% of stream)"
+                      % (abs(index), " distinct" if index < 0 else "", M,
+                         r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
+                         100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
+                         100 * r["frac_of_stream"]), file=sys.stderr, flush=True)
 
     cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -428,6 +457,8 @@ def main():
             "achieved": round(head["ceiling_gbs"], 2),
             "unit": "GB/s",
             "kernel_frac_of_ceiling": round(head["frac_of_ceiling"], 4),
+            "stream_achieved": round(head["stream_gbs"], 2),
+            "kernel_frac_of_stream": round(head["frac_of_stream"], 4),
         },
         "cpu_baseline": cpu,
     }

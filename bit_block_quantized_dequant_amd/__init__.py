@@ -20,7 +20,8 @@ __all__ = [
     "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "moe_q4_gemv", "dequant_q4k",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
-    "Q4_READ_GATE_UP", "Q4_READ_MOE", "LIB_PATH", "q4_0_row_bytes", "q4k_row_bytes",
+    "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "LIB_PATH", "q4_0_row_bytes",
+    "q4k_row_bytes",
 ]
 
 # Q4GEMV_LIB may name another build of the same library (e.g. a tuning variant).
@@ -31,6 +32,7 @@ Q4_READ_Q4_0_GEMV = 0
 Q4_READ_Q4K_GEMV = 1
 Q4_READ_GATE_UP = 2
 Q4_READ_MOE = 3
+Q4_READ_STREAM = 4
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_BATCH", 4: "Q4_ERR_ALIGN",
           5: "Q4_ERR_ARG", 6: "Q4_ERR_HIP"}
@@ -206,6 +208,8 @@ def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=Non
     if kernel_id == Q4_READ_MOE:
         rows, nmat, rb = E * N, 2, q4_0_row_bytes(K)
         ncks = 2 * M * top_k * N
+    elif kernel_id == Q4_READ_STREAM:
+        rows, nmat, rb, ncks = N, 1, q4k_row_bytes(K), N
     else:
         nmat = 2 if kernel_id == Q4_READ_GATE_UP else 1
         rb = q4_0_row_bytes(K) if kernel_id == Q4_READ_Q4_0_GEMV else q4k_row_bytes(K)

@@ -568,6 +568,39 @@ void gemv_kernel_xr(const GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Reference stream: rows of rb bytes (a multiple of 16) read front to back,
+// one row per wave at a time in contiguous 16-byte-per-lane instructions,
+// rows strided over all waves; writes each row's word checksum.  Loads are
+// unconditional (lanes past the row end re-read its last 16 bytes and drop
+// them).
+// ---------------------------------------------------------------------------
+constexpr int kStreamBlock = 256;
+
+__global__ __launch_bounds__(kStreamBlock) void stream_read_kernel(uint32_t* __restrict__ cks,
+                                                                   const uint8_t* __restrict__ w,
+                                                                   int nrows, int rb) {
+    const int lane = threadIdx.x & 63;
+    const int gw =
+        __builtin_amdgcn_readfirstlane(blockIdx.x * (kStreamBlock / kWave) + (threadIdx.x >> 6));
+    const int nw = gridDim.x * (kStreamBlock / kWave);
+    const int nch = rb >> 4;                // 16-byte chunks per row
+    const int nins = (nch + kWave - 1) / kWave;
+    for (int r = gw; r < nrows; r += nw) {
+        const uint8_t* row = w + (long long)r * rb;
+        uint32_t s = 0;
+#pragma unroll 4
+        for (int n = 0; n < nins; ++n) {
+            const int c = n * kWave + lane;
+            const u32x4 v = ldg16(row + min(c, nch - 1) * 16);
+            const uint32_t t = v.x + v.y + v.z + v.w;
+            s += c < nch ? t : 0u;
+        }
+        s = group_total(s, kWave);
+        if (lane == kWave - 1) cks[r] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dequantization: one lane per 64-weight unit, writing 16 float4.
 // Q4_K: w = fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are exact in fp32 (at
 // most 17 significant bits), so the single rounding of the fma gives the

@@ -461,8 +461,25 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream) 
 int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
                  const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
                  void* stream) {
-    if (kernel_id < Q4_READ_Q4_0_GEMV || kernel_id > Q4_READ_MOE) return Q4_ERR_ARG;
+    if (kernel_id < Q4_READ_Q4_0_GEMV || kernel_id > Q4_READ_STREAM) return Q4_ERR_ARG;
     if (!checksum || !w0) return Q4_ERR_NULL;
+    if (kernel_id == Q4_READ_STREAM) {
+        if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+        if (K / 256 * kQ4KBytes > INT32_MAX / 2) return Q4_ERR_SHAPE;
+        if (!aligned(w0, 16) || !aligned(checksum, 4)) return Q4_ERR_ALIGN;
+        int cus = 0;
+        int st = device_cus(&cus);
+        if (st) return st;
+        static std::atomic<int> resident[kMaxDevices];
+        const int res = resident_per_cu((const void*)stream_read_kernel, kStreamBlock, 0, resident);
+        long long blocks = (long long)cus * res;
+        const long long need = (N + kStreamBlock / kWave - 1) / (kStreamBlock / kWave);
+        if (blocks > need) blocks = need;
+        hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kStreamBlock), 0,
+                           (hipStream_t)stream, checksum, (const uint8_t*)w0, (int)N,
+                           (int)(K / 256 * kQ4KBytes));
+        return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+    }
     if ((kernel_id == Q4_READ_GATE_UP || kernel_id == Q4_READ_MOE) && !w1) return Q4_ERR_NULL;
     if (kernel_id == Q4_READ_MOE && !ids) return Q4_ERR_NULL;
     int st = kernel_id == Q4_READ_MOE ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K);

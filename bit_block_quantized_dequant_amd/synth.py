@@ -86,6 +86,11 @@ def expert_ids(rng, M: int, top_k: int, E: int) -> np.ndarray:
     return np.stack([rng.choice(E, size=top_k, replace=False) for _ in range(M)]).astype(np.int32)
 
 
+def expert_ids_distinct(rng, M: int, top_k: int, E: int) -> np.ndarray:
+    """All M * top_k ids distinct (every pair reads its own expert)."""
+    return rng.choice(E, size=M * top_k, replace=False).reshape(M, top_k).astype(np.int32)
+
+
 def q4_0_row_bytes(K: int) -> int:
     return (K // 32) * 18
 
@@ -108,10 +113,11 @@ WORKLOADS = {
 }
 
 
-def workload_inputs(index: int, M: int = None, rows: int = None) -> dict:
+def workload_inputs(index: int, M: int = None, rows: int = None, distinct: bool = False) -> dict:
     """Inputs of workload `index` (1..5) at batch M; `rows` < N draws only the
     first rows of every matrix (the same bytes the full draw would not give, so
-    use it only where a reduced problem is wanted)."""
+    use it only where a reduced problem is wanted).  For workload 5,
+    distinct=True replaces the ids by a draw of M * top_k distinct experts."""
     wl = WORKLOADS[index]
     M = wl["M"][0] if M is None else M
     N = wl["N"] if rows is None else rows
@@ -138,4 +144,6 @@ def workload_inputs(index: int, M: int = None, rows: int = None) -> dict:
         out["w_up"] = q4_0_matrix(rng, E * N, K)
         out["x"] = activations(rng, M, K)
         out["ids"] = expert_ids(rng, M, wl["top_k"], E)
+        if distinct:  # drawn after the primary ids, so the weights are the same
+            out["ids"] = expert_ids_distinct(rng, M, wl["top_k"], E)
     return out

@@ -159,6 +159,12 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream);
  *   Q4_READ_Q4K_GEMV    w0: Q4_K [N, K]                     [N]
  *   Q4_READ_GATE_UP     w0, w1: Q4_K [N, K] each            [2, N]  (w0 rows, then w1)
  *   Q4_READ_MOE         w0, w1: Q4_0 experts as moe_q4_gemv [2, M, top_k, N]
+ *   Q4_READ_STREAM      w0: N rows of K*9/16 bytes          [N]
+ *
+ * Q4_READ_STREAM is the reference "ideal" stream of the same byte count as
+ * a GEMV of N rows and K columns (both formats use 9/16 byte per weight):
+ * each wave reads whole rows front to back in contiguous 1 KiB
+ * instructions, rows in a strided order over all waves.  M is ignored.
  *
  * M selects the launch shape of the mirrored call (and, for Q4_READ_MOE,
  * the number of tokens); ids, top_k and E are used by Q4_READ_MOE only
@@ -169,7 +175,8 @@ enum {
     Q4_READ_Q4_0_GEMV = 0,
     Q4_READ_Q4K_GEMV = 1,
     Q4_READ_GATE_UP = 2,
-    Q4_READ_MOE = 3
+    Q4_READ_MOE = 3,
+    Q4_READ_STREAM = 4
 };
 int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
                  const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,

@@ -138,6 +138,12 @@ def test_pure_read_validation(q4lib):
     assert f(A, 1, A, None, None, 1, 0, 0, 16, 300, None) == SHAPE
     assert f(A, 3, A, A, A, 4, 0, 64, 16, 256, None) == SHAPE
     assert f(A + 1, 0, A, None, None, 1, 0, 0, 16, 256, None) == ALIGN
+    # reference stream (kernel_id 4)
+    assert f(A, 5, A, None, None, 1, 0, 0, 16, 256, None) == ARG
+    assert f(A, 4, A, None, None, 1, 0, 0, 16, 300, None) == SHAPE
+    assert f(A, 4, A, None, None, 1, 0, 0, 0, 256, None) == SHAPE
+    assert f(A, 4, A + 4, None, None, 1, 0, 0, 16, 256, None) == ALIGN
+    assert f(None, 4, A, None, None, 1, 0, 0, 16, 256, None) == NULL
 
 
 def test_binding_refuses_host_tensors():

@@ -335,6 +335,18 @@ def test_pure_read_checksums(dev, orc, M):
     assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w0, N, rb))
 
 
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 512), (301, 3584), (1000, 4096), (3, 32768)])
+def test_stream_read_checksums(dev, orc, N, K):
+    """The reference stream reads every byte of N rows of K*9/16 bytes once."""
+    import torch
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(78 + N)
+    w = synth.q4k_matrix(rng, N, K)
+    c = empty((N,), dev, torch.int32)
+    q4.q4_pure_read(c, q4.Q4_READ_STREAM, T(w, dev), None, None, 1, 0, 0, N, K)
+    assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w, N, synth.q4k_row_bytes(K)))
+
+
 def test_pure_read_moe_checksums(dev, orc):
     import torch
     import bit_block_quantized_dequant_amd as q4
