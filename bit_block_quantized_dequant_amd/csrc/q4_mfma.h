@@ -66,19 +66,30 @@ __host__ __device__ constexpr int slot_byte(int t) {
     return (t & 4) | ((t & 1) << 1) | ((t >> 1) & 1);
 }
 
+// A step is 256 elements of a row: one Q4_K super-block or eight Q4_0
+// blocks, 144 bytes either way.
 template <int FMT>
 struct MStep {
-    static constexpr int kElems = FMT == kFmtQ4K ? 256 : 128;  // elements per step
-    static constexpr int kBytes = FMT == kFmtQ4K ? 144 : 72;   // bytes per row per step
+    static constexpr int kElems = 256;
+    static constexpr int kBytes = 144;
 };
+
+// Q4_0 tile-steps (16 rows x 144 bytes) are loaded as 144 contiguous
+// 16-byte chunks, 3 per lane, and regrouped through a wave-private LDS copy.
+constexpr int kQ40Chunks = 16 * 9;
+constexpr int kQ40WaveBytes = kQ40Chunks * 16;
+
+// tokens per row of the Q4_0 block-sum table (M rounded up to even)
+__host__ __device__ constexpr int sums_stride(int M) { return M + (M & 1); }
 
 // LDS map (bytes) for M tokens and K columns.
 struct MLayout {
     int frag;  // A fragments: 2M rows x (K/8 + 1) pieces x 16 bytes (see fslot)
     int aux;   // Q4_K: Dmin A operand, (K/256) x 4 groups x 2M rows x 2 halves
-               // Q4_0: block sums X, (K/32) blocks x 8 tokens x fp32
+               // Q4_0: block sums X, (K/32) blocks x sums_stride(M) tokens x fp32
     int exps;  // e_m, 8 ints (padded to 64 bytes)
     int part;  // partial sums, 2 buffers x 8 waves x 64 lanes x float2
+    int wbuf;  // Q4_0: one tile-step of raw weight bytes per wave
     int bytes;
 };
 
@@ -86,9 +97,12 @@ __host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
     MLayout l;
     l.frag = 0;
     l.aux = pure ? 0 : (K / 8 + 1) * 2 * M * 16;
-    l.exps = l.aux + (pure ? 0 : (fmt == kFmtQ4K ? (K / 256) * 4 * 2 * M * 4 : (K / 32) * 8 * 4));
+    l.exps = l.aux + (pure ? 0
+                           : (fmt == kFmtQ4K ? (K / 256) * 4 * 2 * M * 4
+                                             : (K / 32) * sums_stride(M) * 4));
     l.part = l.exps + 64;
-    l.bytes = l.part + 2 * kMWaves * 64 * 8;
+    l.wbuf = l.part + 2 * kMWaves * 64 * 8;
+    l.bytes = l.wbuf + (fmt == kFmtQ4_0 ? kMWaves * kQ40WaveBytes : 0);
     return l;
 }
 
@@ -237,7 +251,7 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
             if ((pp & 3) == 0) {
                 const int g32 = pp >> 2;  // Q4_0 block / Q4_K sub-block index
                 if constexpr (FMT == kFmtQ4_0) {
-                    ((float*)(lds + ly.aux))[g32 * 8 + m] = part;
+                    ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
                 } else {
                     // Dmin A operand: group c = J/2 of super-block sb holds
                     // the sums of sub-blocks 2c (half 0) and 2c+1 (half 1),
@@ -270,12 +284,15 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int KS = p.ks;              // waves per tile (1, 2, 4 or 8; at most S)
+    const int S = p.K / St::kElems;
+    // waves per tile (1, 2, 4 or 8), at most S so that every wave has steps
+    // (a wave without steps would skip the end-of-round reduction)
+    int KS = p.ks;
+    while (KS > S) KS >>= 1;
     const int TG = kMWaves / KS;      // tiles per workgroup and round
     const int grp = wave / KS, sl = wave - grp * KS;
     const int jrow = lane & 15;  // tile row of this lane's B column and D values
     const int c = lane >> 4;     // k group
-    const int S = p.K / St::kElems;
     const int st0 = sl * S / KS, st1 = (sl + 1) * S / KS;  // st1 > st0 as KS <= S
     const int tpm = (p.N + 15) >> 4;
     const int ntiles = NMAT * tpm;
@@ -287,6 +304,15 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     struct WR {
         uint32_t v[12];
     };
+    // Q4_0: this lane's three chunks of a tile-step (row, byte offset)
+    int q0chunk[3], q0row[3];
+    uint32_t q0col[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        q0chunk[k] = min(lane + kWave * k, kQ40Chunks - 1);
+        q0row[k] = q0chunk[k] / 9;
+        q0col[k] = (uint32_t)(q0chunk[k] - 9 * q0row[k]) * 16u;
+    }
     // Loads past the wave's last step, and those of a group without a tile
     // in the last round, are not consumed: they go to the group's own
     // last-round tile with every lane on one address (spread over the chip,
@@ -313,20 +339,16 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             w.v[4] = q0.x; w.v[5] = q0.y; w.v[6] = q0.z; w.v[7] = q0.w;
             w.v[8] = q1.x; w.v[9] = q1.y; w.v[10] = q1.z; w.v[11] = q1.w;
         } else {
-            // per block pair (36 bytes, words 0..8): words 2h..2h+2 hold the
-            // lane's bytes of block A, words 5+2h..6+2h those of block B, and
-            // word 4 (h = 0) or word 0 (h = 1) the scale the others lack
-            const uint32_t h8o = idle ? 0u : 8u * (uint32_t)(c & 1);
-            const uint32_t zo = idle ? 0u : 16u - 2u * h8o;
+            // chunks lane, lane + 64, lane + 128 (clamped) of the tile-step:
+            // chunk ch is bytes 16 (ch % 9) .. of the step's 144 bytes of
+            // tile row ch / 9
+            const uint32_t so = (uint32_t)st * St::kBytes;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint8_t* pr = base + off + 36 * k;
-                const uint32_t* a = (const uint32_t*)__builtin_assume_aligned(pr + h8o, 4);
-                const uint32_t* b = (const uint32_t*)__builtin_assume_aligned(pr + 20 + h8o, 4);
-                const uint32_t* z = (const uint32_t*)__builtin_assume_aligned(pr + zo, 4);
-                w.v[6 * k + 0] = a[0]; w.v[6 * k + 1] = a[1]; w.v[6 * k + 2] = a[2];
-                w.v[6 * k + 3] = b[0]; w.v[6 * k + 4] = b[1];
-                w.v[6 * k + 5] = z[0];
+            for (int k = 0; k < 3; ++k) {
+                const uint32_t ro = (uint32_t)min(q0row[k], p.N - 1 - row0) * rb;
+                const uint32_t o = idle ? 0u : ro + so + q0col[k];
+                const u32x4 v = ldg16(base + o);
+                w.v[4 * k] = v.x; w.v[4 * k + 1] = v.y; w.v[4 * k + 2] = v.z; w.v[4 * k + 3] = v.w;
             }
         }
     };
@@ -335,6 +357,37 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     const int i_lane = min(jrow, 2 * M - 1);
     const char* arow = lds + ly.frag + fslot(p.K, i_lane, 0) * 16;
     auto afrag = [&](int pp) { return *(const h8*)(arow + pp * 16); };
+
+    // Q4_0: write the tile-step to this wave's LDS copy and read back, per
+    // block pair k (36 bytes, words 0..8 at word 9k of row jrow): words
+    // 2h..2h+2 (the lane's bytes of block A), 5+2h, 6+2h (block B) and word
+    // 4 (h = 0) or word 0 (h = 1), the scale the others lack; h = c & 1.
+    // LDS operations of one wave are performed in order, so the reads see
+    // the writes, and the next step's writes follow this step's reads.
+    struct WQ {
+        uint32_t v[4][6];
+    };
+    char* wb = lds + ly.wbuf + wave * kQ40WaveBytes;
+    auto gather = [&](const WR& w, WQ& q) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            *(u32x4*)(wb + q0chunk[k] * 16) =
+                u32x4{w.v[4 * k], w.v[4 * k + 1], w.v[4 * k + 2], w.v[4 * k + 3]};
+        __asm__ volatile("" ::: "memory");
+        const uint32_t* wd = (const uint32_t*)wb + jrow * 36;
+        const int hh = c & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t* pa = wd + 9 * k + 2 * hh;
+            q.v[k][0] = pa[0];
+            q.v[k][1] = pa[1];
+            q.v[k][2] = pa[2];
+            q.v[k][3] = pa[5];
+            q.v[k][4] = pa[6];
+            q.v[k][5] = wd[9 * k + 4 - 4 * hh];
+        }
+        __asm__ volatile("" ::: "memory");
+    };
 
     auto compute = [&](const WR& w, int st, float2& y) {
         if constexpr (FMT == kFmtQ4K) {
@@ -406,26 +459,29 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             y.x += t[0] + t[1];
             y.y += t[2] + t[3];
         } else {
+            WQ q;
+            gather(w, q);
             const uint32_t hsel = (uint32_t)(c & 1);
             const uint32_t mask = c >= 2 ? 0x00F000F0u : 0x000F000Fu;
-            const float* xsum = (const float*)(lds + ly.aux);
+            constexpr int MP = sums_stride(M);
+            const float* xsum = (const float*)(lds + ly.aux) + min(2 * c, MP - 2);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint32_t a0 = w.v[6 * k], a1 = w.v[6 * k + 1], a2 = w.v[6 * k + 2];
-                const uint32_t b0 = w.v[6 * k + 3], b1 = w.v[6 * k + 4], z = w.v[6 * k + 5];
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a0 = q.v[k][0], a1 = q.v[k][1], a2 = q.v[k][2];
+                const uint32_t b0 = q.v[k][3], b1 = q.v[k][4], z = q.v[k][5];
                 const uint32_t qa0 = __builtin_amdgcn_alignbit(a1, a0, 16);
                 const uint32_t qa1 = __builtin_amdgcn_alignbit(a2, a1, 16);
                 const float dA = h_lo(hsel ? z : a0);
                 const float dB = h_hi(hsel ? a2 : z);
                 const u32x4m ba = {qa0 & mask, (qa0 >> 8) & mask, qa1 & mask, (qa1 >> 8) & mask};
                 const u32x4m bb = {b0 & mask, (b0 >> 8) & mask, b1 & mask, (b1 >> 8) & mask};
-                const int blk = st * 4 + 2 * k;  // block index of block A in the row
+                const int blk = st * 8 + 2 * k;  // block index of block A in the row
                 const f4 DA = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     afrag(blk * 4 + c), __builtin_bit_cast(h8, ba), (f4)(0.f), 0, 0, 0);
                 const f4 DB = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     afrag(blk * 4 + 4 + c), __builtin_bit_cast(h8, bb), (f4)(0.f), 0, 0, 0);
-                const float2 XA = *(const float2*)(xsum + blk * 8 + 2 * c);
-                const float2 XB = *(const float2*)(xsum + blk * 8 + 8 + 2 * c);
+                const float2 XA = *(const float2*)(xsum + blk * MP);
+                const float2 XB = *(const float2*)(xsum + (blk + 1) * MP);
                 // d (D - 8 X 2^-24): X holds sums of x 2^e, D carries 2^(e-24)
                 y.x = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.x, DA[0] + DA[1]), y.x);
                 y.y = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.y, DA[2] + DA[3]), y.y);
@@ -444,10 +500,12 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             if (c == 0) s += w.v[0] + w.v[1] + w.v[2] + w.v[3];
         } else {
             // lane group 0: words 0,1 (a), 5,6 (b), 4 (z); group 1: 2,3 (a), 7,8 (b)
+            WQ q;
+            gather(w, q);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                uint32_t t = w.v[6 * k] + w.v[6 * k + 1] + w.v[6 * k + 3] + w.v[6 * k + 4];
-                if (c == 0) t += w.v[6 * k + 5];
+            for (int k = 0; k < 4; ++k) {
+                uint32_t t = q.v[k][0] + q.v[k][1] + q.v[k][3] + q.v[k][4];
+                if (c == 0) t += q.v[k][5];
                 s += c < 2 ? t : 0u;
             }
         }

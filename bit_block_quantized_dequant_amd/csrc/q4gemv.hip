@@ -86,6 +86,9 @@ size_t gemv_lds_bytes(int M, int K, bool pure) {
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
 // the static shared state), capped at 2 (16 waves of 512-thread groups).
+// static shared memory of the batched kernel (its reduction scratch) plus margin
+constexpr int kMfmaStaticLds = 1024;
+
 int wg_per_cu(size_t lds) {
     const size_t cap = 160 * 1024 - 2048;
     int by_lds = lds == 0 ? 2 : (int)(cap / lds);
@@ -95,13 +98,14 @@ int wg_per_cu(size_t lds) {
     return w < 1 ? 1 : w;
 }
 
-// Raise a kernel's dynamic-LDS limit to the full 160 KB once per device.
-int allow_big_lds(const void* kern, std::atomic<int>* done) {
+// Raise a kernel's dynamic-LDS limit once per device: to 160 KB less
+// `reserve` bytes kept for its static shared variables.
+int allow_big_lds(const void* kern, std::atomic<int>* done, int reserve = 2048) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
     if (done[dev].load(std::memory_order_acquire)) return Q4_OK;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024 - 2048);
+                                       160 * 1024 - reserve);
     if (e != hipSuccess) return Q4_ERR_HIP;
     done[dev].store(1, std::memory_order_release);
     return Q4_OK;
@@ -123,9 +127,9 @@ int resident_per_cu(const void* kern, int threads, size_t lds, std::atomic<int>*
 
 template <typename Kern>
 int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
-           std::atomic<int>* big_lds_done, int threads = kBlock) {
+           std::atomic<int>* big_lds_done, int threads = kBlock, int reserve = 2048) {
     if (lds > 64 * 1024) {
-        int st = allow_big_lds((const void*)kern, big_lds_done);
+        int st = allow_big_lds((const void*)kern, big_lds_done, reserve);
         if (st) return st;
     }
     void* args[] = {(void*)&p};
@@ -277,20 +281,20 @@ int run_mfma_m(GemvParams& p, int cus, void* stream) {
     if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
         static std::atomic<int> big_lds_mirror[kMaxDevices];
         int st = allow_big_lds((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
-                               big_lds_mirror);
+                               big_lds_mirror, kMfmaStaticLds);
         if (st) return st;
     }
     const int res = resident_per_cu((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
                                     kMBlock, call_lds, resident);
     if (wgc > res) wgc = res;
     const long long ntiles = (long long)NMAT * ((p.N + 15) / 16);
-    p.ks = mfma_ks(ntiles, p.K / (FMT == kFmtQ4K ? 256 : 128), cus);
+    p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
     const int TG = kMWaves / p.ks;
     long long blocks = (long long)cus * wgc;
     const long long need = (ntiles + TG - 1) / TG;
     if (blocks > need) blocks = need;
     return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
-                  big_lds_done, kMBlock);
+                  big_lds_done, kMBlock, kMfmaStaticLds);
 }
 
 template <int FMT, int NMAT, int MODE, bool PURE>

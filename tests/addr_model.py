@@ -123,16 +123,24 @@ def check(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
 # ---------------------------------------------------------------------------
 # Matrix-core kernel (batched calls, M >= 2): q4_mfma.h and run_mfma_m().
 # ---------------------------------------------------------------------------
-LDS_CAP = 160 * 1024 - 2048  # dynamic LDS a kernel may ask for
+LDS_CAP = 160 * 1024 - 1024  # dynamic LDS the batched kernel may ask for
+Q40_WAVE_BYTES = 16 * 144    # Q4_0 tile-step copy per wave
+
+
+def sums_stride(M):
+    return M + (M & 1)
 
 
 def mlayout(fmt, M, K, pure=False):
     """Byte offsets of the kernel's LDS regions (mlayout() in q4_mfma.h)."""
     aux = 0 if pure else (K // 8 + 1) * 2 * M * 16
-    aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k" else (K // 32) * 8 * 4)
+    aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k"
+                                else (K // 32) * sums_stride(M) * 4)
     exps = aux + aux_bytes
     part = exps + 64
-    return dict(frag=0, aux=aux, exps=exps, part=part, bytes=part + 2 * 8 * 64 * 8)
+    wbuf = part + 2 * 8 * 64 * 8
+    nbytes = wbuf + (8 * Q40_WAVE_BYTES if fmt == "q4_0" else 0)
+    return dict(frag=0, aux=aux, exps=exps, part=part, wbuf=wbuf, bytes=nbytes)
 
 
 def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
@@ -147,7 +155,7 @@ def mfma_plan(fmt, M, K, N, nmat, cus=256):
     lds = mlayout(fmt, M, K)["bytes"]
     wgc = max(1, min(2, LDS_CAP // lds))
     ntiles = nmat * ((N + 15) // 16)
-    steps = K // (256 if fmt == "q4k" else 128)
+    steps = K // 256
     KS = mfma_ks(ntiles, steps, cus)
     TG = 8 // KS
     blocks = min(cus * wgc, (ntiles + TG - 1) // TG)
@@ -170,7 +178,7 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
     """Yield (matrix, byte offset, nbytes) of every weight load."""
     pl = mfma_plan(fmt, M, K, N, nmat, cus)
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
-    SB, PD = (144, 2) if fmt == "q4k" else (72, 3)
+    SB, PD = 144, (2 if fmt == "q4k" else 3)
     S, KS = pl["steps"], pl["KS"]
     tpm = (N + 15) // 16
     ntiles, TG, G = pl["ntiles"], pl["TG"], pl["blocks"]
@@ -196,13 +204,11 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
                         yield mt, base + off + co + 16, 16
                         yield mt, base + off + co + 80, 16
                     else:
-                        h8o = 0 if idle else 8 * (c & 1)
-                        zo = 0 if idle else 16 - 2 * h8o
-                        for k in range(2):
-                            pr = off + 36 * k
-                            yield mt, base + pr + h8o, 12
-                            yield mt, base + pr + 20 + h8o, 8
-                            yield mt, base + pr + zo, 4
+                        for k in range(3):
+                            ch = min(lane + 64 * k, 143)
+                            ro = (min(ch // 9, N - 1 - row0) * rb) & U32
+                            o = 0 if idle else (ro + st * SB + (ch % 9) * 16) & U32
+                            yield mt, base + o, 16
 
 
 def mfma_check(fmt, M, N, K, nmat, cus=256):
@@ -233,7 +239,7 @@ def mfma_lds_check(fmt, M, K):
             if pp & 3 == 0:
                 g32 = pp >> 2
                 if fmt == "q4_0":
-                    o = ly["aux"] + (g32 * 8 + m) * 4
+                    o = ly["aux"] + (g32 * sums_stride(M) + m) * 4
                     assert o + 4 <= ly["exps"]
                     aux_w.add(o)
                 else:
@@ -243,7 +249,7 @@ def mfma_lds_check(fmt, M, K):
                         o = ly["aux"] + 2 * hh
                         assert o + 2 <= ly["exps"]
                         aux_w.add(o)
-    S = K // (256 if fmt == "q4k" else 128)
+    S = K // 256
     for st in range(S):
         for lane in range(64):
             jrow, c = lane & 15, lane >> 4
@@ -257,18 +263,29 @@ def mfma_lds_check(fmt, M, K):
                 assert o in aux_w and o + 2 in aux_w
             else:
                 pps = []
-                for k in range(2):
-                    blk = st * 4 + 2 * k
+                MP = sums_stride(M)
+                for k in range(4):
+                    blk = st * 8 + 2 * k
                     pps += [blk * 4 + c, blk * 4 + 4 + c]
                     for bb in (blk, blk + 1):
-                        o = ly["aux"] + (bb * 8 + 2 * c) * 4
+                        o = ly["aux"] + (bb * MP + min(2 * c, MP - 2)) * 4
                         assert o + 8 <= ly["exps"]
                         # token 2c (and 2c + 1) sums exist when those tokens do
                         for hm in range(2):
                             if 2 * c + hm < M:
                                 assert o + 4 * hm in aux_w
+                    # the wave's tile-step copy: words read by this lane
+                    h = c & 1
+                    for wd in [jrow * 36 + 9 * k + 2 * h + d for d in (0, 1, 2, 5, 6)] + \
+                              [jrow * 36 + 9 * k + 4 - 4 * h]:
+                        assert 0 <= wd * 4 and wd * 4 + 4 <= Q40_WAVE_BYTES
             for pp in pps:
                 o = (i * (K // 8 + 1) + pp) * 16
                 assert o + 16 <= ly["aux"] and o in frag_w
-    assert ly["part"] + 2 * 8 * 64 * 8 == ly["bytes"]
+    if fmt == "q4_0":
+        for lane in range(64):
+            for k in range(3):
+                ch = min(lane + 64 * k, 143)
+                assert ch * 16 + 16 <= Q40_WAVE_BYTES
+    assert ly["part"] + 2 * 8 * 64 * 8 == ly["wbuf"]
     return True

@@ -81,7 +81,7 @@ def test_batched_lds_fits_every_shape():
     for fmt in ("q4k", "q4_0"):
         for M in range(2, 9):
             for K in range(256, 32768 // M + 1, 256):
-                assert A.mlayout(fmt, M, K)["bytes"] + 256 <= 160 * 1024, (fmt, M, K)
+                assert A.mlayout(fmt, M, K)["bytes"] <= A.LDS_CAP, (fmt, M, K)
 
 
 def test_batched_ks_choices():
