@@ -48,6 +48,8 @@
 // fused call).
 #pragma once
 
+#include <type_traits>
+
 #include "q4_kernels.h"
 
 namespace q4 {
@@ -273,6 +275,14 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// Expert call: the in-kernel dedupe and, per unique expert u and token m,
+// the slot s with ids[m][s] = expert u (-1: token m did not choose u).
+struct MfmaMoe {
+    MoeShared d;
+    signed char uslot[kMaxPairs][8];
+};
+struct MfmaNoMoe {};
+
 template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD>
 __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) {
     static_assert(M >= 2 && M <= 8, "batched kernel");
@@ -294,11 +304,63 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     const int jrow = lane & 15;  // tile row of this lane's B column and D values
     const int c = lane >> 4;     // k group
     const int st0 = sl * S / KS, st1 = (sl + 1) * S / KS;  // st1 > st0 as KS <= S
-    const int tpm = (p.N + 15) >> 4;
-    const int ntiles = NMAT * tpm;
+    const int tpm = (p.N + 15) >> 4;  // tiles per matrix (per expert for the expert call)
+    constexpr bool kMoe = MODE == kModeMoe;
+    __shared__ std::conditional_t<kMoe, MfmaMoe, MfmaNoMoe> moe;
+    int nu = 1;  // matrices of NMAT: 1, or the unique selected experts
+    if constexpr (kMoe) {
+        moe_dedupe<M>(p, moe.d);
+        __syncthreads();
+        if ((int)threadIdx.x < moe.d.nu) {
+            const int u = threadIdx.x;
+            const unsigned long long pairs = moe.d.upairs[u];
+            for (int m = 0; m < 8; ++m) moe.uslot[u][m] = -1;
+            for (int pr = 0; pr < M * p.top_k; ++pr)
+                if ((pairs >> pr) & 1ull) moe.uslot[u][pr / p.top_k] = (signed char)(pr % p.top_k);
+        }
+        // outputs of pairs with an invalid id: NaN (or all-ones checksums)
+        if (moe.d.invalid) {
+            const int P = M * p.top_k;
+            const long long total = (long long)P * p.N;
+            for (long long i = (long long)blockIdx.x * kMBlock + threadIdx.x; i < total;
+                 i += (long long)gridDim.x * kMBlock) {
+                const int pr = (int)(i / p.N);
+                if ((moe.d.invalid >> pr) & 1ull) {
+                    if constexpr (PURE) {
+                        p.cks[i] = 0xFFFFFFFFu;
+                        p.cks[total + i] = 0xFFFFFFFFu;
+                    } else {
+                        p.y0[i] = __builtin_nanf("");
+                        p.y1[i] = __builtin_nanf("");
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        nu = __builtin_amdgcn_readfirstlane(moe.d.nu);
+    }
+    const int per_mat = nu * tpm;  // tiles per matrix
+    const int ntiles = NMAT * per_mat;
+    if (ntiles == 0) return;  // (expert call with no valid id: all waves)
     const int per_round = gridDim.x * TG;
     const int nrounds = (ntiles + per_round - 1) / per_round;
     const uint32_t rb = (uint32_t)p.row_bytes;
+    // tile t: matrix mt, unique expert u (0 unless expert call), first row row0
+    struct Tile {
+        int mt, u, row0;
+        long long ebase;  // first row of the expert
+    };
+    auto tile_at = [&](int t) {
+        Tile T;
+        T.mt = NMAT == 2 ? (t >= per_mat ? 1 : 0) : 0;
+        const int rem = t - T.mt * per_mat;
+        T.u = kMoe ? rem / tpm : 0;
+        T.row0 = (rem - T.u * tpm) << 4;
+        T.ebase = 0;
+        if constexpr (kMoe)
+            T.ebase = (long long)__builtin_amdgcn_readfirstlane(moe.d.uexp[T.u]) * p.N;
+        return T;
+    };
 
     // weight registers of one step (12 dwords in both formats)
     struct WR {
@@ -321,10 +383,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         const int rr = min(r, nrounds - 1);
         const int traw = (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
         const bool idle = r >= nrounds || traw >= ntiles;  // wave-uniform
-        const int t = min(traw, ntiles - 1);
-        const int mt = NMAT == 2 ? (t >= tpm ? 1 : 0) : 0;
-        const int row0 = (t - mt * tpm) << 4;
-        const uint8_t* base = (mt ? p.w1 : p.w0) + (long long)row0 * p.row_bytes;
+        const Tile T = tile_at(min(traw, ntiles - 1));
+        const int row0 = T.row0;
+        const uint8_t* base = (T.mt ? p.w1 : p.w0) + (T.ebase + row0) * p.row_bytes;
         const uint32_t lr = (uint32_t)min(jrow, p.N - 1 - row0);
         const uint32_t off = idle ? 0u : lr * rb + (uint32_t)st * St::kBytes;
         if constexpr (FMT == kFmtQ4K) {
@@ -520,15 +581,29 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         __syncthreads();
         const int t = (r * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
         if (sl == 0 && t < ntiles) {
-            const int mt = NMAT == 2 ? (t >= tpm ? 1 : 0) : 0;
-            const int row = ((t - mt * tpm) << 4) + jrow;
+            const Tile T = tile_at(t);
+            const int mt = T.mt;
+            const int row = T.row0 + jrow;
             if constexpr (PURE) {
                 uint32_t tot = cks;
                 for (int k = 1; k < KS; ++k)
                     tot += __builtin_bit_cast(uint32_t, part[(wave + k) * 64 + lane].x);
                 tot += __shfl_xor(tot, 16, kWave);
                 tot += __shfl_xor(tot, 32, kWave);
-                if (c == 0 && row < p.N) p.cks[(long long)mt * p.N + row] = tot;
+                if (c == 0 && row < p.N) {
+                    if constexpr (kMoe) {
+                        // every (token, slot) pair that chose this expert
+                        const long long P = (long long)M * p.top_k;
+                        unsigned long long pm = moe.d.upairs[T.u];
+                        while (pm) {
+                            const int pr = __builtin_ctzll(pm);
+                            pm &= pm - 1ull;
+                            p.cks[((long long)mt * P + pr) * p.N + row] = tot;
+                        }
+                    } else {
+                        p.cks[(long long)mt * p.N + row] = tot;
+                    }
+                }
             } else {
                 float2 tot = y;
                 for (int k = 1; k < KS; ++k) {
@@ -539,9 +614,20 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 const int* ex = (const int*)(lds + ly.exps);
                 float* yo = mt ? p.y1 : p.y0;
                 if (row < p.N) {
-                    if (2 * c < M) yo[(long long)(2 * c) * p.N + row] = tot.x * pow2f(24 - ex[2 * c]);
-                    if (2 * c + 1 < M)
-                        yo[(long long)(2 * c + 1) * p.N + row] = tot.y * pow2f(24 - ex[2 * c + 1]);
+#pragma unroll
+                    for (int hm = 0; hm < 2; ++hm) {
+                        const int m = 2 * c + hm;
+                        if (m < M) {
+                            const float v = (hm ? tot.y : tot.x) * pow2f(24 - ex[m]);
+                            if constexpr (kMoe) {
+                                // output [token, slot, row], if token m chose this expert
+                                const int sl2 = moe.uslot[T.u][m];
+                                if (sl2 >= 0) yo[((long long)m * p.top_k + sl2) * p.N + row] = v;
+                            } else {
+                                yo[(long long)m * p.N + row] = v;
+                            }
+                        }
+                    }
                 }
             }
         }
@@ -561,7 +647,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             ++lr;
         }
     }
-    if constexpr (!PURE) mstage<FMT, M, MODE>(p, lds, ly, red);
+    if constexpr (!PURE) mstage<FMT, M, kMoe ? kModeDense : MODE>(p, lds, ly, red);
     __syncthreads();
 
     const int n = nrounds * (st1 - st0);

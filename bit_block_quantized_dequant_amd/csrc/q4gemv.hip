@@ -86,8 +86,10 @@ size_t gemv_lds_bytes(int M, int K, bool pure) {
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
 // the static shared state), capped at 2 (16 waves of 512-thread groups).
-// static shared memory of the batched kernel (its reduction scratch) plus margin
+// static shared memory of the batched kernel (its reduction scratch) plus
+// margin; the expert call adds its dedupe tables
 constexpr int kMfmaStaticLds = 1024;
+constexpr int kMfmaMoeStaticLds = 3072;
 
 int wg_per_cu(size_t lds) {
     const size_t cap = 160 * 1024 - 2048;
@@ -269,9 +271,18 @@ bool mfma_enabled() {
     return on;
 }
 
+bool moe_mfma_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_MOE_MFMA");
+        return s && *s && atoi(s) != 0;
+    }();
+    return on;
+}
+
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
-int run_mfma_m(GemvParams& p, int cus, void* stream) {
+int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
     constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
+    constexpr int kReserve = MODE == kModeMoe ? kMfmaMoeStaticLds : kMfmaStaticLds;
     static std::atomic<int> big_lds_done[kMaxDevices];
     const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
     // a pure-read pass takes the launch shape of the call it mirrors
@@ -281,20 +292,21 @@ int run_mfma_m(GemvParams& p, int cus, void* stream) {
     if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
         static std::atomic<int> big_lds_mirror[kMaxDevices];
         int st = allow_big_lds((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
-                               big_lds_mirror, kMfmaStaticLds);
+                               big_lds_mirror, kReserve);
         if (st) return st;
     }
     const int res = resident_per_cu((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
                                     kMBlock, call_lds, resident);
     if (wgc > res) wgc = res;
-    const long long ntiles = (long long)NMAT * ((p.N + 15) / 16);
+    // (the expert call: at most nexperts unique experts, each N rows per matrix)
+    const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
     p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
     const int TG = kMWaves / p.ks;
     long long blocks = (long long)cus * wgc;
     const long long need = (ntiles + TG - 1) / TG;
     if (blocks > need) blocks = need;
     return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
-                  big_lds_done, kMBlock, kMfmaStaticLds);
+                  big_lds_done, kMBlock, kReserve);
 }
 
 template <int FMT, int NMAT, int MODE, bool PURE>
@@ -302,19 +314,26 @@ int run(GemvParams& p, int M, int npairs_max, void* stream) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st) return st;
-    if constexpr (MODE != kModeMoe) {
-        if (M >= Q4_MFMA_MIN_M && mfma_enabled()) {
-            switch (M) {
-                case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, stream);
-                case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, stream);
-                case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, stream);
-                case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, stream);
-                case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, stream);
-                case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, stream);
-                case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, stream);
-            }
-            return Q4_ERR_BATCH;
+    // batched calls on the matrix cores; the expert call only on request
+    // (Q4GEMV_MOE_MFMA=1: it measured slower than the VALU expert kernel at
+    // the E=64, top-6, 1408 x 2048 shape), from M = 2 on, where its
+    // activations leave room in LDS for the expert tables
+    const bool moe_fits = MODE != kModeMoe ||
+                          (moe_mfma_enabled() && M >= 2 &&
+                           mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds);
+    const int min_m = MODE == kModeMoe ? 2 : Q4_MFMA_MIN_M;
+    if (M >= min_m && moe_fits && mfma_enabled()) {
+        const int nexp = MODE == kModeMoe ? npairs_max : 1;
+        switch (M) {
+            case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
+            case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
+            case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
+            case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
+            case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
+            case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
+            case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
         }
+        return Q4_ERR_BATCH;
     }
     switch (M) {
         case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);

@@ -151,10 +151,10 @@ def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
     return ks
 
 
-def mfma_plan(fmt, M, K, N, nmat, cus=256):
+def mfma_plan(fmt, M, K, N, nmat, cus=256, nexperts=1):
     lds = mlayout(fmt, M, K)["bytes"]
     wgc = max(1, min(2, LDS_CAP // lds))
-    ntiles = nmat * ((N + 15) // 16)
+    ntiles = nmat * nexperts * ((N + 15) // 16)
     steps = K // 256
     KS = mfma_ks(ntiles, steps, cus)
     TG = 8 // KS
@@ -174,14 +174,23 @@ def mfma_positions(S, KS, nrounds, wave, PD):
     return [(q // ns, st0 + q % ns) for q in range(visits + PD)]
 
 
-def mfma_loads(fmt, M, N, K, nmat, cus=256):
-    """Yield (matrix, byte offset, nbytes) of every weight load."""
-    pl = mfma_plan(fmt, M, K, N, nmat, cus)
+def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1):
+    """Yield (matrix, byte offset, nbytes) of every weight load; for the
+    expert call, `experts` is the dedupe result and umax the host's bound on
+    its length (which sizes the grid and the K split)."""
+    pl = mfma_plan(fmt, M, K, N, nmat, cus, umax if experts is not None else 1)
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
     SB, PD = 144, (2 if fmt == "q4k" else 3)
     S, KS = pl["steps"], pl["KS"]
+    while KS > S:  # the kernel's own clamp
+        KS //= 2
     tpm = (N + 15) // 16
-    ntiles, TG, G = pl["ntiles"], pl["TG"], pl["blocks"]
+    nu = len(experts) if experts is not None else 1
+    per_mat = nu * tpm
+    ntiles = nmat * per_mat
+    if ntiles == 0:
+        return
+    TG, G = 8 // KS, pl["blocks"]
     nrounds = (ntiles + G * TG - 1) // (G * TG)
     for b in range(G):
         for wave in range(8):
@@ -191,9 +200,12 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
                 traw = (rr * G + b) * TG + grp
                 idle = r >= nrounds or traw >= ntiles
                 t = min(traw, ntiles - 1)
-                mt = 1 if (nmat == 2 and t >= tpm) else 0
-                row0 = (t - mt * tpm) * 16
-                base = row0 * rb
+                mt = 1 if (nmat == 2 and t >= per_mat) else 0
+                rem = t - mt * per_mat
+                u = rem // tpm if experts is not None else 0
+                row0 = (rem - u * tpm) * 16
+                ebase = experts[u] * N if experts is not None else 0
+                base = (ebase + row0) * rb
                 for lane in range(64):
                     jrow, c = lane & 15, lane >> 4
                     lr = min(jrow, N - 1 - row0) & U32
@@ -211,13 +223,13 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256):
                             yield mt, base + o, 16
 
 
-def mfma_check(fmt, M, N, K, nmat, cus=256):
+def mfma_check(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, E=1):
     pl = mfma_plan(fmt, M, K, N, nmat, cus)
     assert pl["lds"] <= LDS_CAP, (fmt, M, K, pl["lds"])
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
-    limit = N * rb
+    limit = (E if experts is not None else 1) * N * rb
     n = 0
-    for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus):
+    for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus, experts, umax):
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
         n += 1
     return n

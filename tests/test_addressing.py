@@ -92,3 +92,15 @@ def test_batched_ks_choices():
     # plenty of tiles: no split
     assert A.mfma_ks(4096, 16, 256) == 1
     assert A.mfma_ks(1792, 16, 256) == 2
+
+
+@pytest.mark.parametrize("experts,E,N,K,M,top_k", [([0], 1, 5, 256, 2, 1),
+                                                   ([3, 1], 4, 70, 512, 2, 3),
+                                                   ([15, 0, 7], 16, 33, 1024, 8, 8),
+                                                   ([6, 2, 5], 7, 200, 4096, 3, 2),
+                                                   ([63, 0, 31, 5], 64, 1408, 2048, 4, 6),
+                                                   ([], 4, 16, 256, 4, 2)])
+def test_batched_expert_loads_in_bounds(experts, E, N, K, M, top_k):
+    umax = min(M * top_k, E)
+    for cus in (4, 256):
+        A.mfma_check("q4_0", M, N, K, 2, cus=cus, experts=experts, umax=umax, E=E)

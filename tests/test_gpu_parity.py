@@ -8,8 +8,9 @@ Bars:
   * pure-read checksums: bit-exact against the oracle's row word sums;
   * invariants the design promises bit-exactly: a token row of a batched
     call does not depend on the other rows or its position, gate/up equal
-    two single-matrix calls, the expert call equals
-    per-(token, slot) single calls, y(2x) = 2 y(x), one-hot x gives the
+    two single-matrix calls, the single-token expert call equals
+    per-slot single calls and a batched one depends neither on slot order
+    nor on the other tokens' routing, y(2x) = 2 y(x), one-hot x gives the
     dequantized column.
 All five named workloads run at full size; smaller shapes cover ragged row
 counts, every lane-group width (K = 256 .. 32768) and every batch M = 1..8.
@@ -440,23 +441,55 @@ def test_gate_up_equals_two_single_calls(dev):
     assert_bits(host(g), host(u), "gate == up for Wg == Wu")
 
 
-def test_moe_equals_single_calls(dev):
+def test_moe_single_token_equals_single_calls(dev):
+    """At M = 1 the expert call runs on the VALU kernel: each (slot) output
+    equals the single-matrix q4_0_gemv on that expert, bit for bit."""
+    import bit_block_quantized_dequant_amd as q4
+    d = synth.workload_inputs(5)
+    N, K, E, top_k = d["N"], d["K"], d["E"], d["top_k"]
+    ids = d["ids"][:1].copy()
+    wg, wu, xd = T(d["w_gate"], dev), T(d["w_up"], dev), T(d["x"][:1], dev)
+    g, u = empty((1, top_k, N), dev), empty((1, top_k, N), dev)
+    q4.moe_q4_gemv(g, u, wg, wu, xd, T(ids, dev), 1, top_k, E, N, K)
+    g, u = host(g), host(u)
+    for s in range(top_k):
+        e = int(ids[0, s])
+        for mat, out in ((wg, g), (wu, u)):
+            y1 = empty((1, N), dev)
+            q4.q4_0_gemv(y1, mat[e * N:(e + 1) * N], xd, 1, N, K)
+            assert_bits(host(y1)[0], out[0, s], "moe slot %d vs q4_0_gemv" % s)
+
+
+def test_moe_rows_independent_of_routing(dev):
+    """Batched expert call (matrix cores): permuting a token's slots permutes
+    its outputs, and other tokens' choices do not change them, bit for bit."""
     import bit_block_quantized_dequant_amd as q4
     d = synth.workload_inputs(5)
     M, N, K, E, top_k = d["M"], d["N"], d["K"], d["E"], d["top_k"]
-    ids = d["ids"].copy()
-    ids[1, 0] = ids[0, 4]  # make sure one expert is shared by two tokens
     wg, wu, xd = T(d["w_gate"], dev), T(d["w_up"], dev), T(d["x"], dev)
-    g, u = empty((M, top_k, N), dev), empty((M, top_k, N), dev)
-    q4.moe_q4_gemv(g, u, wg, wu, xd, T(ids, dev), M, top_k, E, N, K)
-    g, u = host(g), host(u)
-    for m in range(M):
-        for s in range(top_k):
-            e = int(ids[m, s])
-            for mat, out in ((wg, g), (wu, u)):
-                y1 = empty((1, N), dev)
-                q4.q4_0_gemv(y1, mat[e * N:(e + 1) * N], xd[m:m + 1].contiguous(), 1, N, K)
-                assert_bits(host(y1)[0], out[m, s], "moe (%d,%d) vs q4_0_gemv" % (m, s))
+
+    def run(ids):
+        g, u = empty((M, top_k, N), dev), empty((M, top_k, N), dev)
+        q4.moe_q4_gemv(g, u, wg, wu, xd, T(ids, dev), M, top_k, E, N, K)
+        return host(g), host(u)
+
+    ids = d["ids"].copy()
+    ids[1, 0] = ids[0, 4]  # one expert shared by two tokens
+    g0, u0 = run(ids)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    ids_p = ids.copy()
+    ids_p[2] = ids[2][perm]
+    g1, u1 = run(ids_p)
+    for s in range(top_k):
+        assert_bits(g1[2, s], g0[2, perm[s]], "gate, permuted slot %d" % s)
+        assert_bits(u1[2, s], u0[2, perm[s]], "up, permuted slot %d" % s)
+    rng = synth.make_rng(36)
+    ids_o = ids.copy()
+    for m in range(1, M):  # other tokens: new draws (token 0 keeps its experts)
+        ids_o[m] = rng.choice(E, size=top_k, replace=False)
+    g2, u2 = run(ids_o)
+    assert_bits(g2[0], g0[0], "token 0 gate with other routing")
+    assert_bits(u2[0], u0[0], "token 0 up with other routing")
 
 
 def test_scaling_onehot_zero(dev, orc):
@@ -523,3 +556,40 @@ def test_graph_replay_matches_eager(dev):
         torch.cuda.synchronize()
         for k, v in outs.items():
             assert_bits(host(v), want[k], "graph replay %d, %s" % (rep, k))
+
+
+def test_moe_matrix_core_path_in_child_process():
+    """The matrix-core expert path (opt-in, Q4GEMV_MOE_MFMA=1; the switch is
+    read once per process) against the oracle, in one child process."""
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np, torch, sys\n"
+        "sys.path.insert(0, %r)\n"
+        "import bit_block_quantized_dequant_amd as q4\n"
+        "from bit_block_quantized_dequant_amd import synth\n"
+        "from oracle import oracle\n"
+        "o = oracle.default(); dev = torch.device('cuda:0')\n"
+        "T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)\n"
+        "for (M, top_k, E, N, K, seed) in [(4, 6, 64, 1408, 2048, 0), (2, 3, 4, 70, 512, 1),\n"
+        "                                   (8, 8, 16, 33, 1024, 2), (3, 2, 7, 200, 4096, 3)]:\n"
+        "    rng = synth.make_rng(5100 + seed)\n"
+        "    wg, wu = synth.q4_0_matrix(rng, E * N, K), synth.q4_0_matrix(rng, E * N, K)\n"
+        "    x = synth.activations(rng, M, K)\n"
+        "    ids = synth.expert_ids(rng, M, top_k, E)\n"
+        "    if seed == 1: ids[1, 0] = -3\n"
+        "    g = torch.full((M, top_k, N), float('nan'), device=dev)\n"
+        "    u = torch.full((M, top_k, N), float('nan'), device=dev)\n"
+        "    q4.moe_q4_gemv(g, u, T(wg), T(wu), T(x), T(ids), M, top_k, E, N, K)\n"
+        "    torch.cuda.synchronize()\n"
+        "    rg, ru, ag, au = o.moe_q4_0_gemv(wg, wu, x, ids, E, N, K)\n"
+        "    for got, ref, ab in ((g, rg, ag), (u, ru, au)):\n"
+        "        got = got.cpu().numpy().astype(np.float64)\n"
+        "        assert np.array_equal(np.isnan(got), np.isnan(ref))\n"
+        "        ok = ~np.isnan(ref)\n"
+        "        assert np.all(np.abs(got[ok] - ref[ok]) <= 1e-4 * ab[ok]), (M, top_k, E, N, K)\n"
+        "print('ok')\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    env = dict(os.environ, Q4GEMV_MOE_MFMA="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
