@@ -84,13 +84,13 @@ size_t gemv_lds_bytes(int M, int K, bool pure) {
     return (size_t)M * (K / 64) * 17 * 16 + (size_t)M * (K / 32) * 4;
 }
 
-// Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
-// the static shared state), capped at 2 (16 waves of 512-thread groups).
 // static shared memory of the batched kernel (its reduction scratch) plus
 // margin; the expert call adds its dedupe tables
 constexpr int kMfmaStaticLds = 1024;
 constexpr int kMfmaMoeStaticLds = 3072;
 
+// Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
+// the static shared state), capped at 2 (16 waves of 512-thread groups).
 int wg_per_cu(size_t lds) {
     const size_t cap = 160 * 1024 - 2048;
     int by_lds = lds == 0 ? 2 : (int)(cap / lds);
