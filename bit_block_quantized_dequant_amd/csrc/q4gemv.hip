@@ -90,7 +90,9 @@ constexpr int kMfmaStaticLds = 1024;
 constexpr int kMfmaMoeStaticLds = 3072;
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
-// the static shared state), capped at 2 (16 waves of 512-thread groups).
+// the static shared state), capped at 2: 16 waves of 512-thread groups, 8 of
+// 256-thread ones (four 256-thread groups per CU measured 4 % slower on the
+// large single-token calls than two).
 int wg_per_cu(size_t lds) {
     const size_t cap = 160 * 1024 - 2048;
     int by_lds = lds == 0 ? 2 : (int)(cap / lds);
@@ -141,10 +143,10 @@ int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
 }
 
 // Fill the work-split fields of p for a call with `rows` rows per matrix
-// and RR rows per lane; returns the number of workgroups (at most `resident`
-// per CU, the kernel's occupancy limit).
+// and RR rows per lane; returns the number of workgroups of `threads`
+// threads (at most `resident` per CU, the kernel's occupancy limit).
 int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
-         int cus, int resident) {
+         int cus, int resident, int threads) {
     p.K = K;
     p.upr = K / kUnitElems;
     p.lg = p.upr >= kWave ? kWave : pow2ceil(p.upr);
@@ -161,7 +163,7 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
         p.ntasks = (nrg + p.rgw - 1) / p.rgw;
         tasks = p.ntasks;
     }
-    const int wpb = kBlock / kWave;
+    const int wpb = threads / kWave;
     int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure));
     if (wgc > resident) wgc = resident;
     // Every CU gets the same number of workgroups (the per-CU load/issue rate
@@ -171,6 +173,11 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
     long long blocks_ll = (long long)cus * bpc;
     const long long need = (tasks + wpb - 1) / wpb;  // no more waves than tasks
     if (blocks_ll > need) blocks_ll = need;
+    // At least two steps per wave (a wave with one step has nothing to
+    // overlap its loads with), down to one workgroup per CU.
+    long long two = (tasks * p.upl / 2 + wpb - 1) / wpb;
+    if (two < cus) two = cus;
+    if (blocks_ll > two) blocks_ll = two;
     int blocks = (int)(blocks_ll < 1 ? 1 : blocks_ll);
     p.nwaves = blocks * wpb;
     return blocks;
@@ -199,22 +206,24 @@ bool xr_enabled() {
 template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
 int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
+    constexpr int BS = M == 1 ? kBlock1 : kBlock;
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors
     auto kern = [](bool pure) {
         if constexpr (XR)
-            return pure ? gemv_kernel_xr<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH>
-                        : gemv_kernel_xr<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH>;
+            return pure ? gemv_kernel_xr<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, BS>
+                        : gemv_kernel_xr<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, BS>;
         else
-            return pure ? gemv_kernel<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, TAIL>
-                        : gemv_kernel<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, TAIL>;
+            return pure ? gemv_kernel<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, TAIL, BS>
+                        : gemv_kernel<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, TAIL, BS>;
     };
-    const int res = resident_per_cu((const void*)kern(false), kBlock,
+    const int res = resident_per_cu((const void*)kern(false), BS,
                                     gemv_lds_bytes(M, p.K, false), resident);
-    const int blocks = plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res);
+    const int blocks =
+        plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res, BS);
     const size_t lds = gemv_lds_bytes(M, p.K, PURE);
-    return launch(kern(PURE), p, blocks, lds, stream, big_lds_done);
+    return launch(kern(PURE), p, blocks, lds, stream, big_lds_done, BS);
 }
 
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
@@ -225,7 +234,7 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         if (p.K <= kWave * kUnitElems && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
-    if ((long long)M * p.K > (long long)kXReg * 4 * kBlock)
+    if ((long long)M * p.K > (long long)kXReg * 4 * (M == 1 ? kBlock1 : kBlock))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }

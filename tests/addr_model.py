@@ -17,7 +17,13 @@ def pow2ceil(v):
     return p
 
 
-def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=2, wpb=8):
+def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None):
+    # single-token calls run 256-thread workgroups (4 waves), the others
+    # 512-thread ones (8 waves); up to 2 workgroups per CU
+    if wpb is None:
+        wpb = 4 if M == 1 else 8
+    if bpc is None:
+        bpc = 2
     upr = K // 64
     lg = 64 if upr >= 64 else pow2ceil(upr)
     upl = (upr + lg - 1) // lg
@@ -31,6 +37,8 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=2, wpb=8):
         ntasks = (nrg + rgw - 1) // rgw
         tasks = ntasks
     blocks = min(cus * bpc, (tasks + wpb - 1) // wpb)
+    # at least two steps per wave, down to one workgroup per CU
+    blocks = min(blocks, max(cus, (tasks * upl // 2 + wpb - 1) // wpb))
     blocks = max(1, blocks)
     return dict(upr=upr, lg=lg, upl=upl, rgw=rgw, nrg=nrg, ntasks=ntasks, nwaves=blocks * wpb)
 
@@ -45,7 +53,7 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
     of unique valid experts the in-kernel dedupe would produce."""
     moe = moe_experts is not None
     pl = plan(M, K, N, RR, moe, kw.get("npairs_max", 1), **{k: v for k, v in kw.items()
-                                                             if k in ("cus", "bpc")})
+                                                             if k in ("cus", "bpc", "wpb")})
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
     upr, lg, upl, rgw = pl["upr"], pl["lg"], pl["upl"], pl["rgw"]
     u_last = upr - 1

@@ -24,6 +24,16 @@ def test_two_matrix_loads_in_bounds(M, N, K):
     assert A.check("q4k", M, N, K, RR=1, nmat=2, cus=8) > 0
 
 
+@pytest.mark.parametrize("fmt,N,K,nmat", [("q4_0", 4096, 4096, 1), ("q4_0", 256, 512, 1),
+                                          ("q4k", 18944, 3584, 1), ("q4k", 3, 4096, 2)])
+def test_single_token_plans_at_full_chip(fmt, N, K, nmat):
+    # 256 CUs: the grid is cut to two steps per wave (one workgroup per CU)
+    RR = 2 if nmat == 1 else 1
+    pl = A.plan(1, K, N, RR, False, 1, cus=256)
+    assert pl["nwaves"] <= 2 * 4 * 256 and pl["nwaves"] * 4 >= min(pl["ntasks"], 4 * 256)
+    assert A.check(fmt, 1, N, K, RR=RR, nmat=nmat, cus=256) > 0
+
+
 @pytest.mark.parametrize("experts,E,N,K,npairs", [([0], 1, 5, 256, 1), ([3, 1], 4, 70, 512, 6),
                                                   ([15, 0, 7], 16, 33, 1024, 64),
                                                   ([6, 2, 5], 7, 200, 4096, 6),
