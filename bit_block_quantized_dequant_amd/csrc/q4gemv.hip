@@ -90,13 +90,11 @@ constexpr int kMfmaStaticLds = 1024;
 constexpr int kMfmaMoeStaticLds = 3072;
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
-// the static shared state), capped at 2: 16 waves of 512-thread groups, 8 of
-// 256-thread ones (four 256-thread groups per CU measured 4 % slower on the
-// large single-token calls than two).
-int wg_per_cu(size_t lds) {
+// the static shared state), capped at `mx`.
+int wg_per_cu(size_t lds, int mx = 2) {
     const size_t cap = 160 * 1024 - 2048;
-    int by_lds = lds == 0 ? 2 : (int)(cap / lds);
-    int w = by_lds < 2 ? by_lds : 2;
+    int by_lds = lds == 0 ? mx : (int)(cap / lds);
+    int w = by_lds < mx ? by_lds : mx;
     static const int override_wg = env_int("Q4GEMV_WG_PER_CU", 0);
     if (override_wg > 0 && override_wg < w) w = override_wg;
     return w < 1 ? 1 : w;
@@ -144,9 +142,10 @@ int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
 
 // Fill the work-split fields of p for a call with `rows` rows per matrix
 // and RR rows per lane; returns the number of workgroups of `threads`
-// threads (at most `resident` per CU, the kernel's occupancy limit).
+// threads (at most `wgmax` and `resident` per CU, the second being the
+// kernel's occupancy limit).
 int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
-         int cus, int resident, int threads) {
+         int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = K / kUnitElems;
     p.lg = p.upr >= kWave ? kWave : pow2ceil(p.upr);
@@ -164,7 +163,7 @@ int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max
         tasks = p.ntasks;
     }
     const int wpb = threads / kWave;
-    int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure));
+    int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure), wgmax);
     if (wgc > resident) wgc = resident;
     // Every CU gets the same number of workgroups (the per-CU load/issue rate
     // is shared by its waves); tasks are then split evenly over all waves.
@@ -206,7 +205,13 @@ bool xr_enabled() {
 template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
 int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
-    constexpr int BS = M == 1 ? kBlock1 : kBlock;
+    // Workgroup shape (measured): single-token and expert calls run 256-thread
+    // groups; dense single-token calls at most two per CU (four were 4 %
+    // slower), expert calls up to four (their 136 VGPRs allow three: 12
+    // waves per CU instead of 8 with 512-thread groups, 9-14 % faster).
+    // Dense batched calls on this kernel run two 512-thread groups.
+    constexpr int BS = gemv_threads(M, MODE);
+    constexpr int WGMAX = MODE == kModeMoe ? 4 : 2;
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors
@@ -221,7 +226,7 @@ int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     const int res = resident_per_cu((const void*)kern(false), BS,
                                     gemv_lds_bytes(M, p.K, false), resident);
     const int blocks =
-        plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res, BS);
+        plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res, BS, WGMAX);
     const size_t lds = gemv_lds_bytes(M, p.K, PURE);
     return launch(kern(PURE), p, blocks, lds, stream, big_lds_done, BS);
 }
@@ -234,7 +239,7 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         if (p.K <= kWave * kUnitElems && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
-    if ((long long)M * p.K > (long long)kXReg * 4 * (M == 1 ? kBlock1 : kBlock))
+    if ((long long)M * p.K > (long long)kXReg * 4 * gemv_threads(M, MODE))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }

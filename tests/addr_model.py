@@ -18,12 +18,13 @@ def pow2ceil(v):
 
 
 def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None):
-    # single-token calls run 256-thread workgroups (4 waves), the others
-    # 512-thread ones (8 waves); up to 2 workgroups per CU
+    # single-token and expert calls run 256-thread workgroups (4 waves), the
+    # others 512-thread ones (8 waves); up to 2 workgroups per CU, expert calls
+    # up to 4 (their occupancy allows 3)
     if wpb is None:
-        wpb = 4 if M == 1 else 8
+        wpb = 4 if (M == 1 or moe) else 8
     if bpc is None:
-        bpc = 2
+        bpc = 3 if moe else 2
     upr = K // 64
     lg = 64 if upr >= 64 else pow2ceil(upr)
     upl = (upr + lg - 1) // lg

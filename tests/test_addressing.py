@@ -39,8 +39,10 @@ def test_single_token_plans_at_full_chip(fmt, N, K, nmat):
                                                   ([6, 2, 5], 7, 200, 4096, 6),
                                                   ([63, 0, 31, 5], 64, 1408, 2048, 24),
                                                   ([], 4, 16, 256, 8)])
-def test_expert_loads_in_bounds(experts, E, N, K, npairs):
-    A.check("q4_0", 4, N, K, RR=1, nmat=2, moe_experts=experts, E=E, npairs_max=npairs, cus=8)
+@pytest.mark.parametrize("bpc", [3, 4])
+def test_expert_loads_in_bounds(experts, E, N, K, npairs, bpc):
+    A.check("q4_0", 4, N, K, RR=1, nmat=2, moe_experts=experts, E=E, npairs_max=npairs, cus=8,
+            bpc=bpc)
 
 
 def test_model_catches_the_unclamped_base():
