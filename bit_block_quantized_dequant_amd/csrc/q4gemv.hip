@@ -257,14 +257,16 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
 #endif
 
 // Waves that split one 16-row tile's K range (1, 2, 4 or 8): the fewest that
-// give every CU its share of waves, at most one per step of the row.  It
-// depends on the matrix shape and the CU count only, so a token's result
-// does not depend on the batch it is computed in.
+// give the CUs at least three quarters of their share of waves, at most one
+// per step of the row (gate+up, 1792 tiles: one wave per tile, 16 steps each,
+// measured 4 % faster than two waves of 8 steps).  It depends on the matrix
+// shape and the CU count only, so a token's result does not depend on the
+// batch it is computed in.
 int mfma_ks(long long ntiles, int steps, int cus) {
     static const int forced = env_int("Q4GEMV_MFMA_KS", 0);
     const long long want = (long long)cus * Q4_MFMA_WAVES_PER_CU;
     int ks = 1;
-    while (ks < kMWaves && 2 * ks <= steps && ntiles * ks < want) ks *= 2;
+    while (ks < kMWaves && 2 * ks <= steps && 4 * ntiles * ks < 3 * want) ks *= 2;
     if (forced == 1 || forced == 2 || forced == 4 || forced == 8)
         ks = forced <= steps ? forced : ks;
     return ks;

@@ -155,7 +155,7 @@ def mlayout(fmt, M, K, pure=False):
 def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
     """Waves per tile (mfma_ks() in q4gemv.hip)."""
     ks = 1
-    while ks < 8 and 2 * ks <= steps and ntiles * ks < cus * waves_per_cu:
+    while ks < 8 and 2 * ks <= steps and 4 * ntiles * ks < 3 * cus * waves_per_cu:
         ks *= 2
     return ks
 

@@ -101,9 +101,13 @@ def test_batched_ks_choices():
     assert A.mfma_ks(1, 32, 256) == 8
     assert A.mfma_ks(1, 1, 256) == 1
     assert A.mfma_ks(1, 3, 256) == 2
-    # plenty of tiles: no split
+    # plenty of tiles: no split (1792 tiles give 7/8 of the 2048 wanted waves)
     assert A.mfma_ks(4096, 16, 256) == 1
-    assert A.mfma_ks(1792, 16, 256) == 2
+    assert A.mfma_ks(1792, 16, 256) == 1
+    assert A.mfma_ks(1536, 16, 256) == 1
+    assert A.mfma_ks(1535, 16, 256) == 2
+    # the small Q4_0 call: 256 tiles, split eight ways
+    assert A.mfma_ks(256, 16, 256) == 8
 
 
 @pytest.mark.parametrize("experts,E,N,K,M,top_k", [([0], 1, 5, 256, 2, 1),
