@@ -144,11 +144,21 @@ int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
 // and RR rows per lane; returns the number of workgroups of `threads`
 // threads (at most `wgmax` and `resident` per CU, the second being the
 // kernel's occupancy limit).
+// Lanes per row group for a row of `upr` 64-weight units: the whole wave
+// on one row when the row has at least 64 units, else the power of two that
+// covers the row.  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
+// measurements; the kernel takes any such width.
+int choose_lg(int upr) {
+    static const int forced = env_int("Q4GEMV_LG", 0);
+    if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
+    return upr >= kWave ? kWave : pow2ceil(upr);
+}
+
 int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = K / kUnitElems;
-    p.lg = p.upr >= kWave ? kWave : pow2ceil(p.upr);
+    p.lg = choose_lg(p.upr);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
     const int nrg = (rows + RR - 1) / RR;
@@ -236,7 +246,8 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
     if constexpr (M == 1 && MODE != kModeMoe) {
         // one 64-weight unit per lane per row: K <= 64 * 64 (and then the
         // activations need no staging loop beyond the first kXReg chunks)
-        if (p.K <= kWave * kUnitElems && xr_enabled())
+        const int upr = p.K / kUnitElems;
+        if (p.K <= kWave * kUnitElems && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
     if ((long long)M * p.K > (long long)kXReg * 4 * gemv_threads(M, MODE))

@@ -17,7 +17,7 @@ def pow2ceil(v):
     return p
 
 
-def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None):
+def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
     # single-token and expert calls run 256-thread workgroups (4 waves), the
     # others 512-thread ones (8 waves); up to 2 workgroups per CU, expert calls
     # up to 4 (their occupancy allows 3)
@@ -26,7 +26,8 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None):
     if bpc is None:
         bpc = 3 if moe else 2
     upr = K // 64
-    lg = 64 if upr >= 64 else pow2ceil(upr)
+    if lg is None:
+        lg = 64 if upr >= 64 else pow2ceil(upr)
     upl = (upr + lg - 1) // lg
     rgw = 64 // lg
     nrg = (rows + RR - 1) // RR
@@ -54,7 +55,7 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
     of unique valid experts the in-kernel dedupe would produce."""
     moe = moe_experts is not None
     pl = plan(M, K, N, RR, moe, kw.get("npairs_max", 1), **{k: v for k, v in kw.items()
-                                                             if k in ("cus", "bpc", "wpb")})
+                                                             if k in ("cus", "bpc", "wpb", "lg")})
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
     upr, lg, upl, rgw = pl["upr"], pl["lg"], pl["upl"], pl["rgw"]
     u_last = upr - 1

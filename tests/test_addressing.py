@@ -34,6 +34,16 @@ def test_single_token_plans_at_full_chip(fmt, N, K, nmat):
     assert A.check(fmt, 1, N, K, RR=RR, nmat=nmat, cus=256) > 0
 
 
+@pytest.mark.parametrize("lg", [4, 8, 16, 32])
+@pytest.mark.parametrize("fmt,N,K,nmat", [("q4k", 18944, 3584, 1), ("q4k", 14336, 4096, 2),
+                                          ("q4_0", 37, 3584, 1), ("q4k", 5, 1024, 2)])
+def test_lane_group_overrides_load_in_bounds(lg, fmt, N, K, nmat):
+    # Q4GEMV_LG forces the lanes per row group; the kernel's clamping must
+    # keep every lane in bounds for any power-of-two width
+    RR = 2 if nmat == 1 else 1
+    assert A.check(fmt, 1, N, K, RR=RR, nmat=nmat, cus=256, lg=lg) > 0
+
+
 @pytest.mark.parametrize("experts,E,N,K,npairs", [([0], 1, 5, 256, 1), ([3, 1], 4, 70, 512, 6),
                                                   ([15, 0, 7], 16, 33, 1024, 64),
                                                   ([6, 2, 5], 7, 200, 4096, 6),

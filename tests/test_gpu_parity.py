@@ -593,3 +593,43 @@ def test_moe_matrix_core_path_in_child_process():
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+def test_forced_lane_groups_in_child_process():
+    """Single-token calls with the lanes per row group forced to 8 and 16
+    (Q4GEMV_LG, read once per process; this also turns off the
+    register-resident activations) against the oracle, one child process
+    per width."""
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np, torch, sys\n"
+        "sys.path.insert(0, %r)\n"
+        "import bit_block_quantized_dequant_amd as q4\n"
+        "from bit_block_quantized_dequant_amd import synth\n"
+        "from oracle import oracle\n"
+        "o = oracle.default(); dev = torch.device('cuda:0')\n"
+        "T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)\n"
+        "def close(y, ref, ab, what):\n"
+        "    y = y.cpu().numpy().astype(np.float64).reshape(ref.shape)\n"
+        "    assert np.all(np.abs(y - ref) <= 1e-4 * ab), what\n"
+        "for (N, K, seed) in [(37, 3584, 0), (300, 1024, 1), (1000, 4096, 2), (5, 256, 3)]:\n"
+        "    rng = synth.make_rng(5200 + seed)\n"
+        "    wk, wk2, w0 = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K), synth.q4_0_matrix(rng, N, K)\n"
+        "    x = synth.activations(rng, 1, K); gam = synth.gamma(rng, K)\n"
+        "    y = torch.empty(1, N, device=dev); u = torch.empty(1, N, device=dev)\n"
+        "    q4.q4k_gemv(y, T(wk), T(x), 1, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab = o.q4k_gemv(wk, x, N, K); close(y, ry, ab, ('q4k', N, K))\n"
+        "    q4.q4_0_gemv(y, T(w0), T(x), 1, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab = o.q4_0_gemv(w0, x, N, K); close(y, ry, ab, ('q4_0', N, K))\n"
+        "    q4.fused_rmsnorm_q4k_gemv(y, T(wk), T(x), T(gam), 1e-5, 1, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab, _ = o.fused_rmsnorm_q4k_gemv(wk, x, gam, 1e-5, N, K); close(y, ry, ab, ('norm', N, K))\n"
+        "    q4.fused_gate_up_q4k_gemv(y, u, T(wk), T(wk2), T(x), 1, N, K); torch.cuda.synchronize()\n"
+        "    rg, ru, ag, au = o.gate_up_q4k_gemv(wk, wk2, x, N, K)\n"
+        "    close(y, rg, ag, ('gate', N, K)); close(u, ru, au, ('up', N, K))\n"
+        "print('ok')\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    for lg in ("8", "16"):
+        env = dict(os.environ, Q4GEMV_LG=lg)
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0 and r.stdout.strip().endswith("ok"), lg + r.stdout + r.stderr
