@@ -63,6 +63,8 @@ class Oracle:
         L.oracle_moe_q4_0_gemv.argtypes = [_u8p, _u8p, _f32p, _i32p, _i64, _i64, _i64, _i64,
                                            _i64, _f64p, _f64p, _f64p, _f64p, _int]
         L.oracle_moe_q4_0_gemv.restype = None
+        L.oracle_silu_mul.argtypes = [_f64p, _f64p, _i64, _f64p]
+        L.oracle_silu_mul.restype = None
         L.oracle_row_checksum.argtypes = [_u8p, _i64, _i64, _u32p]
         L.oracle_row_checksum.restype = None
         self.L = L
@@ -159,6 +161,15 @@ class Oracle:
                                     M, top_k, E, N, K, *[_p(o, _f64p) for o in outs],
                                     int(nthreads))
         return tuple(outs)
+
+    def silu_mul(self, g, u) -> np.ndarray:
+        """h = silu(g) * u elementwise, float64, same shape as g."""
+        g = _c(np.asarray(g, dtype=np.float64), np.float64)
+        u = _c(np.asarray(u, dtype=np.float64), np.float64)
+        assert g.shape == u.shape
+        h = np.empty_like(g)
+        self.L.oracle_silu_mul(_p(g, _f64p), _p(u, _f64p), g.size, _p(h, _f64p))
+        return h
 
     def row_checksum(self, w, nrows: int, row_bytes: int) -> np.ndarray:
         w = _c(w, np.uint8)

@@ -20,7 +20,8 @@
  *        - GEMV_F16S WGSL (q4_lo / q4_hi: low nibble of byte j is element j,
  *          high nibble is element j+16, both minus 8, times the f16 scale)
  *        - MOE_PURE_READ WGSL and moe_lab (expert-stacked rows
- *          row = eid*rows + r, selection per (column, slot))
+ *          row = eid*rows + r, selection per (column, slot); one output
+ *          per (column, slot, row) from the gate and up matrices)
  *
  * Arithmetic: every dequantized weight is formed exactly in double and
  * rounded to float once (the one correct fp32 value); every GEMV sum is a
@@ -286,6 +287,22 @@ void oracle_moe_q4_0_gemv(const uint8_t* wg, const uint8_t* wu, const float* x,
             oracle_q4_0_gemv(wg + e * mat_bytes, x + m * K, 1, N, K, g, ag, nthreads);
             oracle_q4_0_gemv(wu + e * mat_bytes, x + m * K, 1, N, K, u, au, nthreads);
         }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * SiLU-gated product of a gate and an up projection, elementwise:
+ *   h = silu(g) * u,  silu(g) = g * sigmoid(g) = g / (1 + exp(-g)).
+ * [IL] moe_lab: the expert kernel writes ONE [columns, top_k, rows] output
+ * from the gate (w1) and up (w3) matrices; this is the reading of that
+ * single output (the SwiGLU gate of the two projections).  Double
+ * throughout; a NaN in g or u gives a NaN.
+ * ---------------------------------------------------------------------- */
+void oracle_silu_mul(const double* g, const double* u, int64_t n, double* h)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double s = g[i] / (1.0 + exp(-g[i]));
+        h[i] = s * u[i];
     }
 }
 

@@ -17,8 +17,10 @@ Sources:
     (Q4_K super-block layout, 6-bit scale/min extraction, 64-value chunks).
   inferencelayer 0.2.13, src/bin/kernel_lab.rs --
     GEMV_F16S WGSL (Q4_0 nibble order, d*(q-8)); moe_lab / MOE_PURE_READ
-    (expert-stacked rows, per-(token, slot) selection).
+    (expert-stacked rows, per-(token, slot) selection, one output per
+    (token, slot, row) from the gate and up matrices, read as the SiLU gate).
 """
+import math
 import os
 import struct
 from fractions import Fraction
@@ -371,7 +373,37 @@ def pin_checksum(o):
     assert np.array_equal(got, want)
 
 
+def pin_silu(o):
+    """h = silu(g) * u with silu(g) = g * sigmoid(g): the sigmoid's closed
+    forms at ln 3 (3/4), -ln 3 (1/4) and 0, the odd-part identity
+    silu(g) - silu(-g) = g, the Taylor start g/2 + g^2/4 near 0, both
+    asymptotes, the tanh form of the sigmoid, exact linearity in u, NaN."""
+    ln3 = math.log(3.0)
+    h = o.silu_mul([ln3, -ln3, 0.0, 0.0], [1.0, 1.0, 7.0, -3.0])
+    assert abs(h[0] - 0.75 * ln3) <= 4e-16 * ln3
+    assert abs(h[1] + 0.25 * ln3) <= 4e-16 * ln3
+    assert h[2] == 0.0 and h[3] == 0.0
+    g = np.linspace(-30.0, 30.0, 241)
+    one = np.ones_like(g)
+    d = o.silu_mul(g, one) - o.silu_mul(-g, one)
+    assert np.all(np.abs(d - g) <= 1e-15 * np.maximum(1.0, np.abs(g)))
+    e = 1e-6
+    assert abs(o.silu_mul([e], [1.0])[0] - (e / 2 + e * e / 4)) <= 1e-21
+    h = o.silu_mul([40.0, -40.0], [1.0, 1.0])
+    assert h[0] == 40.0
+    want = -40.0 / (1.0 + math.exp(40.0))
+    assert abs(h[1] - want) <= 1e-15 * abs(want)
+    rng = np.random.default_rng(7)
+    g = rng.normal(0.0, 3.0, 200)
+    u = rng.normal(0.0, 1.0, 200)
+    h = o.silu_mul(g, u)
+    ref = g * (0.5 * (1.0 + np.tanh(0.5 * g))) * u
+    assert np.all(np.abs(h - ref) <= 1e-12 * np.abs(g * u))
+    assert np.array_equal(o.silu_mul(g, 2.0 * u), 2.0 * h)
+    assert np.all(np.isnan(o.silu_mul([np.nan, 1.0], [1.0, np.nan])))
+
+
 # fast pins first: the mutant test stops at the first failing pin
-ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_gemv_onehot_and_scaling,
-            pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
+ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_silu,
+            pin_gemv_onehot_and_scaling, pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
             pin_rmsnorm, pin_composites, pin_f16_decode, pin_bruteforce]

@@ -44,6 +44,10 @@ MUTANTS = {
     "moe gate/up matrices swapped": ("oracle_q4_0_gemv(wg + e * mat_bytes",
                                      "oracle_q4_0_gemv(wu + e * mat_bytes"),
     "checksum byte order": ("((uint32_t)r[b + 2] << 16)", "((uint32_t)r[b + 2] << 8)"),
+    "silu sigmoid of +g": ("exp(-g[i])", "exp(g[i])"),
+    "silu drops up": ("h[i] = s * u[i];", "h[i] = s;"),
+    "silu without g": ("double s = g[i] / (1.0 + exp(-g[i]));",
+                       "double s = 1.0 / (1.0 + exp(-g[i]));"),
 }
 
 
