@@ -158,7 +158,7 @@ def check(status, what):
 # ---------------------------------------------------------------------------
 # workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
 # ---------------------------------------------------------------------------
-def setup_workload(torch, dev, index, M, distinct=False):
+def setup_workload(torch, dev, index, M, distinct=False, silu=False):
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
@@ -219,6 +219,11 @@ def setup_workload(torch, dev, index, M, distinct=False):
 
         def launch(i, stream):
             p = rot.ptr(i)
+            if silu:
+                check(L.fused_gate_up_silu_q4k_gemv(gate.data_ptr(), p, p + half, x.data_ptr(),
+                                                    M, N, K, stream),
+                      "fused_gate_up_silu_q4k_gemv")
+                return
             check(L.fused_gate_up_q4k_gemv(gate.data_ptr(), up.data_ptr(), p, p + half,
                                            x.data_ptr(), M, N, K, stream),
                   "fused_gate_up_q4k_gemv")
@@ -228,7 +233,7 @@ def setup_workload(torch, dev, index, M, distinct=False):
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_GATE_UP, p, p + half, None, M, 0, 0,
                                  N, K, stream), "q4_pure_read")
         keep += [rot, gate, up, cks]
-        outs, couts = [gate, up], [cks]
+        outs, couts = ([gate] if silu else [gate, up]), [cks]
     elif index == 5:
         E, top_k = d["E"], d["top_k"]
         both = np.concatenate([d["w_gate"].reshape(-1), d["w_up"].reshape(-1)])
@@ -246,6 +251,11 @@ def setup_workload(torch, dev, index, M, distinct=False):
 
         def launch(i, stream):
             p = rot.ptr(i)
+            if silu:
+                check(L.moe_q4_gemv_silu(gate.data_ptr(), p, p + half, x.data_ptr(),
+                                         ids.data_ptr(), M, top_k, E, N, K, stream),
+                      "moe_q4_gemv_silu")
+                return
             check(L.moe_q4_gemv(gate.data_ptr(), up.data_ptr(), p, p + half, x.data_ptr(),
                                 ids.data_ptr(), M, top_k, E, N, K, stream), "moe_q4_gemv")
 
@@ -254,7 +264,7 @@ def setup_workload(torch, dev, index, M, distinct=False):
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_MOE, p, p + half, ids.data_ptr(), M,
                                  top_k, E, N, K, stream), "q4_pure_read")
         keep += [rot, gate, up, cks]
-        outs, couts = [gate, up], [cks]
+        outs, couts = ([gate] if silu else [gate, up]), [cks]
     notes["copies"] = rot.ncopies
     # reference stream: the same byte count as contiguous rows of K * 9/16 bytes
     srb = synth.q4k_row_bytes(K)
@@ -268,14 +278,15 @@ def setup_workload(torch, dev, index, M, distinct=False):
     return wbytes, launch, ceil_launch, notes, keep, outs, couts, (stream_launch, [scks])
 
 
-def measure(torch, dev, index, M, warmup, steps, distinct=False):
+def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False):
     (wbytes, launch, ceil_launch, notes, keep, outs, couts,
-     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct)
+     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu)
     wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
     cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
     swall, sdurs, scnts = time_launches(torch, stream_launch, warmup, steps, souts)
     st, cst, sst = stats(durs, cnts), stats(cdurs, ccnts), stats(sdurs, scnts)
-    res = dict(index=index, M=M, distinct=distinct, weight_bytes=wbytes, wall_s=wall, steps=steps,
+    res = dict(index=index, M=M, distinct=distinct, silu=silu, weight_bytes=wbytes, wall_s=wall,
+               steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
                kernel=st, kernel_gbs=wbytes / (st["mean_ms"] * 1e-3) / 1e9,
                kernel_gbs_median=wbytes / (st["median_ms"] * 1e-3) / 1e9,
@@ -374,6 +385,9 @@ def write_report(path, rows, headline):
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         name = names[r["index"]]
+        if r.get("silu"):
+            name = name.replace("fused_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv").replace(
+                "moe_q4_gemv", "moe_q4_gemv_silu")
         if r["index"] == 5:
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
@@ -412,14 +426,16 @@ def main():
 
     rows = []
     if args.all:
-        for index, Ms in ((1, (1,)), (2, (1, 2, 4, 8)), (3, (1,)), (4, (1, 2, 4, 8)), (5, (4,)),
-                          (-5, (4,))):
+        # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output)
+        for index, Ms, dist, silu in ((1, (1,), 0, 0), (2, (1, 2, 4, 8), 0, 0), (3, (1,), 0, 0),
+                                      (4, (1, 2, 4, 8), 0, 0), (4, (1, 4), 0, 1),
+                                      (5, (4,), 0, 0), (5, (4,), 1, 0), (5, (4,), 0, 1)):
             for M in Ms:
-                r = measure(torch, dev, abs(index), M, args.warmup, args.steps, index < 0)
+                r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu))
                 rows.append(r)
-                print("workload %d%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
+                print("workload %d%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
                       "ceiling, %.1f%% of stream)"
-                      % (abs(index), " distinct" if index < 0 else "", M,
+                      % (index, " distinct" if dist else "", " silu" if silu else "", M,
                          r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
                          100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
                          100 * r["frac_of_stream"]), file=sys.stderr, flush=True)

@@ -36,8 +36,24 @@ constexpr int kBlock1 = 256;
 constexpr int kModeDense = 0;
 constexpr int kModeNorm = 1;
 constexpr int kModeMoe = 2;
+// gate+up calls whose one output is the SiLU-gated product silu(gate) * up
+// (dense, and the expert call)
+constexpr int kModeSilu = 3;
+constexpr int kModeMoeSilu = 4;
+constexpr bool mode_moe(int mode) { return mode == kModeMoe || mode == kModeMoeSilu; }
+constexpr bool mode_silu(int mode) { return mode == kModeSilu || mode == kModeMoeSilu; }
 constexpr int gemv_threads(int M, int mode) {
-    return (M == 1 || mode == kModeMoe) ? kBlock1 : kBlock;
+    return (M == 1 || mode_moe(mode)) ? kBlock1 : kBlock;
+}
+
+// silu(g) * u with silu(g) = g / (1 + exp(-g)), in fp32.  With
+// e = exp(-|g|), which never overflows, silu(g) = g / (1 + e) for g >= 0 and
+// g e / (1 + e) for g < 0: a few ulp everywhere, down to the subnormal range
+// of e (g < -87), where the error stays below (|g| + 1) 2^-148 in absolute.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = expf(-fabsf(g));
+    const float s = (g >= 0.0f ? g : g * e) / (1.0f + e);
+    return s * u;
 }
 constexpr int kMaxPairs = 64;  // M * top_k limit of the expert call
 
@@ -257,7 +273,7 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
 // registers once, and the main loop reads no LDS at all.
 template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, bool XR, bool TAIL>
 __device__ __forceinline__ void gemv_body(const GemvParams& p) {
-    static_assert(!XR || (M == 1 && MODE != kModeMoe), "register-resident x: M = 1 only");
+    static_assert(!XR || (M == 1 && !mode_moe(MODE)), "register-resident x: M = 1 only");
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
     __shared__ float red[8 * 16];
@@ -276,7 +292,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // ---- the wave's task range ----
     int ntasks = p.ntasks;
     int tpe = 1;  // tasks per expert (expert call)
-    if constexpr (MODE == kModeMoe) {
+    if constexpr (mode_moe(MODE)) {
         moe_dedupe<M>(p, moe);
         __syncthreads();
         tpe = p.nrg / p.rgw;
@@ -306,8 +322,8 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         Cursor c;
         c.t = t0;
         c.ui = 0;
-        c.ue = MODE == kModeMoe ? t0 / tpe : 0;
-        c.rgt = MODE == kModeMoe ? t0 - c.ue * tpe : t0;
+        c.ue = mode_moe(MODE) ? t0 / tpe : 0;
+        c.rgt = mode_moe(MODE) ? t0 - c.ue * tpe : t0;
         return c;
     };
     auto next_cursor = [&](Cursor c) {
@@ -315,7 +331,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
             c.ui = 0;
             c.t += tstride;
             c.rgt += tstride;
-            if (MODE == kModeMoe && c.rgt >= tpe) {
+            if (mode_moe(MODE) && c.rgt >= tpe) {
                 c.ue += c.rgt / tpe;
                 c.rgt -= (c.rgt / tpe) * tpe;
             }
@@ -349,7 +365,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         // (an expert index past the dedupe result, possible only for a wave
         // with no tasks, reads a valid expert instead)
         long long ubase = 0;
-        if constexpr (MODE == kModeMoe) {
+        if constexpr (mode_moe(MODE)) {
             const int nu = moe.nu;
             ubase = nu > 0 ? (long long)moe.uexp[min(c.ue, nu - 1)] * p.N : 0ll;
         }
@@ -382,7 +398,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL>(p, xst, xl, xsum, red);
     __syncthreads();
 
-    if constexpr (MODE == kModeMoe) {
+    if constexpr (mode_moe(MODE)) {
         // rows of pairs with an invalid id: NaN (or an all-ones checksum)
         if (moe.invalid) {
             const int P = M * p.top_k;
@@ -396,7 +412,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                         p.cks[total + i] = 0xFFFFFFFFu;
                     } else {
                         p.y0[i] = __builtin_nanf("");
-                        p.y1[i] = __builtin_nanf("");
+                        if constexpr (!mode_silu(MODE)) p.y1[i] = __builtin_nanf("");
                     }
                 }
             }
@@ -436,7 +452,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                 const uint32_t v = unit_checksum<FMT>(w[q], uc);
                 cks[q] += act ? v : 0u;
             }
-        } else if constexpr (MODE == kModeMoe) {
+        } else if constexpr (mode_moe(MODE)) {
             // tokens that chose this expert (uniform across the wave)
             const unsigned int tm = moe.utok[c.ue];
 #pragma unroll
@@ -462,6 +478,37 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         const int r0 = group_row(c);
         const bool last_lane = li == p.lg - 1;
         const float oscale = FMT == kFmtQ4K ? 0x1p24f : 1.0f;
+        if constexpr (mode_silu(MODE) && !PURE) {
+            // one output, h = silu(gate) * up: row r's gate total is q = r,
+            // its up total q = RR + r, both in this lane
+            static_assert(NMAT == 2, "the SiLU-gated product needs the gate and up matrices");
+#pragma unroll
+            for (int r = 0; r < RR; ++r) {
+                const int row = r0 + r;
+                const bool wr = last_lane && row < p.N;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const float g = group_total(acc[r][m], p.lg) * oscale;
+                    const float u = group_total(acc[RR + r][m], p.lg) * oscale;
+                    acc[r][m] = 0.f;
+                    acc[RR + r][m] = 0.f;
+                    if (wr) {
+                        const float h = silu_mul(g, u);
+                        if constexpr (mode_moe(MODE)) {
+                            unsigned long long pm = moe.upairs[c.ue];
+                            while (pm) {
+                                const int pr = __builtin_ctzll(pm);
+                                pm &= pm - 1ull;
+                                if (pr / p.top_k == m) p.y0[(long long)pr * p.N + row] = h;
+                            }
+                        } else {
+                            p.y0[(long long)m * p.N + row] = h;
+                        }
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
@@ -473,7 +520,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                     const uint32_t v = group_total(cks[q], p.lg);
                     cks[q] = 0u;
                     if (wr) {
-                        if constexpr (MODE == kModeMoe) {
+                        if constexpr (mode_moe(MODE)) {
                             const long long P = (long long)M * p.top_k;
                             unsigned long long pm = moe.upairs[c.ue];
                             while (pm) {
@@ -492,7 +539,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                         const float v = group_total(acc[q][m], p.lg) * oscale;
                         acc[q][m] = 0.f;
                         if (wr) {
-                            if constexpr (MODE == kModeMoe) {
+                            if constexpr (mode_moe(MODE)) {
                                 unsigned long long pm = moe.upairs[c.ue];
                                 while (pm) {
                                     const int pr = __builtin_ctzll(pm);

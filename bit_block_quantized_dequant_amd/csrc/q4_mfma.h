@@ -304,8 +304,16 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     const int jrow = lane & 15;  // tile row of this lane's B column and D values
     const int c = lane >> 4;     // k group
     const int st0 = sl * S / KS, st1 = (sl + 1) * S / KS;  // st1 > st0 as KS <= S
-    const int tpm = (p.N + 15) >> 4;  // tiles per matrix (per expert for the expert call)
-    constexpr bool kMoe = MODE == kModeMoe;
+    constexpr bool kMoe = mode_moe(MODE);
+    // SiLU-gated gate+up: a tile is 8 rows of the gate matrix (columns
+    // 0-7) and the same 8 rows of the up matrix (columns 8-15), so that a
+    // row's two totals meet in one 16-lane row of the wave
+    constexpr bool kPair = MODE == kModeSilu;
+    static_assert(!mode_silu(MODE) || (kPair && NMAT == 2 && FMT == kFmtQ4K),
+                  "matrix-core SiLU epilogue: dense Q4_K gate+up only");
+    constexpr int kTileShift = kPair ? 3 : 4;
+    const int tpm = (p.N + (1 << kTileShift) - 1) >> kTileShift;  // tiles per matrix (per
+                                                                   // expert for the expert call)
     __shared__ std::conditional_t<kMoe, MfmaMoe, MfmaNoMoe> moe;
     int nu = 1;  // matrices of NMAT: 1, or the unique selected experts
     if constexpr (kMoe) {
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         nu = __builtin_amdgcn_readfirstlane(moe.d.nu);
     }
     const int per_mat = nu * tpm;  // tiles per matrix
-    const int ntiles = NMAT * per_mat;
+    const int ntiles = (kPair ? 1 : NMAT) * per_mat;
     if (ntiles == 0) return;  // (expert call with no valid id: all waves)
     const int per_round = gridDim.x * TG;
     const int nrounds = (ntiles + per_round - 1) / per_round;
@@ -352,10 +360,10 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     };
     auto tile_at = [&](int t) {
         Tile T;
-        T.mt = NMAT == 2 ? (t >= per_mat ? 1 : 0) : 0;
+        T.mt = (NMAT == 2 && !kPair) ? (t >= per_mat ? 1 : 0) : 0;
         const int rem = t - T.mt * per_mat;
         T.u = kMoe ? rem / tpm : 0;
-        T.row0 = (rem - T.u * tpm) << 4;
+        T.row0 = (rem - T.u * tpm) << kTileShift;
         T.ebase = 0;
         if constexpr (kMoe)
             T.ebase = (long long)__builtin_amdgcn_readfirstlane(moe.d.uexp[T.u]) * p.N;
@@ -385,8 +393,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         const bool idle = r >= nrounds || traw >= ntiles;  // wave-uniform
         const Tile T = tile_at(min(traw, ntiles - 1));
         const int row0 = T.row0;
-        const uint8_t* base = (T.mt ? p.w1 : p.w0) + (T.ebase + row0) * p.row_bytes;
-        const uint32_t lr = (uint32_t)min(jrow, p.N - 1 - row0);
+        const bool up = kPair ? jrow >= 8 : T.mt != 0;
+        const uint8_t* base = (up ? p.w1 : p.w0) + (T.ebase + row0) * p.row_bytes;
+        const uint32_t lr = (uint32_t)min(kPair ? (jrow & 7) : jrow, p.N - 1 - row0);
         const uint32_t off = idle ? 0u : lr * rb + (uint32_t)st * St::kBytes;
         if constexpr (FMT == kFmtQ4K) {
             // header, then 16 bytes of each 64-byte half of the nibbles:
@@ -612,6 +621,25 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                     tot.y += o.y;
                 }
                 const int* ex = (const int*)(lds + ly.exps);
+                if constexpr (kPair) {
+                    // columns j and j + 8 hold row row0 + j of gate and of up
+                    const float ux = __shfl_xor(tot.x, 8, kWave);
+                    const float uy = __shfl_xor(tot.y, 8, kWave);
+                    const int prow = T.row0 + (jrow & 7);
+                    if (jrow < 8 && prow < p.N) {
+#pragma unroll
+                        for (int hm = 0; hm < 2; ++hm) {
+                            const int m = 2 * c + hm;
+                            if (m < M) {
+                                const float sm = pow2f(24 - ex[m]);
+                                const float g = (hm ? tot.y : tot.x) * sm;
+                                const float u = (hm ? uy : ux) * sm;
+                                p.y0[(long long)m * p.N + prow] = silu_mul(g, u);
+                            }
+                        }
+                    }
+                    return;
+                }
                 float* yo = mt ? p.y1 : p.y0;
                 if (row < p.N) {
 #pragma unroll
@@ -647,7 +675,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             ++lr;
         }
     }
-    if constexpr (!PURE) mstage<FMT, M, kMoe ? kModeDense : MODE>(p, lds, ly, red);
+    if constexpr (!PURE) mstage<FMT, M, (kMoe || kPair) ? kModeDense : MODE>(p, lds, ly, red);
     __syncthreads();
 
     const int n = nrounds * (st1 - st0);

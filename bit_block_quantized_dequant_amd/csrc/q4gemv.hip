@@ -221,7 +221,7 @@ int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     // waves per CU instead of 8 with 512-thread groups, 9-14 % faster).
     // Dense batched calls on this kernel run two 512-thread groups.
     constexpr int BS = gemv_threads(M, MODE);
-    constexpr int WGMAX = MODE == kModeMoe ? 4 : 2;
+    constexpr int WGMAX = mode_moe(MODE) ? 4 : 2;
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors
@@ -236,14 +236,14 @@ int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     const int res = resident_per_cu((const void*)kern(false), BS,
                                     gemv_lds_bytes(M, p.K, false), resident);
     const int blocks =
-        plan(p, M, p.K, p.N, RR, MODE == kModeMoe, npairs_max, false, cus, res, BS, WGMAX);
+        plan(p, M, p.K, p.N, RR, mode_moe(MODE), npairs_max, false, cus, res, BS, WGMAX);
     const size_t lds = gemv_lds_bytes(M, p.K, PURE);
     return launch(kern(PURE), p, blocks, lds, stream, big_lds_done, BS);
 }
 
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
 int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
-    if constexpr (M == 1 && MODE != kModeMoe) {
+    if constexpr (M == 1 && !mode_moe(MODE)) {
         // one 64-weight unit per lane per row: K <= 64 * 64 (and then the
         // activations need no staging loop beyond the first kXReg chunks)
         const int upr = p.K / kUnitElems;
@@ -309,7 +309,7 @@ bool moe_mfma_enabled() {
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
 int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
     constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
-    constexpr int kReserve = MODE == kModeMoe ? kMfmaMoeStaticLds : kMfmaStaticLds;
+    constexpr int kReserve = mode_moe(MODE) ? kMfmaMoeStaticLds : kMfmaStaticLds;
     static std::atomic<int> big_lds_done[kMaxDevices];
     const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
     // a pure-read pass takes the launch shape of the call it mirrors
@@ -326,11 +326,16 @@ int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
                                     kMBlock, call_lds, resident);
     if (wgc > res) wgc = res;
     // (the expert call: at most nexperts unique experts, each N rows per matrix)
+    // (the K split is chosen from the 16-row tile count of the plain call,
+    // also for the SiLU-gated call and its 8 + 8-row tiles, so that both
+    // accumulate every row alike)
     const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
     p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
+    const long long ntiles_run =
+        MODE == kModeSilu ? (long long)nexperts * ((p.N + 7) / 8) : ntiles;
     const int TG = kMWaves / p.ks;
     long long blocks = (long long)cus * wgc;
-    const long long need = (ntiles + TG - 1) / TG;
+    const long long need = (ntiles_run + TG - 1) / TG;
     if (blocks > need) blocks = need;
     return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
                   big_lds_done, kMBlock, kReserve);
@@ -345,22 +350,25 @@ int run(GemvParams& p, int M, int npairs_max, void* stream) {
     // (Q4GEMV_MOE_MFMA=1: it measured slower than the VALU expert kernel at
     // the E=64, top-6, 1408 x 2048 shape), from M = 2 on, where its
     // activations leave room in LDS for the expert tables
-    const bool moe_fits = MODE != kModeMoe ||
-                          (moe_mfma_enabled() && M >= 2 &&
+    // (the SiLU-gated expert call always runs the VALU kernel)
+    const bool moe_fits = !mode_moe(MODE) ||
+                          (MODE == kModeMoe && moe_mfma_enabled() && M >= 2 &&
                            mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds);
-    const int min_m = MODE == kModeMoe ? 2 : Q4_MFMA_MIN_M;
-    if (M >= min_m && moe_fits && mfma_enabled()) {
-        const int nexp = MODE == kModeMoe ? npairs_max : 1;
-        switch (M) {
-            case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
-            case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
-            case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
-            case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
-            case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
-            case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
-            case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
+    const int min_m = mode_moe(MODE) ? 2 : Q4_MFMA_MIN_M;
+    if constexpr (MODE != kModeMoeSilu) {
+        if (M >= min_m && moe_fits && mfma_enabled()) {
+            const int nexp = mode_moe(MODE) ? npairs_max : 1;
+            switch (M) {
+                case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
+                case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
+                case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
+                case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
+                case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
+                case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
+                case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
+            }
+            return Q4_ERR_BATCH;
         }
-        return Q4_ERR_BATCH;
     }
     switch (M) {
         case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);
@@ -478,6 +486,35 @@ int moe_q4_gemv(float* gate, float* up, const void* w_gate, const void* w_up, co
     p.E = (int)E;
     const int umax = (int)(M * top_k < E ? M * top_k : E);
     return run<kFmtQ4_0, 2, kModeMoe, false>(p, (int)M, umax, stream);
+}
+
+int fused_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
+                                const float* x, int64_t M, int64_t N, int64_t K,
+                                void* stream) {
+    if (!h || !w_gate || !w_up || !x) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(h, 4))
+        return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w_gate, w_up, h, nullptr, x, N, K, kFmtQ4K);
+    return run<kFmtQ4K, 2, kModeSilu, false>(p, (int)M, 0, stream);
+}
+
+int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float* x,
+                     const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N,
+                     int64_t K, void* stream) {
+    if (!h || !w_gate || !w_up || !x || !ids) return Q4_ERR_NULL;
+    int st = check_moe(M, top_k, E, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(h, 4) ||
+        !aligned(ids, 4))
+        return Q4_ERR_ALIGN;
+    GemvParams p = base_params(w_gate, w_up, h, nullptr, x, N, K, kFmtQ4_0);
+    p.ids = ids;
+    p.top_k = (int)top_k;
+    p.E = (int)E;
+    const int umax = (int)(M * top_k < E ? M * top_k : E);
+    return run<kFmtQ4_0, 2, kModeMoeSilu, false>(p, (int)M, umax, stream);
 }
 
 int dequant_q4k(float* out, const void* w, int64_t N, int64_t K, void* stream) {

@@ -114,6 +114,23 @@ int fused_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate, const voi
                            const float* x, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * SiLU-gated gate+up: the one output
+ *   h[m, n] = silu(gate[m, n]) * up[m, n],  silu(g) = g / (1 + exp(-g)),
+ * with gate and up the two products of fused_gate_up_q4k_gemv (same layouts,
+ * same limits), computed from one staging of X and never written out.  h is
+ * fp32 [M, N] and must not overlap the inputs.  The epilogue is fp32 (a few
+ * ulp); gate and up are accumulated exactly as fused_gate_up_q4k_gemv
+ * accumulates them.  The pages' expert kernel emits one output per (token,
+ * slot, row) from the gate and up matrices; this call is that single output
+ * for the dense pair (inferencelayer 0.2.13, kernel_lab.rs, moe_lab: one
+ * [columns, top_k, rows] output; trueno-gpu 0.4.11, fused.rs,
+ * FusedGateUpQ4KGemvKernel: the pair that shares one input load).
+ */
+int fused_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
+                                const float* x, int64_t M, int64_t N, int64_t K,
+                                void* stream);
+
+/*
  * Expert-selected gate/up GEMV over Q4_0 experts.  w_gate and w_up each hold
  * E expert matrices of N rows, stacked: expert e's row r is global row
  * e*N + r.  ids: int32 [M, top_k], the experts chosen for each token.  For
@@ -130,6 +147,18 @@ int fused_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate, const voi
 int moe_q4_gemv(float* gate, float* up, const void* w_gate, const void* w_up,
                 const float* x, const int32_t* ids, int64_t M, int64_t top_k, int64_t E,
                 int64_t N, int64_t K, void* stream);
+
+/*
+ * SiLU-gated expert call: the one output
+ *   h[m, s, r] = silu(gate[m, s, r]) * up[m, s, r]
+ * with gate and up as moe_q4_gemv computes them (same layouts, limits, id
+ * precondition and expert dedupe; an invalid id yields NaN rows of h).  h is
+ * fp32 [M, top_k, N].  (inferencelayer 0.2.13, kernel_lab.rs, moe_lab: the
+ * expert kernel writes one [columns, top_k, rows] output from w1 and w3.)
+ */
+int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float* x,
+                     const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N,
+                     int64_t K, void* stream);
 
 /*
  * Dequantize N rows of Q4_K to fp32 out[N, K], bit-exact: every weight is

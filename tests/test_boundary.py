@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["q4_0_gemv", "q4k_gemv", "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv",
-              "moe_q4_gemv", "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
+              "fused_gate_up_silu_q4k_gemv", "moe_q4_gemv", "moe_q4_gemv_silu", "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
               "q4_version"]:
         assert n in names, n
 
@@ -98,6 +98,19 @@ def test_gate_up_validation(q4lib):
     assert f(A, A, A, A, A, 1, 16, 100, None) == SHAPE
 
 
+def test_gate_up_silu_validation(q4lib):
+    f = L().fused_gate_up_silu_q4k_gemv
+    assert f(None, A, A, A, 1, 16, 256, None) == NULL
+    assert f(A, A, None, A, 1, 16, 256, None) == NULL
+    assert f(A, A, A, None, 1, 16, 256, None) == NULL
+    assert f(A + 2, A, A, A, 1, 16, 256, None) == ALIGN
+    assert f(A, A + 4, A, A, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A + 8, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A, 1, 16, 100, None) == SHAPE
+    assert f(A, A, A, A, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, 0, 16, 256, None) == BATCH
+
+
 @pytest.mark.parametrize("M,top_k,E,N,K,want", [
     (4, 0, 64, 1408, 2048, SHAPE),
     (4, 65, 64, 1408, 2048, SHAPE),
@@ -110,12 +123,18 @@ def test_gate_up_validation(q4lib):
 ])
 def test_moe_validation(q4lib, M, top_k, E, N, K, want):
     assert L().moe_q4_gemv(A, A, A, A, A, A, M, top_k, E, N, K, None) == want
+    assert L().moe_q4_gemv_silu(A, A, A, A, A, M, top_k, E, N, K, None) == want
 
 
 def test_moe_null_and_align(q4lib):
     f = L().moe_q4_gemv
     assert f(A, A, A, A, A, None, 4, 6, 64, 1408, 2048, None) == NULL
     assert f(A, A, A, A, A, A + 2, 4, 6, 64, 1408, 2048, None) == ALIGN
+    g = L().moe_q4_gemv_silu
+    assert g(None, A, A, A, A, 4, 6, 64, 1408, 2048, None) == NULL
+    assert g(A, A, A, A, None, 4, 6, 64, 1408, 2048, None) == NULL
+    assert g(A + 2, A, A, A, A, 4, 6, 64, 1408, 2048, None) == ALIGN
+    assert g(A, A, A, A, A + 2, 4, 6, 64, 1408, 2048, None) == ALIGN
 
 
 def test_dequant_validation(q4lib):
