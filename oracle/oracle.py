@@ -65,6 +65,11 @@ class Oracle:
         L.oracle_moe_q4_0_gemv.restype = None
         L.oracle_silu_mul.argtypes = [_f64p, _f64p, _i64, _f64p]
         L.oracle_silu_mul.restype = None
+        L.oracle_topk_softmax.argtypes = [_f64p, _i64, _i64, _i64, _int, _i32p, _f64p]
+        L.oracle_topk_softmax.restype = None
+        L.oracle_moe_router_q4_0.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64, _int, _i32p,
+                                             _f64p, _f64p, _f64p]
+        L.oracle_moe_router_q4_0.restype = None
         L.oracle_row_checksum.argtypes = [_u8p, _i64, _i64, _u32p]
         L.oracle_row_checksum.restype = None
         self.L = L
@@ -170,6 +175,32 @@ class Oracle:
         h = np.empty_like(g)
         self.L.oracle_silu_mul(_p(g, _f64p), _p(u, _f64p), g.size, _p(h, _f64p))
         return h
+
+    def topk_softmax(self, logits, top_k: int, normalize: bool):
+        """Returns (ids int32 [M, top_k], weights float64 [M, top_k])."""
+        lg = _c(np.atleast_2d(np.asarray(logits, dtype=np.float64)), np.float64)
+        M, E = lg.shape
+        ids = np.empty((M, top_k), dtype=np.int32)
+        wts = np.empty((M, top_k), dtype=np.float64)
+        self.L.oracle_topk_softmax(_p(lg, _f64p), M, E, top_k, int(bool(normalize)),
+                                   _p(ids, _i32p), _p(wts, _f64p))
+        return ids, wts
+
+    def moe_router_q4_0(self, w, x, E: int, K: int, top_k: int, normalize: bool):
+        """Returns (ids, weights, logits, abslogits): int32 [M, top_k], float64
+        [M, top_k], float64 [M, E] twice."""
+        w = _c(w, np.uint8)
+        x = _c(np.atleast_2d(x), np.float32)
+        M = x.shape[0]
+        assert x.shape[1] == K and w.size == E * (K // 32) * 18
+        ids = np.empty((M, top_k), dtype=np.int32)
+        wts = np.empty((M, top_k), dtype=np.float64)
+        lg = np.empty((M, E), dtype=np.float64)
+        ab = np.empty((M, E), dtype=np.float64)
+        self.L.oracle_moe_router_q4_0(_p(w, _u8p), _p(x, _f32p), M, E, K, top_k,
+                                      int(bool(normalize)), _p(ids, _i32p), _p(wts, _f64p),
+                                      _p(lg, _f64p), _p(ab, _f64p))
+        return ids, wts, lg, ab
 
     def row_checksum(self, w, nrows: int, row_bytes: int) -> np.ndarray:
         w = _c(w, np.uint8)

@@ -16,6 +16,9 @@
  *          6-bit scale/min extraction for sub-blocks 0-3 and 4-7; 64-value
  *          qs chunks with low nibbles first; value = d*scale*q - dmin*min)
  *        - FusedGateUpQ4KGemvKernel doc comment (two outputs, one input)
+ *  [AT]  atlas, spark_model/layers/ops/gemm_quant.rs
+ *        - moe_gate_topk_fused (router: gate GEMV over the experts, top-K
+ *          indices and softmax weights, normalize flag)
  *  [IL]  inferencelayer 0.2.13, src/bin/kernel_lab.rs
  *        - GEMV_F16S WGSL (q4_lo / q4_hi: low nibble of byte j is element j,
  *          high nibble is element j+16, both minus 8, times the f16 scale)
@@ -304,6 +307,75 @@ void oracle_silu_mul(const double* g, const double* u, int64_t n, double* h)
         double s = g[i] / (1.0 + exp(-g[i]));
         h[i] = s * u[i];
     }
+}
+
+/* ------------------------------------------------------------------------
+ * Router top-k with softmax weights, per token row of logits [M, E]
+ * ([AT] moe_gate_topk_fused: gate logits over the experts, then the top-K
+ * indices and their softmax weights, with a normalize flag).
+ *   ids[m, s]: the s-th largest logit's expert (s = 0 first), by repeated
+ *              argmax; equal logits go to the lower expert index, and a NaN
+ *              logit ranks as -inf.
+ *   weights:   p_e = exp(l_e - lmax) / D with lmax the largest logit and D
+ *              the sum over the selected experts (normalize != 0) or over
+ *              all E experts (normalize == 0: the full softmax's entries).
+ * Double throughout.
+ * ---------------------------------------------------------------------- */
+void oracle_topk_softmax(const double* logits, int64_t M, int64_t E, int64_t top_k,
+                         int normalize, int32_t* ids, double* weights)
+{
+    char* taken = (char*)malloc((size_t)E);
+    for (int64_t m = 0; m < M; ++m) {
+        const double* l = logits + m * E;
+        memset(taken, 0, (size_t)E);
+        for (int64_t s = 0; s < top_k; ++s) {
+            int64_t best = -1;
+            double bv = 0.0;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                double v = isnan(l[e]) ? -INFINITY : l[e];
+                if (best < 0 || v > bv) {
+                    best = e;
+                    bv = v;
+                }
+            }
+            taken[best] = 1;
+            ids[m * top_k + s] = (int32_t)best;
+        }
+        double lmax = l[ids[m * top_k]];
+        if (isnan(lmax)) lmax = -INFINITY;
+        double den = 0.0;
+        if (normalize) {
+            for (int64_t s = 0; s < top_k; ++s) {
+                double v = l[ids[m * top_k + s]];
+                den += isnan(v) ? 0.0 : exp(v - lmax);
+            }
+        } else {
+            for (int64_t e = 0; e < E; ++e) den += isnan(l[e]) ? 0.0 : exp(l[e] - lmax);
+        }
+        for (int64_t s = 0; s < top_k; ++s) {
+            double v = l[ids[m * top_k + s]];
+            weights[m * top_k + s] = isnan(v) ? 0.0 : exp(v - lmax) / den;
+        }
+    }
+    free(taken);
+}
+
+/* The router: Q4_0 gate logits over E expert rows (the plain GEMV), then
+ * oracle_topk_softmax.  logits / abslogits ([M, E], may be NULL) receive the
+ * logits and their sums of |w x|. */
+void oracle_moe_router_q4_0(const uint8_t* w, const float* x, int64_t M, int64_t E, int64_t K,
+                            int64_t top_k, int normalize, int32_t* ids, double* weights,
+                            double* logits, double* abslogits)
+{
+    double* l = (double*)malloc(sizeof(double) * (size_t)(M * E));
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * E));
+    oracle_q4_0_gemv(w, x, M, E, K, l, a, 1);
+    oracle_topk_softmax(l, M, E, top_k, normalize, ids, weights);
+    if (logits) memcpy(logits, l, sizeof(double) * (size_t)(M * E));
+    if (abslogits) memcpy(abslogits, a, sizeof(double) * (size_t)(M * E));
+    free(l);
+    free(a);
 }
 
 /* Per-row checksum of packed weight rows: the sum of the row's little-endian

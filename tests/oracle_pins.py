@@ -19,6 +19,9 @@ Sources:
     GEMV_F16S WGSL (Q4_0 nibble order, d*(q-8)); moe_lab / MOE_PURE_READ
     (expert-stacked rows, per-(token, slot) selection, one output per
     (token, slot, row) from the gate and up matrices, read as the SiLU gate).
+  atlas, spark_model/layers/ops/gemm_quant.rs --
+    moe_gate_topk_fused (router: gate GEMV, top-K indices, softmax weights,
+    normalize flag).
 """
 import math
 import os
@@ -403,7 +406,61 @@ def pin_silu(o):
     assert np.all(np.isnan(o.silu_mul([np.nan, 1.0], [1.0, np.nan])))
 
 
+def pin_topk_softmax(o):
+    """Router selection and weights: numpy's stable descending argsort (ties
+    to the lower expert), numpy softmax over the selected experts
+    (normalize) or over all experts; all-equal logits give 1/top_k and 1/E;
+    logits (0, ln 3) give weights 3/4, 1/4; large logits stay finite (the
+    max is subtracted); shift invariance; a NaN logit ranks last with weight
+    0; normalized weights sum to 1."""
+    rng = np.random.default_rng(31)
+    lg = np.round(rng.normal(0.0, 2.0, (5, 37)), 1)  # rounding makes ties
+    for k in (1, 3, 8, 37):
+        for norm in (True, False):
+            ids, w = o.topk_softmax(lg, k, norm)
+            want = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+            assert np.array_equal(ids, want), (k, norm)
+            sel = np.take_along_axis(lg, want, axis=1)
+            ex = np.exp(sel - lg.max(axis=1, keepdims=True))
+            den = ex.sum(axis=1, keepdims=True) if norm else \
+                np.exp(lg - lg.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)
+            assert np.allclose(w, ex / den, rtol=1e-14, atol=0.0), (k, norm)
+            if norm:
+                assert np.allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+            ids2, w2 = o.topk_softmax(lg + 123.0, k, norm)
+            assert np.array_equal(ids2, ids) and np.allclose(w2, w, rtol=1e-13, atol=0.0)
+    ids, w = o.topk_softmax(np.zeros((1, 10)), 4, True)
+    assert np.array_equal(ids[0], [0, 1, 2, 3]) and np.all(w == 0.25)
+    ids, w = o.topk_softmax(np.zeros((1, 10)), 4, False)
+    assert np.all(w == 0.1)
+    ids, w = o.topk_softmax([[0.0, math.log(3.0)]], 2, True)
+    assert np.array_equal(ids[0], [1, 0])
+    assert abs(w[0, 0] - 0.75) <= 1e-15 and abs(w[0, 1] - 0.25) <= 1e-15
+    ids, w = o.topk_softmax([[1000.0, 999.0, 0.0]], 2, True)
+    e1 = math.exp(-1.0)
+    assert np.array_equal(ids[0], [0, 1])
+    assert abs(w[0, 0] - 1.0 / (1.0 + e1)) <= 1e-15 and abs(w[0, 1] - e1 / (1.0 + e1)) <= 1e-15
+    ids, w = o.topk_softmax([[np.nan, 1.0, 2.0], [np.nan, np.nan, 1.0]], 3, True)
+    assert np.array_equal(ids, [[2, 1, 0], [2, 0, 1]])
+    assert w[0, 2] == 0.0 and w[1, 1] == 0.0 and w[1, 2] == 0.0 and w[1, 0] == 1.0
+
+
+def pin_router(o):
+    """The router is the plain Q4_0 GEMV of the token rows against the E
+    expert rows, followed by the top-k softmax of those logits."""
+    rng = synth.make_rng(37)
+    E, K, M = 24, 512, 3
+    w = synth.q4_0_matrix(rng, E, K)
+    x = synth.activations(rng, M, K)
+    for k, norm in ((2, True), (6, False), (24, True)):
+        ids, wts, lg, ab = o.moe_router_q4_0(w, x, E, K, k, norm)
+        y, a = o.q4_0_gemv(w, x, E, K)
+        assert np.array_equal(lg, y) and np.array_equal(ab, a)
+        ids2, w2 = o.topk_softmax(y, k, norm)
+        assert np.array_equal(ids, ids2) and np.array_equal(wts, w2)
+
+
 # fast pins first: the mutant test stops at the first failing pin
-ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_silu,
-            pin_gemv_onehot_and_scaling, pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
+ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_silu, pin_topk_softmax,
+            pin_router, pin_gemv_onehot_and_scaling, pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
             pin_rmsnorm, pin_composites, pin_f16_decode, pin_bruteforce]

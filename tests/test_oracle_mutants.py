@@ -46,6 +46,12 @@ MUTANTS = {
     "checksum byte order": ("((uint32_t)r[b + 2] << 16)", "((uint32_t)r[b + 2] << 8)"),
     "silu sigmoid of +g": ("exp(-g[i])", "exp(g[i])"),
     "silu drops up": ("h[i] = s * u[i];", "h[i] = s;"),
+    "top-k ties to the higher index": ("if (best < 0 || v > bv) {", "if (best < 0 || v >= bv) {"),
+    "softmax without the max shift": ("den += isnan(v) ? 0.0 : exp(v - lmax);",
+                                      "den += isnan(v) ? 0.0 : exp(v);"),
+    "normalize flag ignored": ("if (normalize) {", "if (0) {"),
+    "router logits of token 0 only": ("oracle_q4_0_gemv(w, x, M, E, K, l, a, 1);",
+                                      "oracle_q4_0_gemv(w, x, 1, E, K, l, a, 1);"),
     "silu without g": ("double s = g[i] / (1.0 + exp(-g[i]));",
                        "double s = 1.0 / (1.0 + exp(-g[i]));"),
 }
