@@ -300,6 +300,33 @@ def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False):
     return res
 
 
+def measure_router(torch, dev, warmup, steps):
+    """The router at the expert call's shape (4 tokens, 64 experts, K = 2048,
+    top-6, normalized): 73,728 bytes of Q4_0 router weights per call, rotated
+    over 1 GiB of copies like the other workloads; one launch, latency-bound,
+    so only its duration is reported."""
+    import numpy as np
+
+    import bit_block_quantized_dequant_amd as q4
+    from bit_block_quantized_dequant_amd import synth
+    L = q4.lib()
+    d = synth.workload_inputs(5)
+    M, E, K, top_k = d["M"], d["E"], d["K"], d["top_k"]
+    rng = synth.make_rng(8100)
+    wr = synth.q4_0_matrix(rng, E, K)
+    rot = Rotation(torch, dev, wr)
+    x = torch.from_numpy(np.ascontiguousarray(d["x"])).to(dev)
+    ids = torch.empty(M, top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(M, top_k, device=dev)
+
+    def launch(i, stream):
+        check(L.moe_router_q4_0(ids.data_ptr(), wts.data_ptr(), rot.ptr(i), x.data_ptr(), M, E,
+                                K, top_k, 1, stream), "moe_router_q4_0")
+    wall, durs, cnts = time_launches(torch, launch, warmup, steps, [ids, wts])
+    st = stats(durs, cnts)
+    return dict(M=M, E=E, K=K, top_k=top_k, weight_bytes=int(wr.nbytes), kernel=st)
+
+
 def cpu_baseline(seconds):
     """The oracle's gate+up GEMV of the headline workload, timed on the host."""
     from bit_block_quantized_dequant_amd import synth
@@ -374,9 +401,9 @@ def copy_calibration(torch, dev, mib):
           % (20, n * 4, n * 4), flush=True)
 
 
-def write_report(path, rows, headline):
+def write_report(path, rows, headline, router=None):
     with open(path + ".json", "w") as f:
-        json.dump(dict(headline=headline, workloads=rows), f, indent=1)
+        json.dump(dict(headline=headline, workloads=rows, router=router), f, indent=1)
     names = {1: "q4_0_gemv K=512 N=256", 2: "q4_0_gemv K=4096 N=4096",
              3: "fused_rmsnorm_q4k_gemv K=3584 N=18944", 4: "fused_gate_up_q4k_gemv K=4096 N=14336x2",
              5: "moe_q4_gemv E=64 top6 N=1408 K=2048"}
@@ -397,6 +424,12 @@ def write_report(path, rows, headline):
                          r["kernel_gbs"], 100 * r["frac_of_peak"], r["ceiling_gbs"],
                          100 * r["frac_of_ceiling"], r["stream_gbs"], 100 * r["frac_of_stream"],
                          r["kernel"]["spread"]))
+    if router:
+        lines += ["", "router (moe_router_q4_0) M=%d E=%d K=%d top-%d: %.2f us median, %.2f us "
+                  "min (latency-bound: %d bytes of weights)"
+                  % (router["M"], router["E"], router["K"], router["top_k"],
+                     router["kernel"]["median_ms"] * 1e3, router["kernel"]["min_ms"] * 1e3,
+                     router["weight_bytes"])]
     with open(path + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -440,6 +473,12 @@ def main():
                          100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
                          100 * r["frac_of_stream"]), file=sys.stderr, flush=True)
 
+    router = None
+    if args.all:
+        router = measure_router(torch, dev, args.warmup, args.steps)
+        print("router M=4 E=64 K=2048 top-6: %.2f us (median)"
+              % (router["kernel"]["median_ms"] * 1e3), file=sys.stderr, flush=True)
+
     cpu = cpu_baseline(args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     ms_per_step = head["wall_s"] / head["steps"] * 1e3
@@ -479,7 +518,7 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.all:
-        write_report(args.all, rows, line)
+        write_report(args.all, rows, line, router)
     print(json.dumps(line), flush=True)
 
 

@@ -19,7 +19,7 @@ import os
 __all__ = [
     "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv",
-    "moe_q4_gemv", "moe_q4_gemv_silu", "dequant_q4k",
+    "moe_q4_gemv", "moe_q4_gemv_silu", "moe_router_q4_0", "dequant_q4k",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "LIB_PATH", "q4_0_row_bytes",
     "q4k_row_bytes",
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "fused_gate_up_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
             "fused_gate_up_silu_q4k_gemv": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
             "moe_q4_gemv_silu": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
+            "moe_router_q4_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp],
             "moe_q4_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "dequant_q4k": [_vp, _vp, _i64, _i64, _vp],
             "dequant_q4_0": [_vp, _vp, _i64, _i64, _vp],
@@ -211,6 +212,17 @@ def moe_q4_gemv_silu(h, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
     pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4), dev)
     _ok(lib().moe_q4_gemv_silu(ph, pwg, pwu, px, pi, M, top_k, E, N, K, _stream(stream, dev)),
         "moe_q4_gemv_silu")
+
+
+def moe_router_q4_0(ids, weights, w_router, x, M, E, K, top_k, normalize, stream=None):
+    """ids/weights[M, top_k]: each token's top_k experts by Q4_0 gate logit and
+    their softmax weights (normalized over the selection, or the full softmax's)."""
+    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4))
+    pw, dev = _ptr(weights, "weights", _sz(M * top_k, 4), dev)
+    pr, dev = _ptr(w_router, "w_router", _sz(E, q4_0_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    _ok(lib().moe_router_q4_0(pi, pw, pr, px, M, E, K, top_k, int(normalize),
+                              _stream(stream, dev)), "moe_router_q4_0")
 
 
 def dequant_q4k(out, w, N, K, stream=None):

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4gemv.so")
 SOURCES = [os.path.join(CSRC, "q4gemv.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("q4_device.h", "q4_kernels.h")] + [
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("q4_device.h", "q4_kernels.h", "q4_mfma.h",
+                                                  "q4_router.h")] + [
     os.path.join(ROOT, "include", "q4gemv.h")]
 ARCH = "gfx950"
 

@@ -17,6 +17,7 @@
 
 #include "q4_kernels.h"
 #include "q4_mfma.h"
+#include "q4_router.h"
 #include "q4gemv.h"
 
 using namespace q4;
@@ -515,6 +516,29 @@ int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float
     p.E = (int)E;
     const int umax = (int)(M * top_k < E ? M * top_k : E);
     return run<kFmtQ4_0, 2, kModeMoeSilu, false>(p, (int)M, umax, stream);
+}
+
+int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const float* x,
+                    int64_t M, int64_t E, int64_t K, int64_t top_k, int normalize,
+                    void* stream) {
+    if (!ids || !weights || !w_router || !x) return Q4_ERR_NULL;
+    if (M < 1 || M > 8) return Q4_ERR_BATCH;
+    if (K <= 0 || K % 256 != 0 || K > kRouterMaxK) return Q4_ERR_SHAPE;
+    if (E < 1 || E > kRouterMaxE || top_k < 1 || top_k > E || top_k > kRouterMaxTopK)
+        return Q4_ERR_SHAPE;
+    if (normalize != 0 && normalize != 1) return Q4_ERR_ARG;
+    if (!aligned(w_router, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4))
+        return Q4_ERR_ALIGN;
+    const size_t lds = router_lds_bytes((int)K, (int)E);
+    if (lds > 64 * 1024) {
+        static std::atomic<int> big_lds_done[kMaxDevices];
+        int st = allow_big_lds((const void*)router_kernel, big_lds_done);
+        if (st) return st;
+    }
+    hipLaunchKernelGGL(router_kernel, dim3((unsigned)M), dim3(kRouterBlock), lds,
+                       (hipStream_t)stream, ids, weights, (const uint8_t*)w_router, x, (int)E,
+                       (int)K, (int)top_k, normalize);
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
 }
 
 int dequant_q4k(float* out, const void* w, int64_t N, int64_t K, void* stream) {

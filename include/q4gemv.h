@@ -161,6 +161,32 @@ int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float
                      int64_t K, void* stream);
 
 /*
+ * Expert router: the gate logits of each token row against E expert rows,
+ * then its top_k experts and their softmax weights, in one launch
+ * (atlas, spark_model/layers/ops/gemm_quant.rs, moe_gate_topk_fused: gate
+ * GEMV over the experts, top-K indices and softmax weights, normalize flag;
+ * here over Q4_0 router weights and for M <= 8 token rows).
+ *   logits l[m, e] = sum_k Wr[e, k] * x[m, k], Wr: E rows of Q4_0 (K/32
+ *                    blocks of 18 bytes each), x: fp32 [M, K]
+ *   ids[m, s]      int32 [M, top_k]: the s-th largest logit's expert, s = 0
+ *                  first; equal logits go to the lower expert index and a
+ *                  NaN logit ranks as -inf
+ *   weights[m, s]  fp32 [M, top_k]: exp(l - lmax) / D, with D summed over
+ *                  the selected experts (normalize = 1: the weights sum to
+ *                  1) or over all E experts (normalize = 0: the entries of
+ *                  the full softmax)
+ * The ids are in the layout moe_q4_gemv and moe_q4_gemv_silu take.  The
+ * logits are fp32 sums within 1e-4 * sum_k |w x| of the exact ones; where
+ * two experts' logits are closer than that, either order is correct.
+ * Limits: M in [1, 8] (Q4_ERR_BATCH); K % 256 == 0 and K <= 32768;
+ * 1 <= E <= 1024; 1 <= top_k <= min(E, 64) (Q4_ERR_SHAPE); normalize 0 or
+ * 1 (Q4_ERR_ARG).  Alignment: Wr and x 16 bytes, ids and weights 4.
+ */
+int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const float* x,
+                    int64_t M, int64_t E, int64_t K, int64_t top_k, int normalize,
+                    void* stream);
+
+/*
  * Dequantize N rows of Q4_K to fp32 out[N, K], bit-exact: every weight is
  * the correctly rounded fp32 value of d*sc*q - dmin*m.
  * (trueno-gpu 0.4.11, fused.rs, FusedRmsNormQ4KGemvKernel PHASE 3.)

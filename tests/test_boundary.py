@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["q4_0_gemv", "q4k_gemv", "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv",
-              "fused_gate_up_silu_q4k_gemv", "moe_q4_gemv", "moe_q4_gemv_silu", "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
+              "fused_gate_up_silu_q4k_gemv", "moe_q4_gemv", "moe_q4_gemv_silu", "moe_router_q4_0",
+              "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
               "q4_version"]:
         assert n in names, n
 
@@ -135,6 +136,32 @@ def test_moe_null_and_align(q4lib):
     assert g(A, A, A, A, None, 4, 6, 64, 1408, 2048, None) == NULL
     assert g(A + 2, A, A, A, A, 4, 6, 64, 1408, 2048, None) == ALIGN
     assert g(A, A, A, A, A + 2, 4, 6, 64, 1408, 2048, None) == ALIGN
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, A, A, A, 4, 64, 2048, 6, 1, None), NULL),
+    ((A, None, A, A, 4, 64, 2048, 6, 1, None), NULL),
+    ((A, A, None, A, 4, 64, 2048, 6, 1, None), NULL),
+    ((A, A, A, None, 4, 64, 2048, 6, 1, None), NULL),
+    ((A, A, A, A, 0, 64, 2048, 6, 1, None), BATCH),
+    ((A, A, A, A, 9, 64, 2048, 6, 1, None), BATCH),
+    ((A, A, A, A, 4, 0, 2048, 1, 1, None), SHAPE),
+    ((A, A, A, A, 4, 1025, 2048, 6, 1, None), SHAPE),
+    ((A, A, A, A, 4, 64, 2000, 6, 1, None), SHAPE),
+    ((A, A, A, A, 4, 64, 65536, 6, 1, None), SHAPE),
+    ((A, A, A, A, 4, 64, 2048, 0, 1, None), SHAPE),
+    ((A, A, A, A, 4, 64, 2048, 65, 1, None), SHAPE),
+    ((A, A, A, A, 4, 100, 2048, 65, 1, None), SHAPE),
+    ((A, A, A, A, 4, 4, 2048, 5, 1, None), SHAPE),
+    ((A, A, A, A, 4, 64, 2048, 6, 2, None), ARG),
+    ((A, A, A, A, 4, 64, 2048, 6, -1, None), ARG),
+    ((A + 2, A, A, A, 4, 64, 2048, 6, 1, None), ALIGN),
+    ((A, A + 2, A, A, 4, 64, 2048, 6, 1, None), ALIGN),
+    ((A, A, A + 4, A, 4, 64, 2048, 6, 1, None), ALIGN),
+    ((A, A, A, A + 8, 4, 64, 2048, 6, 1, None), ALIGN),
+])
+def test_router_validation(q4lib, args, want):
+    assert L().moe_router_q4_0(*args) == want
 
 
 def test_dequant_validation(q4lib):
