@@ -58,6 +58,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--all", metavar="REPORT", default=None,
                     help="also time every named workload; write REPORT.json / REPORT.md")
+    ap.add_argument("--chain", action="store_true",
+                    help="only time dispatch chains: the smallest call back to back, and the "
+                         "router + SiLU expert call sequence, eager and as HIP graph replays")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 20 times (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -327,6 +330,74 @@ def measure_router(torch, dev, warmup, steps):
     return dict(M=M, E=E, K=K, top_k=top_k, weight_bytes=int(wr.nbytes), kernel=st)
 
 
+def measure_chain(torch, dev, n=300):
+    """Dispatch cost on one stream (inferencelayer kernel_lab: the dependent-
+    dispatch chain probe, N tiny dispatches in one submission).  Two chains:
+    n back-to-back calls of the smallest workload (Q4_0 K=512 N=256, M=1),
+    each reading what the stream order makes it wait for; and n decode steps
+    of the expert path at the expert call's shape (router over 64 Q4_0 expert
+    rows, then moe_q4_gemv_silu on the ids it wrote, which never leave the
+    device).  Each chain runs eagerly (one host launch per call, through the
+    binding's ctypes calls) and as one captured HIP graph; returns the wall
+    time per call or step, after a device synchronization on both sides."""
+    import numpy as np
+
+    import bit_block_quantized_dequant_amd as q4
+    from bit_block_quantized_dequant_amd import synth
+    L = q4.lib()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    d1 = synth.workload_inputs(1)
+    w1, x1 = T(d1["w"]), T(d1["x"])
+    y1 = torch.empty(d1["M"], d1["N"], device=dev)
+    d5 = synth.workload_inputs(5)
+    M, E, N, K, top_k = d5["M"], d5["E"], d5["N"], d5["K"], d5["top_k"]
+    wr = T(synth.q4_0_matrix(synth.make_rng(8100), E, K))
+    wg, wu, x5 = T(d5["w_gate"]), T(d5["w_up"]), T(d5["x"])
+    ids = torch.empty(M, top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(M, top_k, device=dev)
+    h = torch.empty(M, top_k, N, device=dev)
+
+    def small(stream):
+        check(L.q4_0_gemv(y1.data_ptr(), w1.data_ptr(), x1.data_ptr(), 1, d1["N"], d1["K"],
+                          stream), "q4_0_gemv")
+
+    def step(stream):
+        check(L.moe_router_q4_0(ids.data_ptr(), wts.data_ptr(), wr.data_ptr(), x5.data_ptr(), M,
+                                E, K, top_k, 1, stream), "moe_router_q4_0")
+        check(L.moe_q4_gemv_silu(h.data_ptr(), wg.data_ptr(), wu.data_ptr(), x5.data_ptr(),
+                                 ids.data_ptr(), M, top_k, E, N, K, stream), "moe_q4_gemv_silu")
+
+    out = {}
+    s = torch.cuda.Stream()  # default priority
+    for name, fn in (("small_call", small), ("router_then_silu_expert_call", step)):
+        with torch.cuda.stream(s):
+            for _ in range(20):
+                fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            for _ in range(n):
+                fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / n
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            for _ in range(n):
+                fn(s.cuda_stream)
+            g.capture_end()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        graph = (time.perf_counter() - t0) / n
+        out[name] = dict(n=n, eager_us=eager * 1e6, graph_us=graph * 1e6)
+        print("chain %-30s %d in a row: eager %.2f us each, graph replay %.2f us each"
+              % (name, n, eager * 1e6, graph * 1e6), file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_baseline(seconds):
     """The oracle's gate+up GEMV of the headline workload, timed on the host."""
     from bit_block_quantized_dequant_amd import synth
@@ -449,6 +520,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration > 0:
         copy_calibration(torch, dev, args.copy_calibration)
+        return
+    if args.chain:
+        print(json.dumps({"chain": measure_chain(torch, dev)}), flush=True)
         return
 
     head = measure(torch, dev, 4, 1, args.warmup, args.steps)
