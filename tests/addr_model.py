@@ -161,13 +161,17 @@ def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
     return ks
 
 
-def mfma_plan(fmt, M, K, N, nmat, cus=256, nexperts=1):
+def mfma_plan(fmt, M, K, N, nmat, cus=256, nexperts=1, pair=False):
+    """pair: the SiLU-gated gate+up call, whose tiles are 8 gate rows and the
+    same 8 up rows; its K split still comes from the 16-row tile count."""
     lds = mlayout(fmt, M, K)["bytes"]
     wgc = max(1, min(2, LDS_CAP // lds))
     ntiles = nmat * nexperts * ((N + 15) // 16)
     steps = K // 256
     KS = mfma_ks(ntiles, steps, cus)
     TG = 8 // KS
+    if pair:
+        ntiles = nexperts * ((N + 7) // 8)
     blocks = min(cus * wgc, (ntiles + TG - 1) // TG)
     return dict(lds=lds, blocks=blocks, ntiles=ntiles, TG=TG, KS=KS, steps=steps)
 
@@ -184,20 +188,21 @@ def mfma_positions(S, KS, nrounds, wave, PD):
     return [(q // ns, st0 + q % ns) for q in range(visits + PD)]
 
 
-def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1):
+def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, pair=False):
     """Yield (matrix, byte offset, nbytes) of every weight load; for the
     expert call, `experts` is the dedupe result and umax the host's bound on
     its length (which sizes the grid and the K split)."""
-    pl = mfma_plan(fmt, M, K, N, nmat, cus, umax if experts is not None else 1)
+    pl = mfma_plan(fmt, M, K, N, nmat, cus, umax if experts is not None else 1, pair)
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
     SB, PD = 144, (2 if fmt == "q4k" else 3)
     S, KS = pl["steps"], pl["KS"]
     while KS > S:  # the kernel's own clamp
         KS //= 2
-    tpm = (N + 15) // 16
+    shift = 3 if pair else 4
+    tpm = (N + (1 << shift) - 1) >> shift
     nu = len(experts) if experts is not None else 1
     per_mat = nu * tpm
-    ntiles = nmat * per_mat
+    ntiles = (1 if pair else nmat) * per_mat
     if ntiles == 0:
         return
     TG, G = 8 // KS, pl["blocks"]
@@ -210,15 +215,16 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1):
                 traw = (rr * G + b) * TG + grp
                 idle = r >= nrounds or traw >= ntiles
                 t = min(traw, ntiles - 1)
-                mt = 1 if (nmat == 2 and t >= per_mat) else 0
-                rem = t - mt * per_mat
+                tmt = 1 if (nmat == 2 and not pair and t >= per_mat) else 0
+                rem = t - tmt * per_mat
                 u = rem // tpm if experts is not None else 0
-                row0 = (rem - u * tpm) * 16
+                row0 = (rem - u * tpm) << shift
                 ebase = experts[u] * N if experts is not None else 0
                 base = (ebase + row0) * rb
                 for lane in range(64):
                     jrow, c = lane & 15, lane >> 4
-                    lr = min(jrow, N - 1 - row0) & U32
+                    mt = (1 if jrow >= 8 else 0) if pair else tmt
+                    lr = min(jrow & 7 if pair else jrow, N - 1 - row0) & U32
                     off = 0 if idle else (lr * rb + st * SB) & U32
                     if fmt == "q4k":
                         co = 0 if idle else 16 * c
@@ -233,13 +239,13 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1):
                             yield mt, base + o, 16
 
 
-def mfma_check(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, E=1):
-    pl = mfma_plan(fmt, M, K, N, nmat, cus)
+def mfma_check(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, E=1, pair=False):
+    pl = mfma_plan(fmt, M, K, N, nmat, cus, pair=pair)
     assert pl["lds"] <= LDS_CAP, (fmt, M, K, pl["lds"])
     rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
     limit = (E if experts is not None else 1) * N * rb
     n = 0
-    for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus, experts, umax):
+    for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus, experts, umax, pair):
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
         n += 1
     return n
@@ -311,3 +317,43 @@ def mfma_lds_check(fmt, M, K):
                 assert ch * 16 + 16 <= Q40_WAVE_BYTES
     assert ly["part"] + 2 * 8 * 64 * 8 == ly["wbuf"]
     return True
+
+
+# ---------------------------------------------------------------------------
+# Router (q4_router.h): one workgroup of 8 waves per token.
+# ---------------------------------------------------------------------------
+def router_loads(E, K, waves=8, rows=4):
+    """Yield (byte offset, nbytes) of every weight load of one token's
+    workgroup (router_kernel's logits loop)."""
+    upr = K // 64
+    lgw = 1
+    while lgw < upr and lgw < 64:
+        lgw <<= 1
+    rpp = 64 // lgw
+    upl = (upr + lgw - 1) // lgw
+    rb = (K // 32) * 18
+    step = waves * rpp * rows
+    for wave in range(waves):
+        e0 = wave * rpp * rows
+        while e0 < E:
+            for lane in range(64):
+                gi, li = lane // lgw, lane % lgw
+                for i in range(upl):
+                    u = li + lgw * i
+                    uc = u if u < upr else upr - 1
+                    for q in range(rows):
+                        e = min(e0 + q * rpp + gi, E - 1)
+                        base = e * rb + uc * Q40_PAIR
+                        yield base, 16
+                        yield base + 16, 16
+                        yield base + 32, 4
+            e0 += step
+
+
+def router_check(E, K):
+    limit = E * (K // 32) * 18
+    n = 0
+    for off, nb in router_loads(E, K):
+        assert 0 <= off and off + nb <= limit, (E, K, off, nb, limit)
+        n += 1
+    return n

@@ -130,3 +130,19 @@ def test_batched_expert_loads_in_bounds(experts, E, N, K, M, top_k):
     umax = min(M * top_k, E)
     for cus in (4, 256):
         A.mfma_check("q4_0", M, N, K, 2, cus=cus, experts=experts, umax=umax, E=E)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 1, 256), (4, 8, 256), (5, 9, 512), (8, 17, 2048),
+                                   (6, 40, 4096), (7, 1000, 1024), (4, 14336, 4096),
+                                   (2, 3, 8192)])
+def test_batched_silu_pair_loads_in_bounds(M, N, K):
+    # SiLU-gated gate+up on the matrix cores: 8 gate rows + the same 8 up rows
+    # per tile, each lane reading its own matrix
+    assert A.mfma_check("q4k", M, N, K, 2, cus=8, pair=True) > 0
+    assert A.mfma_check("q4k", M, N, K, 2, cus=256, pair=True) > 0
+
+
+@pytest.mark.parametrize("E,K", [(1, 256), (3, 256), (8, 512), (64, 2048), (65, 1024),
+                                 (100, 4096), (1024, 512), (7, 32768)])
+def test_router_loads_in_bounds(E, K):
+    assert A.router_check(E, K) > 0

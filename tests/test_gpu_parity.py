@@ -633,3 +633,46 @@ def test_forced_lane_groups_in_child_process():
         r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                            timeout=300)
         assert r.returncode == 0 and r.stdout.strip().endswith("ok"), lg + r.stdout + r.stderr
+
+
+def test_valu_kernel_for_batches_in_child_process():
+    """Batches of M >= 3 on the VALU kernel (Q4GEMV_MFMA=0, read once per
+    process; the library sends such batches to the matrix cores by default)
+    against the oracle: every dense call, the SiLU-gated one included."""
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np, torch, sys\n"
+        "sys.path.insert(0, %r)\n"
+        "import bit_block_quantized_dequant_amd as q4\n"
+        "from bit_block_quantized_dequant_amd import synth\n"
+        "from oracle import oracle\n"
+        "o = oracle.default(); dev = torch.device('cuda:0')\n"
+        "T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)\n"
+        "def close(y, ref, ab, what):\n"
+        "    y = y.cpu().numpy().astype(np.float64).reshape(ref.shape)\n"
+        "    assert np.all(np.abs(y - ref) <= 1e-4 * ab), what\n"
+        "for (M, N, K, seed) in [(3, 37, 1024, 0), (5, 130, 2048, 1), (8, 64, 4096, 2), (4, 9, 256, 3)]:\n"
+        "    rng = synth.make_rng(5300 + seed)\n"
+        "    wk, wk2, w0 = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K), synth.q4_0_matrix(rng, N, K)\n"
+        "    x = synth.activations(rng, M, K); gam = synth.gamma(rng, K)\n"
+        "    y = torch.empty(M, N, device=dev); u = torch.empty(M, N, device=dev)\n"
+        "    q4.q4k_gemv(y, T(wk), T(x), M, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab = o.q4k_gemv(wk, x, N, K); close(y, ry, ab, ('q4k', M, N, K))\n"
+        "    q4.q4_0_gemv(y, T(w0), T(x), M, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab = o.q4_0_gemv(w0, x, N, K); close(y, ry, ab, ('q4_0', M, N, K))\n"
+        "    q4.fused_rmsnorm_q4k_gemv(y, T(wk), T(x), T(gam), 1e-5, M, N, K); torch.cuda.synchronize()\n"
+        "    ry, ab, _ = o.fused_rmsnorm_q4k_gemv(wk, x, gam, 1e-5, N, K); close(y, ry, ab, ('norm', M, N, K))\n"
+        "    q4.fused_gate_up_q4k_gemv(y, u, T(wk), T(wk2), T(x), M, N, K); torch.cuda.synchronize()\n"
+        "    rg, ru, ag, au = o.gate_up_q4k_gemv(wk, wk2, x, N, K)\n"
+        "    close(y, rg, ag, ('gate', M, N, K)); close(u, ru, au, ('up', M, N, K))\n"
+        "    h = torch.empty(M, N, device=dev)\n"
+        "    q4.fused_gate_up_silu_q4k_gemv(h, T(wk), T(wk2), T(x), M, N, K); torch.cuda.synchronize()\n"
+        "    hh = h.cpu().numpy().astype(np.float64); ref = o.silu_mul(y.cpu().numpy().astype(np.float64),\n"
+        "                                                         u.cpu().numpy().astype(np.float64))\n"
+        "    assert np.all(np.abs(hh - ref) <= 2.0 ** -20 * np.abs(ref) + 1e-30), ('silu', M, N, K)\n"
+        "print('ok')\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    env = dict(os.environ, Q4GEMV_MFMA="0")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
