@@ -530,13 +530,26 @@ def test_graph_replay_matches_eager(dev):
     gam = synth.gamma(rng, K)
     x = synth.activations(rng, 8, K)
     wgd, wud, w0d, gd, xd = T(wg, dev), T(wu, dev), T(w0, dev), T(gam, dev), T(x, dev)
-    outs = {k: empty((8, N), dev) for k in ("g1", "u1", "n1", "k4", "q8")}
+    outs = {k: empty((8, N), dev) for k in ("g1", "u1", "n1", "k4", "q8", "h1", "h5")}
+    # the router (64 Q4_0 expert rows) and the SiLU expert call on its ids,
+    # whose ids stay on the device between the two captured launches
+    E, NE, top_k = 64, 40, 4
+    wr = T(synth.q4_0_matrix(rng, E, K), dev)
+    mg, mu = T(synth.q4_0_matrix(rng, E * NE, K), dev), T(synth.q4_0_matrix(rng, E * NE, K), dev)
+    outs["ids"] = empty((4, top_k), dev, dtype=torch.int32)
+    outs["wts"] = empty((4, top_k), dev)
+    outs["hm"] = empty((4, top_k, NE), dev)
 
     def calls(stream):
         q4.fused_gate_up_q4k_gemv(outs["g1"], outs["u1"], wgd, wud, xd, 1, N, K, stream=stream)
         q4.fused_rmsnorm_q4k_gemv(outs["n1"], wgd, xd, gd, 1e-5, 3, N, K, stream=stream)
         q4.q4k_gemv(outs["k4"], wud, xd, 4, N, K, stream=stream)
         q4.q4_0_gemv(outs["q8"], w0d, xd, 8, N, K, stream=stream)
+        q4.fused_gate_up_silu_q4k_gemv(outs["h1"], wgd, wud, xd, 1, N, K, stream=stream)
+        q4.fused_gate_up_silu_q4k_gemv(outs["h5"], wgd, wud, xd, 5, N, K, stream=stream)
+        q4.moe_router_q4_0(outs["ids"], outs["wts"], wr, xd, 4, E, K, top_k, 1, stream=stream)
+        q4.moe_q4_gemv_silu(outs["hm"], mg, mu, xd, outs["ids"], 4, top_k, E, NE, K,
+                            stream=stream)
 
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -550,7 +563,7 @@ def test_graph_replay_matches_eager(dev):
         g.capture_end()
     for rep in range(3):
         for v in outs.values():
-            v.fill_(float("nan"))
+            v.fill_(float("nan") if v.dtype == torch.float32 else -7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
