@@ -48,6 +48,20 @@
  *     pointers 16-byte aligned, all other pointers 4-byte aligned
  *     (Q4_ERR_ALIGN).  Values out of range are refused, never clamped.
  *   - The library is re-entrant; calls on different streams may overlap.
+ *
+ * Environment variables (read once per process; for measurements and
+ * comparisons only, results stay within the same bounds):
+ *   Q4GEMV_MFMA=0          batches of M >= 3 on the VALU kernel instead of
+ *                          the matrix cores
+ *   Q4GEMV_MOE_MFMA=1      the expert call (M >= 2) on the matrix cores
+ *   Q4GEMV_XR=0            single-token activations read from LDS instead of
+ *                          registers
+ *   Q4GEMV_LG=n            lanes per row group of the VALU kernel (power of
+ *                          two, 4..64)
+ *   Q4GEMV_WG_PER_CU=n     at most n resident workgroups per CU
+ *   Q4GEMV_BLOCKS_PER_CU=n workgroups per CU in the VALU kernel's grid
+ *   Q4GEMV_MFMA_KS=n       waves splitting a matrix-core tile's K range
+ *                          (1, 2, 4 or 8)
  */
 #ifndef Q4GEMV_H
 #define Q4GEMV_H
