@@ -43,9 +43,10 @@
 // groups of KS; each group takes one tile per round and its KS waves split
 // the tile's K range, adding their partial sums through LDS at the end of
 // the round.  Every wave keeps PD steps of weight loads in flight in a
-// register ring, across rounds too; the first PD go out before the
-// activations are staged (once per workgroup, RMS-normalized first for the
-// fused call).
+// register ring, across rounds too.  Order at the start: the activation
+// loads, then the first PD steps of weight loads, then the staging
+// arithmetic (once per workgroup, RMS-normalized first for the fused call),
+// so the staging waits only for the activations.
 #pragma once
 
 #include <type_traits>
@@ -126,14 +127,20 @@ __device__ __forceinline__ bool piece_is_high(int pp) {
     return FMT == kFmtQ4K ? ((pp >> 2) & 1) : ((pp >> 1) & 1);
 }
 
-template <int FMT, int M, int MODE>
-__device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLayout& ly,
-                                       float* red) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ppt = p.K >> 3;  // pieces per token
-    const int np = M * ppt;
+// The activation pieces of one thread (8 consecutive elements each) and
+// their tokens, loaded by mstage_issue before the first weight loads: loads
+// complete in issue order, so activations loaded after the weights would
+// wait for the weights' HBM latency before the staging could start.
+struct MStageX {
     float v[kMPieces][8];
     int um[kMPieces];
+};
+
+template <int M>
+__device__ __forceinline__ void mstage_issue(const GemvParams& p, MStageX& sx) {
+    const int tid = threadIdx.x;
+    const int ppt = p.K >> 3;  // pieces per token
+    const int np = M * ppt;
     // unconditional loads of clamped pieces keep the load-counter waits exact
 #pragma unroll
     for (int k = 0; k < kMPieces; ++k) {
@@ -141,12 +148,22 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         int m = 0;
 #pragma unroll
         for (int mm = 1; mm < M; ++mm) m += pc >= mm * ppt;
-        um[k] = m;
+        sx.um[k] = m;
         const float4* src = (const float4*)(p.x + (long long)m * p.K + 8 * (pc - m * ppt));
         const float4 a = src[0], b = src[1];
-        v[k][0] = a.x; v[k][1] = a.y; v[k][2] = a.z; v[k][3] = a.w;
-        v[k][4] = b.x; v[k][5] = b.y; v[k][6] = b.z; v[k][7] = b.w;
+        sx.v[k][0] = a.x; sx.v[k][1] = a.y; sx.v[k][2] = a.z; sx.v[k][3] = a.w;
+        sx.v[k][4] = b.x; sx.v[k][5] = b.y; sx.v[k][6] = b.z; sx.v[k][7] = b.w;
     }
+}
+
+template <int FMT, int M, int MODE>
+__device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLayout& ly,
+                                       float* red, MStageX& sx) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ppt = p.K >> 3;  // pieces per token
+    const int np = M * ppt;
+    float (&v)[kMPieces][8] = sx.v;
+    const int (&um)[kMPieces] = sx.um;
     auto valid = [&](int k) { return tid + k * kMBlock < np; };
 
     // RMSNorm: r_m = 1 / sqrt(sum(x^2) / K + eps), xhat = (x * r_m) * gamma
@@ -667,6 +684,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     // so the loads stay unconditional and the load-counter waits exact).
     WR w[PD];
     int lr = 0, ls = st0;
+    MStageX sx;
+    if constexpr (!PURE) mstage_issue<M>(p, sx);
+    __builtin_amdgcn_sched_barrier(0);  // the activation loads go out first
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
         load(lr, ls, w[j]);
@@ -675,7 +695,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             ++lr;
         }
     }
-    if constexpr (!PURE) mstage<FMT, M, (kMoe || kPair) ? kModeDense : MODE>(p, lds, ly, red);
+    if constexpr (!PURE) mstage<FMT, M, (kMoe || kPair) ? kModeDense : MODE>(p, lds, ly, red, sx);
     __syncthreads();
 
     const int n = nrounds * (st1 - st0);
