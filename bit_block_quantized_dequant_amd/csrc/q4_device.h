@@ -328,6 +328,21 @@ __device__ __forceinline__ T dpp_add(T v, int ctrl_sel) {
     return v + __builtin_bit_cast(T, t);
 }
 
+// Largest value of a whole wave of NON-NEGATIVE floats, exact in lane 63:
+// the same DPP pattern as group_total with max in place of the sum (lanes a
+// row operation does not write read 0, which max ignores for v >= 0).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    auto mx = [](float a, int t) { return fmaxf(a, __builtin_bit_cast(float, t)); };
+    const int iv0 = __builtin_bit_cast(int, v);
+    v = mx(v, __builtin_amdgcn_update_dpp(0, iv0, 0xB1, 0xF, 0xF, false));  // quad xor 1
+    v = mx(v, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v = mx(v, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v = mx(v, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    v = mx(v, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    v = mx(v, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
 template <typename T>
 __device__ __forceinline__ T group_total(T v, int width) {
     v = dpp_add(v, 0);

@@ -224,10 +224,8 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float t = am[m];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) t = fmaxf(t, __shfl_xor(t, off, kWave));
-            if (lane == 0) red[m * kMWaves + wave] = t;
+            const float t = wave_max_nonneg(am[m]);  // am >= 0: largest |x|
+            if (lane == kWave - 1) red[m * kMWaves + wave] = t;
         }
         __syncthreads();
         if (tid < M) {
