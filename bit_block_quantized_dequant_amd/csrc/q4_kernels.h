@@ -96,24 +96,28 @@ struct MoeShared {
 // kModeNorm the rows are first RMS-normalized in fp32:
 //   r = 1 / sqrt(sum(x^2) / K + eps),  xhat = (x * r) * gamma.
 // Split in two so that the first weight loads can be issued in between: the
-// global loads of the first kXReg chunks per thread go out first (the load
+// global loads of the first NX chunks per thread go out first (the load
 // counter is in order, so waiting for them later does not wait for the
-// weights); chunks beyond that (M*K > 8192 floats) load in the second half.
+// weights); chunks beyond that load in the second half, behind the weights.
+// NX is kXReg, or 8 for the expert call, whose 4 tokens of K = 2048 make 8
+// chunks per thread of its 256-thread workgroups.
 constexpr int kXReg = 4;
+constexpr int xreg_chunks(int mode) { return mode_moe(mode) ? 2 * kXReg : kXReg; }
 
+template <int NX = kXReg>
 struct XStage {
-    float4 x[kXReg];
-    float4 g[kXReg];
+    float4 x[NX];
+    float4 g[NX];
 };
 
-template <int MODE>
-__device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage& st) {
+template <int MODE, int NX = kXReg>
+__device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage<NX>& st) {
     const int kq = p.K >> 2;
     const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
     const float4* g4 = (const float4*)p.gamma;
 #pragma unroll
-    for (int k = 0; k < kXReg; ++k) {
+    for (int k = 0; k < NX; ++k) {
         // unconditional (clamped) loads keep the load-counter waits exact
         const int i = min((int)threadIdx.x + k * (int)blockDim.x, total - 1);
         st.x[k] = x4[i];
@@ -142,12 +146,12 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
     if (store) xl[m * xrow_chunks(p.K) + xchunk(c >> 4, c & 15)] = v;
 }
 
-// TAIL: the call may have more than kXReg chunks per thread (M * K > kXReg *
-// 4 * blockDim); kernels that cannot are compiled without the extra loops,
+// TAIL: the call may have more than NX chunks per thread (M * K > NX * 4 *
+// blockDim); kernels that cannot are compiled without the extra loops,
 // whose load waits would otherwise also cover the weight loads in flight.
-template <int FMT, int M, int MODE, bool TAIL>
-__device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage& st, float4* xl,
-                                               float* xsum, float* red) {
+template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg>
+__device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
+                                               float4* xl, float* xsum, float* red) {
     const int tid = threadIdx.x;
     const int bs = blockDim.x;
     const int kq = p.K >> 2;
@@ -175,14 +179,14 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
                 if (m == mm) ss[mm] += t;
         };
 #pragma unroll
-        for (int k = 0; k < kXReg; ++k) {
+        for (int k = 0; k < NX; ++k) {
             const int i = tid + k * bs;
             const float4 v = st.x[k];
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
             acc_sq(i < total ? v : z, min(i, total - 1));
         }
         if constexpr (TAIL)
-            for (int i = tid + kXReg * bs; i < total; i += bs) acc_sq(x4[i], i);
+            for (int i = tid + NX * bs; i < total; i += bs) acc_sq(x4[i], i);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float v = group_total(ss[m], kWave);
@@ -212,13 +216,13 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         return v;
     };
 #pragma unroll
-    for (int k = 0; k < kXReg; ++k) {
+    for (int k = 0; k < NX; ++k) {
         const int i = tid + k * bs;
         const int ic = min(i, total - 1);
         stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum);
     }
     if constexpr (TAIL) {
-        for (int i = tid + kXReg * bs; i < total; i += bs) {
+        for (int i = tid + NX * bs; i < total; i += bs) {
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
             if constexpr (MODE == kModeNorm) g = g4[i % kq];
             stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
@@ -392,10 +396,11 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     Cursor ca = first_cursor();
     // Activation loads first, then the first weight loads, then the staging
     // arithmetic: the HBM latency of the first step overlaps the staging.
-    XStage xst;
-    if constexpr (!PURE) stage_x_issue<MODE>(p, M, xst);
+    constexpr int NX = xreg_chunks(MODE);
+    XStage<NX> xst;
+    if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
-    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL>(p, xst, xl, xsum, red);
+    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL, NX>(p, xst, xl, xsum, red);
     __syncthreads();
 
     if constexpr (mode_moe(MODE)) {

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
     GemvParams p = {};
     p.x = x + (long long)m * K;
     p.K = K;
-    XStage st;
+    XStage<> st;
     stage_x_issue<kModeDense>(p, 1, st);
     stage_x_finish<kFmtQ4_0, 1, kModeDense, true>(p, st, xl, xsum, red);
     __syncthreads();

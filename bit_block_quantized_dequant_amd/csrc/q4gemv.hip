@@ -251,7 +251,7 @@ int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         if (p.K <= kWave * kUnitElems && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
-    if ((long long)M * p.K > (long long)kXReg * 4 * gemv_threads(M, MODE))
+    if ((long long)M * p.K > (long long)xreg_chunks(MODE) * 4 * gemv_threads(M, MODE))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }
