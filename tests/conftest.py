@@ -26,3 +26,13 @@ def q4lib():
         from bit_block_quantized_dequant_amd import build
         build.build()
     return q4.lib()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    """cuda:0, for the GPU tests; fails loudly if the HIP library is missing."""
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bit_block_quantized_dequant_amd as q4
+    q4.lib()
+    return torch.device("cuda:0")

@@ -21,67 +21,9 @@ import numpy as np
 import pytest
 
 from bit_block_quantized_dequant_amd import synth
+from gpu_helpers import NT, T, assert_bits, assert_bound, empty, host
 
 pytestmark = pytest.mark.gpu
-
-NT = min(16, os.cpu_count() or 1)
-
-
-@pytest.fixture(scope="module")
-def dev():
-    import torch
-    assert torch.cuda.is_available(), "GPU tests need a GPU"
-    import bit_block_quantized_dequant_amd as q4
-    q4.lib()  # fail loudly if the library is missing
-    return torch.device("cuda:0")
-
-
-def T(a, dev):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-
-def empty(shape, dev, dtype=None):
-    import torch
-    # filled with NaN so that an output the kernel forgets to write fails
-    t = torch.empty(shape, dtype=dtype or torch.float32, device=dev)
-    if t.dtype == torch.float32:
-        t.fill_(float("nan"))
-    else:
-        t.fill_(0x5A5A5A5A)
-    return t
-
-
-def host(t):
-    import torch
-    torch.cuda.synchronize()
-    return t.cpu().numpy()
-
-
-def assert_bound(y, ref, absdot, what):
-    y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
-    assert not np.any(np.isnan(y)), "%s: NaN in output" % what
-    err = np.abs(y - ref)
-    bound = 1e-4 * absdot
-    bad = err > bound
-    if np.any(bad):
-        i = np.unravel_index(np.argmax(err / np.maximum(bound, 1e-300)), err.shape)
-        raise AssertionError("%s: %d outputs out of bound; worst at %s: gpu %r ref %r bound %r"
-                             % (what, int(bad.sum()), i, y[i], ref[i], bound[i]))
-
-
-def assert_bits(got, want, what):
-    got = np.asarray(got, np.float32)
-    want = np.asarray(want, np.float32)
-    gn, wn = np.isnan(got), np.isnan(want)
-    assert np.array_equal(gn, wn), "%s: NaN positions differ" % what
-    g = got[~gn]
-    w = want[~wn]
-    same = (g.view(np.uint32) == w.view(np.uint32)) | ((g == 0) & (w == 0))
-    if not np.all(same):
-        i = int(np.argmin(same))
-        raise AssertionError("%s: %d values differ, first %r vs %r" % (what, int((~same).sum()),
-                                                                        g[i], w[i]))
 
 
 # ---------------------------------------------------------------------------

@@ -24,7 +24,7 @@ import pytest
 
 from bit_block_quantized_dequant_amd import synth
 
-from test_gpu_parity import NT, T, dev, empty, host  # noqa: F401  (dev is a fixture)
+from gpu_helpers import NT, T, assert_silu, empty, host
 
 pytestmark = pytest.mark.gpu
 
@@ -126,7 +126,6 @@ def test_router_then_silu_expert_call_on_device(dev, orc):
     import torch
 
     import bit_block_quantized_dequant_amd as q4
-    from test_gpu_silu import assert_silu
     M, E, K, N, top_k = 3, 16, 1024, 96, 4
     rng = synth.make_rng(8400)
     wr = synth.q4_0_matrix(rng, E, K)

@@ -24,50 +24,9 @@ import pytest
 
 from bit_block_quantized_dequant_amd import synth
 
-from test_gpu_parity import NT, T, dev, empty, host  # noqa: F401  (dev is a fixture)
+from gpu_helpers import NT, T, assert_epilogue, assert_silu, empty, host
 
 pytestmark = pytest.mark.gpu
-
-EPI = 2.0 ** -20    # relative: the fp32 epilogue
-UNDER = 2.0 ** -140  # absolute, per unit of (|g| + 1) |u|: fp32 subnormal exp(-|g|)
-
-
-def silu_bound(orc, g, u, ag, au):
-    dg, du = 1e-4 * ag, 1e-4 * au
-    s = np.abs(orc.silu_mul(g, np.ones_like(g)))
-    uu = np.abs(u) + du
-    return (1.1 * dg * uu + s * du + EPI * (s + 1.1 * dg) * uu
-            + UNDER * (np.abs(g) + 1.0) * uu + 2.0 ** -149)
-
-
-def assert_silu(orc, h, g, u, ag, au, what):
-    h = np.asarray(h, np.float64).reshape(g.shape)
-    ref = orc.silu_mul(g, u)
-    nan = np.isnan(ref)
-    assert np.array_equal(np.isnan(h), nan), "%s: NaN positions differ" % what
-    ok = ~nan
-    err = np.abs(h[ok] - ref[ok])
-    bound = silu_bound(orc, g[ok], u[ok], ag[ok], au[ok])
-    bad = err > bound
-    if np.any(bad):
-        i = int(np.argmax(err / np.maximum(bound, 1e-300)))
-        raise AssertionError("%s: %d outputs out of bound; worst gpu %r ref %r bound %r"
-                             % (what, int(bad.sum()), h[ok][i], ref[ok][i], bound[i]))
-
-
-def assert_epilogue(orc, h, g_gpu, u_gpu, what):
-    g = np.asarray(g_gpu, np.float64)
-    u = np.asarray(u_gpu, np.float64).reshape(g.shape)
-    h = np.asarray(h, np.float64).reshape(g.shape)
-    ref = orc.silu_mul(g, u)
-    nan = np.isnan(ref)
-    assert np.array_equal(np.isnan(h), nan), "%s: NaN positions differ" % what
-    err = np.abs(h[~nan] - ref[~nan])
-    bound = (EPI * np.abs(ref[~nan]) + UNDER * (np.abs(g[~nan]) + 1.0) * np.abs(u[~nan])
-             + 2.0 ** -149)
-    assert np.all(err <= bound), "%s: epilogue off by %g (relative)" % (
-        what, float(np.max(err / np.maximum(np.abs(ref[~nan]), 1e-300))))
-
 
 def run_gate_up(dev, orc, wg, wu, x, M, N, K, what):
     import bit_block_quantized_dequant_amd as q4
