@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
-    "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv",
+    "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv",
+    "fused_gate_up_silu_q4k_gemv",
     "moe_q4_gemv", "moe_q4_gemv_silu", "moe_router_q4_0", "dequant_q4k",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "LIB_PATH", "q4_0_row_bytes",
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "fused_rmsnorm_q4k_gemv": [_vp, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _i64,
                                        _vp],
             "fused_gate_up_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "fused_rmsnorm_gate_up_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                               _i64, _i64, _i64, _vp],
             "fused_gate_up_silu_q4k_gemv": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
             "moe_q4_gemv_silu": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "moe_router_q4_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp],
@@ -191,6 +194,20 @@ def moe_q4_gemv(gate, up, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
     pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4), dev)
     _ok(lib().moe_q4_gemv(pg, pu, pwg, pwu, px, pi, M, top_k, E, N, K, _stream(stream, dev)),
         "moe_q4_gemv")
+
+
+def fused_rmsnorm_gate_up_q4k_gemv(gate, up, w_gate, w_up, x, gamma, eps, M, N, K,
+                                   stream=None):
+    """gate/up = RMSNorm(x; gamma, eps) . Wg^T / Wu^T (Q4_K), one staging."""
+    pg, dev = _ptr(gate, "gate", _sz(M * N, 4))
+    pu, dev = _ptr(up, "up", _sz(M * N, 4), dev)
+    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
+    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    pga, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    _ok(lib().fused_rmsnorm_gate_up_q4k_gemv(pg, pu, pwg, pwu, px, pga, float(eps), M, N, K,
+                                             _stream(stream, dev)),
+        "fused_rmsnorm_gate_up_q4k_gemv")
 
 
 def fused_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, M, N, K, stream=None):

@@ -489,6 +489,22 @@ int moe_q4_gemv(float* gate, float* up, const void* w_gate, const void* w_up, co
     return run<kFmtQ4_0, 2, kModeMoe, false>(p, (int)M, umax, stream);
 }
 
+int fused_rmsnorm_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate,
+                                   const void* w_up, const float* x, const float* gamma,
+                                   float eps, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!gate || !up || !w_gate || !w_up || !x || !gamma) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gamma, 16) ||
+        !aligned(gate, 4) || !aligned(up, 4))
+        return Q4_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return Q4_ERR_ARG;
+    GemvParams p = base_params(w_gate, w_up, gate, up, x, N, K, kFmtQ4K);
+    p.gamma = gamma;
+    p.eps = eps;
+    return run<kFmtQ4K, 2, kModeNorm, false>(p, (int)M, 0, stream);
+}
+
 int fused_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
                                 const float* x, int64_t M, int64_t N, int64_t K,
                                 void* stream) {

@@ -128,6 +128,20 @@ int fused_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate, const voi
                            const float* x, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * RMSNorm feeding the gate+up pair in one launch: with xhat the normalized
+ * rows of fused_rmsnorm_q4k_gemv (fp32, on chip, never written out),
+ *   gate[M, N] = Xhat . Wg^T and up[M, N] = Xhat . Wu^T,
+ * both Q4_K with N rows, from one staging of the normalized rows (same
+ * layouts, limits and eps rule as the two calls it combines).  gate and up
+ * must not overlap.  (trueno-gpu 0.4.11, fused.rs: FusedRmsNormQ4KGemvKernel,
+ * the normalization kept on chip, and FusedGateUpQ4KGemvKernel, the pair
+ * that shares one input load.)
+ */
+int fused_rmsnorm_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate,
+                                   const void* w_up, const float* x, const float* gamma,
+                                   float eps, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * SiLU-gated gate+up: the one output
  *   h[m, n] = silu(gate[m, n]) * up[m, n],  silu(g) = g / (1 + exp(-g)),
  * with gate and up the two products of fused_gate_up_q4k_gemv (same layouts,

@@ -365,6 +365,46 @@ def test_batched_token_magnitudes(dev, orc, fmt):
     assert np.all(y[2] == 0.0)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (4, 14336, 4096), (1, 37, 3584),
+                                   (2, 300, 1024), (3, 77, 512), (8, 40, 4096), (5, 1, 256)])
+def test_rmsnorm_gate_up(dev, orc, M, N, K):
+    """RMSNorm feeding the gate+up pair: against the oracle's normalized rows
+    and its plain GEMVs, within 1e-4 * sum |w xhat| (xhat as the oracle
+    computes it)."""
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(4400 + M + N + K)
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K, sigma=2.0)
+    gam = synth.gamma(rng, K)
+    g, u = empty((M, N), dev), empty((M, N), dev)
+    q4.fused_rmsnorm_gate_up_q4k_gemv(g, u, T(wg, dev), T(wu, dev), T(x, dev), T(gam, dev),
+                                      1e-5, M, N, K)
+    xhat = orc.rmsnorm(x, gam, 1e-5)
+    rg, ru, ag, au = orc.gate_up_q4k_gemv(wg, wu, xhat, N, K, NT)
+    assert_bound(host(g), rg, ag, "norm gate M=%d N=%d K=%d" % (M, N, K))
+    assert_bound(host(u), ru, au, "norm up M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_rmsnorm_gate_up_equals_two_norm_calls(dev, M):
+    """Each output equals fused_rmsnorm_q4k_gemv on that matrix, bit for bit
+    (same staging, same accumulation; N = 513 gives both calls the same K
+    split on the matrix cores)."""
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(33)
+    N, K = 513, 4096
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K, sigma=2.0)
+    gam = synth.gamma(rng, K)
+    wgd, wud, xd, gd = T(wg, dev), T(wu, dev), T(x, dev), T(gam, dev)
+    g, u, g1, u1 = (empty((M, N), dev) for _ in range(4))
+    q4.fused_rmsnorm_gate_up_q4k_gemv(g, u, wgd, wud, xd, gd, 1e-5, M, N, K)
+    q4.fused_rmsnorm_q4k_gemv(g1, wgd, xd, gd, 1e-5, M, N, K)
+    q4.fused_rmsnorm_q4k_gemv(u1, wud, xd, gd, 1e-5, M, N, K)
+    assert_bits(host(g), host(g1), "norm gate vs fused_rmsnorm_q4k_gemv M=%d" % M)
+    assert_bits(host(u), host(u1), "norm up vs fused_rmsnorm_q4k_gemv M=%d" % M)
+
+
 def test_gate_up_equals_two_single_calls(dev):
     import bit_block_quantized_dequant_amd as q4
     rng = synth.make_rng(32)
