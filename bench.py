@@ -161,7 +161,7 @@ def check(status, what):
 # ---------------------------------------------------------------------------
 # workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
 # ---------------------------------------------------------------------------
-def setup_workload(torch, dev, index, M, distinct=False, silu=False):
+def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False):
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
@@ -220,12 +220,20 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False):
         cks = torch.empty(2 * N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
 
+        gam = T(synth.gamma(synth.make_rng(8500), K)) if norm else None
+
         def launch(i, stream):
             p = rot.ptr(i)
             if silu:
                 check(L.fused_gate_up_silu_q4k_gemv(gate.data_ptr(), p, p + half, x.data_ptr(),
                                                     M, N, K, stream),
                       "fused_gate_up_silu_q4k_gemv")
+                return
+            if norm:
+                check(L.fused_rmsnorm_gate_up_q4k_gemv(gate.data_ptr(), up.data_ptr(), p,
+                                                       p + half, x.data_ptr(), gam.data_ptr(),
+                                                       1e-5, M, N, K, stream),
+                      "fused_rmsnorm_gate_up_q4k_gemv")
                 return
             check(L.fused_gate_up_q4k_gemv(gate.data_ptr(), up.data_ptr(), p, p + half,
                                            x.data_ptr(), M, N, K, stream),
@@ -281,14 +289,15 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False):
     return wbytes, launch, ceil_launch, notes, keep, outs, couts, (stream_launch, [scks])
 
 
-def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False):
+def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False, norm=False):
     (wbytes, launch, ceil_launch, notes, keep, outs, couts,
-     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu)
+     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu, norm)
     wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
     cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
     swall, sdurs, scnts = time_launches(torch, stream_launch, warmup, steps, souts)
     st, cst, sst = stats(durs, cnts), stats(cdurs, ccnts), stats(sdurs, scnts)
-    res = dict(index=index, M=M, distinct=distinct, silu=silu, weight_bytes=wbytes, wall_s=wall,
+    res = dict(index=index, M=M, distinct=distinct, silu=silu, norm=norm, weight_bytes=wbytes,
+               wall_s=wall,
                steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
                kernel=st, kernel_gbs=wbytes / (st["mean_ms"] * 1e-3) / 1e9,
@@ -486,6 +495,8 @@ def write_report(path, rows, headline, router=None):
         if r.get("silu"):
             name = name.replace("fused_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv").replace(
                 "moe_q4_gemv", "moe_q4_gemv_silu")
+        if r.get("norm"):
+            name = name.replace("fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv")
         if r["index"] == 5:
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
@@ -533,16 +544,21 @@ def main():
 
     rows = []
     if args.all:
-        # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output)
-        for index, Ms, dist, silu in ((1, (1,), 0, 0), (2, (1, 2, 4, 8), 0, 0), (3, (1,), 0, 0),
-                                      (4, (1, 2, 4, 8), 0, 0), (4, (1, 4), 0, 1),
-                                      (5, (4,), 0, 0), (5, (4,), 1, 0), (5, (4,), 0, 1)):
+        # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output,
+        #  RMSNorm feeding the pair)
+        for index, Ms, dist, silu, norm in ((1, (1,), 0, 0, 0), (2, (1, 2, 4, 8), 0, 0, 0),
+                                            (3, (1,), 0, 0, 0), (4, (1, 2, 4, 8), 0, 0, 0),
+                                            (4, (1, 4), 0, 1, 0), (4, (1, 4), 0, 0, 1),
+                                            (5, (4,), 0, 0, 0), (5, (4,), 1, 0, 0),
+                                            (5, (4,), 0, 1, 0)):
             for M in Ms:
-                r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu))
+                r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu),
+                            bool(norm))
                 rows.append(r)
-                print("workload %d%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
+                print("workload %d%s%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
                       "ceiling, %.1f%% of stream)"
-                      % (index, " distinct" if dist else "", " silu" if silu else "", M,
+                      % (index, " distinct" if dist else "", " silu" if silu else "",
+                         " norm" if norm else "", M,
                          r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
                          100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
                          100 * r["frac_of_stream"]), file=sys.stderr, flush=True)
