@@ -19,7 +19,7 @@ import os
 __all__ = [
     "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv",
-    "fused_gate_up_silu_q4k_gemv",
+    "fused_gate_up_silu_q4k_gemv", "fused_rmsnorm_gate_up_silu_q4k_gemv",
     "moe_q4_gemv", "moe_q4_gemv_silu", "moe_router_q4_0", "dequant_q4k",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "LIB_PATH", "q4_0_row_bytes",
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "fused_rmsnorm_gate_up_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                                _i64, _i64, _i64, _vp],
             "fused_gate_up_silu_q4k_gemv": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "fused_rmsnorm_gate_up_silu_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                                    _i64, _i64, _i64, _vp],
             "moe_q4_gemv_silu": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "moe_router_q4_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp],
             "moe_q4_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
@@ -218,6 +220,19 @@ def fused_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, M, N, K, stream=None):
     px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
     _ok(lib().fused_gate_up_silu_q4k_gemv(ph, pwg, pwu, px, M, N, K, _stream(stream, dev)),
         "fused_gate_up_silu_q4k_gemv")
+
+
+def fused_rmsnorm_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, gamma, eps, M, N, K,
+                                        stream=None):
+    """h = silu(xhat . Wg^T) * (xhat . Wu^T), xhat = RMSNorm(x; gamma, eps); one launch."""
+    ph, dev = _ptr(h, "h", _sz(M * N, 4))
+    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
+    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
+    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    pga, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    _ok(lib().fused_rmsnorm_gate_up_silu_q4k_gemv(ph, pwg, pwu, px, pga, float(eps), M, N, K,
+                                                  _stream(stream, dev)),
+        "fused_rmsnorm_gate_up_silu_q4k_gemv")
 
 
 def moe_q4_gemv_silu(h, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):

@@ -40,8 +40,13 @@ constexpr int kModeMoe = 2;
 // (dense, and the expert call)
 constexpr int kModeSilu = 3;
 constexpr int kModeMoeSilu = 4;
+// RMSNorm feeding the gate+up pair, with the SiLU-gated product as the output
+constexpr int kModeNormSilu = 5;
 constexpr bool mode_moe(int mode) { return mode == kModeMoe || mode == kModeMoeSilu; }
-constexpr bool mode_silu(int mode) { return mode == kModeSilu || mode == kModeMoeSilu; }
+constexpr bool mode_silu(int mode) {
+    return mode == kModeSilu || mode == kModeMoeSilu || mode == kModeNormSilu;
+}
+constexpr bool mode_norm(int mode) { return mode == kModeNorm || mode == kModeNormSilu; }
 constexpr int gemv_threads(int M, int mode) {
     return (M == 1 || mode_moe(mode)) ? kBlock1 : kBlock;
 }
@@ -121,7 +126,7 @@ __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage
         // unconditional (clamped) loads keep the load-counter waits exact
         const int i = min((int)threadIdx.x + k * (int)blockDim.x, total - 1);
         st.x[k] = x4[i];
-        if constexpr (MODE == kModeNorm) st.g[k] = g4[i % kq];
+        if constexpr (mode_norm(MODE)) st.g[k] = g4[i % kq];
     }
 }
 
@@ -161,7 +166,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
     float rnorm[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) rnorm[m] = 1.0f;
-    if constexpr (MODE == kModeNorm) {
+    if constexpr (mode_norm(MODE)) {
         const int nw = bs >> 6;
         const int wave = tid >> 6, lane = tid & 63;
         float ss[M];
@@ -202,7 +207,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
     }
     auto norm = [&](float4 v, float4 g, int i) {
-        if constexpr (MODE == kModeNorm) {
+        if constexpr (mode_norm(MODE)) {
             const int m = i / kq;
             float r = rnorm[0];
 #pragma unroll
@@ -224,7 +229,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
     if constexpr (TAIL) {
         for (int i = tid + NX * bs; i < total; i += bs) {
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (MODE == kModeNorm) g = g4[i % kq];
+            if constexpr (mode_norm(MODE)) g = g4[i % kq];
             stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
         }
     }

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     // SiLU-gated gate+up: a tile is 8 rows of the gate matrix (columns
     // 0-7) and the same 8 rows of the up matrix (columns 8-15), so that a
     // row's two totals meet in one 16-lane row of the wave
-    constexpr bool kPair = MODE == kModeSilu;
+    constexpr bool kPair = MODE == kModeSilu || MODE == kModeNormSilu;
     static_assert(!mode_silu(MODE) || (kPair && NMAT == 2 && FMT == kFmtQ4K),
                   "matrix-core SiLU epilogue: dense Q4_K gate+up only");
     constexpr int kTileShift = kPair ? 3 : 4;
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             ++lr;
         }
     }
-    if constexpr (!PURE) mstage<FMT, M, (kMoe || kPair) ? kModeDense : MODE>(p, lds, ly, red, sx);
+    if constexpr (!PURE) mstage<FMT, M, mode_norm(MODE) ? kModeNorm : kModeDense>(p, lds, ly, red, sx);
     __syncthreads();
 
     const int n = nrounds * (st1 - st0);

@@ -333,7 +333,8 @@ int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
     const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
     p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
     const long long ntiles_run =
-        MODE == kModeSilu ? (long long)nexperts * ((p.N + 7) / 8) : ntiles;
+        (MODE == kModeSilu || MODE == kModeNormSilu) ? (long long)nexperts * ((p.N + 7) / 8)
+                                                      : ntiles;
     const int TG = kMWaves / p.ks;
     long long blocks = (long long)cus * wgc;
     const long long need = (ntiles_run + TG - 1) / TG;
@@ -515,6 +516,22 @@ int fused_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
         return Q4_ERR_ALIGN;
     GemvParams p = base_params(w_gate, w_up, h, nullptr, x, N, K, kFmtQ4K);
     return run<kFmtQ4K, 2, kModeSilu, false>(p, (int)M, 0, stream);
+}
+
+int fused_rmsnorm_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
+                                        const float* x, const float* gamma, float eps,
+                                        int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!h || !w_gate || !w_up || !x || !gamma) return Q4_ERR_NULL;
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gamma, 16) ||
+        !aligned(h, 4))
+        return Q4_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return Q4_ERR_ARG;
+    GemvParams p = base_params(w_gate, w_up, h, nullptr, x, N, K, kFmtQ4K);
+    p.gamma = gamma;
+    p.eps = eps;
+    return run<kFmtQ4K, 2, kModeNormSilu, false>(p, (int)M, 0, stream);
 }
 
 int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float* x,

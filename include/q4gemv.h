@@ -159,6 +159,16 @@ int fused_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
                                 void* stream);
 
 /*
+ * The two above together: RMSNorm feeding the gate+up pair, with the one
+ * output h[m, n] = silu(gate[m, n]) * up[m, n] of fused_rmsnorm_gate_up_q4k_gemv's
+ * gate and up (same layouts, limits and eps rule; gate and up are never
+ * written out).
+ */
+int fused_rmsnorm_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void* w_up,
+                                        const float* x, const float* gamma, float eps,
+                                        int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Expert-selected gate/up GEMV over Q4_0 experts.  w_gate and w_up each hold
  * E expert matrices of N rows, stacked: expert e's row r is global row
  * e*N + r.  ids: int32 [M, top_k], the experts chosen for each token.  For

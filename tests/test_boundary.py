@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ["q4_0_gemv", "q4k_gemv", "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv",
-              "fused_rmsnorm_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv", "moe_q4_gemv",
+              "fused_rmsnorm_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv",
+              "fused_rmsnorm_gate_up_silu_q4k_gemv", "moe_q4_gemv",
               "moe_q4_gemv_silu", "moe_router_q4_0",
               "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
               "q4_version"]:
@@ -110,6 +111,17 @@ def test_rmsnorm_gate_up_validation(q4lib):
     assert f(A, A, A, A, A, A, float("nan"), 1, 16, 256, None) == ARG
     assert f(A, A, A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
     assert f(A, A, A, A, A, A, 1e-5, 1, 16, 100, None) == SHAPE
+
+
+def test_rmsnorm_gate_up_silu_validation(q4lib):
+    f = L().fused_rmsnorm_gate_up_silu_q4k_gemv
+    assert f(None, A, A, A, A, 1e-5, 1, 16, 256, None) == NULL
+    assert f(A, A, A, A, None, 1e-5, 1, 16, 256, None) == NULL
+    assert f(A + 2, A, A, A, A, 1e-5, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A, A + 4, 1e-5, 1, 16, 256, None) == ALIGN
+    assert f(A, A, A, A, A, -1.0, 1, 16, 256, None) == ARG
+    assert f(A, A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, A, 1e-5, 1, 16, 100, None) == SHAPE
 
 
 def test_gate_up_silu_validation(q4lib):

@@ -1,5 +1,5 @@
-"""GPU parity of the SiLU-gated calls, fused_gate_up_silu_q4k_gemv and
-moe_q4_gemv_silu, through the C ABI.
+"""GPU parity of the SiLU-gated calls, fused_gate_up_silu_q4k_gemv,
+fused_rmsnorm_gate_up_silu_q4k_gemv and moe_q4_gemv_silu, through the C ABI.
 
 Two bars per output element h = silu(g) * u:
   * against the oracle: g and u are each within 1e-4 * sum_k |w x| of the
@@ -56,6 +56,33 @@ def test_gate_up_silu_shapes(dev, orc, M, N, K):
     wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
     x = synth.activations(rng, M, K, sigma=3.0)
     run_gate_up(dev, orc, wg, wu, x, M, N, K, "silu M=%d N=%d K=%d" % (M, N, K))
+
+
+def run_norm_gate_up(dev, orc, wg, wu, x, gam, M, N, K, what):
+    import bit_block_quantized_dequant_amd as q4
+    tg, tu, tx, tga = T(wg, dev), T(wu, dev), T(x, dev), T(gam, dev)
+    h = empty((M, N), dev)
+    q4.fused_rmsnorm_gate_up_silu_q4k_gemv(h, tg, tu, tx, tga, 1e-5, M, N, K)
+    g, u = empty((M, N), dev), empty((M, N), dev)
+    q4.fused_rmsnorm_gate_up_q4k_gemv(g, u, tg, tu, tx, tga, 1e-5, M, N, K)
+    h, g, u = host(h), host(g), host(u)
+    xhat = orc.rmsnorm(x, gam, 1e-5)
+    rg, ru, ag, au = orc.gate_up_q4k_gemv(wg, wu, xhat, N, K, NT)
+    assert_silu(orc, h, rg, ru, ag, au, what)
+    assert_epilogue(orc, h, g, u, what + " (epilogue)")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (4, 14336, 4096), (1, 37, 3584),
+                                   (2, 300, 1024), (3, 77, 512), (8, 17, 2048), (6, 9, 4096)])
+def test_rmsnorm_gate_up_silu(dev, orc, M, N, K):
+    """RMSNorm feeding the SiLU-gated pair, against the oracle's normalized
+    rows, gate and up; and the epilogue against the GPU's own RMSNorm +
+    gate/up call."""
+    rng = synth.make_rng(6500 + M + N + K)
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K, sigma=2.0)
+    gam = synth.gamma(rng, K)
+    run_norm_gate_up(dev, orc, wg, wu, x, gam, M, N, K, "norm silu M=%d N=%d K=%d" % (M, N, K))
 
 
 def run_moe(dev, orc, wg, wu, x, ids, E, N, K, what):
