@@ -220,10 +220,16 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
         cks = torch.empty(2 * N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
 
-        gam = T(synth.gamma(synth.make_rng(8500), K)) if norm else None
+        gam = T(synth.gamma(synth.make_rng(8500), K)) if norm else None  # (K floats)
 
         def launch(i, stream):
             p = rot.ptr(i)
+            if silu and norm:
+                check(L.fused_rmsnorm_gate_up_silu_q4k_gemv(gate.data_ptr(), p, p + half,
+                                                            x.data_ptr(), gam.data_ptr(), 1e-5,
+                                                            M, N, K, stream),
+                      "fused_rmsnorm_gate_up_silu_q4k_gemv")
+                return
             if silu:
                 check(L.fused_gate_up_silu_q4k_gemv(gate.data_ptr(), p, p + half, x.data_ptr(),
                                                     M, N, K, stream),
@@ -496,7 +502,7 @@ def write_report(path, rows, headline, router=None):
             name = name.replace("fused_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv").replace(
                 "moe_q4_gemv", "moe_q4_gemv_silu")
         if r.get("norm"):
-            name = name.replace("fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv")
+            name = name.replace("fused_gate_up", "fused_rmsnorm_gate_up")
         if r["index"] == 5:
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
@@ -549,6 +555,7 @@ def main():
         for index, Ms, dist, silu, norm in ((1, (1,), 0, 0, 0), (2, (1, 2, 4, 8), 0, 0, 0),
                                             (3, (1,), 0, 0, 0), (4, (1, 2, 4, 8), 0, 0, 0),
                                             (4, (1, 4), 0, 1, 0), (4, (1, 4), 0, 0, 1),
+                                            (4, (1, 4), 0, 1, 1),
                                             (5, (4,), 0, 0, 0), (5, (4,), 1, 0, 0),
                                             (5, (4,), 0, 1, 0)):
             for M in Ms:
