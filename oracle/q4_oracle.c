@@ -316,11 +316,26 @@ void oracle_silu_mul(const double* g, const double* u, int64_t n, double* h)
  *   ids[m, s]: the s-th largest logit's expert (s = 0 first), by repeated
  *              argmax; equal logits go to the lower expert index, and a NaN
  *              logit ranks as -inf.
- *   weights:   p_e = exp(l_e - lmax) / D with lmax the largest logit and D
- *              the sum over the selected experts (normalize != 0) or over
- *              all E experts (normalize == 0: the full softmax's entries).
+ *   weights:   p_e = exp(l_e - lmax) / D with lmax the largest non-NaN
+ *              logit and D the sum over the selected experts (normalize !=
+ *              0) or over all E experts (normalize == 0: the full softmax's
+ *              entries).  The page gives no rule for infinite or NaN logits;
+ *              the reading here: a logit equal to lmax has term exactly 1
+ *              (also for an infinite lmax), a NaN logit term 0, and a zero
+ *              D gives zero weights.
  * Double throughout.
  * ---------------------------------------------------------------------- */
+/* The unnormalized softmax term of logit v against the largest logit lmax:
+ * exp(v - lmax), with v - lmax taken as 0 where v equals lmax (experts tied
+ * at an infinite maximum share its weight, as equal logits do) and 0 for a
+ * NaN logit. */
+static double softmax_term(double v, double lmax)
+{
+    if (isnan(v)) return 0.0;
+    if (v == lmax) return 1.0;
+    return exp(v - lmax);
+}
+
 void oracle_topk_softmax(const double* logits, int64_t M, int64_t E, int64_t top_k,
                          int normalize, int32_t* ids, double* weights)
 {
@@ -342,20 +357,19 @@ void oracle_topk_softmax(const double* logits, int64_t M, int64_t E, int64_t top
             taken[best] = 1;
             ids[m * top_k + s] = (int32_t)best;
         }
-        double lmax = l[ids[m * top_k]];
-        if (isnan(lmax)) lmax = -INFINITY;
+        /* lmax: the largest non-NaN logit (NaN when every logit is NaN). */
+        double lmax = NAN;
+        for (int64_t e = 0; e < E; ++e)
+            if (!isnan(l[e]) && (isnan(lmax) || l[e] > lmax)) lmax = l[e];
         double den = 0.0;
         if (normalize) {
-            for (int64_t s = 0; s < top_k; ++s) {
-                double v = l[ids[m * top_k + s]];
-                den += isnan(v) ? 0.0 : exp(v - lmax);
-            }
+            for (int64_t s = 0; s < top_k; ++s) den += softmax_term(l[ids[m * top_k + s]], lmax);
         } else {
-            for (int64_t e = 0; e < E; ++e) den += isnan(l[e]) ? 0.0 : exp(l[e] - lmax);
+            for (int64_t e = 0; e < E; ++e) den += softmax_term(l[e], lmax);
         }
         for (int64_t s = 0; s < top_k; ++s) {
-            double v = l[ids[m * top_k + s]];
-            weights[m * top_k + s] = isnan(v) ? 0.0 : exp(v - lmax) / den;
+            double t = softmax_term(l[ids[m * top_k + s]], lmax);
+            weights[m * top_k + s] = den > 0.0 ? t / den : 0.0;
         }
     }
     free(taken);

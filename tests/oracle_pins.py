@@ -277,7 +277,7 @@ def pin_gemv_onehot_and_scaling(o):
         assert np.array_equal(y2, 2 * y1) and np.array_equal(a2, 2 * a1), fmt
 
 
-def pin_bruteforce(o, seeds=range(6)):
+def pin_bruteforce(o, seeds=range(100)):
     """Independent bit-gathering evaluator with exact rationals on tiny shapes:
     dequant bit-exact, GEMV within double rounding, |w*x| sum likewise."""
     for seed in seeds:
@@ -322,14 +322,24 @@ def pin_gemv_vs_numpy(o):
 
 
 def pin_rmsnorm(o):
-    """Constant rows with gamma = 1 give c/sqrt(c^2 + eps) (closed form);
-    random rows match the float64 formula to float32 rounding."""
+    """Constant rows give c/sqrt(c^2 + eps) times gamma (closed form), with
+    gamma = 1 and with gamma_k = 2^(k mod 8 - 4), a power of two per column
+    (so (x r) gamma is exact and a wrong gamma index moves the columns);
+    rows are normalized independently; random rows match the float64
+    formula to float32 rounding."""
     eps = 1e-5
     K = 512
     for c in (0.75, -3.0, 1e-3, 20.0):
         xh = o.rmsnorm(np.full((1, K), c, np.float32), np.ones(K, np.float32), eps)
         want = c / np.sqrt(c * c + eps)
         assert np.all(np.abs(xh - want) <= 4 * np.spacing(np.float32(abs(want)))), (c, xh[0, 0])
+    gam = (2.0 ** (np.arange(K) % 8 - 4)).astype(np.float32)
+    cs = np.array([0.75, -3.0, 20.0], np.float32)
+    x = np.repeat(cs[:, None], K, axis=1)
+    xh = o.rmsnorm(x, gam, eps)
+    for m, c in enumerate(cs.astype(np.float64)):
+        want = gam.astype(np.float64) * (c / np.sqrt(c * c + eps))
+        assert np.all(np.abs(xh[m] - want) <= 4 * np.spacing(np.abs(want).astype(np.float32))), m
     rng = synth.make_rng(19)
     x = synth.activations(rng, 3, K, 2.0)
     g = synth.gamma(rng, K)
@@ -339,6 +349,14 @@ def pin_rmsnorm(o):
     assert np.all(np.abs(xh - ref) <= 1e-6 * np.abs(ref) + 1e-12)
     y, a, xh2 = o.fused_rmsnorm_q4k_gemv(synth.q4k_matrix(rng, 5, K), x, g, eps, 5, K)
     assert np.array_equal(xh2, xh)
+    # huge rows: the sum of squares does not overflow (the mean does only
+    # beyond float32's range, where r = 0); tiny rows are eps-dominated
+    big = np.full((1, K), 2.0 ** 60, np.float32)
+    assert np.all(np.abs(o.rmsnorm(big, gam, eps) - gam) <= 4 * np.spacing(gam))
+    assert np.all(o.rmsnorm(np.full((1, K), 2.0 ** 100, np.float32), gam, eps) == 0.0)
+    tiny = np.full((1, K), 2.0 ** -120, np.float32)
+    want = gam.astype(np.float64) * 2.0 ** -120 / np.sqrt(eps)
+    assert np.all(np.abs(o.rmsnorm(tiny, gam, eps) - want) <= 4 * np.spacing(want.astype(np.float32)))
 
 
 def pin_composites(o):
@@ -443,6 +461,21 @@ def pin_topk_softmax(o):
     ids, w = o.topk_softmax([[np.nan, 1.0, 2.0], [np.nan, np.nan, 1.0]], 3, True)
     assert np.array_equal(ids, [[2, 1, 0], [2, 0, 1]])
     assert w[0, 2] == 0.0 and w[1, 1] == 0.0 and w[1, 2] == 0.0 and w[1, 0] == 1.0
+    # rows without a finite maximum: all -inf is the limit of equal logits
+    # (uniform), experts tied at +inf share the weight, a NaN weighs 0, an
+    # all-NaN row has zero weights; a NaN ahead of a -inf (lower index)
+    # still weighs 0
+    inf = np.inf
+    ids, w = o.topk_softmax([[-inf] * 5, [1.0, inf, 3.0, inf, np.nan],
+                             [np.nan] * 5, [np.nan, -inf, -inf, np.nan, -inf]], 3, True)
+    assert np.array_equal(ids, [[0, 1, 2], [1, 3, 2], [0, 1, 2], [0, 1, 2]])
+    assert np.all(w[0] == 1.0 / 3.0)
+    assert np.array_equal(w[1], [0.5, 0.5, 0.0])
+    assert np.all(w[2] == 0.0)
+    assert w[3, 0] == 0.0 and w[3, 1] == 0.5 and w[3, 2] == 0.5
+    ids, w = o.topk_softmax([[-inf] * 5, [np.nan, -inf, -inf, np.nan, -inf]], 2, False)
+    assert np.all(w[0] == 0.2)
+    assert w[1, 0] == 0.0 and w[1, 1] == 1.0 / 3.0
 
 
 def pin_router(o):

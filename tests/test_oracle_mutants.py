@@ -47,8 +47,13 @@ MUTANTS = {
     "silu sigmoid of +g": ("exp(-g[i])", "exp(g[i])"),
     "silu drops up": ("h[i] = s * u[i];", "h[i] = s;"),
     "top-k ties to the higher index": ("if (best < 0 || v > bv) {", "if (best < 0 || v >= bv) {"),
-    "softmax without the max shift": ("den += isnan(v) ? 0.0 : exp(v - lmax);",
-                                      "den += isnan(v) ? 0.0 : exp(v);"),
+    "softmax without the max shift": ("return exp(v - lmax);", "return exp(v);"),
+    "softmax tie at an infinite maximum as exp(nan)": ("if (v == lmax) return 1.0;", ""),
+    "softmax zero denominator unguarded": ("den > 0.0 ? t / den : 0.0", "t / den"),
+    "softmax max includes NaN as +inf": (
+        "if (!isnan(l[e]) && (isnan(lmax) || l[e] > lmax)) lmax = l[e];",
+        "if (isnan(l[e]) || isnan(lmax) || l[e] > lmax) lmax = isnan(l[e]) ? INFINITY : l[e];"),
+    "rmsnorm gamma index reversed": ("(xm[k] * r) * gamma[k]", "(xm[k] * r) * gamma[K - 1 - k]"),
     "normalize flag ignored": ("if (normalize) {", "if (0) {"),
     "router logits of token 0 only": ("oracle_q4_0_gemv(w, x, M, E, K, l, a, 1);",
                                       "oracle_q4_0_gemv(w, x, 1, E, K, l, a, 1);"),
