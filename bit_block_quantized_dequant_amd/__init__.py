@@ -9,8 +9,10 @@ kernels of libq4gemv.so; there is no other implementation to fall back to,
 and a missing library raises ImportError on first use.
 
 The binding adds guards the C ABI cannot make by itself: every tensor must
-live on a GPU, be contiguous and be at least as large as the call will touch,
-so that a wrong argument raises here instead of reaching a kernel.  A nonzero
+have the call's element type (float32 activations, gamma and outputs, int32
+expert ids, byte weights), live on a GPU, be contiguous and be at least as
+large as the call will touch, so that a wrong argument raises here instead of
+reaching a kernel.  A nonzero
 status from the library raises Q4Error.
 """
 import ctypes
@@ -109,12 +111,32 @@ def q4k_row_bytes(K: int) -> int:
 # --------------------------------------------------------------------------
 # marshalling helpers
 # --------------------------------------------------------------------------
-def _ptr(t, name, min_bytes=None, device=None):
-    """Device pointer of tensor `t` (None passes NULL), after the guards."""
+F32, I32, U8, CKS = "float32", "int32", "uint8", "checksum"
+
+
+def _dtype_ok(t, kind):
+    import torch
+    if kind == F32:
+        return t.dtype == torch.float32
+    if kind == I32:
+        return t.dtype == torch.int32
+    if kind == U8:  # packed weight bytes
+        return t.dtype in (torch.uint8, torch.int8)
+    if kind == CKS:  # 32-bit checksum words
+        return t.dtype in (torch.int32, getattr(torch, "uint32", torch.int32))
+    raise AssertionError(kind)
+
+
+def _ptr(t, name, min_bytes=None, device=None, kind=None):
+    """Device pointer of tensor `t` (None passes NULL), after the guards:
+    dtype (`kind`: float32 activations/outputs, int32 ids, byte weights,
+    32-bit checksums), GPU residence, contiguity, a common device and size."""
     if t is None:
         return None, device
     if isinstance(t, int):  # a raw device address, passed through unchecked
         return t, device
+    if kind is not None and not _dtype_ok(t, kind):
+        raise ValueError("%s must be a %s tensor, got %s" % (name, kind, t.dtype))
     if not getattr(t, "is_cuda", False):
         raise ValueError("%s must be a GPU tensor" % name)
     if not t.is_contiguous():
@@ -125,6 +147,20 @@ def _ptr(t, name, min_bytes=None, device=None):
         raise ValueError("%s holds %d bytes, the call needs %d" %
                          (name, t.numel() * t.element_size(), min_bytes))
     return t.data_ptr(), t.device
+
+
+def _ptrs(*specs):
+    """Pointers of (tensor, name, min_bytes, kind) specs: every dtype is
+    checked before any other guard, then each tensor as _ptr checks it, all
+    on one device.  Returns (pointers, device)."""
+    for t, name, _, kind in specs:
+        if t is not None and not isinstance(t, int) and not _dtype_ok(t, kind):
+            raise ValueError("%s must be a %s tensor, got %s" % (name, kind, t.dtype))
+    ptrs, dev = [], None
+    for t, name, min_bytes, kind in specs:
+        p, dev = _ptr(t, name, min_bytes, dev, kind)
+        ptrs.append(p)
+    return ptrs, dev
 
 
 def _stream(stream, device):
@@ -151,49 +187,49 @@ def _sz(v, per):
 # --------------------------------------------------------------------------
 def q4_0_gemv(y, w, x, M, N, K, stream=None):
     """y[M,N] = x[M,K] . W^T, W Q4_0 [N rows]."""
-    py, dev = _ptr(y, "y", _sz(M * N, 4))
-    pw, dev = _ptr(w, "w", _sz(N, q4_0_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    (py, pw, px), dev = _ptrs((y, "y", _sz(M * N, 4), F32),
+                              (w, "w", _sz(N, q4_0_row_bytes(K)), U8),
+                              (x, "x", _sz(M * K, 4), F32))
     _ok(lib().q4_0_gemv(py, pw, px, M, N, K, _stream(stream, dev)), "q4_0_gemv")
 
 
 def q4k_gemv(y, w, x, M, N, K, stream=None):
     """y[M,N] = x[M,K] . W^T, W Q4_K [N rows]."""
-    py, dev = _ptr(y, "y", _sz(M * N, 4))
-    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    (py, pw, px), dev = _ptrs((y, "y", _sz(M * N, 4), F32),
+                              (w, "w", _sz(N, q4k_row_bytes(K)), U8),
+                              (x, "x", _sz(M * K, 4), F32))
     _ok(lib().q4k_gemv(py, pw, px, M, N, K, _stream(stream, dev)), "q4k_gemv")
 
 
 def fused_rmsnorm_q4k_gemv(y, w, x, gamma, eps, M, N, K, stream=None):
     """y = RMSNorm(x; gamma, eps) . W^T, W Q4_K."""
-    py, dev = _ptr(y, "y", _sz(M * N, 4))
-    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
-    pg, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    (py, pw, px, pg), dev = _ptrs((y, "y", _sz(M * N, 4), F32),
+                                  (w, "w", _sz(N, q4k_row_bytes(K)), U8),
+                                  (x, "x", _sz(M * K, 4), F32),
+                                  (gamma, "gamma", _sz(K, 4), F32))
     _ok(lib().fused_rmsnorm_q4k_gemv(py, pw, px, pg, float(eps), M, N, K, _stream(stream, dev)),
         "fused_rmsnorm_q4k_gemv")
 
 
 def fused_gate_up_q4k_gemv(gate, up, w_gate, w_up, x, M, N, K, stream=None):
     """gate = x . Wg^T, up = x . Wu^T (Q4_K), one staging of x."""
-    pg, dev = _ptr(gate, "gate", _sz(M * N, 4))
-    pu, dev = _ptr(up, "up", _sz(M * N, 4), dev)
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    (pg, pu, pwg, pwu, px), dev = _ptrs((gate, "gate", _sz(M * N, 4), F32),
+                                        (up, "up", _sz(M * N, 4), F32),
+                                        (w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), U8),
+                                        (w_up, "w_up", _sz(N, q4k_row_bytes(K)), U8),
+                                        (x, "x", _sz(M * K, 4), F32))
     _ok(lib().fused_gate_up_q4k_gemv(pg, pu, pwg, pwu, px, M, N, K, _stream(stream, dev)),
         "fused_gate_up_q4k_gemv")
 
 
 def moe_q4_gemv(gate, up, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
     """gate/up[M, top_k, N] of the selected Q4_0 experts (expert-stacked rows)."""
-    pg, dev = _ptr(gate, "gate", _sz(M * top_k * N, 4))
-    pu, dev = _ptr(up, "up", _sz(M * top_k * N, 4), dev)
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(E * N, q4_0_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(E * N, q4_0_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
-    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4), dev)
+    (pg, pu, pwg, pwu, px, pi), dev = _ptrs((gate, "gate", _sz(M * top_k * N, 4), F32),
+                                            (up, "up", _sz(M * top_k * N, 4), F32),
+                                            (w_gate, "w_gate", _sz(E * N, q4_0_row_bytes(K)), U8),
+                                            (w_up, "w_up", _sz(E * N, q4_0_row_bytes(K)), U8),
+                                            (x, "x", _sz(M * K, 4), F32),
+                                            (ids, "ids", _sz(M * top_k, 4), I32))
     _ok(lib().moe_q4_gemv(pg, pu, pwg, pwu, px, pi, M, top_k, E, N, K, _stream(stream, dev)),
         "moe_q4_gemv")
 
@@ -201,12 +237,12 @@ def moe_q4_gemv(gate, up, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
 def fused_rmsnorm_gate_up_q4k_gemv(gate, up, w_gate, w_up, x, gamma, eps, M, N, K,
                                    stream=None):
     """gate/up = RMSNorm(x; gamma, eps) . Wg^T / Wu^T (Q4_K), one staging."""
-    pg, dev = _ptr(gate, "gate", _sz(M * N, 4))
-    pu, dev = _ptr(up, "up", _sz(M * N, 4), dev)
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
-    pga, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    (pg, pu, pwg, pwu, px, pga), dev = _ptrs((gate, "gate", _sz(M * N, 4), F32),
+                                             (up, "up", _sz(M * N, 4), F32),
+                                             (w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), U8),
+                                             (w_up, "w_up", _sz(N, q4k_row_bytes(K)), U8),
+                                             (x, "x", _sz(M * K, 4), F32),
+                                             (gamma, "gamma", _sz(K, 4), F32))
     _ok(lib().fused_rmsnorm_gate_up_q4k_gemv(pg, pu, pwg, pwu, px, pga, float(eps), M, N, K,
                                              _stream(stream, dev)),
         "fused_rmsnorm_gate_up_q4k_gemv")
@@ -214,10 +250,10 @@ def fused_rmsnorm_gate_up_q4k_gemv(gate, up, w_gate, w_up, x, gamma, eps, M, N, 
 
 def fused_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, M, N, K, stream=None):
     """h = silu(x . Wg^T) * (x . Wu^T) (Q4_K), one staging of x, one output."""
-    ph, dev = _ptr(h, "h", _sz(M * N, 4))
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    (ph, pwg, pwu, px), dev = _ptrs((h, "h", _sz(M * N, 4), F32),
+                                    (w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), U8),
+                                    (w_up, "w_up", _sz(N, q4k_row_bytes(K)), U8),
+                                    (x, "x", _sz(M * K, 4), F32))
     _ok(lib().fused_gate_up_silu_q4k_gemv(ph, pwg, pwu, px, M, N, K, _stream(stream, dev)),
         "fused_gate_up_silu_q4k_gemv")
 
@@ -225,11 +261,11 @@ def fused_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, M, N, K, stream=None):
 def fused_rmsnorm_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, gamma, eps, M, N, K,
                                         stream=None):
     """h = silu(xhat . Wg^T) * (xhat . Wu^T), xhat = RMSNorm(x; gamma, eps); one launch."""
-    ph, dev = _ptr(h, "h", _sz(M * N, 4))
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(N, q4k_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
-    pga, dev = _ptr(gamma, "gamma", _sz(K, 4), dev)
+    (ph, pwg, pwu, px, pga), dev = _ptrs((h, "h", _sz(M * N, 4), F32),
+                                         (w_gate, "w_gate", _sz(N, q4k_row_bytes(K)), U8),
+                                         (w_up, "w_up", _sz(N, q4k_row_bytes(K)), U8),
+                                         (x, "x", _sz(M * K, 4), F32),
+                                         (gamma, "gamma", _sz(K, 4), F32))
     _ok(lib().fused_rmsnorm_gate_up_silu_q4k_gemv(ph, pwg, pwu, px, pga, float(eps), M, N, K,
                                                   _stream(stream, dev)),
         "fused_rmsnorm_gate_up_silu_q4k_gemv")
@@ -237,11 +273,11 @@ def fused_rmsnorm_gate_up_silu_q4k_gemv(h, w_gate, w_up, x, gamma, eps, M, N, K,
 
 def moe_q4_gemv_silu(h, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
     """h[M, top_k, N] = silu(gate) * up of the selected Q4_0 experts."""
-    ph, dev = _ptr(h, "h", _sz(M * top_k * N, 4))
-    pwg, dev = _ptr(w_gate, "w_gate", _sz(E * N, q4_0_row_bytes(K)), dev)
-    pwu, dev = _ptr(w_up, "w_up", _sz(E * N, q4_0_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
-    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4), dev)
+    (ph, pwg, pwu, px, pi), dev = _ptrs((h, "h", _sz(M * top_k * N, 4), F32),
+                                        (w_gate, "w_gate", _sz(E * N, q4_0_row_bytes(K)), U8),
+                                        (w_up, "w_up", _sz(E * N, q4_0_row_bytes(K)), U8),
+                                        (x, "x", _sz(M * K, 4), F32),
+                                        (ids, "ids", _sz(M * top_k, 4), I32))
     _ok(lib().moe_q4_gemv_silu(ph, pwg, pwu, px, pi, M, top_k, E, N, K, _stream(stream, dev)),
         "moe_q4_gemv_silu")
 
@@ -249,25 +285,25 @@ def moe_q4_gemv_silu(h, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
 def moe_router_q4_0(ids, weights, w_router, x, M, E, K, top_k, normalize, stream=None):
     """ids/weights[M, top_k]: each token's top_k experts by Q4_0 gate logit and
     their softmax weights (normalized over the selection, or the full softmax's)."""
-    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4))
-    pw, dev = _ptr(weights, "weights", _sz(M * top_k, 4), dev)
-    pr, dev = _ptr(w_router, "w_router", _sz(E, q4_0_row_bytes(K)), dev)
-    px, dev = _ptr(x, "x", _sz(M * K, 4), dev)
+    (pi, pw, pr, px), dev = _ptrs((ids, "ids", _sz(M * top_k, 4), I32),
+                                  (weights, "weights", _sz(M * top_k, 4), F32),
+                                  (w_router, "w_router", _sz(E, q4_0_row_bytes(K)), U8),
+                                  (x, "x", _sz(M * K, 4), F32))
     _ok(lib().moe_router_q4_0(pi, pw, pr, px, M, E, K, top_k, int(normalize),
                               _stream(stream, dev)), "moe_router_q4_0")
 
 
 def dequant_q4k(out, w, N, K, stream=None):
     """out[N,K] fp32 = the Q4_K weights, bit-exact."""
-    po, dev = _ptr(out, "out", _sz(N * K, 4))
-    pw, dev = _ptr(w, "w", _sz(N, q4k_row_bytes(K)), dev)
+    (po, pw), dev = _ptrs((out, "out", _sz(N * K, 4), F32),
+                          (w, "w", _sz(N, q4k_row_bytes(K)), U8))
     _ok(lib().dequant_q4k(po, pw, N, K, _stream(stream, dev)), "dequant_q4k")
 
 
 def dequant_q4_0(out, w, N, K, stream=None):
     """out[N,K] fp32 = the Q4_0 weights, bit-exact."""
-    po, dev = _ptr(out, "out", _sz(N * K, 4))
-    pw, dev = _ptr(w, "w", _sz(N, q4_0_row_bytes(K)), dev)
+    (po, pw), dev = _ptrs((out, "out", _sz(N * K, 4), F32),
+                          (w, "w", _sz(N, q4_0_row_bytes(K)), U8))
     _ok(lib().dequant_q4_0(po, pw, N, K, _stream(stream, dev)), "dequant_q4_0")
 
 
@@ -282,9 +318,10 @@ def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=Non
         nmat = 2 if kernel_id == Q4_READ_GATE_UP else 1
         rb = q4_0_row_bytes(K) if kernel_id == Q4_READ_Q4_0_GEMV else q4k_row_bytes(K)
         rows, ncks = N, nmat * N
-    pc, dev = _ptr(checksum, "checksum", _sz(ncks, 4))
-    p0, dev = _ptr(w0, "w0", _sz(rows, rb), dev)
-    p1, dev = _ptr(w1, "w1", _sz(rows, rb) if nmat == 2 else None, dev)
-    pi, dev = _ptr(ids, "ids", _sz(M * top_k, 4) if kernel_id == Q4_READ_MOE else None, dev)
+    ids_bytes = _sz(M * top_k, 4) if kernel_id == Q4_READ_MOE else None
+    (pc, p0, p1, pi), dev = _ptrs((checksum, "checksum", _sz(ncks, 4), CKS),
+                                  (w0, "w0", _sz(rows, rb), U8),
+                                  (w1, "w1", _sz(rows, rb) if nmat == 2 else None, U8),
+                                  (ids, "ids", ids_bytes, I32))
     _ok(lib().q4_pure_read(pc, int(kernel_id), p0, p1, pi, M, top_k, E, N, K,
                            _stream(stream, dev)), "q4_pure_read")

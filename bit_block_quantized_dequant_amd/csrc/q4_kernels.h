@@ -99,7 +99,16 @@ struct MoeShared {
 // Stage the M activation rows into LDS.  Chunk layout and pre-scaling as in
 // q4_device.h; xs receives per-32-element sums (times -8 for Q4_0).  For
 // kModeNorm the rows are first RMS-normalized in fp32:
-//   r = 1 / sqrt(sum(x^2) / K + eps),  xhat = (x * r) * gamma.
+//   r = 1 / sqrt(sum(x^2) / K + eps),  xhat = (x * r) * gamma,
+// with the sum of squares accumulated in fp64 (every square of an fp32 value
+// is exact there, and no finite row can overflow it); the mean is rounded to
+// fp32 once, as in the definition.
+// Every token row m is also scaled by a power of two 2^e_m, chosen so that
+// its largest magnitude lies in [2^kXTarget, 2^(kXTarget+1)): the partial
+// sums then stay far from both ends of the fp32 range whatever the token's
+// own magnitude, and the output is scaled back by 2^-e_m.  Scaling by a
+// power of two is exact, so for tokens whose arithmetic never leaves the
+// normal fp32 range the result is bit-identical to the unscaled one.
 // Split in two so that the first weight loads can be issued in between: the
 // global loads of the first NX chunks per thread go out first (the load
 // counter is in order, so waiting for them later does not wait for the
@@ -108,12 +117,38 @@ struct MoeShared {
 // chunks per thread of its 256-thread workgroups.
 constexpr int kXReg = 4;
 constexpr int xreg_chunks(int mode) { return mode_moe(mode) ? 2 * kXReg : kXReg; }
+constexpr int kXTarget = 60;
 
 template <int NX = kXReg>
 struct XStage {
     float4 x[NX];
     float4 g[NX];
 };
+
+// Per-workgroup scratch of the staging reductions: per token and wave, the
+// sum of squares and the largest magnitude (workgroups of at most 8 waves).
+constexpr int kMaxStageWaves = 8;
+static_assert(kBlock / kWave <= kMaxStageWaves && kBlock1 / kWave <= kMaxStageWaves,
+              "staging scratch holds 8 waves");
+struct StageRed {
+    double ss[8][kMaxStageWaves];
+    float am[8][kMaxStageWaves];
+};
+
+// Exponent e with amax * 2^e in [2^target, 2^(target+1)), for amax >= 0;
+// a zero or non-finite amax leaves the token unscaled (e = 0).
+__device__ __forceinline__ int xscale_exp(float amax, int target) {
+    if (!(amax > 0.0f) || !(amax < __builtin_inff())) return 0;
+    return target - (__builtin_amdgcn_frexp_expf(amax) - 1);
+}
+
+// Sum of a double over the whole wave, the same value in every lane
+// (butterfly: lanes i and i^k add the same two values).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, kWave);
+    return v;
+}
 
 template <int MODE, int NX = kXReg>
 __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage<NX>& st) {
@@ -130,16 +165,21 @@ __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage
     }
 }
 
-// One float4 chunk i of the activations: its 32-element run sum (over the 8
-// lanes that hold the run) and its pre-scaled, swizzled LDS copy.  Called by
-// every lane; only lanes with `store` write (the others hold a clamped
-// duplicate chunk and only take part in the lane exchange).
+// One float4 chunk i of the activations (of token m = i / (K/4), scaled by
+// 2^e): its 32-element run sum (over the 8 lanes that hold the run) and its
+// pre-scaled, swizzled LDS copy.  Called by every lane; only lanes with
+// `store` write (the others hold a clamped duplicate chunk and only take
+// part in the lane exchange).
 template <int FMT, int M>
 __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i, bool store,
-                                            float4* xl, float* xsum) {
+                                            float4* xl, float* xsum, int e) {
     const int kq = p.K >> 2;
     const int m = i / kq;
     const int c = i - m * kq;
+    v.x = __builtin_ldexpf(v.x, e);
+    v.y = __builtin_ldexpf(v.y, e);
+    v.z = __builtin_ldexpf(v.z, e);
+    v.w = __builtin_ldexpf(v.w, e);
     // 8 consecutive lanes hold one 32-element run
     float s = (v.x + v.y) + (v.z + v.w);
     s = dpp_add(s, 0);
@@ -154,57 +194,87 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
 // TAIL: the call may have more than NX chunks per thread (M * K > NX * 4 *
 // blockDim); kernels that cannot are compiled without the extra loops,
 // whose load waits would otherwise also cover the weight loads in flight.
+// xe[m] receives token m's scale exponent e_m (the same in every thread).
 template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
-                                               float4* xl, float* xsum, float* red) {
+                                               float4* xl, float* xsum, StageRed& red,
+                                               int (&xe)[M]) {
     const int tid = threadIdx.x;
     const int bs = blockDim.x;
     const int kq = p.K >> 2;
     const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
     const float4* g4 = (const float4*)p.gamma;
+    const int nw = bs >> 6;
+    const int wave = tid >> 6, lane = tid & 63;
+    double ss[M];
+    float am[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        ss[m] = 0.0;
+        am[m] = 0.f;
+    }
+    // sum of squares (RMSNorm) and the largest |x| (|x * gamma| for RMSNorm,
+    // whose rows are scaled by r afterwards) of chunk i
+    auto acc = [&](float4 v, float4 g, int i, bool valid) {
+        const int m = i / kq;
+        double t = 0.0;
+        float a;
+        if constexpr (mode_norm(MODE)) {
+            t = (double)v.x * (double)v.x + (double)v.y * (double)v.y +
+                (double)v.z * (double)v.z + (double)v.w * (double)v.w;
+            a = fmaxf(fmaxf(fabsf(v.x * g.x), fabsf(v.y * g.y)),
+                      fmaxf(fabsf(v.z * g.z), fabsf(v.w * g.w)));
+        } else {
+            (void)g;
+            a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        }
+        t = valid ? t : 0.0;
+        a = valid ? a : 0.f;
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm)
+            if (m == mm) {
+                ss[mm] += t;
+                am[mm] = fmaxf(am[mm], a);
+            }
+    };
+#pragma unroll
+    for (int k = 0; k < NX; ++k) {
+        const int i = tid + k * bs;
+        acc(st.x[k], st.g[k], min(i, total - 1), i < total);
+    }
+    if constexpr (TAIL)
+        for (int i = tid + NX * bs; i < total; i += bs) {
+            float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (mode_norm(MODE)) g = g4[i % kq];
+            acc(x4[i], g, i, true);
+        }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float a = wave_max_nonneg(am[m]);  // exact in lane 63
+        if (lane == kWave - 1) red.am[m][wave] = a;
+        if constexpr (mode_norm(MODE)) {
+            const double s = wave_sum_f64(ss[m]);
+            if (lane == kWave - 1) red.ss[m][wave] = s;
+        }
+    }
+    __syncthreads();
     float rnorm[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) rnorm[m] = 1.0f;
-    if constexpr (mode_norm(MODE)) {
-        const int nw = bs >> 6;
-        const int wave = tid >> 6, lane = tid & 63;
-        float ss[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) ss[m] = 0.f;
-        auto acc_sq = [&](float4 v, int i) {
-            const int m = i / kq;
-            float t = 0.f;
-            t = __builtin_fmaf(v.x, v.x, t);
-            t = __builtin_fmaf(v.y, v.y, t);
-            t = __builtin_fmaf(v.z, v.z, t);
-            t = __builtin_fmaf(v.w, v.w, t);
-#pragma unroll
-            for (int mm = 0; mm < M; ++mm)
-                if (m == mm) ss[mm] += t;
-        };
-#pragma unroll
-        for (int k = 0; k < NX; ++k) {
-            const int i = tid + k * bs;
-            const float4 v = st.x[k];
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            acc_sq(i < total ? v : z, min(i, total - 1));
+    for (int m = 0; m < M; ++m) {
+        float a = 0.f;
+        double s = 0.0;
+        for (int i = 0; i < nw; ++i) {
+            a = fmaxf(a, red.am[m][i]);
+            if constexpr (mode_norm(MODE)) s += red.ss[m][i];
         }
-        if constexpr (TAIL)
-            for (int i = tid + NX * bs; i < total; i += bs) acc_sq(x4[i], i);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float v = group_total(ss[m], kWave);
-            if (lane == kWave - 1) red[m * 16 + wave] = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float t = 0.f;
-            for (int i = 0; i < nw; ++i) t += red[m * 16 + i];
-            const float ms = t / (float)p.K;
+        rnorm[m] = 1.0f;
+        if constexpr (mode_norm(MODE)) {
+            const float ms = (float)(s / (double)p.K);
             rnorm[m] = 1.0f / sqrtf(ms + p.eps);
+            a *= rnorm[m];
         }
+        xe[m] = __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
     }
     auto norm = [&](float4 v, float4 g, int i) {
         if constexpr (mode_norm(MODE)) {
@@ -220,17 +290,25 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
         return v;
     };
+    auto tok_e = [&](int i) {
+        const int m = i / kq;
+        int e = xe[0];
+#pragma unroll
+        for (int mm = 1; mm < M; ++mm)
+            if (m == mm) e = xe[mm];
+        return e;
+    };
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
         const int i = tid + k * bs;
         const int ic = min(i, total - 1);
-        stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum);
+        stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum, tok_e(ic));
     }
     if constexpr (TAIL) {
         for (int i = tid + NX * bs; i < total; i += bs) {
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
             if constexpr (mode_norm(MODE)) g = g4[i % kq];
-            stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum);
+            stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum, tok_e(i));
         }
     }
 }
@@ -285,7 +363,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     static_assert(!XR || (M == 1 && !mode_moe(MODE)), "register-resident x: M = 1 only");
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
-    __shared__ float red[8 * 16];
+    __shared__ StageRed red;
 
     constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
     const int tid = threadIdx.x;
@@ -403,10 +481,18 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // arithmetic: the HBM latency of the first step overlaps the staging.
     constexpr int NX = xreg_chunks(MODE);
     XStage<NX> xst;
+    int xe[M];  // per-token scale exponents of the staged activations
+#pragma unroll
+    for (int m = 0; m < M; ++m) xe[m] = 0;
     if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
-    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL, NX>(p, xst, xl, xsum, red);
+    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL, NX>(p, xst, xl, xsum, red, xe);
     __syncthreads();
+    // output scale of token m: 2^(24 - e_m) for Q4_K (whose sums carry the
+    // 6-bit scales as sc * 2^-24), 2^-e_m for Q4_0
+    int osh[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) osh[m] = (FMT == kFmtQ4K ? 24 : 0) - xe[m];
 
     if constexpr (mode_moe(MODE)) {
         // rows of pairs with an invalid id: NaN (or an all-ones checksum)
@@ -487,7 +573,6 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         // ---- end of a task: reduce over the row group; its last lane writes ----
         const int r0 = group_row(c);
         const bool last_lane = li == p.lg - 1;
-        const float oscale = FMT == kFmtQ4K ? 0x1p24f : 1.0f;
         if constexpr (mode_silu(MODE) && !PURE) {
             // one output, h = silu(gate) * up: row r's gate total is q = r,
             // its up total q = RR + r, both in this lane
@@ -498,8 +583,8 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                 const bool wr = last_lane && row < p.N;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const float g = group_total(acc[r][m], p.lg) * oscale;
-                    const float u = group_total(acc[RR + r][m], p.lg) * oscale;
+                    const float g = __builtin_ldexpf(group_total(acc[r][m], p.lg), osh[m]);
+                    const float u = __builtin_ldexpf(group_total(acc[RR + r][m], p.lg), osh[m]);
                     acc[r][m] = 0.f;
                     acc[RR + r][m] = 0.f;
                     if (wr) {
@@ -546,7 +631,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                     float* y = mt == 0 ? p.y0 : p.y1;
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        const float v = group_total(acc[q][m], p.lg) * oscale;
+                        const float v = __builtin_ldexpf(group_total(acc[q][m], p.lg), osh[m]);
                         acc[q][m] = 0.f;
                         if (wr) {
                             if constexpr (mode_moe(MODE)) {

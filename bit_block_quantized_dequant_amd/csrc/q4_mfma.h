@@ -57,6 +57,7 @@ namespace q4 {
 
 constexpr int kMBlock = 512;  // threads per workgroup
 constexpr int kMWaves = kMBlock / kWave;
+static_assert(kMWaves <= kMaxStageWaves, "staging scratch holds 8 waves");
 constexpr int kMaxMK = 32768;  // M * K limit of the library
 constexpr int kMPieces = (kMaxMK / 8 + kMBlock - 1) / kMBlock;  // staging pieces per thread
 
@@ -115,9 +116,6 @@ __host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
 // to consecutive slots; both are free of bank conflicts.
 __device__ __forceinline__ int fslot(int K, int i, int p) { return i * ((K >> 3) + 1) + p; }
 
-__device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-126, 127]
-    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-}
 
 // ---------------------------------------------------------------------------
 // Staging of the activations into A fragments.
@@ -158,7 +156,7 @@ __device__ __forceinline__ void mstage_issue(const GemvParams& p, MStageX& sx) {
 
 template <int FMT, int M, int MODE>
 __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLayout& ly,
-                                       float* red, MStageX& sx) {
+                                       StageRed& red, MStageX& sx) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ppt = p.K >> 3;  // pieces per token
     const int np = M * ppt;
@@ -166,34 +164,35 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
     const int (&um)[kMPieces] = sx.um;
     auto valid = [&](int k) { return tid + k * kMBlock < np; };
 
-    // RMSNorm: r_m = 1 / sqrt(sum(x^2) / K + eps), xhat = (x * r_m) * gamma
+    // RMSNorm: r_m = 1 / sqrt(sum(x^2) / K + eps), xhat = (x * r_m) * gamma,
+    // the sum of squares in fp64 (exact squares, no overflow for finite x)
     if constexpr (MODE == kModeNorm) {
-        float ss[M];
+        double ss[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) ss[m] = 0.f;
+        for (int m = 0; m < M; ++m) ss[m] = 0.0;
 #pragma unroll
         for (int k = 0; k < kMPieces; ++k) {
-            float t = 0.f;
+            double t = 0.0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) t = __builtin_fmaf(v[k][e], v[k][e], t);
-            t = valid(k) ? t : 0.f;
+            for (int e = 0; e < 8; ++e) t += (double)v[k][e] * (double)v[k][e];
+            t = valid(k) ? t : 0.0;
 #pragma unroll
-            for (int m = 0; m < M; ++m) ss[m] += um[k] == m ? t : 0.f;
+            for (int m = 0; m < M; ++m) ss[m] += um[k] == m ? t : 0.0;
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float t = group_total(ss[m], kWave);
-            if (lane == kWave - 1) red[m * kMWaves + wave] = t;
+            const double t = wave_sum_f64(ss[m]);
+            if (lane == kWave - 1) red.ss[m][wave] = t;
         }
         __syncthreads();
         float rn[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float t = 0.f;
-            for (int w = 0; w < kMWaves; ++w) t += red[m * kMWaves + w];
-            rn[m] = 1.0f / sqrtf(t / (float)p.K + p.eps);
+            double t = 0.0;
+            for (int w = 0; w < kMWaves; ++w) t += red.ss[m][w];
+            const float ms = (float)(t / (double)p.K);
+            rn[m] = 1.0f / sqrtf(ms + p.eps);
         }
-        __syncthreads();  // red is written again below
 #pragma unroll
         for (int k = 0; k < kMPieces; ++k) {
             const int pc = min(tid + k * kMBlock, np - 1);
@@ -209,6 +208,8 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
     }
 
     // e_m: the token's largest magnitude times 2^e_m lies in [2^14, 2^15)
+    // (any finite magnitude: the scale is applied with ldexp, not a
+    // constructed power of two)
     {
         float am[M];
 #pragma unroll
@@ -225,16 +226,13 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float t = wave_max_nonneg(am[m]);  // am >= 0: largest |x|
-            if (lane == kWave - 1) red[m * kMWaves + wave] = t;
+            if (lane == kWave - 1) red.am[m][wave] = t;
         }
         __syncthreads();
         if (tid < M) {
             float t = 0.f;
-            for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red[tid * kMWaves + w]);
-            const int ex = (int)((__builtin_bit_cast(uint32_t, t) >> 23) & 0xFF) - 127;
-            int e = t > 0.f ? 14 - ex : 0;
-            e = max(-100, min(120, e));
-            ((int*)(lds + ly.exps))[tid] = e;
+            for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red.am[tid][w]);
+            ((int*)(lds + ly.exps))[tid] = xscale_exp(t, 14);
         }
         __syncthreads();
     }
@@ -247,17 +245,16 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         const int m = um[k];
         const int pp = pc - m * ppt;
         const int e = ex[m];
-        const float s = pow2f(e);
-        const float sf = piece_is_high<FMT>(pp) ? s * 0.0625f : s;
+        const int ef = piece_is_high<FMT>(pp) ? e - 4 : e;
         h8 hi, lo;
         float part = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float xs = v[k][slot_byte(t)] * sf;
+            const float xs = __builtin_ldexpf(v[k][slot_byte(t)], ef);
             const _Float16 h = (_Float16)xs;
             hi[t] = h;
             lo[t] = (_Float16)(xs - (float)h);
-            part += v[k][t] * s;
+            part += __builtin_ldexpf(v[k][t], e);
         }
         // the 4 pieces of one 32-element group are 4 consecutive threads
         part = dpp_add(part, 0);
@@ -304,7 +301,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     using St = MStep<FMT>;
     extern __shared__ float4 smem4[];
     char* lds = (char*)smem4;
-    __shared__ float red[8 * kMWaves];
+    __shared__ StageRed red;
     const MLayout ly = mlayout(FMT, M, p.K, PURE);
 
     const int lane = threadIdx.x & 63;
@@ -646,9 +643,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                         for (int hm = 0; hm < 2; ++hm) {
                             const int m = 2 * c + hm;
                             if (m < M) {
-                                const float sm = pow2f(24 - ex[m]);
-                                const float g = (hm ? tot.y : tot.x) * sm;
-                                const float u = (hm ? uy : ux) * sm;
+                                const int sm = 24 - ex[m];
+                                const float g = __builtin_ldexpf(hm ? tot.y : tot.x, sm);
+                                const float u = __builtin_ldexpf(hm ? uy : ux, sm);
                                 p.y0[(long long)m * p.N + prow] = silu_mul(g, u);
                             }
                         }
@@ -661,7 +658,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                     for (int hm = 0; hm < 2; ++hm) {
                         const int m = 2 * c + hm;
                         if (m < M) {
-                            const float v = (hm ? tot.y : tot.x) * pow2f(24 - ex[m]);
+                            const float v = __builtin_ldexpf(hm ? tot.y : tot.x, 24 - ex[m]);
                             if constexpr (kMoe) {
                                 // output [token, slot, row], if token m chose this expert
                                 const int sl2 = moe.uslot[T.u][m];

@@ -17,7 +17,8 @@
 // lower expert index on equal logits, a NaN logit ranked as -inf), so the
 // cost does not grow with k.  Weights, in fp32 by wave 0:
 // p = exp(l - lmax) / D, D summed over the selected experts (normalize) or
-// over all E (the full softmax's entries).
+// over all E (the full softmax's entries); lmax is the largest non-NaN
+// logit, a NaN logit weighs 0, a logit equal to lmax weighs exactly 1.
 //
 // Loads stay in bounds: unit indices are clamped to the row's last block
 // pair (lanes past the end compute on it and drop the result), expert rows
@@ -33,6 +34,7 @@ constexpr int kRouterRows = 4;  // rows per lane group whose loads go out togeth
 constexpr int kRouterMaxE = 1024;
 constexpr int kRouterMaxTopK = kWave;  // lane s of wave 0 writes pick s
 constexpr int kRouterMaxK = 32768;
+static_assert(kRouterBlock / kWave <= kMaxStageWaves, "staging scratch holds 8 waves");
 
 // dynamic LDS: the staged row (chunks and run sums), E logits (padded to
 // a multiple of 4), E 64-bit rank keys, the picks
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
                                                               const float* __restrict__ x, int E,
                                                               int K, int top_k, int normalize) {
     extern __shared__ float4 smem[];
-    __shared__ float red[8 * 16];  // staging scratch (used by the RMSNorm mode only)
+    __shared__ StageRed red;  // staging scratch
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -62,8 +64,9 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
     p.x = x + (long long)m * K;
     p.K = K;
     XStage<> st;
+    int xe[1];  // the row's scale exponent: the staged row is x * 2^xe
     stage_x_issue<kModeDense>(p, 1, st);
-    stage_x_finish<kFmtQ4_0, 1, kModeDense, true>(p, st, xl, xsum, red);
+    stage_x_finish<kFmtQ4_0, 1, kModeDense, true>(p, st, xl, xsum, red, xe);
     __syncthreads();
 
     // ---- logits ----
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
 #pragma unroll
         for (int q = 0; q < kRouterRows; ++q) {
             const int e = e0 + q * rpp + gi;
-            const float t = group_total(acc[q][0], lgw);
+            const float t = __builtin_ldexpf(group_total(acc[q][0], lgw), -xe[0]);
             if (li == lgw - 1 && e < E) lg[e] = t;
         }
     }
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
     // two-key reads)
     unsigned long long* key = (unsigned long long*)(lg + ((E + 3) & ~3));
     int* sel_e = (int*)(key + E);                      // [top_k] expert of rank s
-    float* sel_v = (float*)(sel_e + kRouterMaxTopK);   // [top_k] its logit (NaN as -inf)
+    float* sel_v = (float*)(sel_e + kRouterMaxTopK);   // [top_k] its logit
     for (int e = threadIdx.x; e < E; e += kRouterBlock) {
         const float v = lg[e];
         const uint32_t b = __builtin_bit_cast(uint32_t, v != v ? -__builtin_inff() : v);
@@ -133,31 +136,36 @@ __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restric
         }
         for (; j < E; ++j) rank += key[j] > ke;
         if (rank < top_k) {
-            const float v = lg[e];
             sel_e[rank] = e;
-            sel_v[rank] = v != v ? -__builtin_inff() : v;
+            sel_v[rank] = lg[e];
         }
     }
     __syncthreads();
     if (wave != 0) return;
 
     // ---- softmax weights (wave 0; lane s writes pick s) ----
-    const float lmax = sel_v[0];
+    // lmax: the largest non-NaN logit (fmaxf drops NaN; NaN if all are NaN).
+    // A logit's term is exp(l - lmax), taken as exp(0) = 1 where l equals
+    // lmax (so experts tied at an infinite maximum share its weight, the
+    // limit of equal logits), 0 for a NaN logit; with a zero denominator
+    // (every term 0) the weights are 0.
+    float lmax = __builtin_nanf("");
+    for (int e = lane; e < E; e += kWave) lmax = fmaxf(lmax, lg[e]);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, k, kWave));
+    auto term = [&](float v) { return v != v ? 0.f : (v == lmax ? 1.f : expf(v - lmax)); };
     float ex = 0.f;
     if (normalize) {
-        if (lane < top_k) ex = expf(sel_v[lane] - lmax);
+        if (lane < top_k) ex = term(sel_v[lane]);
     } else {
-        for (int e = lane; e < E; e += kWave) {
-            const float v = lg[e];
-            ex += v != v ? 0.f : expf(v - lmax);
-        }
+        for (int e = lane; e < E; e += kWave) ex += term(lg[e]);
     }
     // wave total in lane 63, then to every lane
     ex = group_total(ex, kWave);
     ex = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), kWave - 1));
     if (lane < top_k) {
         ids[(long long)m * top_k + lane] = sel_e[lane];
-        weights[(long long)m * top_k + lane] = expf(sel_v[lane] - lmax) / ex;
+        weights[(long long)m * top_k + lane] = ex > 0.f ? term(sel_v[lane]) / ex : 0.f;
     }
 }
 

@@ -27,8 +27,31 @@
  * Activations x / X are fp32 [M, K] row-major; outputs are fp32 [M, N]
  * row-major (for the expert call, [M, top_k, N]).  GEMV means
  * y[m, n] = sum_k w[n, k] * x[m, k], evaluated in fp32 with fp32
- * accumulation; each output is within 1e-4 * sum_k |w[n,k] * x[m,k]| of the
- * exact value for finite inputs with |x| < 2^100.
+ * accumulation.
+ *
+ * Accuracy of every GEMV output (per token row m and output row n):
+ *     |y - y_exact| <= 1e-4 * sum_k |w[n,k] * x[m,k]| + 2^-149
+ * (the last term is the fp32 output's own quantum in the subnormal range),
+ * for every finite x whose outputs are representable (sum_k |w x| < 2^126),
+ * provided two conditions hold; neither depends on the token's magnitude,
+ * because every token row is scaled by a power of two before use:
+ *   (1) the dequant-dot sums the two exact parts of each weight w = a - b
+ *       separately (Q4_0: a = d*q, b = 8*d; Q4_K: a = d*sc*q, b = dmin*m),
+ *       so its rounding error scales with sum_k (|a_k| + |b_k|) |x_k|; the
+ *       bound is guaranteed while that sum is at most 8 * sum_k |w_k x_k|
+ *       (random weights of the formats' usual distributions give about 3.9
+ *       for Q4_0 and 1.3 for Q4_K; a token concentrated on weights whose
+ *       two parts cancel can exceed it);
+ *   (2) batched dense calls with M >= 3 (the matrix-core path) carry each
+ *       x as two f16 parts of x * 2^e, which represents elements down to
+ *       2^-38 * max_k |x[m,k]| to 22 bits and smaller ones with an absolute
+ *       error up to 2^-39 * max_k |x[m,k]|; the bound holds while
+ *       sum_k |w x| >= 2^-24 * max_k |x[m,k]| * sum_k |w[n,k]|.  The other
+ *       paths carry every element at fp32 precision.
+ * The RMSNorm calls accept any finite x and gamma: the normalized row is
+ * the fp32 value of the definition (its sum of squares accumulated in
+ * fp64, so it cannot overflow; a mean square beyond the fp32 range gives
+ * r = 0 and a zero row), and the bound applies with x replaced by it.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
@@ -212,7 +235,10 @@ int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float
  *   weights[m, s]  fp32 [M, top_k]: exp(l - lmax) / D, with D summed over
  *                  the selected experts (normalize = 1: the weights sum to
  *                  1) or over all E experts (normalize = 0: the entries of
- *                  the full softmax)
+ *                  the full softmax); lmax is the largest non-NaN logit, a
+ *                  logit equal to lmax weighs exactly 1 (experts tied at an
+ *                  infinite maximum share the weight, as equal logits do),
+ *                  a NaN logit weighs 0, and a zero D gives zero weights
  * The ids are in the layout moe_q4_gemv and moe_q4_gemv_silu take.  The
  * logits are fp32 sums within 1e-4 * sum_k |w x| of the exact ones; where
  * two experts' logits are closer than that, either order is correct.

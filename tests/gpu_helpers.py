@@ -1,4 +1,4 @@
-"""Helpers shared by the GPU parity tests: host/device copies, NaN-filled
+"""Helpers shared by the parity tests: host/device copies, NaN-filled
 outputs (an output a kernel forgets to write fails), and the two comparison
 bars (bit-exact, and |y - y_ref| <= 1e-4 * sum_k |w x| per element)."""
 import os
@@ -30,11 +30,16 @@ def host(t):
     return t.cpu().numpy()
 
 
+# the fp32 output's own quantum in the subnormal range: no fp32 result can be
+# closer than half of it to an exact value that falls there
+OUT_Q = 2.0 ** -149
+
+
 def assert_bound(y, ref, absdot, what):
     y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
     assert not np.any(np.isnan(y)), "%s: NaN in output" % what
     err = np.abs(y - ref)
-    bound = 1e-4 * absdot
+    bound = 1e-4 * absdot + OUT_Q
     bad = err > bound
     if np.any(bad):
         i = np.unravel_index(np.argmax(err / np.maximum(bound, 1e-300)), err.shape)
@@ -96,3 +101,21 @@ def assert_epilogue(orc, h, g_gpu, u_gpu, what):
              + 2.0 ** -149)
     assert np.all(err <= bound), "%s: epilogue off by %g (relative)" % (
         what, float(np.max(err / np.maximum(np.abs(ref[~nan]), 1e-300))))
+
+
+def split_sum(orc, fmt, w, x, N, K):
+    """sum_k (|a_k| + |b_k|) |x_k| per output, with w = a - b the two exact
+    parts the kernels sum separately (Q4_0: a = d q, b = 8 d; Q4_K:
+    a = d sc q, b = dmin m), from the oracle's dequantization of the same
+    rows with every nibble forced to 0 (which leaves -b)."""
+    deq = (orc.dequant_q4_0 if fmt == "q4_0" else orc.dequant_q4k)(w, N, K).astype(np.float64)
+    w0 = w.copy()
+    if fmt == "q4_0":
+        blk = w0.reshape(N, K // 32, 18)
+        blk[:, :, 2:] = 0
+    else:
+        sb = w0.reshape(N, K // 256, 144)
+        sb[:, :, 16:] = 0
+    b = -(orc.dequant_q4_0 if fmt == "q4_0" else orc.dequant_q4k)(w0, N, K).astype(np.float64)
+    a = deq + b
+    return np.abs(x.astype(np.float64)) @ (np.abs(a) + np.abs(b)).T

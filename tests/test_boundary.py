@@ -228,6 +228,32 @@ def test_binding_refuses_host_tensors():
         q4.dequant_q4k(torch.zeros(16, 256), w, 16, 256)
 
 
+def test_binding_refuses_wrong_dtypes():
+    """int64 ids (what torch.topk returns), half or double activations and
+    outputs, and non-byte weights are refused before any pointer is used."""
+    import torch
+    w = torch.zeros(16 * 144, dtype=torch.uint8)
+    x = torch.zeros(256)
+    y = torch.zeros(16)
+    with pytest.raises(ValueError, match="x must be a float32"):
+        q4.q4k_gemv(y, w, x.half(), 1, 16, 256)
+    with pytest.raises(ValueError, match="y must be a float32"):
+        q4.q4k_gemv(y.double(), w, x, 1, 16, 256)
+    with pytest.raises(ValueError, match="w must be a uint8"):
+        q4.q4k_gemv(y, w.float(), x, 1, 16, 256)
+    gate = torch.zeros(1, 2, 16)
+    ids64 = torch.zeros(1, 2, dtype=torch.int64)
+    wq = torch.zeros(4 * 16 * 144, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="ids must be a int32"):
+        q4.moe_q4_gemv(gate, gate.clone(), wq, wq, torch.zeros(1, 256), ids64, 1, 2, 4, 16, 256)
+    with pytest.raises(ValueError, match="ids must be a int32"):
+        q4.moe_router_q4_0(ids64, torch.zeros(1, 2), wq, torch.zeros(1, 256), 1, 4, 256, 2, 1)
+    with pytest.raises(ValueError, match="gamma must be a float32"):
+        q4.fused_rmsnorm_q4k_gemv(y, w, x, x.half(), 1e-5, 1, 16, 256)
+    with pytest.raises(ValueError, match="checksum must be a checksum"):
+        q4.q4_pure_read(torch.zeros(16), q4.Q4_READ_Q4K_GEMV, w, None, None, 1, 0, 0, 16, 256)
+
+
 def test_binding_raises_q4error(q4lib):
     # a NULL output through the binding surfaces as Q4Error(Q4_ERR_NULL)
     with pytest.raises(q4.Q4Error) as ei:

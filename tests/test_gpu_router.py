@@ -78,8 +78,13 @@ def check_router(orc, ids, wts, w, x, E, K, top_k, normalize, what):
         L = np.max(l[den_set])
         pref = np.exp(l[S] - L) / np.sum(np.exp(l[den_set] - L))
         B = np.max(bb[den_set])
-        bound = pref * (np.expm1(bb[S] + B) + 2.0 ** -16)
+        with np.errstate(over="ignore", invalid="ignore"):
+            bound = pref * (np.expm1(bb[S] + B) + 2.0 ** -16)
+        # logits known only to more than ~700 (huge tokens) leave the weights
+        # undetermined by the bar: inf * 0 there means no bound
+        bound = np.where(np.isnan(bound), np.inf, bound)
         got = wts[m].astype(np.float64)
+        assert np.all((got >= 0.0) & (got <= 1.0)), (what, m, got)
         assert np.all(np.abs(got - pref) <= bound), (what, m, got, pref, bound)
         if normalize:
             assert abs(got.sum() - 1.0) <= top_k * 2.0 ** -21, (what, m)
@@ -141,3 +146,58 @@ def test_router_then_silu_expert_call_on_device(dev, orc):
     check_router(orc, ids_h, wts_h, wr, x, E, K, top_k, 1, "chained router")
     rg, ru, ag, au = orc.moe_q4_0_gemv(wg, wu, x, ids_h, E, N, K, NT)
     assert_silu(orc, h, rg, ru, ag, au, "chained silu expert call")
+
+
+def q4_0_rows_const(E, K, d, nib):
+    """E rows of Q4_0 blocks with scale d and every nibble equal to nib."""
+    blk = np.empty((E * (K // 32), 18), np.uint8)
+    blk[:, 0:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+    blk[:, 2:] = nib | (nib << 4)
+    return blk.reshape(E, (K // 32) * 18)
+
+
+def test_router_degenerate_logits(dev, orc):
+    """Logits without a finite maximum.  d = +inf with all nibbles 0 makes
+    every weight -inf (a -inf logit against x > 0), nibbles 15 make +inf; NaN
+    tokens make NaN logits.  Ids must equal the oracle's (ties to the lower
+    index, NaN as -inf) and the weights its closed forms: uniform over
+    experts tied at -inf, shared by experts tied at +inf, 0 for NaN, 0
+    everywhere for an all-NaN row."""
+    E, K, top_k = 8, 256, 3
+    rng = synth.make_rng(8200)
+    x = np.abs(synth.activations(rng, 2, K)) + 0.5
+    cases = []
+    w = q4_0_rows_const(E, K, np.inf, 0)  # every expert -inf
+    cases.append(("all -inf", w, x))
+    w = synth.q4_0_matrix(rng, E, K)
+    w[[2, 6]] = q4_0_rows_const(2, K, np.inf, 15)  # two experts +inf
+    w[[0, 4]] = q4_0_rows_const(2, K, np.inf, 0)   # two experts -inf
+    cases.append(("+inf ties", w, x))
+    cases.append(("NaN tokens", synth.q4_0_matrix(rng, E, K),
+                  np.full((2, K), np.nan, np.float32)))
+    for name, w, xx in cases:
+        for normalize in (1, 0):
+            ids, wts = run_router(dev, w, xx, E, K, top_k, normalize)
+            rid, rw, lg, _ = orc.moe_router_q4_0(w, xx, E, K, top_k, normalize)
+            assert np.array_equal(ids, rid), (name, normalize, ids, rid)
+            assert np.all(np.abs(wts - rw) <= 2.0 ** -22 * np.abs(rw)), (name, normalize, wts, rw)
+    # the closed forms the oracle gives for these rows
+    _, rw, _, _ = orc.moe_router_q4_0(cases[0][1], x, E, K, top_k, 1)
+    assert np.allclose(rw, 1.0 / 3.0, rtol=1e-15)
+    _, rw, _, _ = orc.moe_router_q4_0(cases[1][1], x, E, K, top_k, 1)
+    assert np.array_equal(rw[:, :2], np.full((2, 2), 0.5)) and np.all(rw[:, 2] == 0.0)
+    _, rw, _, _ = orc.moe_router_q4_0(cases[2][1], cases[2][2], E, K, top_k, 0)
+    assert np.all(rw == 0.0)
+
+
+@pytest.mark.parametrize("scale", [-140, -60, 60, 100])
+def test_router_token_magnitudes(dev, orc, scale):
+    """The router's logits take the same per-token scaling as the GEMV
+    kernels: top-k validity and weights against the oracle hold from
+    subnormal tokens to 2^100."""
+    E, K, top_k, M = 64, 2048, 6, 3
+    w, x = router_inputs(8300 + scale, M, E, K)
+    x = (x.astype(np.float64) * 2.0 ** scale).astype(np.float32)
+    for normalize in (1, 0):
+        ids, wts = run_router(dev, w, x, E, K, top_k, normalize)
+        check_router(orc, ids, wts, w, x, E, K, top_k, normalize, "scale 2^%d" % scale)
