@@ -5,15 +5,20 @@ Default run (one JSON line on stdout): the headline workload, the fused
 gate+up Q4_K GEMV at M=1, K=4096, N=14336 per matrix (66,060,288 weight bytes
 per call), timed over --steps calls after --warmup untimed calls.
 
-  value        whole-job effective weight bandwidth: weight bytes of all timed
-               calls / wall time between two device synchronizations (GB/s)
+  value        whole-job effective weight bandwidth: weight bytes of the
+               --steps timed calls (HIP graphs of >= 100 back-to-back launches,
+               or one graph of all of them) / wall time between two device
+               synchronizations (GB/s)
   roofline     the kernel itself: weight bytes per launch / mean launch
                duration, from HIP events recorded on the launch stream around
-               replays of HIP graphs of back-to-back launches (no host gaps),
-               against the 8 TB/s HBM3E peak
+               4 replays of HIP graphs of 100 back-to-back launches each (no
+               host gaps, graph-launch overhead amortized; whatever --steps
+               is), against the 8 TB/s HBM3E peak
   pure_read    the same for the pure-read ceiling kernel (same bytes, same
-               addressing, no arithmetic) and for the reference stream (the
-               same byte count read as contiguous rows)
+               addressing, no arithmetic), for the reference stream (the same
+               byte count read the fastest way measured: contiguous
+               non-temporal 1 KiB wave loads), and a plain device-to-device
+               copy of the same bytes (read + write) as an external reference
   cpu_baseline the CPU oracle (plain C, float64) timed on this host's cores on
                a bounded sample of the same workload
 
@@ -96,53 +101,84 @@ class Rotation:
         return self.base + (i % self.ncopies) * self.stride
 
 
-def time_launches(torch, launch, warmup, steps, outs, batches=5):
-    """launch(i, stream) enqueues call i.  The warmup calls run eagerly; the
-    timed calls are captured as `batches` HIP graphs of back-to-back launches
-    (so host-side launch overhead cannot leave the GPU idle between them),
-    and each graph replay is bracketed by its own pair of HIP events on the
-    replay stream.  Returns (wall seconds of all timed launches between two
-    device synchronizations, per-launch mean ms of each batch, launches per
-    batch).  Afterwards the last graph's outputs (`outs`) are checked to be
-    bit-identical to an eager launch of the same call."""
+GRAPH_LAUNCHES = 100  # launches per graph of the kernel-duration measurement
+DURATION_BATCHES = 4  # graphs of the kernel-duration measurement
+
+
+def _capture(torch, s, launch, first, count):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        for k in range(count):
+            launch(first + k, s.cuda_stream)
+        g.capture_end()
+    return g
+
+
+def time_launches(torch, launch, warmup, steps, outs):
+    """launch(i, stream) enqueues call i.  Three phases on one stream:
+      1. `warmup` untimed calls, eagerly;
+      2. the timed region: exactly `steps` calls, captured as HIP graphs of
+         at least GRAPH_LAUNCHES back-to-back launches (one graph if steps is
+         smaller), replayed between two device synchronizations -> the wall
+         time of the whole job;
+      3. the kernel duration: DURATION_BATCHES graphs of GRAPH_LAUNCHES
+         launches each, whatever `steps` is, each replay bracketed by HIP
+         events recorded on the replay stream, so graph-launch overhead is
+         amortized over 100 launches -> per-launch mean of each batch.
+    Afterwards the last graph's outputs (`outs`) are checked to be
+    bit-identical to an eager launch of the same call.  Returns (wall
+    seconds of phase 2, per-launch ms of each phase-3 batch, launches per
+    batch)."""
     s = torch.cuda.Stream()  # default priority
     with torch.cuda.stream(s):
         for i in range(warmup):
             launch(i, s.cuda_stream)
     torch.cuda.synchronize()
-    per = max(1, steps // batches)
-    cnts = [per] * (batches - 1) + [steps - per * (batches - 1)]
-    graphs, n = [], warmup
+    n = warmup
+    # phase 2: the timed steps
+    steps = max(1, int(steps))
+    ngraph = max(1, steps // GRAPH_LAUNCHES)
+    cnts = [steps // ngraph] * ngraph
+    cnts[-1] += steps - sum(cnts)
+    graphs = []
     for cnt in cnts:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            g.capture_begin()
-            for k in range(cnt):
-                launch(n + k, s.cuda_stream)
-            g.capture_end()
-        graphs.append(g)
+        graphs.append(_capture(torch, s, launch, n, cnt))
         n += cnt
     for g in graphs:  # first replays upload the graphs
         g.replay()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(batches)]
     t0 = time.perf_counter()
     with torch.cuda.stream(s):
-        for b, g in enumerate(graphs):
-            ev[b][0].record()
+        for g in graphs:
             g.replay()
-            ev[b][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # phase 3: kernel duration
+    dgraphs = []
+    for _ in range(DURATION_BATCHES):
+        dgraphs.append(_capture(torch, s, launch, n, GRAPH_LAUNCHES))
+        n += GRAPH_LAUNCHES
+    for g in dgraphs:
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in dgraphs]
+    with torch.cuda.stream(s):
+        for (e0, e1), g in zip(ev, dgraphs):
+            e0.record()
+            g.replay()
+            e1.record()
+    torch.cuda.synchronize()
     got = [o.clone() for o in outs]
     with torch.cuda.stream(s):
         launch(n - 1, s.cuda_stream)
     torch.cuda.synchronize()
-    for a, b in zip(got, outs):
-        if not torch.equal(a.view(torch.int32), b.view(torch.int32)):
+    for a_, b_ in zip(got, outs):
+        if not torch.equal(a_.view(torch.int32), b_.view(torch.int32)):
             raise RuntimeError("graph replay and eager launch of the same call differ")
-    return wall, [a.elapsed_time(b) / c for (a, b), c in zip(ev, cnts)], cnts
+    dcnts = [GRAPH_LAUNCHES] * DURATION_BATCHES
+    return wall, [e0.elapsed_time(e1) / c for (e0, e1), c in zip(ev, dcnts)], dcnts
 
 
 def stats(batch_ms, cnts):
@@ -286,7 +322,7 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
     # reference stream: the same byte count as contiguous rows of K * 9/16 bytes
     srb = synth.q4k_row_bytes(K)
     srows = wbytes // srb
-    scks = torch.empty(srows, dtype=torch.int32, device=dev)
+    scks = torch.empty((srows * srb + 4095) // 4096, dtype=torch.int32, device=dev)
     keep.append(scks)
 
     def stream_launch(i, stream):
@@ -413,6 +449,18 @@ def measure_chain(torch, dev, n=300):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(seconds):
     """The oracle's gate+up GEMV of the headline workload, timed on the host."""
     from bit_block_quantized_dequant_amd import synth
@@ -435,7 +483,7 @@ def cpu_baseline(seconds):
     o.gate_up_q4k_gemv(d["w_gate"], d["w_up"], d["x"], N, K, 1)
     one = time.perf_counter() - t1
     return dict(value=wbytes * calls / el / 1e9, unit="GB/s", cores=nt, kind="oracle",
-                single_thread_value=wbytes / one / 1e9,
+                cpu_model=cpu_model(), single_thread_value=wbytes / one / 1e9,
                 sample="%d full calls of the oracle's gate+up Q4_K GEMV (M=1, K=4096, "
                        "N=14336x2; float64 accumulation) in %.1f s on %d threads; "
                        "single_thread_value: one full call on 1 thread (%.2f s)"
@@ -473,6 +521,31 @@ def recorded_traffic():
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_copy(torch, dev, nbytes, reps=50):
+    """A plain device-to-device copy (torch's copy_, the runtime's copy
+    kernel) of nbytes, from a rotation of sources totalling at least 1 GiB
+    into one destination, timed with HIP events over `reps` copies after 5
+    warmup copies.  An external reference beside the read ceilings: each copy
+    reads and writes nbytes.  Returns the read+write GB/s and the mean us."""
+    n = nbytes // 4
+    ncopies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    src = torch.ones(ncopies, n, dtype=torch.float32, device=dev)
+    dst = torch.empty(n, dtype=torch.float32, device=dev)
+    for i in range(5):
+        dst.copy_(src[i % ncopies])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst.copy_(src[i % ncopies])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes=n * 4, us_mean=us, read_write_gbs=2 * n * 4 / (us * 1e-6) / 1e9)
 
 
 def copy_calibration(torch, dev, mib):
@@ -548,6 +621,10 @@ def main():
              head["kernel_gbs"], head["ceiling_gbs"], head["value_gbs"]), file=sys.stderr,
           flush=True)
 
+    copy_ref = measure_copy(torch, dev, head["weight_bytes"])
+    print("device copy of the same bytes: %.2f us, %.0f GB/s read+write"
+          % (copy_ref["us_mean"], copy_ref["read_write_gbs"]), file=sys.stderr, flush=True)
+
     rows = []
     if args.all:
         # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output,
@@ -611,6 +688,7 @@ def main():
             "kernel_frac_of_ceiling": round(head["frac_of_ceiling"], 4),
             "stream_achieved": round(head["stream_gbs"], 2),
             "kernel_frac_of_stream": round(head["frac_of_stream"], 4),
+            "device_copy_read_write": round(copy_ref["read_write_gbs"], 2),
         },
         "cpu_baseline": cpu,
     }

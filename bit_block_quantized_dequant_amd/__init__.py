@@ -313,7 +313,8 @@ def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=Non
         rows, nmat, rb = E * N, 2, q4_0_row_bytes(K)
         ncks = 2 * M * top_k * N
     elif kernel_id == Q4_READ_STREAM:
-        rows, nmat, rb, ncks = N, 1, q4k_row_bytes(K), N
+        rows, nmat, rb = N, 1, q4k_row_bytes(K)
+        ncks = (max(0, N) * rb + 4095) // 4096  # one checksum per 4 KiB block
     else:
         nmat = 2 if kernel_id == Q4_READ_GATE_UP else 1
         rb = q4_0_row_bytes(K) if kernel_id == Q4_READ_Q4_0_GEMV else q4k_row_bytes(K)

@@ -1,0 +1,416 @@
+// q4_host.h -- host side of libq4gemv shared by its translation units:
+// argument validation, launch planning and the dispatch from a call to its
+// kernel instantiation.
+//
+// Validation runs before any HIP call, so every refusal path is testable on
+// a machine without a GPU.  Launches go through hipLaunchKernel on the
+// caller's stream; the library allocates nothing and keeps no per-call state
+// (only per-device caches of the compute-unit count, of which kernels have
+// had their LDS limit raised and of their occupancy).  Everything here has
+// internal linkage: each translation unit that includes it instantiates the
+// kernels of its own entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "q4_kernels.h"
+#include "q4_mfma.h"
+#include "q4_router.h"
+#include "q4gemv.h"
+
+using namespace q4;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+static_assert(Q4_MAX_MK == kMaxMK, "staging of the batched kernel is sized for Q4_MAX_MK");
+
+// ---------------------------------------------------------------------------
+// Validation (pure host code)
+// ---------------------------------------------------------------------------
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int check_dims(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > 8) return Q4_ERR_BATCH;
+    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (M * K > Q4_MAX_MK) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+    int cus = 0;
+};
+inline DeviceInfo g_dev[kMaxDevices];
+inline std::mutex g_dev_mu;
+
+inline int device_cus(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return Q4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev[dev].cus == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return Q4_ERR_HIP;
+        g_dev[dev].cus = cus;
+    }
+    *out = g_dev[dev].cus;
+    return Q4_OK;
+}
+
+// Optional tuning override of the resident workgroups per CU (read once).
+inline int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+inline int pow2ceil(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// LDS bytes of a GEMV workgroup: M rows of K floats (17 float4 chunks per
+// 64 elements) plus K/32 run sums each.
+inline size_t gemv_lds_bytes(int M, int K, bool pure) {
+    if (pure) return 0;
+    return (size_t)M * (K / 64) * 17 * 16 + (size_t)M * (K / 32) * 4;
+}
+
+// static shared memory of the batched kernel (its reduction scratch) plus
+// margin; the expert call adds its dedupe tables
+constexpr int kMfmaStaticLds = 1024;
+constexpr int kMfmaMoeStaticLds = 3072;
+
+// Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
+// the static shared state), capped at `mx`.
+inline int wg_per_cu(size_t lds, int mx = 2) {
+    const size_t cap = 160 * 1024 - 2048;
+    int by_lds = lds == 0 ? mx : (int)(cap / lds);
+    int w = by_lds < mx ? by_lds : mx;
+    static const int override_wg = env_int("Q4GEMV_WG_PER_CU", 0);
+    if (override_wg > 0 && override_wg < w) w = override_wg;
+    return w < 1 ? 1 : w;
+}
+
+// Raise a kernel's dynamic-LDS limit once per device: to 160 KB less
+// `reserve` bytes kept for its static shared variables.
+inline int allow_big_lds(const void* kern, std::atomic<int>* done, int reserve = 2048) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
+    if (done[dev].load(std::memory_order_acquire)) return Q4_OK;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - reserve);
+    if (e != hipSuccess) return Q4_ERR_HIP;
+    done[dev].store(1, std::memory_order_release);
+    return Q4_OK;
+}
+
+// Workgroups of `kern` that can be resident on one CU at once (registers,
+// LDS and waves), from the runtime's occupancy calculator; cached per device.
+inline int resident_per_cu(const void* kern, int threads, size_t lds, std::atomic<int>* cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+    int v = cache[dev].load(std::memory_order_acquire);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds) != hipSuccess || n < 1)
+        n = 1;
+    cache[dev].store(n, std::memory_order_release);
+    return n;
+}
+
+template <typename Kern>
+inline int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* stream,
+           std::atomic<int>* big_lds_done, int threads = kBlock, int reserve = 2048) {
+    if (lds > 64 * 1024) {
+        int st = allow_big_lds((const void*)kern, big_lds_done, reserve);
+        if (st) return st;
+    }
+    void* args[] = {(void*)&p};
+    hipError_t e = hipLaunchKernel((const void*)kern, dim3(blocks), dim3(threads), args, lds,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+// Fill the work-split fields of p for a call with `rows` rows per matrix
+// and RR rows per lane; returns the number of workgroups of `threads`
+// threads (at most `wgmax` and `resident` per CU, the second being the
+// kernel's occupancy limit).
+// Lanes per row group for a row of `upr` 64-weight units: the whole wave
+// on one row when the row has at least 64 units, else the power of two that
+// covers the row.  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
+// measurements; the kernel takes any such width.
+inline int choose_lg(int upr) {
+    static const int forced = env_int("Q4GEMV_LG", 0);
+    if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
+    return upr >= kWave ? kWave : pow2ceil(upr);
+}
+
+inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
+         int cus, int resident, int threads, int wgmax) {
+    p.K = K;
+    p.upr = K / kUnitElems;
+    p.lg = choose_lg(p.upr);
+    p.upl = (p.upr + p.lg - 1) / p.lg;
+    p.rgw = kWave / p.lg;
+    const int nrg = (rows + RR - 1) / RR;
+    long long tasks;
+    if (moe) {
+        p.nrg = (nrg + p.rgw - 1) / p.rgw * p.rgw;
+        p.ntasks = 0;
+        tasks = (long long)npairs_max * (p.nrg / p.rgw);
+    } else {
+        p.nrg = nrg;
+        p.ntasks = (nrg + p.rgw - 1) / p.rgw;
+        tasks = p.ntasks;
+    }
+    const int wpb = threads / kWave;
+    int wgc = wg_per_cu(gemv_lds_bytes(M, K, pure), wgmax);
+    if (wgc > resident) wgc = resident;
+    // Every CU gets the same number of workgroups (the per-CU load/issue rate
+    // is shared by its waves); tasks are then split evenly over all waves.
+    static const int bpc_override = env_int("Q4GEMV_BLOCKS_PER_CU", 0);
+    const int bpc = bpc_override > 0 ? bpc_override : wgc;
+    long long blocks_ll = (long long)cus * bpc;
+    const long long need = (tasks + wpb - 1) / wpb;  // no more waves than tasks
+    if (blocks_ll > need) blocks_ll = need;
+    // At least two steps per wave (a wave with one step has nothing to
+    // overlap its loads with), down to one workgroup per CU.
+    long long two = (tasks * p.upl / 2 + wpb - 1) / wpb;
+    if (two < cus) two = cus;
+    if (blocks_ll > two) blocks_ll = two;
+    int blocks = (int)(blocks_ll < 1 ? 1 : blocks_ll);
+    p.nwaves = blocks * wpb;
+    return blocks;
+}
+
+#ifndef Q4_RR_SINGLE
+#define Q4_RR_SINGLE 2  // rows per lane per step, single-matrix calls
+#endif
+#ifndef Q4_RR_PAIR
+#define Q4_RR_PAIR 1  // rows per lane per step and matrix, two-matrix calls
+#endif
+#ifndef Q4_PREFETCH
+#define Q4_PREFETCH 1  // steps of weight loads in flight ahead of the computed one
+#endif
+
+// Q4GEMV_XR=0 keeps the activations in LDS also where they fit in registers
+// (for comparisons).
+inline bool xr_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_XR");
+        return !(s && *s && atoi(s) == 0);
+    }();
+    return on;
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
+inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
+    constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
+    // Workgroup shape (measured): single-token and expert calls run 256-thread
+    // groups; dense single-token calls at most two per CU (four were 4 %
+    // slower), expert calls up to four (their 136 VGPRs allow three: 12
+    // waves per CU instead of 8 with 512-thread groups, 9-14 % faster).
+    // Dense batched calls on this kernel run two 512-thread groups.
+    constexpr int BS = gemv_threads(M, MODE);
+    constexpr int WGMAX = mode_moe(MODE) ? 4 : 2;
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    static std::atomic<int> resident[kMaxDevices];
+    // a pure-read pass takes the launch shape of the call it mirrors
+    auto kern = [](bool pure) {
+        if constexpr (XR)
+            return pure ? gemv_kernel_xr<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, BS>
+                        : gemv_kernel_xr<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, BS>;
+        else
+            return pure ? gemv_kernel<FMT, M, NMAT, RR, MODE, true, Q4_PREFETCH, TAIL, BS>
+                        : gemv_kernel<FMT, M, NMAT, RR, MODE, false, Q4_PREFETCH, TAIL, BS>;
+    };
+    const int res = resident_per_cu((const void*)kern(false), BS,
+                                    gemv_lds_bytes(M, p.K, false), resident);
+    const int blocks =
+        plan(p, M, p.K, p.N, RR, mode_moe(MODE), npairs_max, false, cus, res, BS, WGMAX);
+    const size_t lds = gemv_lds_bytes(M, p.K, PURE);
+    return launch(kern(PURE), p, blocks, lds, stream, big_lds_done, BS);
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
+    if constexpr (M == 1 && !mode_moe(MODE)) {
+        // one 64-weight unit per lane per row: K <= 64 * 64 (and then the
+        // activations need no staging loop beyond the first kXReg chunks)
+        const int upr = p.K / kUnitElems;
+        if (p.K <= kWave * kUnitElems && choose_lg(upr) >= upr && xr_enabled())
+            return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
+    }
+    if ((long long)M * p.K > (long long)xreg_chunks(MODE) * 4 * gemv_threads(M, MODE))
+        return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
+    return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
+}
+
+// Matrix-core kernel: steps of weight loads each wave keeps in flight, and
+// the number of waves per CU the K split aims for.
+#ifndef Q4_MFMA_PD_Q4K
+#define Q4_MFMA_PD_Q4K 2
+#endif
+#ifndef Q4_MFMA_PD_Q4_0
+#define Q4_MFMA_PD_Q4_0 3
+#endif
+#ifndef Q4_MFMA_WAVES_PER_CU
+#define Q4_MFMA_WAVES_PER_CU 8
+#endif
+
+// Waves that split one 16-row tile's K range (1, 2, 4 or 8): the fewest that
+// give the CUs at least three quarters of their share of waves, at most one
+// per step of the row (gate+up, 1792 tiles: one wave per tile, 16 steps each,
+// measured 4 % faster than two waves of 8 steps).  It depends on the matrix
+// shape and the CU count only, so a token's result does not depend on the
+// batch it is computed in.
+inline int mfma_ks(long long ntiles, int steps, int cus) {
+    static const int forced = env_int("Q4GEMV_MFMA_KS", 0);
+    const long long want = (long long)cus * Q4_MFMA_WAVES_PER_CU;
+    int ks = 1;
+    while (ks < kMWaves && 2 * ks <= steps && 4 * ntiles * ks < 3 * want) ks *= 2;
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8)
+        ks = forced <= steps ? forced : ks;
+    return ks;
+}
+
+// Batches of at least this many token rows run on the matrix-core kernel
+// (at M = 2 the VALU kernel is still below its issue limit and faster).
+// Q4GEMV_MFMA=0 sends every batch to the VALU kernel (for comparisons; the
+// results differ only by rounding).
+#ifndef Q4_MFMA_MIN_M
+#define Q4_MFMA_MIN_M 3
+#endif
+inline bool mfma_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_MFMA");
+        return !(s && *s && atoi(s) == 0);
+    }();
+    return on;
+}
+
+inline bool moe_mfma_enabled() {
+    static const bool on = [] {
+        const char* s = getenv("Q4GEMV_MOE_MFMA");
+        return s && *s && atoi(s) != 0;
+    }();
+    return on;
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
+    constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
+    constexpr int kReserve = mode_moe(MODE) ? kMfmaMoeStaticLds : kMfmaStaticLds;
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
+    // a pure-read pass takes the launch shape of the call it mirrors
+    static std::atomic<int> resident[kMaxDevices];
+    const size_t call_lds = (size_t)mlayout(FMT, M, p.K, false).bytes;
+    int wgc = wg_per_cu(call_lds);
+    if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
+        static std::atomic<int> big_lds_mirror[kMaxDevices];
+        int st = allow_big_lds((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
+                               big_lds_mirror, kReserve);
+        if (st) return st;
+    }
+    const int res = resident_per_cu((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
+                                    kMBlock, call_lds, resident);
+    if (wgc > res) wgc = res;
+    // (the expert call: at most nexperts unique experts, each N rows per matrix)
+    // (the K split is chosen from the 16-row tile count of the plain call,
+    // also for the SiLU-gated call and its 8 + 8-row tiles, so that both
+    // accumulate every row alike)
+    const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
+    p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
+    const long long ntiles_run =
+        (MODE == kModeSilu || MODE == kModeNormSilu) ? (long long)nexperts * ((p.N + 7) / 8)
+                                                      : ntiles;
+    const int TG = kMWaves / p.ks;
+    long long blocks = (long long)cus * wgc;
+    const long long need = (ntiles_run + TG - 1) / TG;
+    if (blocks > need) blocks = need;
+    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
+                  big_lds_done, kMBlock, kReserve);
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE>
+inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st) return st;
+    // batched calls on the matrix cores; the expert call only on request
+    // (Q4GEMV_MOE_MFMA=1: it measured slower than the VALU expert kernel at
+    // the E=64, top-6, 1408 x 2048 shape), from M = 2 on, where its
+    // activations leave room in LDS for the expert tables
+    // (the SiLU-gated expert call always runs the VALU kernel)
+    const bool moe_fits = !mode_moe(MODE) ||
+                          (MODE == kModeMoe && moe_mfma_enabled() && M >= 2 &&
+                           mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds);
+    const int min_m = mode_moe(MODE) ? 2 : Q4_MFMA_MIN_M;
+    if constexpr (MODE != kModeMoeSilu) {
+        if (M >= min_m && moe_fits && mfma_enabled()) {
+            const int nexp = mode_moe(MODE) ? npairs_max : 1;
+            switch (M) {
+                case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
+                case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
+                case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
+                case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
+                case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
+                case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
+                case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
+            }
+            return Q4_ERR_BATCH;
+        }
+    }
+    switch (M) {
+        case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);
+        case 2: return run_m<FMT, NMAT, MODE, PURE, 2>(p, cus, npairs_max, stream);
+        case 3: return run_m<FMT, NMAT, MODE, PURE, 3>(p, cus, npairs_max, stream);
+        case 4: return run_m<FMT, NMAT, MODE, PURE, 4>(p, cus, npairs_max, stream);
+        case 5: return run_m<FMT, NMAT, MODE, PURE, 5>(p, cus, npairs_max, stream);
+        case 6: return run_m<FMT, NMAT, MODE, PURE, 6>(p, cus, npairs_max, stream);
+        case 7: return run_m<FMT, NMAT, MODE, PURE, 7>(p, cus, npairs_max, stream);
+        case 8: return run_m<FMT, NMAT, MODE, PURE, 8>(p, cus, npairs_max, stream);
+    }
+    return Q4_ERR_BATCH;
+}
+
+inline GemvParams base_params(const void* w0, const void* w1, float* y0, float* y1, const float* x,
+                       int64_t N, int64_t K, int fmt) {
+    GemvParams p = {};
+    p.w0 = (const uint8_t*)w0;
+    p.w1 = (const uint8_t*)w1;
+    p.y0 = y0;
+    p.y1 = y1;
+    p.x = x;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.row_bytes = fmt == kFmtQ4K ? (K / 256) * kQ4KBytes : (K / 32) * 18;
+    return p;
+}
+
+inline int check_moe(int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K) {
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (E < 1 || E >= (1 << 20) || top_k < 1 || top_k > E || M * top_k > kMaxPairs)
+        return Q4_ERR_SHAPE;
+    if (E * N > INT32_MAX) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+}  // namespace

@@ -62,6 +62,19 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 constexpr int kMaxPairs = 64;  // M * top_k limit of the expert call
 
+// Workgroup barrier for data in LDS only: waits for this wave's LDS
+// operations (lgkmcnt(0)), not for its global loads still in flight, which
+// __syncthreads would also wait for; so the weight loads issued ahead of the
+// activation staging stay in flight across the staging barriers.  LDS is
+// coherent within the workgroup; the empty asm statements keep the compiler
+// from moving memory operations across the barrier.
+__device__ __forceinline__ void sync_lds() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 struct GemvParams {
     const uint8_t* w0;
     const uint8_t* w1;
@@ -133,6 +146,8 @@ static_assert(kBlock / kWave <= kMaxStageWaves && kBlock1 / kWave <= kMaxStageWa
 struct StageRed {
     double ss[8][kMaxStageWaves];
     float am[8][kMaxStageWaves];
+    float r[8];  // per token: the RMSNorm factor
+    int e[8];    // per token: the scale exponent
 };
 
 // Exponent e with amax * 2^e in [2^target, 2^(target+1)), for amax >= 0;
@@ -258,31 +273,32 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             if (lane == kWave - 1) red.ss[m][wave] = s;
         }
     }
-    __syncthreads();
-    float rnorm[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
+    sync_lds();
+    // one thread per token combines the waves' partials (the factor and the
+    // exponent are read back by token index: kept in LDS, not in a
+    // register array, which a runtime index would move to scratch memory)
+    if (tid < M) {
         float a = 0.f;
         double s = 0.0;
         for (int i = 0; i < nw; ++i) {
-            a = fmaxf(a, red.am[m][i]);
-            if constexpr (mode_norm(MODE)) s += red.ss[m][i];
+            a = fmaxf(a, red.am[tid][i]);
+            if constexpr (mode_norm(MODE)) s += red.ss[tid][i];
         }
-        rnorm[m] = 1.0f;
+        float r = 1.0f;
         if constexpr (mode_norm(MODE)) {
             const float ms = (float)(s / (double)p.K);
-            rnorm[m] = 1.0f / sqrtf(ms + p.eps);
-            a *= rnorm[m];
+            r = 1.0f / sqrtf(ms + p.eps);
+            a *= r;
         }
-        xe[m] = __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
+        red.r[tid] = r;
+        red.e[tid] = xscale_exp(a, kXTarget);
     }
+    sync_lds();
+#pragma unroll
+    for (int m = 0; m < M; ++m) xe[m] = __builtin_amdgcn_readfirstlane(red.e[m]);
     auto norm = [&](float4 v, float4 g, int i) {
         if constexpr (mode_norm(MODE)) {
-            const int m = i / kq;
-            float r = rnorm[0];
-#pragma unroll
-            for (int mm = 1; mm < M; ++mm)
-                if (m == mm) r = rnorm[mm];
+            const float r = red.r[i / kq];
             v.x = (v.x * r) * g.x;
             v.y = (v.y * r) * g.y;
             v.z = (v.z * r) * g.z;
@@ -290,14 +306,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
         return v;
     };
-    auto tok_e = [&](int i) {
-        const int m = i / kq;
-        int e = xe[0];
-#pragma unroll
-        for (int mm = 1; mm < M; ++mm)
-            if (m == mm) e = xe[mm];
-        return e;
-    };
+    auto tok_e = [&](int i) { return red.e[i / kq]; };
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
         const int i = tid + k * bs;
@@ -487,7 +496,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
     if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL, NX>(p, xst, xl, xsum, red, xe);
-    __syncthreads();
+    sync_lds();
     // output scale of token m: 2^(24 - e_m) for Q4_K (whose sums carry the
     // 6-bit scales as sc * 2^-24), 2^-e_m for Q4_0
     int osh[M];
@@ -704,44 +713,80 @@ __global__ __launch_bounds__(BS) void gemv_kernel(const GemvParams p) {
     gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, false, TAIL>(p);
 }
 
-// The register-resident variant must fit 128 VGPRs: four waves per SIMD
-// (16 per CU), as for the LDS variant.
+// The register-resident variant runs two 256-thread workgroups per CU (two
+// waves per SIMD), so it may use up to 256 VGPRs.
 template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, int BS>
-__global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(2)))
 void gemv_kernel_xr(const GemvParams p) {
     gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, true, false>(p);
 }
 
 // ---------------------------------------------------------------------------
-// Reference stream: rows of rb bytes (a multiple of 16) read front to back,
-// one row per wave at a time in contiguous 16-byte-per-lane instructions,
-// rows strided over all waves; writes each row's word checksum.  Loads are
-// unconditional (lanes past the row end re-read its last 16 bytes and drop
-// them).
+// Reference stream: the fastest way measured on this part to read a byte
+// range once, used as the read ceiling of a call of the same byte count.
+// Every wave instruction reads 1 KiB contiguous (16 bytes per lane) with the
+// non-temporal hint; a wave step is a block of kStreamU such instructions
+// (4 KiB), and the next block's loads are issued before the current one is
+// summed (two blocks in flight per wave); blocks are strided over all waves
+// of a grid of two 256-thread workgroups per CU.  Each block's 32-bit word
+// sum (modulo 2^32) is written, which proves every byte was read.  (A sweep
+// of launch shapes, bytes in flight per wave and load kinds, including loads
+// straight into LDS, found this shape fastest; the hint helps only when each
+// instruction consumes whole cache lines.)
 // ---------------------------------------------------------------------------
 constexpr int kStreamBlock = 256;
+constexpr int kStreamU = 4;                         // 1 KiB loads per block
+constexpr int kStreamBlockBytes = kStreamU * 1024;  // checksum granule
 
-__global__ __launch_bounds__(kStreamBlock) void stream_read_kernel(uint32_t* __restrict__ cks,
-                                                                   const uint8_t* __restrict__ w,
-                                                                   int nrows, int rb) {
+__device__ __forceinline__ u32x4 ldg16_nt(const uint8_t* p) {
+    return __builtin_nontemporal_load((const u32x4*)__builtin_assume_aligned(p, 16));
+}
+
+static __global__ __launch_bounds__(kStreamBlock) void stream_read_kernel(
+    uint32_t* __restrict__ cks, const uint8_t* __restrict__ w, long long bytes) {
     const int lane = threadIdx.x & 63;
     const int gw =
         __builtin_amdgcn_readfirstlane(blockIdx.x * (kStreamBlock / kWave) + (threadIdx.x >> 6));
     const int nw = gridDim.x * (kStreamBlock / kWave);
-    const int nch = rb >> 4;                // 16-byte chunks per row
-    const int nins = (nch + kWave - 1) / kWave;
-    for (int r = gw; r < nrows; r += nw) {
-        const uint8_t* row = w + (long long)r * rb;
+    const long long nblk = (bytes + kStreamBlockBytes - 1) / kStreamBlockBytes;
+    if (gw >= nblk) return;
+    const long long last = bytes - 16;  // bytes is a multiple of 16
+    // loads are unconditional: a lane past the end re-reads the last 16
+    // bytes and drops them
+    auto load = [&](long long b, u32x4 (&r)[kStreamU]) {
+#pragma unroll
+        for (int i = 0; i < kStreamU; ++i) {
+            const long long o = b * kStreamBlockBytes + 1024 * i + 16 * lane;
+            r[i] = ldg16_nt(w + (o < last ? o : last));
+        }
+    };
+    auto sum = [&](long long b, const u32x4 (&r)[kStreamU]) {
         uint32_t s = 0;
-#pragma unroll 4
-        for (int n = 0; n < nins; ++n) {
-            const int c = n * kWave + lane;
-            const u32x4 v = ldg16(row + min(c, nch - 1) * 16);
-            const uint32_t t = v.x + v.y + v.z + v.w;
-            s += c < nch ? t : 0u;
+#pragma unroll
+        for (int i = 0; i < kStreamU; ++i) {
+            const long long o = b * kStreamBlockBytes + 1024 * i + 16 * lane;
+            s += o <= last ? (r[i].x + r[i].y) + (r[i].z + r[i].w) : 0u;
         }
         s = group_total(s, kWave);
-        if (lane == kWave - 1) cks[r] = s;
+        if (lane == kWave - 1) cks[b] = s;
+    };
+    u32x4 A[kStreamU], B[kStreamU];
+    long long b = gw;
+    load(b, A);
+    for (;;) {
+        const long long nb = b + nw;
+        const bool hb = nb < nblk;
+        load(hb ? nb : b, B);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(b, A);
+        if (!hb) break;
+        const long long nc = nb + nw;
+        const bool hc = nc < nblk;
+        load(hc ? nc : nb, A);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(nb, B);
+        if (!hc) break;
+        b = nc;
     }
 }
 

@@ -184,7 +184,7 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
             const double t = wave_sum_f64(ss[m]);
             if (lane == kWave - 1) red.ss[m][wave] = t;
         }
-        __syncthreads();
+        sync_lds();
         float rn[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -228,13 +228,13 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
             const float t = wave_max_nonneg(am[m]);  // am >= 0: largest |x|
             if (lane == kWave - 1) red.am[m][wave] = t;
         }
-        __syncthreads();
+        sync_lds();
         if (tid < M) {
             float t = 0.f;
             for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red.am[tid][w]);
             ((int*)(lds + ly.exps))[tid] = xscale_exp(t, 14);
         }
-        __syncthreads();
+        sync_lds();
     }
     const int* ex = (const int*)(lds + ly.exps);
 
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         }
     }
     if constexpr (!PURE) mstage<FMT, M, mode_norm(MODE) ? kModeNorm : kModeDense>(p, lds, ly, red, sx);
-    __syncthreads();
+    sync_lds();
 
     const int n = nrounds * (st1 - st0);
     int cs = st0, cr = 0, buf = 0;

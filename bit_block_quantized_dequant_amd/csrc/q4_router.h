@@ -43,7 +43,7 @@ inline size_t router_lds_bytes(int K, int E) {
            (size_t)((E + 3) & ~3) * 4 + (size_t)E * 8 + (size_t)kRouterMaxTopK * 8;
 }
 
-__global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restrict__ ids,
+static __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __restrict__ ids,
                                                               float* __restrict__ weights,
                                                               const uint8_t* __restrict__ w,
                                                               const float* __restrict__ x, int E,

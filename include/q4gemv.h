@@ -278,12 +278,15 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream);
  *   Q4_READ_Q4K_GEMV    w0: Q4_K [N, K]                     [N]
  *   Q4_READ_GATE_UP     w0, w1: Q4_K [N, K] each            [2, N]  (w0 rows, then w1)
  *   Q4_READ_MOE         w0, w1: Q4_0 experts as moe_q4_gemv [2, M, top_k, N]
- *   Q4_READ_STREAM      w0: N rows of K*9/16 bytes          [N]
+ *   Q4_READ_STREAM      w0: N * K * 9/16 bytes              [ceil(bytes / 4096)]
  *
- * Q4_READ_STREAM is the reference "ideal" stream of the same byte count as
- * a GEMV of N rows and K columns (both formats use 9/16 byte per weight):
- * each wave reads whole rows front to back in contiguous 1 KiB
- * instructions, rows in a strided order over all waves.  M is ignored.
+ * Q4_READ_STREAM is the reference stream of the same byte count as a GEMV
+ * of N rows and K columns (both formats use 9/16 byte per weight), read the
+ * fastest way measured on this part: contiguous 1 KiB wave instructions
+ * with the non-temporal hint, 4 KiB blocks per wave step with the next
+ * block in flight, blocks strided over two 256-thread workgroups per CU.
+ * Its checksums are per 4 KiB block of the range (the last one partial),
+ * not per row.  M is ignored.
  *
  * M selects the launch shape of the mirrored call (and, for Q4_READ_MOE,
  * the number of tokens); ids, top_k and E are used by Q4_READ_MOE only

@@ -2,7 +2,7 @@
 split, cursors, clamping), used to prove on the CPU that every load of every
 lane of every wave stays inside the weight buffer for a given call shape.
 
-It restates, in Python, the integer arithmetic of plan() in q4gemv.hip and of
+It restates, in Python, the integer arithmetic of plan() in q4_host.h and of
 the cursor / load() code of gemv_kernel in q4_kernels.h; keep the two in step
 (test_addressing.py runs it over the parity-test shapes and edge cases)."""
 Q4K_BYTES = 144
@@ -154,7 +154,7 @@ def mlayout(fmt, M, K, pure=False):
 
 
 def mfma_ks(ntiles, steps, cus, waves_per_cu=8):
-    """Waves per tile (mfma_ks() in q4gemv.hip)."""
+    """Waves per tile (mfma_ks() in q4_host.h)."""
     ks = 1
     while ks < 8 and 2 * ks <= steps and 4 * ntiles * ks < 3 * cus * waves_per_cu:
         ks *= 2

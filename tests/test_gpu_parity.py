@@ -278,16 +278,23 @@ def test_pure_read_checksums(dev, orc, M):
     assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w0, N, rb))
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (37, 512), (301, 3584), (1000, 4096), (3, 32768)])
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 512), (301, 3584), (1000, 4096), (3, 32768),
+                                 (28672, 4096)])
 def test_stream_read_checksums(dev, orc, N, K):
-    """The reference stream reads every byte of N rows of K*9/16 bytes once."""
+    """The reference stream reads every byte of N * K * 9/16 bytes once: one
+    word sum per 4 KiB block (the last one partial), up to the headline's
+    66 MB (many blocks per wave)."""
     import torch
     import bit_block_quantized_dequant_amd as q4
     rng = synth.make_rng(78 + N)
     w = synth.q4k_matrix(rng, N, K)
-    c = empty((N,), dev, torch.int32)
+    nbytes = w.size
+    nblk = (nbytes + 4095) // 4096
+    c = empty((nblk,), dev, torch.int32)
     q4.q4_pure_read(c, q4.Q4_READ_STREAM, T(w, dev), None, None, 1, 0, 0, N, K)
-    assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(w, N, synth.q4k_row_bytes(K)))
+    padded = np.zeros(nblk * 4096, np.uint8)
+    padded[:nbytes] = w.reshape(-1)
+    assert np.array_equal(host(c).view(np.uint32), orc.row_checksum(padded, nblk, 4096))
 
 
 def test_pure_read_moe_checksums(dev, orc):
