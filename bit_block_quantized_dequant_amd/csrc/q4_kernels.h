@@ -157,11 +157,31 @@ __device__ __forceinline__ int xscale_exp(float amax, int target) {
     return target - (__builtin_amdgcn_frexp_expf(amax) - 1);
 }
 
-// Sum of a double over the whole wave, the same value in every lane
-// (butterfly: lanes i and i^k add the same two values).
+// Sum of a double over the whole wave, exact in lane 63: the DPP pattern
+// of group_total (q4_device.h) applied to both 32-bit halves.
+__device__ __forceinline__ double dpp_add_f64(double v, int ctrl_sel) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+    switch (ctrl_sel) {
+        case 0: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
+        case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
+        case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
+        case 3: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+        case 4: lo = __builtin_amdgcn_update_dpp(0, lo, 0x142, 0xA, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x142, 0xA, 0xF, false); break;
+        default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x143, 0xC, 0xF, false);
+                 hi = __builtin_amdgcn_update_dpp(0, hi, 0x143, 0xC, 0xF, false); break;
+    }
+    const unsigned long long t = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+    return v + __builtin_bit_cast(double, t);
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, kWave);
+    for (int k = 0; k < 6; ++k) v = dpp_add_f64(v, k);
     return v;
 }
 
@@ -185,24 +205,31 @@ __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage
 // pre-scaled, swizzled LDS copy.  Called by every lane; only lanes with
 // `store` write (the others hold a clamped duplicate chunk and only take
 // part in the lane exchange).
-template <int FMT, int M>
+// DEFER: store the chunk and its run sum unscaled (no 2^e, no 2^24 / 2^20);
+// the register-resident kernel applies both when it copies its lane's
+// activations into registers.
+template <int FMT, int M, bool DEFER = false>
 __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i, bool store,
                                             float4* xl, float* xsum, int e) {
     const int kq = p.K >> 2;
     const int m = i / kq;
     const int c = i - m * kq;
-    v.x = __builtin_ldexpf(v.x, e);
-    v.y = __builtin_ldexpf(v.y, e);
-    v.z = __builtin_ldexpf(v.z, e);
-    v.w = __builtin_ldexpf(v.w, e);
+    if constexpr (!DEFER) {
+        v.x = __builtin_ldexpf(v.x, e);
+        v.y = __builtin_ldexpf(v.y, e);
+        v.z = __builtin_ldexpf(v.z, e);
+        v.w = __builtin_ldexpf(v.w, e);
+    }
     // 8 consecutive lanes hold one 32-element run
     float s = (v.x + v.y) + (v.z + v.w);
     s = dpp_add(s, 0);
     s = dpp_add(s, 1);
     s = dpp_add(s, 2);
     if (store && (c & 7) == 7) xsum[m * (p.K >> 5) + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
-    const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
-    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+    if constexpr (!DEFER) {
+        const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
+        v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+    }
     if (store) xl[m * xrow_chunks(p.K) + xchunk(c >> 4, c & 15)] = v;
 }
 
@@ -210,10 +237,14 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
 // blockDim); kernels that cannot are compiled without the extra loops,
 // whose load waits would otherwise also cover the weight loads in flight.
 // xe[m] receives token m's scale exponent e_m (the same in every thread).
-template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg>
+// DEFER (single token, no RMSNorm): no reduction barrier here; the chunks
+// are stored unscaled and each wave's partial maximum is left in red.am[0],
+// to be combined after the caller's barrier (stage_x_exponent).
+template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg, bool DEFER = false>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
                                                float4* xl, float* xsum, StageRed& red,
                                                int (&xe)[M]) {
+    static_assert(!DEFER || (M == 1 && !mode_norm(MODE)), "deferred scaling: one token, no norm");
     const int tid = threadIdx.x;
     const int bs = blockDim.x;
     const int kq = p.K >> 2;
@@ -273,16 +304,34 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             if (lane == kWave - 1) red.ss[m][wave] = s;
         }
     }
+    if constexpr (DEFER) {
+        (void)nw;
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+            const int i = tid + k * bs;
+            const int ic = min(i, total - 1);
+            stage_chunk<FMT, M, true>(p, st.x[k], ic, i < total, xl, xsum, 0);
+        }
+        if constexpr (TAIL)
+            for (int i = tid + NX * bs; i < total; i += bs)
+                stage_chunk<FMT, M, true>(p, x4[i], i, true, xl, xsum, 0);
+        return;
+    }
     sync_lds();
-    // one thread per token combines the waves' partials (the factor and the
-    // exponent are read back by token index: kept in LDS, not in a
-    // register array, which a runtime index would move to scratch memory)
-    if (tid < M) {
+    // Every thread combines the waves' partials of every token (the same
+    // arithmetic, so the same values) and writes the factor and exponent to
+    // LDS, where it reads them back by token index: all threads write the
+    // same values, so each read returns the thread's own result and no
+    // further barrier is needed (a register array indexed at run time would
+    // be moved to scratch memory).
+    float r1 = 1.0f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
         float a = 0.f;
         double s = 0.0;
         for (int i = 0; i < nw; ++i) {
-            a = fmaxf(a, red.am[tid][i]);
-            if constexpr (mode_norm(MODE)) s += red.ss[tid][i];
+            a = fmaxf(a, red.am[m][i]);
+            if constexpr (mode_norm(MODE)) s += red.ss[m][i];
         }
         float r = 1.0f;
         if constexpr (mode_norm(MODE)) {
@@ -290,15 +339,18 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             r = 1.0f / sqrtf(ms + p.eps);
             a *= r;
         }
-        red.r[tid] = r;
-        red.e[tid] = xscale_exp(a, kXTarget);
+        const int e = xscale_exp(a, kXTarget);
+        xe[m] = __builtin_amdgcn_readfirstlane(e);
+        r1 = r;
+        if constexpr (M > 1) {
+            red.r[m] = r;
+            red.e[m] = e;
+        }
     }
-    sync_lds();
-#pragma unroll
-    for (int m = 0; m < M; ++m) xe[m] = __builtin_amdgcn_readfirstlane(red.e[m]);
+    // (one token: the factor and exponent stay in registers)
     auto norm = [&](float4 v, float4 g, int i) {
         if constexpr (mode_norm(MODE)) {
-            const float r = red.r[i / kq];
+            const float r = M == 1 ? r1 : red.r[i / kq];
             v.x = (v.x * r) * g.x;
             v.y = (v.y * r) * g.y;
             v.z = (v.z * r) * g.z;
@@ -306,7 +358,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
         return v;
     };
-    auto tok_e = [&](int i) { return red.e[i / kq]; };
+    auto tok_e = [&](int i) { return M == 1 ? xe[0] : red.e[i / kq]; };
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
         const int i = tid + k * bs;
@@ -320,6 +372,14 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum, tok_e(i));
         }
     }
+}
+
+// The scale exponent of a single token staged with DEFER, from the waves'
+// partial maxima (call after the barrier that follows the staging).
+__device__ __forceinline__ int stage_x_exponent(const StageRed& red, int nwaves) {
+    float a = 0.f;
+    for (int i = 0; i < nwaves; ++i) a = fmaxf(a, red.am[0][i]);
+    return __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
 }
 
 // In-kernel dedupe of the expert ids (wave 0); everyone reads it after the
@@ -493,10 +553,15 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     int xe[M];  // per-token scale exponents of the staged activations
 #pragma unroll
     for (int m = 0; m < M; ++m) xe[m] = 0;
+    // register-resident single token without RMSNorm: the scale is applied
+    // when the lane copies its activations into registers (no extra barrier)
+    constexpr bool kDefer = XR && !mode_norm(MODE);
     if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
-    if constexpr (!PURE) stage_x_finish<FMT, M, MODE, TAIL, NX>(p, xst, xl, xsum, red, xe);
+    if constexpr (!PURE)
+        stage_x_finish<FMT, M, MODE, TAIL, NX, kDefer>(p, xst, xl, xsum, red, xe);
     sync_lds();
+    if constexpr (kDefer && !PURE) xe[0] = stage_x_exponent(red, (int)(blockDim.x >> 6));
     // output scale of token m: 2^(24 - e_m) for Q4_K (whose sums carry the
     // 6-bit scales as sc * 2^-24), 2^-e_m for Q4_0
     int osh[M];
@@ -533,6 +598,21 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
 #pragma unroll
         for (int c = 0; c < kUnitChunks - 1; ++c) xr[c] = xl[xchunk(uc, c)];
         xsr[0] = ((const float2*)xsum)[uc];
+        if constexpr (kDefer) {
+            // 2^e and the 2^24 (2^20 for elements met as high nibbles)
+            // pre-scale of the staging, applied here
+            const int e = xe[0];
+#pragma unroll
+            for (int c = 0; c < kUnitChunks - 1; ++c) {
+                const int sh = e + (elem_is_high<FMT>(4 * c) ? 20 : 24);
+                xr[c].x = __builtin_ldexpf(xr[c].x, sh);
+                xr[c].y = __builtin_ldexpf(xr[c].y, sh);
+                xr[c].z = __builtin_ldexpf(xr[c].z, sh);
+                xr[c].w = __builtin_ldexpf(xr[c].w, sh);
+            }
+            xsr[0].x = __builtin_ldexpf(xsr[0].x, e);
+            xsr[0].y = __builtin_ldexpf(xsr[0].y, e);
+        }
     }
 
     float acc[NR][M];
