@@ -59,9 +59,11 @@ def q4_0_matrix(rng, rows: int, K: int, dlo: float = 0.01, dhi: float = 0.1) -> 
 
 
 def q4k_matrix(rng, rows: int, K: int, lo: float = 0.005, hi: float = 0.05) -> np.ndarray:
-    """Random Q4_K weights, uint8 [rows, K/256*144]."""
-    assert K % 256 == 0
-    nb = rows * (K // 256)
+    """Random Q4_K weights, uint8 [rows, ceil(K/256)*144].  For K not a
+    multiple of 256 the last super-block of every row is only partly used;
+    its unused part is drawn like the rest (random bytes)."""
+    assert K % 32 == 0
+    nb = rows * ((K + 255) // 256)
     d = f16_uniform_bits(rng, nb, lo, hi)
     dmin = f16_uniform_bits(rng, nb, lo, hi)
     scales = rng.integers(0, 256, size=(nb, 12), dtype=np.uint8)
@@ -71,7 +73,7 @@ def q4k_matrix(rng, rows: int, K: int, lo: float = 0.005, hi: float = 0.05) -> n
     _put_f16(blk, 2, dmin)
     blk[:, 4:16] = scales
     blk[:, 16:] = qs
-    return blk.reshape(rows, (K // 256) * 144)
+    return blk.reshape(rows, ((K + 255) // 256) * 144)
 
 
 def activations(rng, M: int, K: int, sigma: float = 1.0) -> np.ndarray:
@@ -96,7 +98,13 @@ def q4_0_row_bytes(K: int) -> int:
 
 
 def q4k_row_bytes(K: int) -> int:
-    return (K // 256) * 144
+    return ((K + 255) // 256) * 144
+
+
+def pair_activations(rng, M: int, top_k: int, K: int, sigma: float = 1.0) -> np.ndarray:
+    """Inputs of the expert down-projection, fp32 [M, top_k, K]: one row per
+    (token, slot) pair."""
+    return (rng.standard_normal((M, top_k, K)) * sigma).astype(np.float32)
 
 
 # The five named workloads (sizes and distributions of the decode path).

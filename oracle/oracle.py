@@ -63,6 +63,9 @@ class Oracle:
         L.oracle_moe_q4_0_gemv.argtypes = [_u8p, _u8p, _f32p, _i32p, _i64, _i64, _i64, _i64,
                                            _i64, _f64p, _f64p, _f64p, _f64p, _int]
         L.oracle_moe_q4_0_gemv.restype = None
+        L.oracle_moe_q4_0_down.argtypes = [_u8p, _f32p, _i32p, _i64, _i64, _i64, _i64, _i64,
+                                           _f64p, _f64p, _int]
+        L.oracle_moe_q4_0_down.restype = None
         L.oracle_silu_mul.argtypes = [_f64p, _f64p, _i64, _f64p]
         L.oracle_silu_mul.restype = None
         L.oracle_topk_softmax.argtypes = [_f64p, _i64, _i64, _i64, _int, _i32p, _f64p]
@@ -94,7 +97,7 @@ class Oracle:
 
     def dequant_q4k(self, w, N: int, K: int) -> np.ndarray:
         w = _c(w, np.uint8)
-        assert w.size == N * (K // 256) * 144
+        assert w.size == N * ((K + 255) // 256) * 144
         out = np.empty((N, K), dtype=np.float32)
         self.L.oracle_dequant_q4k(_p(w, _u8p), N, K, _p(out, _f32p))
         return out
@@ -166,6 +169,19 @@ class Oracle:
                                     M, top_k, E, N, K, *[_p(o, _f64p) for o in outs],
                                     int(nthreads))
         return tuple(outs)
+
+    def moe_q4_0_down(self, wd, h, ids, E: int, N: int, K: int, nthreads: int = 1):
+        """Down-projection of every (token, slot) pair's own input row h[m, s]
+        by its expert's matrix.  Returns (y, absy), each float64 [M, top_k, N]."""
+        wd = _c(wd, np.uint8)
+        ids = _c(np.atleast_2d(ids), np.int32)
+        M, top_k = ids.shape
+        h = _c(np.asarray(h, dtype=np.float32).reshape(M, top_k, K), np.float32)
+        y = np.empty((M, top_k, N), dtype=np.float64)
+        a = np.empty((M, top_k, N), dtype=np.float64)
+        self.L.oracle_moe_q4_0_down(_p(wd, _u8p), _p(h, _f32p), _p(ids, _i32p), M, top_k, E, N,
+                                    K, _p(y, _f64p), _p(a, _f64p), int(nthreads))
+        return y, a
 
     def silu_mul(self, g, u) -> np.ndarray:
         """h = silu(g) * u elementwise, float64, same shape as g."""

@@ -131,13 +131,28 @@ void oracle_dequant_q4_0(const uint8_t* w, int64_t N, int64_t K, float* out)
                                out + n * K + b * Q4_0_BLOCK_ELEMS);
 }
 
+/* Q4_K rows whose K is not a multiple of 256 ([TG] PHASE 3 sizes a row by
+ * ceiling division, (K + 255) / 256 super-blocks, while the format defines
+ * whole super-blocks only).  The reading taken here: a row is
+ * ceil(K/256) super-blocks of 144 bytes, its elements are the first K of
+ * their 256 * ceil(K/256) values, and the rest of the last super-block is
+ * padding that no result depends on. */
+static int64_t q4k_row_superblocks(int64_t K)
+{
+    return (K + Q4K_SB_ELEMS - 1) / Q4K_SB_ELEMS;
+}
+
 void oracle_dequant_q4k(const uint8_t* w, int64_t N, int64_t K, float* out)
 {
-    int64_t nb = K / Q4K_SB_ELEMS;
+    int64_t nb = q4k_row_superblocks(K);
+    float tmp[Q4K_SB_ELEMS];
     for (int64_t n = 0; n < N; ++n)
-        for (int64_t s = 0; s < nb; ++s)
-            dequant_q4k_superblock(w + (n * nb + s) * Q4K_SB_BYTES,
-                                   out + n * K + s * Q4K_SB_ELEMS);
+        for (int64_t s = 0; s < nb; ++s) {
+            int64_t k0 = s * Q4K_SB_ELEMS;
+            int64_t cnt = K - k0 < Q4K_SB_ELEMS ? K - k0 : Q4K_SB_ELEMS;
+            dequant_q4k_superblock(w + (n * nb + s) * Q4K_SB_BYTES, tmp);
+            memcpy(out + n * K + k0, tmp, sizeof(float) * (size_t)cnt);
+        }
 }
 
 /* ------------------------------------------------------------------------
@@ -160,7 +175,7 @@ static void* gemv_worker(void* arg)
     gemv_job* j = (gemv_job*)arg;
     float* row = (float*)malloc(sizeof(float) * (size_t)j->K);
     int64_t row_bytes = j->fmt == 0 ? (j->K / Q4_0_BLOCK_ELEMS) * Q4_0_BLOCK_BYTES
-                                    : (j->K / Q4K_SB_ELEMS) * Q4K_SB_BYTES;
+                                    : q4k_row_superblocks(j->K) * Q4K_SB_BYTES;
     for (int64_t n = j->row0; n < j->row1; ++n) {
         if (j->fmt == 0)
             oracle_dequant_q4_0(j->w + n * row_bytes, 1, j->K, row);
@@ -310,6 +325,36 @@ void oracle_silu_mul(const double* g, const double* u, int64_t n, double* h)
 }
 
 /* ------------------------------------------------------------------------
+ * Expert down-projection over the selected experts, Q4_0: every (token,
+ * slot) pair p = m*top_k + s has its own input row h[p] (the gated
+ * activation its expert produced) and is multiplied by the down matrix of
+ * the same expert e = ids[p]:
+ *   y[p, r] = sum_k Wd[e*N + r, k] * h[p, k].
+ * [IL] moe_lab: expert-stacked rows and the per-(column, slot) selection,
+ * here applied to the projection that follows the gate and up matrices.
+ * An id outside [0, E) yields NaN rows, as for the gate/up call.
+ * ---------------------------------------------------------------------- */
+void oracle_moe_q4_0_down(const uint8_t* wd, const float* h, const int32_t* ids, int64_t M,
+                          int64_t top_k, int64_t E, int64_t N, int64_t K, double* y,
+                          double* absy, int nthreads)
+{
+    int64_t mat_bytes = N * (K / Q4_0_BLOCK_ELEMS) * Q4_0_BLOCK_BYTES;
+    for (int64_t p = 0; p < M * top_k; ++p) {
+        int32_t e = ids[p];
+        double* yp = y + p * N;
+        double* ap = absy ? absy + p * N : NULL;
+        if (e < 0 || e >= E) {
+            for (int64_t r = 0; r < N; ++r) {
+                yp[r] = NAN;
+                if (ap) ap[r] = NAN;
+            }
+            continue;
+        }
+        oracle_q4_0_gemv(wd + e * mat_bytes, h + p * K, 1, N, K, yp, ap, nthreads);
+    }
+}
+
+/* ------------------------------------------------------------------------
  * Router top-k with softmax weights, per token row of logits [M, E]
  * ([AT] moe_gate_topk_fused: gate logits over the experts, then the top-K
  * indices and their softmax weights, with a normalize flag).
@@ -407,4 +452,4 @@ void oracle_row_checksum(const uint8_t* w, int64_t nrows, int64_t row_bytes, uin
     }
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }

@@ -279,10 +279,13 @@ def pin_gemv_onehot_and_scaling(o):
 
 def pin_bruteforce(o, seeds=range(100)):
     """Independent bit-gathering evaluator with exact rationals on tiny shapes:
-    dequant bit-exact, GEMV within double rounding, |w*x| sum likewise."""
+    dequant bit-exact, GEMV within double rounding, |w*x| sum likewise.  K
+    cycles through whole super-blocks and tails (K % 256 != 0: a Q4_K row is
+    ceil(K/256) super-blocks of which the first K values count; Q4_0 takes
+    an odd block count there too)."""
     for seed in seeds:
         rng = synth.make_rng(100 + seed)
-        K = 256 * (1 + seed % 2)
+        K = (256, 512, 96, 352)[seed % 4]
         N, M = 2 + seed % 3, 1 + seed % 3
         x = synth.activations(rng, M, K)
         for fmt in ("q4_0", "q4k"):
@@ -493,7 +496,95 @@ def pin_router(o):
         assert np.array_equal(ids, ids2) and np.array_equal(wts, w2)
 
 
+def _q4k_padding_mask(K):
+    """Byte mask of one Q4_K row of K elements: the bits of the last
+    super-block that belong to no element (nibbles of sub-blocks at or past
+    K, and those sub-blocks' 6-bit scale and min fields)."""
+    S = (K + 255) // 256
+    mask = np.zeros(S * 144, np.uint8)
+    kt = K - 256 * (S - 1)  # elements used in the last super-block
+    base = 144 * (S - 1)
+    for t in range(kt, 256):
+        byte = base + 16 + 32 * (t // 64) + t % 32
+        mask[byte] |= 0x0F << (4 * ((t % 64) // 32))
+    for j in range(kt // 32, 8):
+        for src in sum(_q4k_field_bits(j), []):
+            mask[base + 4 + src // 8] |= 1 << (src % 8)
+    return mask
+
+
+def pin_q4k_tail(o):
+    """Rows whose K is not a multiple of 256: the values are the first K of
+    the same bytes read as whole super-blocks (the prefix property ties the
+    tail to the whole-super-block path, which the other pins fix); the
+    padding bits decide nothing (flipping all of them changes no value, no
+    GEMV sum); the rows are ceil(K/256) * 144 bytes apart."""
+    rng = synth.make_rng(41)
+    N = 5
+    x_full = synth.activations(rng, 2, 768)
+    for K in (32, 96, 224, 288, 480, 736):
+        w = synth.q4k_matrix(rng, N, K)
+        S = (K + 255) // 256
+        assert w.shape == (N, S * 144)
+        full = o.dequant_q4k(w, N, 256 * S)
+        part = o.dequant_q4k(w, N, K)
+        assert np.array_equal(part, full[:, :K]), K
+        x = np.ascontiguousarray(x_full[:, :K])
+        y, a = o.q4k_gemv(w, x, N, K)
+        xz = np.zeros((2, 256 * S), np.float32)
+        xz[:, :K] = x
+        yf, af = o.q4k_gemv(w, xz, N, 256 * S)
+        assert np.array_equal(y, yf) and np.array_equal(a, af), K
+        w2 = w ^ _q4k_padding_mask(K)[None, :]
+        assert not np.array_equal(w2, w) or K % 256 == 0
+        assert np.array_equal(o.dequant_q4k(w2, N, K), part), K
+        y2, a2 = o.q4k_gemv(w2, x, N, K)
+        assert np.array_equal(y2, y) and np.array_equal(a2, a), K
+
+
+def pin_moe_down(o):
+    """Expert down-projection: each (token, slot) pair's own row against its
+    expert's matrix, checked against the bit-gathering evaluator with exact
+    rationals; an id outside [0, E) gives NaN rows; all-equal nibbles c give
+    sum_b d_b (c - 8) H_b (H: block sums of the pair's row)."""
+    rng = synth.make_rng(43)
+    M, top_k, E, N, K = 2, 3, 4, 3, 96
+    wd = synth.q4_0_matrix(rng, E * N, K)
+    h = synth.pair_activations(rng, M, top_k, K)
+    ids = np.array([[3, 0, 2], [2, 9, 1]], np.int32)
+    y, a = o.moe_q4_0_down(wd, h, ids, E, N, K)
+    for m in range(M):
+        for s in range(top_k):
+            e = ids[m, s]
+            if e >= E:
+                assert np.all(np.isnan(y[m, s])) and np.all(np.isnan(a[m, s]))
+                continue
+            for r in range(N):
+                row = wd[e * N + r]
+                wf = [_to_f32(brute_weight_q4_0(row, k)) for k in range(K)]
+                exact = sum(Fraction(float(wk)) * Fraction(float(hk))
+                            for wk, hk in zip(wf, h[m, s]))
+                aex = sum(abs(Fraction(float(wk)) * Fraction(float(hk)))
+                          for wk, hk in zip(wf, h[m, s]))
+                tol = K * 2.0 ** -52 * float(aex)
+                assert abs(y[m, s, r] - float(exact)) <= tol, (m, s, r)
+                assert abs(a[m, s, r] - float(aex)) <= tol, (m, s, r)
+    c = 13
+    ds = rng.uniform(0.01, 0.1, (E * N, K // 32)).astype(np.float16)
+    wc = np.stack([np.concatenate([q4_0_block(d, np.full(16, c | (c << 4), np.uint8))
+                                   for d in drow]) for drow in ds])
+    ids = np.array([[1, 0, 3], [3, 2, 1]], np.int32)
+    y, _ = o.moe_q4_0_down(wc, h, ids, E, N, K)
+    H = h.astype(np.float64).reshape(M, top_k, K // 32, 32).sum(-1)
+    for m in range(M):
+        for s in range(top_k):
+            e = ids[m, s]
+            want = (ds[e * N:(e + 1) * N].astype(np.float64) * (c - 8)) @ H[m, s]
+            assert np.allclose(y[m, s], want, rtol=1e-12, atol=1e-12), (m, s)
+
+
 # fast pins first: the mutant test stops at the first failing pin
 ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_silu, pin_topk_softmax,
             pin_router, pin_gemv_onehot_and_scaling, pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
-            pin_rmsnorm, pin_composites, pin_f16_decode, pin_bruteforce]
+            pin_rmsnorm, pin_composites, pin_q4k_tail, pin_moe_down, pin_f16_decode,
+            pin_bruteforce]

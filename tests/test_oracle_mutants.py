@@ -57,6 +57,17 @@ MUTANTS = {
     "normalize flag ignored": ("if (normalize) {", "if (0) {"),
     "router logits of token 0 only": ("oracle_q4_0_gemv(w, x, M, E, K, l, a, 1);",
                                       "oracle_q4_0_gemv(w, x, 1, E, K, l, a, 1);"),
+    "q4k tail rows of floor(K/256) super-blocks": (
+        "return (K + Q4K_SB_ELEMS - 1) / Q4K_SB_ELEMS;", "return K / Q4K_SB_ELEMS;"),
+    "q4k tail drops the last sub-block": (
+        "int64_t cnt = K - k0 < Q4K_SB_ELEMS ? K - k0 : Q4K_SB_ELEMS;",
+        "int64_t cnt = K - k0 < Q4K_SB_ELEMS ? K - k0 - 32 : Q4K_SB_ELEMS;"),
+    "q4k gemv row stride of whole super-blocks": (
+        ": q4k_row_superblocks(j->K) * Q4K_SB_BYTES;", ": (j->K / Q4K_SB_ELEMS) * Q4K_SB_BYTES;"),
+    "down uses the token's row for every slot": (
+        "h + p * K, 1, N, K, yp", "h + (p / top_k) * K, 1, N, K, yp"),
+    "down ignores the expert id": ("oracle_q4_0_gemv(wd + e * mat_bytes", "oracle_q4_0_gemv(wd"),
+    "down invalid id not NaN": ("yp[r] = NAN;", "yp[r] = 0.0;"),
     "silu without g": ("double s = g[i] / (1.0 + exp(-g[i]));",
                        "double s = 1.0 / (1.0 + exp(-g[i]));"),
 }
