@@ -105,7 +105,7 @@ def q4_0_row_bytes(K: int) -> int:
 
 
 def q4k_row_bytes(K: int) -> int:
-    return K // 256 * 144
+    return (K + 255) // 256 * 144
 
 
 # --------------------------------------------------------------------------

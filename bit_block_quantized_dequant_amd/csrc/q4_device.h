@@ -181,7 +181,7 @@ __device__ __forceinline__ void nib_dot(uint32_t q, const float4& xa, const floa
 // LDS instruction, no address arithmetic per step).
 constexpr int kUnitChunks = 17;
 __device__ __forceinline__ int xchunk(int u, int c) { return u * kUnitChunks + c; }
-__device__ __forceinline__ int xrow_chunks(int K) { return (K >> 6) * kUnitChunks; }
+__device__ __forceinline__ int xrow_chunks(int upr) { return upr * kUnitChunks; }
 
 // Is element e (within its row) met as a high nibble?  Q4_K: elements 32..63
 // of each 64-element chunk; Q4_0: elements 16..31 of each 32-element block.

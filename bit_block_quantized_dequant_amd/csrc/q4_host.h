@@ -37,11 +37,27 @@ static_assert(Q4_MAX_MK == kMaxMK, "staging of the batched kernel is sized for Q
 // ---------------------------------------------------------------------------
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-inline int check_dims(int64_t M, int64_t N, int64_t K) {
+// K granularity of a format: a Q4_K row may end inside its last super-block
+// at any multiple of 32 (the rest of that super-block is padding); a Q4_0
+// row must hold an even number of 18-byte blocks, so that every row starts
+// on a 4-byte boundary for the kernels' word loads.
+inline bool k_ok(int64_t K, int fmt) {
+    return K > 0 && K <= INT32_MAX && K % (fmt == kFmtQ4K ? 32 : 64) == 0;
+}
+
+// Staged columns of a call: K rounded up to whole 64-weight units.
+inline int64_t k_units(int64_t K) { return (K + kUnitElems - 1) / kUnitElems; }
+
+inline int check_dims(int64_t M, int64_t N, int64_t K, int fmt) {
     if (M < 1 || M > 8) return Q4_ERR_BATCH;
-    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
-    if (M * K > Q4_MAX_MK) return Q4_ERR_SHAPE;
+    if (!k_ok(K, fmt) || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (M * k_units(K) * kUnitElems > Q4_MAX_MK) return Q4_ERR_SHAPE;
     return Q4_OK;
+}
+
+// Bytes of one weight row: ceil(K/256) super-blocks (Q4_K), K/32 blocks (Q4_0).
+inline long long row_bytes_of(int64_t K, int fmt) {
+    return fmt == kFmtQ4K ? (long long)((K + 255) / 256) * kQ4KBytes : (long long)(K / 32) * 18;
 }
 
 // ---------------------------------------------------------------------------
@@ -83,11 +99,12 @@ inline int pow2ceil(int v) {
     return p;
 }
 
-// LDS bytes of a GEMV workgroup: M rows of K floats (17 float4 chunks per
-// 64 elements) plus K/32 run sums each.
+// LDS bytes of a GEMV workgroup: M rows of ceil(K/64) units of 64 floats
+// (17 float4 chunks each) plus two run sums per unit.
 inline size_t gemv_lds_bytes(int M, int K, bool pure) {
     if (pure) return 0;
-    return (size_t)M * (K / 64) * 17 * 16 + (size_t)M * (K / 32) * 4;
+    const size_t upr = (size_t)k_units(K);
+    return (size_t)M * upr * 17 * 16 + (size_t)M * upr * 2 * 4;
 }
 
 // static shared memory of the batched kernel (its reduction scratch) plus
@@ -152,18 +169,18 @@ inline int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* 
 // kernel's occupancy limit).
 // Lanes per row group for a row of `upr` 64-weight units: the whole wave
 // on one row when the row has at least 64 units, else the power of two that
-// covers the row.  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
+// covers the row, at least 4 (the group reduction sums whole quads).  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
 // measurements; the kernel takes any such width.
 inline int choose_lg(int upr) {
     static const int forced = env_int("Q4GEMV_LG", 0);
     if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
-    return upr >= kWave ? kWave : pow2ceil(upr);
+    return upr >= kWave ? kWave : (upr <= 4 ? 4 : pow2ceil(upr));
 }
 
 inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
-    p.upr = K / kUnitElems;
+    p.upr = (int)k_units(K);
     p.lg = choose_lg(p.upr);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
@@ -250,10 +267,10 @@ inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
 inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
     if constexpr (M == 1 && !mode_moe(MODE)) {
-        // one 64-weight unit per lane per row: K <= 64 * 64 (and then the
-        // activations need no staging loop beyond the first kXReg chunks)
-        const int upr = p.K / kUnitElems;
-        if (p.K <= kWave * kUnitElems && choose_lg(upr) >= upr && xr_enabled())
+        // one 64-weight unit per lane per row: at most 64 units (and then
+        // the activations need no staging loop beyond the first kXReg chunks)
+        const int upr = (int)k_units(p.K);
+        if (upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
     if ((long long)M * p.K > (long long)xreg_chunks(MODE) * 4 * gemv_threads(M, MODE))
@@ -336,7 +353,7 @@ inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
     // also for the SiLU-gated call and its 8 + 8-row tiles, so that both
     // accumulate every row alike)
     const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
-    p.ks = mfma_ks(ntiles, p.K / MStep<FMT>::kElems, cus);
+    p.ks = mfma_ks(ntiles, msteps(p.K), cus);
     const long long ntiles_run =
         (MODE == kModeSilu || MODE == kModeNormSilu) ? (long long)nexperts * ((p.N + 7) / 8)
                                                       : ntiles;
@@ -362,8 +379,13 @@ inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
                           (MODE == kModeMoe && moe_mfma_enabled() && M >= 2 &&
                            mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds);
     const int min_m = mode_moe(MODE) ? 2 : Q4_MFMA_MIN_M;
+    // (its staging covers whole 256-column steps; a call whose padded
+    // activations would not fit in LDS runs the VALU kernel)
+    const bool lds_fits =
+        mlayout(FMT, M, p.K, false).bytes <=
+        160 * 1024 - (mode_moe(MODE) ? kMfmaMoeStaticLds : kMfmaStaticLds);
     if constexpr (MODE != kModeMoeSilu) {
-        if (M >= min_m && moe_fits && mfma_enabled()) {
+        if (M >= min_m && moe_fits && lds_fits && mfma_enabled()) {
             const int nexp = mode_moe(MODE) ? npairs_max : 1;
             switch (M) {
                 case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
@@ -400,12 +422,13 @@ inline GemvParams base_params(const void* w0, const void* w1, float* y0, float* 
     p.x = x;
     p.N = (int)N;
     p.K = (int)K;
-    p.row_bytes = fmt == kFmtQ4K ? (K / 256) * kQ4KBytes : (K / 32) * 18;
+    p.upr = (int)k_units(K);
+    p.row_bytes = row_bytes_of(K, fmt);
     return p;
 }
 
 inline int check_moe(int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K) {
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4_0);
     if (st) return st;
     if (E < 1 || E >= (1 << 20) || top_k < 1 || top_k > E || M * top_k > kMaxPairs)
         return Q4_ERR_SHAPE;

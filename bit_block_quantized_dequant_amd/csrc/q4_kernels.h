@@ -90,7 +90,7 @@ struct GemvParams {
     int top_k;
     int E;
     long long row_bytes;
-    int upr;        // units per row = K / 64
+    int upr;        // units per row = ceil(K / 64) (the last one half used when K % 64 == 32)
     int lg;         // lanes per row group (power of two, <= 64)
     int upl;        // units per lane per row = ceil(upr / lg)
     int rgw;        // row groups per wave pass = 64 / lg
@@ -225,12 +225,29 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
     s = dpp_add(s, 0);
     s = dpp_add(s, 1);
     s = dpp_add(s, 2);
-    if (store && (c & 7) == 7) xsum[m * (p.K >> 5) + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
+    if (store && (c & 7) == 7) xsum[m * 2 * p.upr + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
     if constexpr (!DEFER) {
         const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
         v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
     }
-    if (store) xl[m * xrow_chunks(p.K) + xchunk(c >> 4, c & 15)] = v;
+    if (store) xl[m * xrow_chunks(p.upr) + xchunk(c >> 4, c & 15)] = v;
+}
+
+// A row whose K is not a multiple of 64 ends in a half unit: its upper 32
+// staged activations and their run sum are zero, so the weights past K (the
+// padding of a Q4_K row's last super-block, whose nibbles and 6-bit fields
+// are finite whatever they hold) add exactly nothing.
+template <int M>
+__device__ __forceinline__ void stage_pad(const GemvParams& p, float4* xl, float* xsum) {
+    if ((p.K & 63) == 0) return;
+    const int kq = xrow_chunks(p.upr);
+    for (int i = threadIdx.x; i < M * 9; i += blockDim.x) {
+        const int m = i / 9, j = i - 9 * m;
+        if (j < 8)
+            xl[m * kq + xchunk(p.upr - 1, 8 + j)] = make_float4(0.f, 0.f, 0.f, 0.f);
+        else
+            xsum[m * 2 * p.upr + 2 * p.upr - 1] = 0.f;
+    }
 }
 
 // TAIL: the call may have more than NX chunks per thread (M * K > NX * 4 *
@@ -304,6 +321,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
             if (lane == kWave - 1) red.ss[m][wave] = s;
         }
     }
+    stage_pad<M>(p, xl, xsum);
     if constexpr (DEFER) {
         (void)nw;
 #pragma unroll
@@ -440,8 +458,8 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // the wave index is wave-uniform; say so, so that all task bookkeeping
     // stays in scalar registers and the loops are scalar branches
     const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (tid >> 6));
-    const int kq = xrow_chunks(p.K);  // LDS float4 chunks per token row
-    const int k64 = p.K >> 6;
+    const int kq = xrow_chunks(p.upr);  // LDS float4 chunks per token row
+    const int k64 = p.upr;
     float4* xl = smem;
     float* xsum = (float*)(smem + M * kq);
 
@@ -876,10 +894,12 @@ static __global__ __launch_bounds__(kStreamBlock) void stream_read_kernel(
 // most 17 significant bits), so the single rounding of the fma gives the
 // correctly rounded value of d*sc*q - dmin*m.  Q4_0: d*(q-8) is exact.
 // ---------------------------------------------------------------------------
+// A Q4_K row whose K is not a multiple of 64 ends in a half unit: only its
+// low-nibble sub-block is written (out rows are K floats).
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
                                                       const uint8_t* __restrict__ w,
-                                                      long long nunits, int upr,
+                                                      long long nunits, int upr, int K,
                                                       long long row_bytes) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= nunits) return;
@@ -887,7 +907,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
     const int u = (int)(gid - n * upr);
     uint32_t r[kUnitWords];
     load_unit<FMT>(unit_ptr<FMT>(w + n * row_bytes, u), u & 3, r);
-    float4* o = (float4*)(out + n * (long long)upr * kUnitElems + (long long)u * kUnitElems);
+    const bool half = (u + 1) * kUnitElems > K;
+    float4* o = (float4*)(out + n * (long long)K + (long long)u * kUnitElems);
     if constexpr (FMT == kFmtQ4K) {
         uint32_t scp, mp;
         q4k_scale_pairs(r[1], r[2], r[3], q4k_sel(u & 3), scp, mp);
@@ -907,7 +928,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
             hi.z = __builtin_fmaf(ds1, (float)((q >> 20) & 15u), -dm1);
             hi.w = __builtin_fmaf(ds1, (float)(q >> 28), -dm1);
             o[i] = lo;
-            o[8 + i] = hi;
+            if (!half) o[8 + i] = hi;
         }
     } else {
         uint32_t qa[4] = {__builtin_amdgcn_alignbit(r[1], r[0], 16),
@@ -915,12 +936,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
                           __builtin_amdgcn_alignbit(r[3], r[2], 16),
                           __builtin_amdgcn_alignbit(r[4], r[3], 16)};
         const float da = h_lo(r[0]), db = h_hi(r[4]);
+        (void)half;  // (Q4_0 rows are whole units)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const float d = half ? db : da;
+        for (int hb = 0; hb < 2; ++hb) {
+            const float d = hb ? db : da;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t q = half ? r[5 + i] : qa[i];
+                const uint32_t q = hb ? r[5 + i] : qa[i];
                 float4 lo, hi;
                 lo.x = d * (float)((int)(q & 15u) - 8);
                 lo.y = d * (float)((int)((q >> 8) & 15u) - 8);
@@ -930,8 +952,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
                 hi.y = d * (float)((int)((q >> 12) & 15u) - 8);
                 hi.z = d * (float)((int)((q >> 20) & 15u) - 8);
                 hi.w = d * (float)((int)(q >> 28) - 8);
-                o[half * 8 + i] = lo;
-                o[half * 8 + 4 + i] = hi;
+                o[hb * 8 + i] = lo;
+                o[hb * 8 + 4 + i] = hi;
             }
         }
     }

@@ -71,12 +71,17 @@ __host__ __device__ constexpr int slot_byte(int t) {
 }
 
 // A step is 256 elements of a row: one Q4_K super-block or eight Q4_0
-// blocks, 144 bytes either way.
+// blocks, 144 bytes either way.  A row whose K is not a multiple of 256
+// ends in a partial step: its activations past K are staged as zeros (a
+// Q4_K row's padding is read and multiplied by them; a Q4_0 row's blocks
+// past its end are masked, see load() and compute()).
 template <int FMT>
 struct MStep {
     static constexpr int kElems = 256;
     static constexpr int kBytes = 144;
 };
+__host__ __device__ inline int msteps(int K) { return (K + 255) / 256; }
+__host__ __device__ inline int mpadk(int K) { return msteps(K) * 256; }
 
 // Q4_0 tile-steps (16 rows x 144 bytes) are loaded as 144 contiguous
 // 16-byte chunks, 3 per lane, and regrouped through a wave-private LDS copy.
@@ -97,7 +102,8 @@ struct MLayout {
     int bytes;
 };
 
-__host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
+__host__ __device__ inline MLayout mlayout(int fmt, int M, int K0, bool pure) {
+    const int K = mpadk(K0);  // staged columns: whole steps
     MLayout l;
     l.frag = 0;
     l.aux = pure ? 0 : (K / 8 + 1) * 2 * M * 16;
@@ -110,7 +116,8 @@ __host__ __device__ inline MLayout mlayout(int fmt, int M, int K, bool pure) {
     return l;
 }
 
-// 16-byte slot of the A fragment of piece p, row i: rows of K/8 + 1 slots.
+// 16-byte slot of the A fragment of piece p, row i: rows of K/8 + 1 slots
+// (K the staged column count, mpadk of the call's K).
 // The odd row length puts the rows a lane group reads 4 banks apart (all 64
 // banks for 16 rows), and the staging writes consecutive pieces of a row
 // to consecutive slots; both are free of bank conflicts.
@@ -160,6 +167,7 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ppt = p.K >> 3;  // pieces per token
     const int np = M * ppt;
+    const int kp = mpadk(p.K);  // staged columns
     float (&v)[kMPieces][8] = sx.v;
     const int (&um)[kMPieces] = sx.um;
     auto valid = [&](int k) { return tid + k * kMBlock < np; };
@@ -260,8 +268,8 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         part = dpp_add(part, 0);
         part = dpp_add(part, 1);
         if (valid(k)) {
-            *(h8*)(lds + ly.frag + fslot(p.K, 2 * m, pp) * 16) = hi;
-            *(h8*)(lds + ly.frag + fslot(p.K, 2 * m + 1, pp) * 16) = lo;
+            *(h8*)(lds + ly.frag + fslot(kp, 2 * m, pp) * 16) = hi;
+            *(h8*)(lds + ly.frag + fslot(kp, 2 * m + 1, pp) * 16) = lo;
             if ((pp & 3) == 0) {
                 const int g32 = pp >> 2;  // Q4_0 block / Q4_K sub-block index
                 if constexpr (FMT == kFmtQ4_0) {
@@ -279,6 +287,27 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
                     a[base] = h;
                     a[base + 2] = l;
                 }
+            }
+        }
+    }
+    // columns K .. kp of a partial last step: zero fragments and zero sums
+    const int padp = (kp - p.K) >> 3;  // padded pieces per token
+    for (int i = tid; i < M * padp; i += kMBlock) {
+        const int m = i / padp;
+        const int pp = ppt + (i - m * padp);
+        const h8 z = (h8)((_Float16)0.0f);
+        *(h8*)(lds + ly.frag + fslot(kp, 2 * m, pp) * 16) = z;
+        *(h8*)(lds + ly.frag + fslot(kp, 2 * m + 1, pp) * 16) = z;
+        if ((pp & 3) == 0) {
+            const int g32 = pp >> 2;
+            if constexpr (FMT == kFmtQ4_0) {
+                ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = 0.f;
+            } else {
+                const int sb = g32 >> 3, J = g32 & 7;
+                _Float16* a = (_Float16*)(lds + ly.aux);
+                const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
+                a[base] = (_Float16)0.0f;
+                a[base + 2] = (_Float16)0.0f;
             }
         }
     }
@@ -306,7 +335,15 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int S = p.K / St::kElems;
+    const int S = msteps(p.K);
+    const int kp = mpadk(p.K);
+    // Q4_0: blocks of the row (a partial last step has fewer than 8), and
+    // the largest byte offset of a 16-byte chunk inside the last step
+    const int nblk = p.K >> 5;
+    const uint32_t last_end = (uint32_t)(18 * (nblk - 8 * (S - 1)));  // bytes of the row in it
+    const uint32_t last_col = last_end - 16;
+    // Q4_K: elements of the row in its last super-block
+    const int klast = p.K - 256 * (S - 1);
     // waves per tile (1, 2, 4 or 8), at most S so that every wave has steps
     // (a wave without steps would skip the end-of-round reduction)
     int KS = p.ks;
@@ -424,11 +461,17 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             // chunks lane, lane + 64, lane + 128 (clamped) of the tile-step:
             // chunk ch is bytes 16 (ch % 9) .. of the step's 144 bytes of
             // tile row ch / 9
+            // (in a partial last step, a chunk that would cross the row's
+            // end is loaded from the row's last 16 bytes instead, and
+            // gather() moves its words back into place; chunks past the end
+            // load the same bytes, and their blocks are masked)
             const uint32_t so = (uint32_t)st * St::kBytes;
+            const bool part = st == S - 1;
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
                 const uint32_t ro = (uint32_t)min(q0row[k], p.N - 1 - row0) * rb;
-                const uint32_t o = idle ? 0u : ro + so + q0col[k];
+                const uint32_t col = part ? min(q0col[k], last_col) : q0col[k];
+                const uint32_t o = idle ? 0u : ro + so + col;
                 const u32x4 v = ldg16(base + o);
                 w.v[4 * k] = v.x; w.v[4 * k + 1] = v.y; w.v[4 * k + 2] = v.z; w.v[4 * k + 3] = v.w;
             }
@@ -437,7 +480,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     // A fragment of piece pp for this lane (rows i >= 2M repeat row 2M-1)
     const int i_lane = min(jrow, 2 * M - 1);
-    const char* arow = lds + ly.frag + fslot(p.K, i_lane, 0) * 16;
+    const char* arow = lds + ly.frag + fslot(kp, i_lane, 0) * 16;
     auto afrag = [&](int pp) { return *(const h8*)(arow + pp * 16); };
 
     // Q4_0: write the tile-step to this wave's LDS copy and read back, per
@@ -450,11 +493,20 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         uint32_t v[4][6];
     };
     char* wb = lds + ly.wbuf + wave * kQ40WaveBytes;
-    auto gather = [&](const WR& w, WQ& q) {
+    auto gather = [&](const WR& w, int st, WQ& q) {
+        const bool part = st == S - 1;
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-            *(u32x4*)(wb + q0chunk[k] * 16) =
-                u32x4{w.v[4 * k], w.v[4 * k + 1], w.v[4 * k + 2], w.v[4 * k + 3]};
+        for (int k = 0; k < 3; ++k) {
+            const uint32_t a0 = w.v[4 * k], a1 = w.v[4 * k + 1], a2 = w.v[4 * k + 2],
+                           a3 = w.v[4 * k + 3];
+            // a chunk loaded from the row's last 16 bytes (see load()):
+            // word i of the chunk is word i + sh of what was loaded
+            const int sh = part ? max(0, (int)(q0col[k] + 16u) - (int)last_end) >> 2 : 0;
+            const uint32_t b0 = sh == 0 ? a0 : sh == 1 ? a1 : sh == 2 ? a2 : a3;
+            const uint32_t b1 = sh == 0 ? a1 : sh == 1 ? a2 : a3;
+            const uint32_t b2 = sh == 0 ? a2 : a3;
+            *(u32x4*)(wb + q0chunk[k] * 16) = u32x4{b0, b1, b2, a3};
+        }
         __asm__ volatile("" ::: "memory");
         const uint32_t* wd = (const uint32_t*)wb + jrow * 36;
         const int hh = c & 1;
@@ -542,7 +594,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             y.y += t[2] + t[3];
         } else {
             WQ q;
-            gather(w, q);
+            gather(w, st, q);
             const uint32_t hsel = (uint32_t)(c & 1);
             const uint32_t mask = c >= 2 ? 0x00F000F0u : 0x000F000Fu;
             constexpr int MP = sums_stride(M);
@@ -553,11 +605,14 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 const uint32_t b0 = q.v[k][3], b1 = q.v[k][4], z = q.v[k][5];
                 const uint32_t qa0 = __builtin_amdgcn_alignbit(a1, a0, 16);
                 const uint32_t qa1 = __builtin_amdgcn_alignbit(a2, a1, 16);
-                const float dA = h_lo(hsel ? z : a0);
-                const float dB = h_hi(hsel ? a2 : z);
+                const int blk0 = st * 8 + 2 * k;  // block index of block A in the row
+                // blocks past the row's end (partial last step) hold other
+                // bytes: their scales are masked (their activations are 0)
+                const float dA = blk0 < nblk ? h_lo(hsel ? z : a0) : 0.f;
+                const float dB = blk0 + 1 < nblk ? h_hi(hsel ? a2 : z) : 0.f;
                 const u32x4m ba = {qa0 & mask, (qa0 >> 8) & mask, qa1 & mask, (qa1 >> 8) & mask};
                 const u32x4m bb = {b0 & mask, (b0 >> 8) & mask, b1 & mask, (b1 >> 8) & mask};
-                const int blk = st * 8 + 2 * k;  // block index of block A in the row
+                const int blk = blk0;
                 const f4 DA = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     afrag(blk * 4 + c), __builtin_bit_cast(h8, ba), (f4)(0.f), 0, 0, 0);
                 const f4 DB = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -574,21 +629,31 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     };
 
     // word checksum of the step's bytes, each word counted by one lane
-    auto checksum = [&](const WR& w) {
+    // (the words a call reads: in a Q4_K row's last super-block, the nibble
+    // chunks that hold no element < K are left out; in a Q4_0 row, the
+    // masked blocks past its end)
+    auto checksum = [&](const WR& w, int st) {
         uint32_t s = 0;
         if constexpr (FMT == kFmtQ4K) {
+            const bool last = st == S - 1;
 #pragma unroll
-            for (int i = 4; i < 12; ++i) s += w.v[i];
+            for (int hh = 0; hh < 2; ++hh) {
+                const int g = 2 * hh + (c >> 1);  // nibble chunk of these words
+                uint32_t t = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t += w.v[4 + 4 * hh + i];
+                s += (!last || 64 * g < klast) ? t : 0u;
+            }
             if (c == 0) s += w.v[0] + w.v[1] + w.v[2] + w.v[3];
         } else {
             // lane group 0: words 0,1 (a), 5,6 (b), 4 (z); group 1: 2,3 (a), 7,8 (b)
             WQ q;
-            gather(w, q);
+            gather(w, st, q);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 uint32_t t = q.v[k][0] + q.v[k][1] + q.v[k][3] + q.v[k][4];
                 if (c == 0) t += q.v[k][5];
-                s += c < 2 ? t : 0u;
+                s += (c < 2 && st * 8 + 2 * k < nblk) ? t : 0u;
             }
         }
         return s;
@@ -703,7 +768,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             const bool act = base + j < n;  // wave-uniform
             if (act) {
                 if constexpr (PURE) {
-                    cks += checksum(w[j]);
+                    cks += checksum(w[j], cs);
                 } else {
                     compute(w[j], cs, y);
                 }

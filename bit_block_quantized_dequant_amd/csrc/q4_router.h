@@ -54,7 +54,7 @@ static __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     constexpr int kWaves = kRouterBlock / kWave;
-    const int kq = xrow_chunks(K);
+    const int kq = xrow_chunks(K / kUnitElems);
     const int k64 = K >> 6;
     float4* xl = smem;
     float* xsum = (float*)(smem + kq);
@@ -63,6 +63,7 @@ static __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __
     GemvParams p = {};
     p.x = x + (long long)m * K;
     p.K = K;
+    p.upr = K / kUnitElems;
     XStage<> st;
     int xe[1];  // the row's scale exponent: the staged row is x * 2^xe
     stage_x_issue<kModeDense>(p, 1, st);
@@ -71,7 +72,7 @@ static __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __
 
     // ---- logits ----
     const int upr = K / kUnitElems;
-    int lgw = 1;
+    int lgw = 4;  // (group_total sums at least a quad)
     while (lgw < upr && lgw < kWave) lgw <<= 1;
     const int rpp = kWave / lgw;           // rows per wave pass
     const int gi = lane / lgw, li = lane - gi * lgw;

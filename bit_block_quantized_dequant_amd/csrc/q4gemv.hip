@@ -24,7 +24,7 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
                     void* stream) {
     if (!ids || !weights || !w_router || !x) return Q4_ERR_NULL;
     if (M < 1 || M > 8) return Q4_ERR_BATCH;
-    if (K <= 0 || K % 256 != 0 || K > kRouterMaxK) return Q4_ERR_SHAPE;
+    if (!k_ok(K, kFmtQ4_0) || K > kRouterMaxK) return Q4_ERR_SHAPE;
     if (E < 1 || E > kRouterMaxE || top_k < 1 || top_k > E || top_k > kRouterMaxTopK)
         return Q4_ERR_SHAPE;
     if (normalize != 0 && normalize != 1) return Q4_ERR_ARG;
@@ -44,29 +44,29 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
 
 int dequant_q4k(float* out, const void* w, int64_t N, int64_t K, void* stream) {
     if (!out || !w) return Q4_ERR_NULL;
-    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (!k_ok(K, kFmtQ4K) || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
-    const long long upr = K / kUnitElems;
+    const long long upr = k_units(K);
     const long long nunits = (long long)N * upr;
     const long long blocks = (nunits + 255) / 256;
     if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
     hipLaunchKernelGGL(dequant_kernel<kFmtQ4K>, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr,
-                       (long long)(K / 256) * kQ4KBytes);
+                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr, (int)K,
+                       row_bytes_of(K, kFmtQ4K));
     return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
 }
 
 int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream) {
     if (!out || !w) return Q4_ERR_NULL;
-    if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (!k_ok(K, kFmtQ4_0) || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
-    const long long upr = K / kUnitElems;
+    const long long upr = k_units(K);
     const long long nunits = (long long)N * upr;
     const long long blocks = (nunits + 255) / 256;
     if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
     hipLaunchKernelGGL(dequant_kernel<kFmtQ4_0>, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr,
-                       (long long)(K / 32) * 18);
+                       (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr, (int)K,
+                       row_bytes_of(K, kFmtQ4_0));
     return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
 }
 

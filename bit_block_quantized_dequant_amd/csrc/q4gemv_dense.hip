@@ -7,7 +7,7 @@ extern "C" {
 int q4_0_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
               void* stream) {
     if (!y || !w || !x) return Q4_ERR_NULL;
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4_0);
     if (st) return st;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
     GemvParams p = base_params(w, w, y, y, x, N, K, kFmtQ4_0);
@@ -17,7 +17,7 @@ int q4_0_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int
 int q4k_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
              void* stream) {
     if (!y || !w || !x) return Q4_ERR_NULL;
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4K);
     if (st) return st;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
     GemvParams p = base_params(w, w, y, y, x, N, K, kFmtQ4K);
@@ -27,7 +27,7 @@ int q4k_gemv(float* y, const void* w, const float* x, int64_t M, int64_t N, int6
 int fused_rmsnorm_q4k_gemv(float* y, const void* w, const float* x, const float* gamma,
                            float eps, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!y || !w || !x || !gamma) return Q4_ERR_NULL;
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4K);
     if (st) return st;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 4))
         return Q4_ERR_ALIGN;

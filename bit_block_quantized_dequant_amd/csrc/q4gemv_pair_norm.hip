@@ -8,7 +8,7 @@ int fused_rmsnorm_gate_up_q4k_gemv(float* gate, float* up, const void* w_gate,
                                    const void* w_up, const float* x, const float* gamma,
                                    float eps, int64_t M, int64_t N, int64_t K, void* stream) {
     if (!gate || !up || !w_gate || !w_up || !x || !gamma) return Q4_ERR_NULL;
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4K);
     if (st) return st;
     if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gamma, 16) ||
         !aligned(gate, 4) || !aligned(up, 4))
@@ -24,7 +24,7 @@ int fused_rmsnorm_gate_up_silu_q4k_gemv(float* h, const void* w_gate, const void
                                         const float* x, const float* gamma, float eps,
                                         int64_t M, int64_t N, int64_t K, void* stream) {
     if (!h || !w_gate || !w_up || !x || !gamma) return Q4_ERR_NULL;
-    int st = check_dims(M, N, K);
+    int st = check_dims(M, N, K, kFmtQ4K);
     if (st) return st;
     if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(gamma, 16) ||
         !aligned(h, 4))

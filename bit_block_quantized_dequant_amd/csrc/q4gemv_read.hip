@@ -29,13 +29,13 @@ int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* 
     }
     if ((kernel_id == Q4_READ_GATE_UP || kernel_id == Q4_READ_MOE) && !w1) return Q4_ERR_NULL;
     if (kernel_id == Q4_READ_MOE && !ids) return Q4_ERR_NULL;
-    int st = kernel_id == Q4_READ_MOE ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K);
+    const int fmt = (kernel_id == Q4_READ_Q4_0_GEMV || kernel_id == Q4_READ_MOE) ? kFmtQ4_0
+                                                                                 : kFmtQ4K;
+    int st = kernel_id == Q4_READ_MOE ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K, fmt);
     if (st) return st;
     if (!aligned(w0, 16) || (w1 && !aligned(w1, 16)) || !aligned(checksum, 4) ||
         (ids && !aligned(ids, 4)))
         return Q4_ERR_ALIGN;
-    const int fmt = (kernel_id == Q4_READ_Q4_0_GEMV || kernel_id == Q4_READ_MOE) ? kFmtQ4_0
-                                                                                 : kFmtQ4K;
     GemvParams p = base_params(w0, w1 ? w1 : w0, nullptr, nullptr, nullptr, N, K, fmt);
     p.cks = checksum;
     switch (kernel_id) {

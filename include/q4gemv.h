@@ -12,7 +12,8 @@
  *     (inferencelayer 0.2.13, src/bin/kernel_lab.rs, GEMV_F16S WGSL:
  *      q4_lo / q4_hi and the per-block scale.)
  *
- *   Q4_K, 144 bytes per super-block of 256 weights, row_bytes = K/256 * 144:
+ *   Q4_K, 144 bytes per super-block of 256 weights,
+ *   row_bytes = ceil(K/256) * 144:
  *     +0  f16 d, +2 f16 dmin, +4 twelve bytes S packing eight 6-bit scales
  *     and eight 6-bit mins, +16 128 bytes of nibbles.  Sub-block j (32
  *     weights) has scale sc_j and min m_j: for j < 4, sc_j = S[j] & 63 and
@@ -20,9 +21,13 @@
  *     and m_j = (S[j+4] >> 4) | (S[j] >> 6) << 4.  Element t of the
  *     super-block is in byte 32*(t/64) + t%32 of the nibbles, low nibble when
  *     t%64 < 32, high nibble otherwise; weight = d*sc_j*q - dmin*m_j with
- *     j = t/32.
+ *     j = t/32.  When K is not a multiple of 256 (it must be one of 32),
+ *     a row's last super-block holds only its first K % 256 weights; the
+ *     rest of it (nibbles and the 6-bit fields of the unused sub-blocks) is
+ *     padding that no result depends on.
  *     (trueno-gpu 0.4.11, src/kernels/quantize/fused.rs,
- *      FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3.)
+ *      FusedRmsNormQ4KGemvKernel::build_ptx, PHASE 3; that page sizes a row
+ *      by ceiling division, (K + 255) / 256 super-blocks.)
  *
  * Activations x / X are fp32 [M, K] row-major; outputs are fp32 [M, N]
  * row-major (for the expert call, [M, top_k, N]).  GEMV means
@@ -66,8 +71,10 @@
  *     validation error nothing is launched and a status > 0 is returned.
  *     Q4_ERR_HIP means the launch itself failed; kernel faults surface, as
  *     usual for HIP, on a later synchronization.
- *   - Limits: 1 <= M <= 8 (Q4_ERR_BATCH); K > 0, K % 256 == 0,
- *     M * K <= Q4_MAX_MK, 1 <= N < 2^31 (Q4_ERR_SHAPE).  Weight and x
+ *   - Limits: 1 <= M <= 8 (Q4_ERR_BATCH); K > 0 with K % 32 == 0 for Q4_K
+ *     and K % 64 == 0 for Q4_0 (an even block count keeps every Q4_0 row
+ *     4-byte aligned), M * ceil(K/64) * 64 <= Q4_MAX_MK, 1 <= N < 2^31
+ *     (Q4_ERR_SHAPE).  Weight and x
  *     pointers 16-byte aligned, all other pointers 4-byte aligned
  *     (Q4_ERR_ALIGN).  Values out of range are refused, never clamped.
  *   - The library is re-entrant; calls on different streams may overlap.
@@ -105,8 +112,9 @@ enum {
     Q4_ERR_HIP = 6     /* the HIP runtime refused the launch */
 };
 
-/* Largest M * K accepted: the activations of one call are staged whole in
- * the 160 KB LDS of a compute unit. */
+/* Largest M * K accepted (K rounded up to a multiple of 64): the
+ * activations of one call are staged whole in the 160 KB LDS of a compute
+ * unit. */
 #define Q4_MAX_MK 32768
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -242,7 +250,7 @@ int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float
  * The ids are in the layout moe_q4_gemv and moe_q4_gemv_silu take.  The
  * logits are fp32 sums within 1e-4 * sum_k |w x| of the exact ones; where
  * two experts' logits are closer than that, either order is correct.
- * Limits: M in [1, 8] (Q4_ERR_BATCH); K % 256 == 0 and K <= 32768;
+ * Limits: M in [1, 8] (Q4_ERR_BATCH); K % 64 == 0 and K <= 32768;
  * 1 <= E <= 1024; 1 <= top_k <= min(E, 64) (Q4_ERR_SHAPE); normalize 0 or
  * 1 (Q4_ERR_ARG).  Alignment: Wr and x 16 bytes, ids and weights 4.
  */
@@ -280,7 +288,10 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream);
  *   Q4_READ_MOE         w0, w1: Q4_0 experts as moe_q4_gemv [2, M, top_k, N]
  *   Q4_READ_STREAM      w0: N * K * 9/16 bytes              [ceil(bytes / 4096)]
  *
- * Q4_READ_STREAM is the reference stream of the same byte count as a GEMV
+ * For a Q4_K row whose K is not a multiple of 256, the checksum covers what
+ * the call reads: the super-block headers and the 32-byte nibble chunks
+ * that hold an element < K (a chunk of padding only is not read).
+ * Q4_READ_STREAM (K % 256 == 0) is the reference stream of the same byte count as a GEMV
  * of N rows and K columns (both formats use 9/16 byte per weight), read the
  * fastest way measured on this part: contiguous 1 KiB wave instructions
  * with the non-temporal hint, 4 KiB blocks per wave step with the next

@@ -10,6 +10,17 @@ Q40_PAIR = 36
 U32 = 0xFFFFFFFF
 
 
+def row_bytes(fmt, K):
+    """ceil(K/256) super-blocks (Q4_K rows may end inside the last one),
+    K/32 blocks (Q4_0)."""
+    return (K + 255) // 256 * 144 if fmt == "q4k" else (K // 32) * 18
+
+
+def mpadk(K):
+    """Columns the batched kernel stages: whole 256-column steps."""
+    return (K + 255) // 256 * 256
+
+
 def pow2ceil(v):
     p = 1
     while p < v:
@@ -25,9 +36,9 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
         wpb = 4 if (M == 1 or moe) else 8
     if bpc is None:
         bpc = 3 if moe else 2
-    upr = K // 64
+    upr = (K + 63) // 64
     if lg is None:
-        lg = 64 if upr >= 64 else pow2ceil(upr)
+        lg = 64 if upr >= 64 else max(4, pow2ceil(upr))
     upl = (upr + lg - 1) // lg
     rgw = 64 // lg
     nrg = (rows + RR - 1) // RR
@@ -56,7 +67,7 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
     moe = moe_experts is not None
     pl = plan(M, K, N, RR, moe, kw.get("npairs_max", 1), **{k: v for k, v in kw.items()
                                                              if k in ("cus", "bpc", "wpb", "lg")})
-    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    rb = row_bytes(fmt, K)
     upr, lg, upl, rgw = pl["upr"], pl["lg"], pl["upl"], pl["rgw"]
     u_last = upr - 1
     if moe:
@@ -121,11 +132,12 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
 
 def check(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
     rows_total = (E if moe_experts is not None else 1) * N
-    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    rb = row_bytes(fmt, K)
     limit = rows_total * rb
     n = 0
     for mt, off, nb in loads(fmt, M, N, K, RR, nmat, moe_experts, E, **kw):
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
+        assert off % 4 == 0, ("word loads need 4-byte alignment", fmt, K, off)
         n += 1
     return n
 
@@ -143,6 +155,7 @@ def sums_stride(M):
 
 def mlayout(fmt, M, K, pure=False):
     """Byte offsets of the kernel's LDS regions (mlayout() in q4_mfma.h)."""
+    K = mpadk(K)
     aux = 0 if pure else (K // 8 + 1) * 2 * M * 16
     aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k"
                                 else (K // 32) * sums_stride(M) * 4)
@@ -167,7 +180,7 @@ def mfma_plan(fmt, M, K, N, nmat, cus=256, nexperts=1, pair=False):
     lds = mlayout(fmt, M, K)["bytes"]
     wgc = max(1, min(2, LDS_CAP // lds))
     ntiles = nmat * nexperts * ((N + 15) // 16)
-    steps = K // 256
+    steps = (K + 255) // 256
     KS = mfma_ks(ntiles, steps, cus)
     TG = 8 // KS
     if pair:
@@ -193,7 +206,7 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, pair=False):
     expert call, `experts` is the dedupe result and umax the host's bound on
     its length (which sizes the grid and the K split)."""
     pl = mfma_plan(fmt, M, K, N, nmat, cus, umax if experts is not None else 1, pair)
-    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    rb = row_bytes(fmt, K)
     SB, PD = 144, (2 if fmt == "q4k" else 3)
     S, KS = pl["steps"], pl["KS"]
     while KS > S:  # the kernel's own clamp
@@ -232,30 +245,38 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, pair=False):
                         yield mt, base + off + co + 16, 16
                         yield mt, base + off + co + 80, 16
                     else:
+                        # a partial last step clamps its chunk columns to
+                        # the row's last 16 bytes
+                        last_col = 18 * (K // 32 - 8 * (S - 1)) - 16
                         for k in range(3):
                             ch = min(lane + 64 * k, 143)
                             ro = (min(ch // 9, N - 1 - row0) * rb) & U32
-                            o = 0 if idle else (ro + st * SB + (ch % 9) * 16) & U32
+                            col = (ch % 9) * 16
+                            if st == S - 1:
+                                col = min(col, last_col)
+                            o = 0 if idle else (ro + st * SB + col) & U32
                             yield mt, base + o, 16
 
 
 def mfma_check(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, E=1, pair=False):
     pl = mfma_plan(fmt, M, K, N, nmat, cus, pair=pair)
     assert pl["lds"] <= LDS_CAP, (fmt, M, K, pl["lds"])
-    rb = (K // 256) * 144 if fmt == "q4k" else (K // 32) * 18
+    rb = row_bytes(fmt, K)
     limit = (E if experts is not None else 1) * N * rb
     n = 0
     for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus, experts, umax, pair):
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
+        assert off % 4 == 0, ("word loads need 4-byte alignment", fmt, K, off)
         n += 1
     return n
 
 
-def mfma_lds_check(fmt, M, K):
+def mfma_lds_check(fmt, M, K0):
     """Every LDS byte the kernel writes while staging or reads while
     computing lies inside its region, and every fragment and sum a compute
     step reads was written by the staging."""
-    ly = mlayout(fmt, M, K)
+    ly = mlayout(fmt, M, K0)
+    K = mpadk(K0)  # staged columns: real pieces, then zero pieces up to K
     ppt = K // 8
     frag_w, aux_w = set(), set()
     for m in range(M):
@@ -326,7 +347,7 @@ def router_loads(E, K, waves=8, rows=4):
     """Yield (byte offset, nbytes) of every weight load of one token's
     workgroup (router_kernel's logits loop)."""
     upr = K // 64
-    lgw = 1
+    lgw = 4
     while lgw < upr and lgw < 64:
         lgw <<= 1
     rpp = 64 // lgw

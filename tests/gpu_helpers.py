@@ -114,7 +114,7 @@ def split_sum(orc, fmt, w, x, N, K):
         blk = w0.reshape(N, K // 32, 18)
         blk[:, :, 2:] = 0
     else:
-        sb = w0.reshape(N, K // 256, 144)
+        sb = w0.reshape(N, (K + 255) // 256, 144)
         sb[:, :, 16:] = 0
     b = -(orc.dequant_q4_0 if fmt == "q4_0" else orc.dequant_q4k)(w0, N, K).astype(np.float64)
     a = deq + b

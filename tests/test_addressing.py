@@ -142,7 +142,58 @@ def test_batched_silu_pair_loads_in_bounds(M, N, K):
     assert A.mfma_check("q4k", M, N, K, 2, cus=256, pair=True) > 0
 
 
-@pytest.mark.parametrize("E,K", [(1, 256), (3, 256), (8, 512), (64, 2048), (65, 1024),
+@pytest.mark.parametrize("E,K", [(1, 256), (3, 256), (8, 512), (64, 2048), (65, 1024), (7, 64), (9, 128),
                                  (100, 4096), (1024, 512), (7, 32768)])
 def test_router_loads_in_bounds(E, K):
     assert A.router_check(E, K) > 0
+
+
+# ---------------------------------------------------------------------------
+# K tails: Q4_K rows ending inside their last super-block (K % 32 == 0),
+# Q4_0 rows of an even block count (K % 64 == 0)
+# ---------------------------------------------------------------------------
+Q4K_TAIL_K = [32, 96, 288, 1408, 2080, 3616]
+Q4_0_TAIL_K = [64, 192, 1408]
+
+
+@pytest.mark.parametrize("K", Q4K_TAIL_K + [14336])
+@pytest.mark.parametrize("M", [1, 2])
+def test_tail_loads_in_bounds_q4k(M, K):
+    assert A.check("q4k", M, 301, K, RR=2, nmat=1, cus=8) > 0
+    assert A.check("q4k", M, 203, K, RR=1, nmat=2, cus=8) > 0
+
+
+@pytest.mark.parametrize("K", Q4_0_TAIL_K + [14336])
+@pytest.mark.parametrize("M", [1, 2])
+def test_tail_loads_in_bounds_q4_0(M, K):
+    assert A.check("q4_0", M, 299, K, RR=2, nmat=1, cus=8) > 0
+
+
+@pytest.mark.parametrize("K", Q4K_TAIL_K)
+@pytest.mark.parametrize("M", [3, 8])
+def test_tail_batched_loads_in_bounds_q4k(M, K):
+    if M * ((K + 63) // 64) * 64 > 32768:
+        pytest.skip("over the staging limit")
+    assert A.mfma_check("q4k", M, 301, K, 1, cus=8) > 0
+    assert A.mfma_check("q4k", M, 203, K, 2, cus=8, pair=True) > 0
+    assert A.mfma_lds_check("q4k", M, K)
+
+
+@pytest.mark.parametrize("K", Q4_0_TAIL_K)
+@pytest.mark.parametrize("M", [3, 8])
+def test_tail_batched_loads_in_bounds_q4_0(M, K):
+    assert A.mfma_check("q4_0", M, 299, K, 1, cus=8) > 0
+    assert A.mfma_lds_check("q4_0", M, K)
+
+
+def test_tail_expert_and_router_loads_in_bounds():
+    assert A.check("q4_0", 4, 160, 1408, RR=1, nmat=2, moe_experts=[3, 0, 15, 7], E=16,
+                   npairs_max=16, cus=8) > 0
+    assert A.router_check(64, 1408) > 0
+
+
+def test_odd_q4_0_block_count_would_misalign():
+    """Why Q4_0 rows need K % 64 == 0: with an odd block count, every other
+    row starts 2 bytes off a word boundary."""
+    with pytest.raises(AssertionError, match="alignment"):
+        A.check("q4_0", 1, 4, 96, RR=2, nmat=1, cus=8)

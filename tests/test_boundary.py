@@ -69,7 +69,7 @@ def L():
     ((A, A, A, 1, 0, 256, None), SHAPE),
     ((A, A, A, 1, 2 ** 31, 256, None), SHAPE),
     ((A, A, A, 1, 16, 0, None), SHAPE),
-    ((A, A, A, 1, 16, 288, None), SHAPE),
+    ((A, A, A, 1, 16, 272, None), SHAPE),  # not a multiple of 32
     ((A, A, A, 1, 16, -256, None), SHAPE),
     ((A, A, A, 2, 16, 32768, None), SHAPE),  # M*K over the LDS limit
     ((A, MIS, A, 1, 16, 256, None), ALIGN),
@@ -80,6 +80,25 @@ def L():
 @pytest.mark.parametrize("fn", ["q4_0_gemv", "q4k_gemv"])
 def test_dense_validation(q4lib, fn, args, want):
     assert getattr(L(), fn)(*args) == want
+
+
+def test_k_granularity(q4lib):
+    """Q4_K rows may end at any multiple of 32 (inside their last
+    super-block); Q4_0 rows need an even block count (K % 64 == 0).  A
+    shape that passes is shown by the next check refusing a misaligned
+    pointer instead."""
+    for K in (32, 96, 288, 1408, 2080):
+        assert L().q4k_gemv(A, MIS, A, 1, 16, K, None) == ALIGN, K
+        assert L().dequant_q4k(A, MIS, 16, K, None) == ALIGN, K
+    for K in (32, 96, 288, 2080):
+        assert L().q4_0_gemv(A, MIS, A, 1, 16, K, None) == SHAPE, K
+        assert L().dequant_q4_0(A, MIS, 16, K, None) == SHAPE, K
+    for K in (64, 1408, 14336):
+        assert L().q4_0_gemv(A, MIS, A, 1, 16, K, None) == ALIGN, K
+    # the padded staging counts whole 64-column units: M * ceil(K/64) * 64
+    # (3 * 10912 = 32736 fits, but 3 * 10944 does not)
+    assert L().q4k_gemv(A, MIS, A, 3, 16, 10912, None) == SHAPE
+    assert L().q4k_gemv(A, MIS, A, 3, 16, 10880, None) == ALIGN
 
 
 def test_rmsnorm_validation(q4lib):
