@@ -64,8 +64,9 @@ def parse_args():
     ap.add_argument("--all", metavar="REPORT", default=None,
                     help="also time every named workload; write REPORT.json / REPORT.md")
     ap.add_argument("--chain", action="store_true",
-                    help="only time dispatch chains: the smallest call back to back, and the "
-                         "router + SiLU expert call sequence, eager and as HIP graph replays")
+                    help="only time dispatch chains (the smallest call back to back, a dense "
+                         "FFN decode step, an expert decode step; eager and as HIP graph "
+                         "replays) and the submit+wait / submit+spin turnaround")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 20 times (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -204,7 +205,8 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
     from bit_block_quantized_dequant_amd import synth
 
     L = q4.lib()
-    d = synth.workload_inputs(index, M=M, distinct=distinct)
+    d = synth.down_inputs(M, distinct) if index == 6 else \
+        synth.workload_inputs(index, M=M, distinct=distinct)
     N, K = d["N"], d["K"]
     keep = []
 
@@ -213,7 +215,7 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
         keep.append(t)
         return t
 
-    x = T(d["x"])
+    x = T(d["h"] if index == 6 else d["x"])
     notes = {}
     rot = None
     if index in (1, 2):
@@ -318,16 +320,39 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
                                  top_k, E, N, K, stream), "q4_pure_read")
         keep += [rot, gate, up, cks]
         outs, couts = ([gate] if silu else [gate, up]), [cks]
+    elif index == 6:
+        # the expert down-projection (x holds the pair rows h[M, top_k, K])
+        E, top_k = d["E"], d["top_k"]
+        rot = Rotation(torch, dev, d["w_down"])
+        ids = T(d["ids"])
+        y = torch.empty(M, top_k, N, device=dev)
+        cks = torch.empty(M * top_k * N, dtype=torch.int32, device=dev)
+        uniq = len(set(int(e) for e in d["ids"].reshape(-1)))
+        per_expert = N * synth.q4_0_row_bytes(K)
+        wbytes = uniq * per_expert
+        notes = dict(unique_experts=uniq, pairs=M * top_k,
+                     pair_counted_bytes=M * top_k * per_expert)
+
+        def launch(i, stream):
+            check(L.moe_q4_gemv_down(y.data_ptr(), rot.ptr(i), x.data_ptr(), ids.data_ptr(), M,
+                                     top_k, E, N, K, stream), "moe_q4_gemv_down")
+
+        def ceil_launch(i, stream):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_MOE_DOWN, rot.ptr(i), None,
+                                 ids.data_ptr(), M, top_k, E, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+        outs, couts = [y], [cks]
     notes["copies"] = rot.ncopies
-    # reference stream: the same byte count as contiguous rows of K * 9/16 bytes
-    srb = synth.q4k_row_bytes(K)
+    # reference stream: the same byte count as contiguous rows of 256 * 9/16
+    # bytes (rounded down to whole rows)
+    srb = synth.q4k_row_bytes(256)
     srows = wbytes // srb
     scks = torch.empty((srows * srb + 4095) // 4096, dtype=torch.int32, device=dev)
     keep.append(scks)
 
     def stream_launch(i, stream):
         check(L.q4_pure_read(scks.data_ptr(), q4.Q4_READ_STREAM, rot.ptr(i), None, None, 1, 0, 0,
-                             srows, K, stream), "q4_pure_read")
+                             srows, 256, stream), "q4_pure_read")
     return wbytes, launch, ceil_launch, notes, keep, outs, couts, (stream_launch, [scks])
 
 
@@ -381,16 +406,27 @@ def measure_router(torch, dev, warmup, steps):
     return dict(M=M, E=E, K=K, top_k=top_k, weight_bytes=int(wr.nbytes), kernel=st)
 
 
-def measure_chain(torch, dev, n=300):
+def measure_chain(torch, dev, n=300, reps=50):
     """Dispatch cost on one stream (inferencelayer kernel_lab: the dependent-
-    dispatch chain probe, N tiny dispatches in one submission).  Two chains:
-    n back-to-back calls of the smallest workload (Q4_0 K=512 N=256, M=1),
-    each reading what the stream order makes it wait for; and n decode steps
-    of the expert path at the expert call's shape (router over 64 Q4_0 expert
-    rows, then moe_q4_gemv_silu on the ids it wrote, which never leave the
-    device).  Each chain runs eagerly (one host launch per call, through the
-    binding's ctypes calls) and as one captured HIP graph; returns the wall
-    time per call or step, after a device synchronization on both sides."""
+    dispatch chain probe, N tiny dispatches in one submission, and the
+    submit + wait against submit + spin turnaround probe).
+
+    Chains, each run n times back to back eagerly (one host launch per call,
+    through the binding's ctypes calls) and as one captured HIP graph, wall
+    time per call or step between two device synchronizations:
+      small_call       the smallest workload (Q4_0 K=512 N=256, M=1), each
+                       call ordered after the previous one by the stream;
+      dense_ffn_step   one decode step of a dense FFN: RMSNorm + gate/up +
+                       SiLU (Q4_K, K=4096, N=14336 per matrix) writing h, then
+                       the down-projection of h (Q4_K, 4096 rows x 14336);
+      moe_step         one decode step of the expert path at the expert
+                       call's shape: the router over 64 Q4_0 expert rows, the
+                       SiLU-gated expert gate/up on the ids it wrote (which
+                       never leave the device), then the expert down-
+                       projection of those rows (2048 rows x 1408 per expert).
+    Turnaround (reps single launches of the smallest call, each alone on an
+    idle device): submit then hipDeviceSynchronize (wait), against submit
+    then polling an event recorded after it (spin)."""
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
@@ -400,41 +436,68 @@ def measure_chain(torch, dev, n=300):
     d1 = synth.workload_inputs(1)
     w1, x1 = T(d1["w"]), T(d1["x"])
     y1 = torch.empty(d1["M"], d1["N"], device=dev)
+    # dense FFN: gate/up of workload 4, a down matrix of its own seed
+    d4 = synth.workload_inputs(4, M=1)
+    K4, N4 = d4["K"], d4["N"]
+    wg4, wu4, x4 = T(d4["w_gate"]), T(d4["w_up"]), T(d4["x"])
+    rng = synth.make_rng(8600)
+    gam4 = T(synth.gamma(rng, K4))
+    DN, DK = synth.DENSE_DOWN["N"], synth.DENSE_DOWN["K"]
+    wd4 = T(synth.q4k_matrix(rng, DN, DK))
+    h4 = torch.empty(1, N4, device=dev)
+    y4 = torch.empty(1, DN, device=dev)
+    assert DK == N4
+    # expert path
     d5 = synth.workload_inputs(5)
     M, E, N, K, top_k = d5["M"], d5["E"], d5["N"], d5["K"], d5["top_k"]
+    dd = synth.down_inputs(M)
     wr = T(synth.q4_0_matrix(synth.make_rng(8100), E, K))
     wg, wu, x5 = T(d5["w_gate"]), T(d5["w_up"]), T(d5["x"])
+    wd = T(dd["w_down"])
     ids = torch.empty(M, top_k, dtype=torch.int32, device=dev)
     wts = torch.empty(M, top_k, device=dev)
     h = torch.empty(M, top_k, N, device=dev)
+    y5 = torch.empty(M, top_k, dd["N"], device=dev)
+    assert dd["K"] == N
 
     def small(stream):
         check(L.q4_0_gemv(y1.data_ptr(), w1.data_ptr(), x1.data_ptr(), 1, d1["N"], d1["K"],
                           stream), "q4_0_gemv")
 
-    def step(stream):
+    def ffn(stream):
+        check(L.fused_rmsnorm_gate_up_silu_q4k_gemv(h4.data_ptr(), wg4.data_ptr(), wu4.data_ptr(),
+                                                    x4.data_ptr(), gam4.data_ptr(), 1e-5, 1, N4,
+                                                    K4, stream),
+              "fused_rmsnorm_gate_up_silu_q4k_gemv")
+        check(L.q4k_gemv(y4.data_ptr(), wd4.data_ptr(), h4.data_ptr(), 1, DN, DK, stream),
+              "q4k_gemv")
+
+    def moe(stream):
         check(L.moe_router_q4_0(ids.data_ptr(), wts.data_ptr(), wr.data_ptr(), x5.data_ptr(), M,
                                 E, K, top_k, 1, stream), "moe_router_q4_0")
         check(L.moe_q4_gemv_silu(h.data_ptr(), wg.data_ptr(), wu.data_ptr(), x5.data_ptr(),
                                  ids.data_ptr(), M, top_k, E, N, K, stream), "moe_q4_gemv_silu")
+        check(L.moe_q4_gemv_down(y5.data_ptr(), wd.data_ptr(), h.data_ptr(), ids.data_ptr(), M,
+                                 top_k, E, dd["N"], N, stream), "moe_q4_gemv_down")
 
     out = {}
     s = torch.cuda.Stream()  # default priority
-    for name, fn in (("small_call", small), ("router_then_silu_expert_call", step)):
+    for name, fn, cnt in (("small_call", small, n), ("dense_ffn_step", ffn, n // 3),
+                          ("moe_step", moe, n // 3)):
         with torch.cuda.stream(s):
-            for _ in range(20):
+            for _ in range(10):
                 fn(s.cuda_stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(s):
-            for _ in range(n):
+            for _ in range(cnt):
                 fn(s.cuda_stream)
         torch.cuda.synchronize()
-        eager = (time.perf_counter() - t0) / n
+        eager = (time.perf_counter() - t0) / cnt
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
             g.capture_begin()
-            for _ in range(n):
+            for _ in range(cnt):
                 fn(s.cuda_stream)
             g.capture_end()
         g.replay()
@@ -442,10 +505,36 @@ def measure_chain(torch, dev, n=300):
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
-        graph = (time.perf_counter() - t0) / n
-        out[name] = dict(n=n, eager_us=eager * 1e6, graph_us=graph * 1e6)
-        print("chain %-30s %d in a row: eager %.2f us each, graph replay %.2f us each"
-              % (name, n, eager * 1e6, graph * 1e6), file=sys.stderr, flush=True)
+        graph = (time.perf_counter() - t0) / cnt
+        out[name] = dict(n=cnt, eager_us=eager * 1e6, graph_us=graph * 1e6)
+        print("chain %-16s %d in a row: eager %.2f us each, graph replay %.2f us each"
+              % (name, cnt, eager * 1e6, graph * 1e6), file=sys.stderr, flush=True)
+        del g
+    # turnaround of one submission on an idle device
+    waits, spins = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            small(s.cuda_stream)
+        torch.cuda.synchronize()
+        waits.append(time.perf_counter() - t0)
+        ev = torch.cuda.Event()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            small(s.cuda_stream)
+            ev.record()
+        while not ev.query():
+            pass
+        spins.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+    waits.sort()
+    spins.sort()
+    out["turnaround"] = dict(reps=reps, wait_us_median=waits[reps // 2] * 1e6,
+                             wait_us_min=waits[0] * 1e6, spin_us_median=spins[reps // 2] * 1e6,
+                             spin_us_min=spins[0] * 1e6)
+    print("turnaround of one small call: submit+wait %.1f us, submit+spin %.1f us (medians of %d)"
+          % (waits[reps // 2] * 1e6, spins[reps // 2] * 1e6, reps), file=sys.stderr, flush=True)
     return out
 
 
@@ -565,7 +654,8 @@ def write_report(path, rows, headline, router=None):
         json.dump(dict(headline=headline, workloads=rows, router=router), f, indent=1)
     names = {1: "q4_0_gemv K=512 N=256", 2: "q4_0_gemv K=4096 N=4096",
              3: "fused_rmsnorm_q4k_gemv K=3584 N=18944", 4: "fused_gate_up_q4k_gemv K=4096 N=14336x2",
-             5: "moe_q4_gemv E=64 top6 N=1408 K=2048"}
+             5: "moe_q4_gemv E=64 top6 N=1408 K=2048",
+             6: "moe_q4_gemv_down E=64 top6 N=2048 K=1408"}
     lines = ["| workload | M | weight MB | kernel us (median) | GB/s (mean dur) | % of 8 TB/s | "
              "ceiling GB/s | % of ceiling | stream GB/s | % of stream | spread |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -576,7 +666,7 @@ def write_report(path, rows, headline, router=None):
                 "moe_q4_gemv", "moe_q4_gemv_silu")
         if r.get("norm"):
             name = name.replace("fused_gate_up", "fused_rmsnorm_gate_up")
-        if r["index"] == 5:
+        if r["index"] in (5, 6):
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
         lines.append("| %s | %d | %.2f | %.2f | %.0f | %.1f%% | %.0f | %.1f%% | %.0f | %.1f%% | "
@@ -634,7 +724,8 @@ def main():
                                             (4, (1, 4), 0, 1, 0), (4, (1, 4), 0, 0, 1),
                                             (4, (1, 4), 0, 1, 1),
                                             (5, (4,), 0, 0, 0), (5, (4,), 1, 0, 0),
-                                            (5, (4,), 0, 1, 0)):
+                                            (5, (4,), 0, 1, 0), (6, (4,), 0, 0, 0),
+                                            (6, (1, 8), 0, 0, 0)):
             for M in Ms:
                 r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu),
                             bool(norm))

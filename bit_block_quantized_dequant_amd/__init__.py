@@ -22,9 +22,9 @@ __all__ = [
     "Q4Error", "lib", "q4_version", "q4_strerror", "q4_0_gemv", "q4k_gemv",
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv",
     "fused_gate_up_silu_q4k_gemv", "fused_rmsnorm_gate_up_silu_q4k_gemv",
-    "moe_q4_gemv", "moe_q4_gemv_silu", "moe_router_q4_0", "dequant_q4k",
+    "moe_q4_gemv", "moe_q4_gemv_silu", "moe_q4_gemv_down", "moe_router_q4_0", "dequant_q4k",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
-    "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "LIB_PATH", "q4_0_row_bytes",
+    "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "Q4_READ_MOE_DOWN", "LIB_PATH", "q4_0_row_bytes",
     "q4k_row_bytes",
 ]
 
@@ -37,6 +37,7 @@ Q4_READ_Q4K_GEMV = 1
 Q4_READ_GATE_UP = 2
 Q4_READ_MOE = 3
 Q4_READ_STREAM = 4
+Q4_READ_MOE_DOWN = 5
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_BATCH", 4: "Q4_ERR_ALIGN",
           5: "Q4_ERR_ARG", 6: "Q4_ERR_HIP"}
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "fused_rmsnorm_gate_up_silu_q4k_gemv": [_vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                                     _i64, _i64, _i64, _vp],
             "moe_q4_gemv_silu": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
+            "moe_q4_gemv_down": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "moe_router_q4_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp],
             "moe_q4_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "dequant_q4k": [_vp, _vp, _i64, _i64, _vp],
@@ -282,6 +284,17 @@ def moe_q4_gemv_silu(h, w_gate, w_up, x, ids, M, top_k, E, N, K, stream=None):
         "moe_q4_gemv_silu")
 
 
+def moe_q4_gemv_down(y, w_down, h, ids, M, top_k, E, N, K, stream=None):
+    """y[M, top_k, N] = each (token, slot) pair's own row h[m, s] times the
+    down matrix of its selected Q4_0 expert."""
+    (py, pw, ph, pi), dev = _ptrs((y, "y", _sz(M * top_k * N, 4), F32),
+                                  (w_down, "w_down", _sz(E * N, q4_0_row_bytes(K)), U8),
+                                  (h, "h", _sz(M * top_k * K, 4), F32),
+                                  (ids, "ids", _sz(M * top_k, 4), I32))
+    _ok(lib().moe_q4_gemv_down(py, pw, ph, pi, M, top_k, E, N, K, _stream(stream, dev)),
+        "moe_q4_gemv_down")
+
+
 def moe_router_q4_0(ids, weights, w_router, x, M, E, K, top_k, normalize, stream=None):
     """ids/weights[M, top_k]: each token's top_k experts by Q4_0 gate logit and
     their softmax weights (normalized over the selection, or the full softmax's)."""
@@ -312,6 +325,9 @@ def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=Non
     if kernel_id == Q4_READ_MOE:
         rows, nmat, rb = E * N, 2, q4_0_row_bytes(K)
         ncks = 2 * M * top_k * N
+    elif kernel_id == Q4_READ_MOE_DOWN:
+        rows, nmat, rb = E * N, 1, q4_0_row_bytes(K)
+        ncks = M * top_k * N
     elif kernel_id == Q4_READ_STREAM:
         rows, nmat, rb = N, 1, q4k_row_bytes(K)
         ncks = (max(0, N) * rb + 4095) // 4096  # one checksum per 4 KiB block
@@ -319,7 +335,7 @@ def q4_pure_read(checksum, kernel_id, w0, w1, ids, M, top_k, E, N, K, stream=Non
         nmat = 2 if kernel_id == Q4_READ_GATE_UP else 1
         rb = q4_0_row_bytes(K) if kernel_id == Q4_READ_Q4_0_GEMV else q4k_row_bytes(K)
         rows, ncks = N, nmat * N
-    ids_bytes = _sz(M * top_k, 4) if kernel_id == Q4_READ_MOE else None
+    ids_bytes = _sz(M * top_k, 4) if kernel_id in (Q4_READ_MOE, Q4_READ_MOE_DOWN) else None
     (pc, p0, p1, pi), dev = _ptrs((checksum, "checksum", _sz(ncks, 4), CKS),
                                   (w0, "w0", _sz(rows, rb), U8),
                                   (w1, "w1", _sz(rows, rb) if nmat == 2 else None, U8),

@@ -22,6 +22,7 @@
 
 #include "q4_kernels.h"
 #include "q4_mfma.h"
+#include "q4_moe_down.h"
 #include "q4_router.h"
 #include "q4gemv.h"
 
@@ -408,6 +409,88 @@ inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
         case 6: return run_m<FMT, NMAT, MODE, PURE, 6>(p, cus, npairs_max, stream);
         case 7: return run_m<FMT, NMAT, MODE, PURE, 7>(p, cus, npairs_max, stream);
         case 8: return run_m<FMT, NMAT, MODE, PURE, 8>(p, cus, npairs_max, stream);
+    }
+    return Q4_ERR_BATCH;
+}
+
+// Expert down-projection: rows per lane group and the lane-group width.
+#ifndef Q4_RR_DOWN
+#define Q4_RR_DOWN 1
+#endif
+
+// Lane-group width that wastes the fewest lanes on a row of `upr` units:
+// the widest power of two (64 .. 4) whose last pass over the row leaves at
+// most one lane in eight idle, else the one that idles the fewest (rows of
+// 22 units, K = 1408: 8 lanes, 3 units each, against 32 lanes with 10 idle).
+inline int choose_lg_waste(int upr) {
+    static const int forced = env_int("Q4GEMV_LG", 0);
+    if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
+    int best = 4, best_idle = 1 << 30, best_slots = 1;
+    for (int lg = kWave; lg >= 4; lg >>= 1) {
+        const int slots = (upr + lg - 1) / lg * lg;
+        const int idle = slots - upr;
+        if (8 * idle <= slots) return lg;
+        if ((long long)idle * best_slots < (long long)best_idle * slots) {
+            best = lg;
+            best_idle = idle;
+            best_slots = slots;
+        }
+    }
+    return best;
+}
+
+template <int M, int RR, bool PURE>
+inline int run_down_rr(GemvParams& p, int cus, int npairs_max, void* stream) {
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    static std::atomic<int> resident[kMaxDevices];
+    p.upr = (int)k_units(p.K);
+    p.lg = choose_lg_waste(p.upr);
+    p.upl = (p.upr + p.lg - 1) / p.lg;
+    p.rgw = kWave / p.lg;
+    p.nrg = (p.N + RR - 1) / RR;
+    const size_t lds = PURE ? 0 : down_lds_bytes(M, p.upr);
+    const int res = resident_per_cu((const void*)moe_down_kernel<M, RR, false>, kDownBlock,
+                                    down_lds_bytes(M, p.upr), resident);
+    static const int wgmax = env_int("Q4GEMV_DOWN_WG_PER_CU", 4);
+    int wgc = wg_per_cu(down_lds_bytes(M, p.upr), wgmax);
+    if (wgc > res) wgc = res;
+    // ks workgroups per possible unique expert, so that the grid fills the
+    // CUs (at least one workgroup pass over the rows per share)
+    const long long per_pass = (long long)kDownWaves * p.rgw;
+    long long ks = ((long long)cus * wgc + npairs_max - 1) / npairs_max;
+    const long long ks_max = (p.nrg + per_pass - 1) / per_pass;
+    if (ks > ks_max) ks = ks_max;
+    if (ks < 1) ks = 1;
+    p.ks = (int)ks;
+    const long long blocks = ks * npairs_max;
+    if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
+    p.nwaves = (int)blocks * kDownWaves;
+    return launch(moe_down_kernel<M, RR, PURE>, p, (int)blocks, lds, stream, big_lds_done,
+                  kDownBlock);
+}
+
+// Q4GEMV_DOWN_RR=1 or 2 overrides the rows per lane group (measurements).
+template <int M, bool PURE>
+inline int run_down_m(GemvParams& p, int cus, int npairs_max, void* stream) {
+    static const int rr = env_int("Q4GEMV_DOWN_RR", Q4_RR_DOWN);
+    if (rr == 2) return run_down_rr<M, 2, PURE>(p, cus, npairs_max, stream);
+    return run_down_rr<M, 1, PURE>(p, cus, npairs_max, stream);
+}
+
+template <bool PURE>
+inline int run_down(GemvParams& p, int M, int npairs_max, void* stream) {
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st) return st;
+    switch (M) {
+        case 1: return run_down_m<1, PURE>(p, cus, npairs_max, stream);
+        case 2: return run_down_m<2, PURE>(p, cus, npairs_max, stream);
+        case 3: return run_down_m<3, PURE>(p, cus, npairs_max, stream);
+        case 4: return run_down_m<4, PURE>(p, cus, npairs_max, stream);
+        case 5: return run_down_m<5, PURE>(p, cus, npairs_max, stream);
+        case 6: return run_down_m<6, PURE>(p, cus, npairs_max, stream);
+        case 7: return run_down_m<7, PURE>(p, cus, npairs_max, stream);
+        case 8: return run_down_m<8, PURE>(p, cus, npairs_max, stream);
     }
     return Q4_ERR_BATCH;
 }

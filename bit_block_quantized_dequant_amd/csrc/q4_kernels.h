@@ -410,26 +410,26 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
         const bool in = tid < P;
         const int e = in ? p.ids[tid] : -1;
         const bool ok = in && e >= 0 && e < p.E;
-        // first appearance of e among the valid pairs?
+        // (pair t's id and validity are read with v_readlane into scalar
+        // registers: t is uniform, so no LDS permute round trip per pair)
+        const int eo = ok ? e : -1;  // -1: an invalid pair matches nothing
+        // first appearance of e among the valid pairs; the pairs and tokens
+        // that chose it
         bool first = ok;
-        for (int t = 0; t < P; ++t) {
-            const int et = __shfl(e, t, kWave);
-            const bool okt = __shfl((int)ok, t, kWave) != 0;
-            if (t < tid && okt && et == e) first = false;
-        }
-        const unsigned long long fb = __ballot(first);
-        const unsigned long long bad = __ballot(in && !ok);
-        const int uidx = __popcll(fb & ((1ull << tid) - 1ull));
         unsigned long long pairs = 0;
         unsigned int toks = 0;
         for (int t = 0; t < P; ++t) {
-            const int et = __shfl(e, t, kWave);
-            const bool okt = __shfl((int)ok, t, kWave) != 0;
-            if (okt && et == e) {
+            const int et = __builtin_amdgcn_readlane(eo, t);
+            const bool same = ok && et == e;
+            if (t < tid && same) first = false;
+            if (same) {
                 pairs |= 1ull << t;
                 toks |= 1u << (t / p.top_k);
             }
         }
+        const unsigned long long fb = __ballot(first);
+        const unsigned long long bad = __ballot(in && !ok);
+        const int uidx = __popcll(fb & ((1ull << tid) - 1ull));
         if (first) {
             sh.uexp[uidx] = e;
             sh.upairs[uidx] = pairs;

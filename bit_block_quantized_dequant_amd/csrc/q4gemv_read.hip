@@ -7,7 +7,7 @@ extern "C" {
 int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
                  const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
                  void* stream) {
-    if (kernel_id < Q4_READ_Q4_0_GEMV || kernel_id > Q4_READ_STREAM) return Q4_ERR_ARG;
+    if (kernel_id < Q4_READ_Q4_0_GEMV || kernel_id > Q4_READ_MOE_DOWN) return Q4_ERR_ARG;
     if (!checksum || !w0) return Q4_ERR_NULL;
     if (kernel_id == Q4_READ_STREAM) {
         if (K <= 0 || K % 256 != 0 || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
@@ -28,10 +28,10 @@ int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* 
         return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
     }
     if ((kernel_id == Q4_READ_GATE_UP || kernel_id == Q4_READ_MOE) && !w1) return Q4_ERR_NULL;
-    if (kernel_id == Q4_READ_MOE && !ids) return Q4_ERR_NULL;
-    const int fmt = (kernel_id == Q4_READ_Q4_0_GEMV || kernel_id == Q4_READ_MOE) ? kFmtQ4_0
-                                                                                 : kFmtQ4K;
-    int st = kernel_id == Q4_READ_MOE ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K, fmt);
+    const bool moe = kernel_id == Q4_READ_MOE || kernel_id == Q4_READ_MOE_DOWN;
+    if (moe && !ids) return Q4_ERR_NULL;
+    const int fmt = (kernel_id == Q4_READ_Q4_0_GEMV || moe) ? kFmtQ4_0 : kFmtQ4K;
+    int st = moe ? check_moe(M, top_k, E, N, K) : check_dims(M, N, K, fmt);
     if (st) return st;
     if (!aligned(w0, 16) || (w1 && !aligned(w1, 16)) || !aligned(checksum, 4) ||
         (ids && !aligned(ids, 4)))
@@ -48,6 +48,13 @@ int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* 
             p.E = (int)E;
             const int umax = (int)(M * top_k < E ? M * top_k : E);
             return run<kFmtQ4_0, 2, kModeMoe, true>(p, (int)M, umax, stream);
+        }
+        case Q4_READ_MOE_DOWN: {
+            p.ids = ids;
+            p.top_k = (int)top_k;
+            p.E = (int)E;
+            const int umax = (int)(M * top_k < E ? M * top_k : E);
+            return run_down<true>(p, (int)M, umax, stream);
         }
     }
     return Q4_ERR_ARG;

@@ -121,6 +121,28 @@ WORKLOADS = {
 }
 
 
+# The step after the expert gate/up call: the down-projection of the SiLU-
+# gated rows, one Q4_0 matrix of 2048 rows x 1408 columns per expert, same
+# experts and ids as the gate/up workload (draws from their own seed).
+DOWN = dict(name="moe_q4_gemv_down M=4 E=64 top_k=6 N=2048 K=1408", E=64, top_k=6, N=2048,
+            K=1408)
+
+# The dense down-projection after the gate+up pair of the 14336 x 4096
+# workload: Q4_K, 4096 rows x 14336 columns.
+DENSE_DOWN = dict(N=4096, K=14336)
+
+
+def down_inputs(M: int = 4, distinct: bool = False) -> dict:
+    """Inputs of the expert down-projection at batch M: the gate/up
+    workload's ids, then (seed 20261202 + 6) the expert-stacked down
+    matrices and one N(0, 1) input row per (token, slot) pair."""
+    d5 = workload_inputs(5, M=M, distinct=distinct)
+    rng = config_rng(6)
+    E, N, K, top_k = DOWN["E"], DOWN["N"], DOWN["K"], DOWN["top_k"]
+    return dict(M=M, E=E, N=N, K=K, top_k=top_k, ids=d5["ids"],
+                w_down=q4_0_matrix(rng, E * N, K), h=pair_activations(rng, M, top_k, K))
+
+
 def workload_inputs(index: int, M: int = None, rows: int = None, distinct: bool = False) -> dict:
     """Inputs of workload `index` (1..5) at batch M; `rows` < N draws only the
     first rows of every matrix (the same bytes the full draw would not give, so

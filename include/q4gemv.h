@@ -230,6 +230,27 @@ int moe_q4_gemv_silu(float* h, const void* w_gate, const void* w_up, const float
                      int64_t K, void* stream);
 
 /*
+ * Expert down-projection over the selected experts, Q4_0: every (token,
+ * slot) pair p = m * top_k + s has its own input row h[m, s] (the gated
+ * activation of its expert) and is multiplied by the down matrix of the
+ * same expert e = ids[m, s]:
+ *   y[m, s, r] = sum_k Wd[e*N + r, k] * h[m, s, k],
+ * w_down holding E expert matrices of N rows and K columns, stacked as for
+ * moe_q4_gemv (expert e's row r is global row e*N + r).  h: fp32
+ * [M, top_k, K]; y: fp32 [M, top_k, N].  Only the selected experts' rows
+ * are read, each once per call however many pairs chose it; per expert,
+ * only the input rows of the pairs that chose it are staged on chip.  Same
+ * id precondition (an invalid id yields NaN rows of y), limits and
+ * alignment (w_down and h 16 bytes) as moe_q4_gemv.
+ * (inferencelayer 0.2.13, kernel_lab.rs, moe_lab: expert-stacked rows and
+ * the per-(column, slot) expert selection, here for the projection that
+ * follows the gate and up matrices.)
+ */
+int moe_q4_gemv_down(float* y, const void* w_down, const float* h, const int32_t* ids,
+                     int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,
+                     void* stream);
+
+/*
  * Expert router: the gate logits of each token row against E expert rows,
  * then its top_k experts and their softmax weights, in one launch
  * (atlas, spark_model/layers/ops/gemm_quant.rs, moe_gate_topk_fused: gate
@@ -287,6 +308,7 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream);
  *   Q4_READ_GATE_UP     w0, w1: Q4_K [N, K] each            [2, N]  (w0 rows, then w1)
  *   Q4_READ_MOE         w0, w1: Q4_0 experts as moe_q4_gemv [2, M, top_k, N]
  *   Q4_READ_STREAM      w0: N * K * 9/16 bytes              [ceil(bytes / 4096)]
+ *   Q4_READ_MOE_DOWN    w0: Q4_0 experts as moe_q4_gemv_down [M, top_k, N]
  *
  * For a Q4_K row whose K is not a multiple of 256, the checksum covers what
  * the call reads: the super-block headers and the 32-byte nibble chunks
@@ -309,7 +331,8 @@ enum {
     Q4_READ_Q4K_GEMV = 1,
     Q4_READ_GATE_UP = 2,
     Q4_READ_MOE = 3,
-    Q4_READ_STREAM = 4
+    Q4_READ_STREAM = 4,
+    Q4_READ_MOE_DOWN = 5
 };
 int q4_pure_read(uint32_t* checksum, int kernel_id, const void* w0, const void* w1,
                  const int32_t* ids, int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K,

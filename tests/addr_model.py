@@ -378,3 +378,80 @@ def router_check(E, K):
         assert 0 <= off and off + nb <= limit, (E, K, off, nb, limit)
         n += 1
     return n
+
+
+# ---------------------------------------------------------------------------
+# Expert down-projection (q4_moe_down.h, run_down_m() in q4_host.h): one
+# contiguous slice of the (unique expert, row group) space per workgroup of
+# 4 waves.
+# ---------------------------------------------------------------------------
+def choose_lg_waste(upr):
+    best, best_idle, best_slots = 4, 1 << 30, 1
+    lg = 64
+    while lg >= 4:
+        slots = (upr + lg - 1) // lg * lg
+        idle = slots - upr
+        if 8 * idle <= slots:
+            return lg
+        if idle * best_slots < best_idle * slots:
+            best, best_idle, best_slots = lg, idle, slots
+        lg //= 2
+    return best
+
+
+def down_plan(N, K, npairs_max, cus=256, wgc=4, RR=1):
+    upr = (K + 63) // 64
+    lg = choose_lg_waste(upr)
+    upl = (upr + lg - 1) // lg
+    rgw = 64 // lg
+    nrg = (N + RR - 1) // RR
+    per_pass = 4 * rgw
+    ks = (cus * wgc + npairs_max - 1) // npairs_max
+    ks = max(1, min(ks, (nrg + per_pass - 1) // per_pass))
+    return dict(upr=upr, lg=lg, upl=upl, rgw=rgw, nrg=nrg, per_pass=per_pass, ks=ks,
+                blocks=ks * npairs_max)
+
+
+def down_loads(N, K, experts, npairs_max, cus=256, wgc=4, RR=1):
+    """Yield (byte offset, nbytes) of every weight load of the down kernel,
+    for the dedupe result `experts` (unique valid ids): workgroup b serves
+    expert b // ks and share b % ks of its row groups."""
+    pl = down_plan(N, K, npairs_max, cus, wgc, RR)
+    upr, lg, upl, rgw, nrg, per_pass, ks, G = (pl[k] for k in (
+        "upr", "lg", "upl", "rgw", "nrg", "per_pass", "ks", "blocks"))
+    rb = (K // 32) * 18
+    for b in range(G):
+        ux, part = divmod(b, ks)
+        if ux >= len(experts):
+            continue
+        g0, g1 = part * nrg // ks, (part + 1) * nrg // ks
+        if g0 >= g1:
+            continue
+        e = experts[ux]
+        nsteps = -(-(g1 - g0) // per_pass) * upl
+        for wave in range(4):
+            for q in range(nsteps):
+                pss, ui = divmod(q, upl)
+                gw = min(g0 + pss * per_pass + wave * rgw, g1 - 1)
+                R0 = gw * RR
+                lrow_max = N - 1 - R0
+                assert lrow_max >= 0
+                for lane in range(64):
+                    gi, li = lane // lg, lane % lg
+                    uoff = min(li + ui * lg, upr - 1) * Q40_PAIR
+                    for r in range(RR):
+                        lr = min(gi * RR + r, lrow_max)
+                        off = (e * N + R0) * rb + ((lr * rb + uoff) & U32)
+                        yield off, 16
+                        yield off + 16, 16
+                        yield off + 32, 4
+
+
+def down_check(N, K, experts, E, npairs_max, cus=256, wgc=4, RR=1):
+    limit = E * N * (K // 32) * 18
+    n = 0
+    for off, nb in down_loads(N, K, experts, npairs_max, cus, wgc, RR):
+        assert 0 <= off and off + nb <= limit, (N, K, off, nb, limit)
+        assert off % 4 == 0
+        n += 1
+    return n

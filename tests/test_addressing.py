@@ -197,3 +197,20 @@ def test_odd_q4_0_block_count_would_misalign():
     row starts 2 bytes off a word boundary."""
     with pytest.raises(AssertionError, match="alignment"):
         A.check("q4_0", 1, 4, 96, RR=2, nmat=1, cus=8)
+
+
+@pytest.mark.parametrize("experts,E,N,K,npairs", [([0], 1, 5, 64, 1), ([3, 1], 4, 70, 1408, 6),
+                                                  ([63, 0, 17], 64, 333, 2048, 24),
+                                                  ([5], 8, 1, 1408, 8),
+                                                  (list(range(20)), 20, 200, 192, 20)])
+@pytest.mark.parametrize("wgc", [1, 2, 4])
+@pytest.mark.parametrize("RR", [1, 2])
+def test_down_loads_in_bounds(experts, E, N, K, npairs, wgc, RR):
+    assert A.down_check(N, K, experts, E, npairs, cus=8, wgc=wgc, RR=RR) > 0
+
+
+def test_down_lane_groups():
+    # rows of 22 units (K = 1408): 8 lanes x 3 units (2 idle of 24), not 32
+    assert A.choose_lg_waste(22) == 8
+    assert A.choose_lg_waste(32) == 32 and A.choose_lg_waste(64) == 64
+    assert A.choose_lg_waste(56) == 64 and A.choose_lg_waste(1) == 4

@@ -30,7 +30,7 @@ def test_header_declares_the_calls():
     for n in ["q4_0_gemv", "q4k_gemv", "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv",
               "fused_rmsnorm_gate_up_q4k_gemv", "fused_gate_up_silu_q4k_gemv",
               "fused_rmsnorm_gate_up_silu_q4k_gemv", "moe_q4_gemv",
-              "moe_q4_gemv_silu", "moe_router_q4_0",
+              "moe_q4_gemv_silu", "moe_q4_gemv_down", "moe_router_q4_0",
               "dequant_q4k", "dequant_q4_0", "q4_pure_read", "q4_strerror",
               "q4_version"]:
         assert n in names, n
@@ -169,6 +169,7 @@ def test_gate_up_silu_validation(q4lib):
 def test_moe_validation(q4lib, M, top_k, E, N, K, want):
     assert L().moe_q4_gemv(A, A, A, A, A, A, M, top_k, E, N, K, None) == want
     assert L().moe_q4_gemv_silu(A, A, A, A, A, M, top_k, E, N, K, None) == want
+    assert L().moe_q4_gemv_down(A, A, A, A, M, top_k, E, N, K, None) == want
 
 
 def test_moe_null_and_align(q4lib):
@@ -180,6 +181,15 @@ def test_moe_null_and_align(q4lib):
     assert g(A, A, A, A, None, 4, 6, 64, 1408, 2048, None) == NULL
     assert g(A + 2, A, A, A, A, 4, 6, 64, 1408, 2048, None) == ALIGN
     assert g(A, A, A, A, A + 2, 4, 6, 64, 1408, 2048, None) == ALIGN
+    d = L().moe_q4_gemv_down
+    for i in range(4):
+        args = [A] * 4
+        args[i] = None
+        assert d(*args, 4, 6, 64, 2048, 1408, None) == NULL, i
+        args[i] = A + 2 if i != 1 else A + 4
+        assert d(*args, 4, 6, 64, 2048, 1408, None) == ALIGN, i
+    assert d(A, A, A + 8, A, 4, 6, 64, 2048, 1408, None) == ALIGN  # h: 16 bytes
+    assert d(A, A, A, A, 4, 6, 64, 2048, 1376, None) == SHAPE      # K % 64 != 0
 
 
 @pytest.mark.parametrize("args,want", [
@@ -229,7 +239,9 @@ def test_pure_read_validation(q4lib):
     assert f(A, 3, A, A, A, 4, 0, 64, 16, 256, None) == SHAPE
     assert f(A + 1, 0, A, None, None, 1, 0, 0, 16, 256, None) == ALIGN
     # reference stream (kernel_id 4)
-    assert f(A, 5, A, None, None, 1, 0, 0, 16, 256, None) == ARG
+    assert f(A, 6, A, None, None, 1, 0, 0, 16, 256, None) == ARG
+    assert f(A, 5, A, None, None, 4, 6, 64, 16, 1408, None) == NULL  # down needs ids
+    assert f(A, 5, A, None, A, 4, 6, 64, 16, 1376, None) == SHAPE
     assert f(A, 4, A, None, None, 1, 0, 0, 16, 300, None) == SHAPE
     assert f(A, 4, A, None, None, 1, 0, 0, 0, 256, None) == SHAPE
     assert f(A, 4, A + 4, None, None, 1, 0, 0, 16, 256, None) == ALIGN
