@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 static_assert(Q4_MAX_MK == kMaxMK, "staging of the batched kernel is sized for Q4_MAX_MK");
+static_assert(Q4_MAX_M == kMaxM, "token rows of the batched kernel");
 
 // ---------------------------------------------------------------------------
 // Validation (pure host code)
@@ -49,11 +50,19 @@ inline bool k_ok(int64_t K, int fmt) {
 // Staged columns of a call: K rounded up to whole 64-weight units.
 inline int64_t k_units(int64_t K) { return (K + kUnitElems - 1) / kUnitElems; }
 
+// Dense calls: 1 <= M <= Q4_MAX_M.  A single token is staged whole by the
+// VALU kernel (K <= Q4_MAX_MK); batches run the matrix-core kernel, which
+// stages K in slices when the rows do not fit in LDS at once.
 inline int check_dims(int64_t M, int64_t N, int64_t K, int fmt) {
-    if (M < 1 || M > 8) return Q4_ERR_BATCH;
-    if (!k_ok(K, fmt) || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
-    if (M * k_units(K) * kUnitElems > Q4_MAX_MK) return Q4_ERR_SHAPE;
+    if (M < 1 || M > Q4_MAX_M) return Q4_ERR_BATCH;
+    if (!k_ok(K, fmt) || K > Q4_MAX_K || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (M == 1 && k_units(K) * kUnitElems > Q4_MAX_MK) return Q4_ERR_SHAPE;
     return Q4_OK;
+}
+
+// Can the VALU kernel stage this batch whole?
+inline bool valu_fits(int64_t M, int64_t K) {
+    return M <= 8 && M * k_units(K) * kUnitElems <= Q4_MAX_MK;
 }
 
 // Bytes of one weight row: ceil(K/256) super-blocks (Q4_K), K/32 blocks (Q4_0).
@@ -109,9 +118,13 @@ inline size_t gemv_lds_bytes(int M, int K, bool pure) {
 }
 
 // static shared memory of the batched kernel (its reduction scratch) plus
-// margin; the expert call adds its dedupe tables
+// margin; the expert call adds its dedupe tables; batches of more than 8
+// tokens a larger reduction scratch
 constexpr int kMfmaStaticLds = 1024;
 constexpr int kMfmaMoeStaticLds = 3072;
+constexpr int kMfmaBigStaticLds = 2048;
+static_assert(sizeof(StageRedT<8>) + 64 <= kMfmaStaticLds, "static LDS margin");
+static_assert(sizeof(StageRedT<16>) + 64 <= kMfmaBigStaticLds, "static LDS margin");
 
 // Resident workgroups per CU that LDS allows (160 KB per CU on gfx950, less
 // the static shared state), capped at `mx`.
@@ -330,40 +343,86 @@ inline bool moe_mfma_enabled() {
     return on;
 }
 
-template <int FMT, int NMAT, int MODE, bool PURE, int M>
-inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
+template <int FMT, int NMAT, int MODE, bool PURE, int M, bool SLICED>
+inline int run_mfma_launch(GemvParams& p, int cus, int nexperts, int reserve, void* stream) {
     constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
-    constexpr int kReserve = mode_moe(MODE) ? kMfmaMoeStaticLds : kMfmaStaticLds;
     static std::atomic<int> big_lds_done[kMaxDevices];
-    const size_t lds = (size_t)mlayout(FMT, M, p.K, PURE).bytes;
-    // a pure-read pass takes the launch shape of the call it mirrors
     static std::atomic<int> resident[kMaxDevices];
-    const size_t call_lds = (size_t)mlayout(FMT, M, p.K, false).bytes;
+    const int S = msteps(p.K);
+    int kse = p.ks;
+    while (kse > S) kse >>= 1;  // (the kernel's own clamp)
+    const int steps = SLICED ? mslice_regions(kse, p.npg) * p.msl : S;
+    // a pure-read pass takes the launch shape of the call it mirrors
+    const size_t lds = (size_t)mlayout_steps(FMT, M, steps, PURE).bytes;
+    const size_t call_lds = (size_t)mlayout_steps(FMT, M, steps, false).bytes;
     int wgc = wg_per_cu(call_lds);
     if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
         static std::atomic<int> big_lds_mirror[kMaxDevices];
-        int st = allow_big_lds((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
-                               big_lds_mirror, kReserve);
+        int st = allow_big_lds(
+            (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, SLICED>, big_lds_mirror,
+            reserve);
         if (st) return st;
     }
-    const int res = resident_per_cu((const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD>,
-                                    kMBlock, call_lds, resident);
+    const int res = resident_per_cu(
+        (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, SLICED>, kMBlock, call_lds,
+        resident);
     if (wgc > res) wgc = res;
+    const long long ntiles_run =
+        (MODE == kModeSilu || MODE == kModeNormSilu)
+            ? (long long)nexperts * ((p.N + 7) / 8)
+            : (long long)NMAT * nexperts * ((p.N + 15) / 16);
+    const int TG = kMWaves / p.ks;
+    long long blocks = (long long)cus * wgc;
+    const long long need = (ntiles_run + TG - 1) / TG;
+    if (blocks > need) blocks = need;
+    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD, SLICED>, p, (int)blocks, lds,
+                  stream, big_lds_done, kMBlock, reserve);
+}
+
+template <int FMT, int NMAT, int MODE, bool PURE, int M>
+inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
+    const int reserve =
+        mode_moe(MODE) ? kMfmaMoeStaticLds : (M > 8 ? kMfmaBigStaticLds : kMfmaStaticLds);
+    const int budget = 160 * 1024 - reserve;
     // (the expert call: at most nexperts unique experts, each N rows per matrix)
     // (the K split is chosen from the 16-row tile count of the plain call,
     // also for the SiLU-gated call and its 8 + 8-row tiles, so that both
     // accumulate every row alike)
     const long long ntiles = (long long)NMAT * nexperts * ((p.N + 15) / 16);
-    p.ks = mfma_ks(ntiles, msteps(p.K), cus);
-    const long long ntiles_run =
-        (MODE == kModeSilu || MODE == kModeNormSilu) ? (long long)nexperts * ((p.N + 7) / 8)
-                                                      : ntiles;
-    const int TG = kMWaves / p.ks;
-    long long blocks = (long long)cus * wgc;
-    const long long need = (ntiles_run + TG - 1) / TG;
-    if (blocks > need) blocks = need;
-    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD>, p, (int)blocks, lds, stream,
-                  big_lds_done, kMBlock, kReserve);
+    const int S = msteps(p.K);
+    p.ks = mfma_ks(ntiles, S, cus);
+    p.nsl = 1;
+    p.msl = S;
+    p.npg = 1;
+    const bool whole = (long long)M * mpadk(p.K) <= kMaxMK &&
+                       mlayout(FMT, M, p.K, false).bytes <= budget;
+    if (whole || mode_moe(MODE))  // (expert calls are only sent here whole)
+        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, false>(p, cus, nexperts, reserve,
+                                                                stream);
+    if constexpr (mode_moe(MODE)) {
+        return Q4_ERR_SHAPE;
+    } else {
+        // K slices: the fewest whose staged steps (msl per wave range) fit;
+        // past one step per range, wave positions staged in turn
+        int kse = p.ks;
+        while (kse > S) kse >>= 1;
+        const int lmax = (S + kse - 1) / kse;  // longest wave range, in steps
+        int nsl = 1, msl = lmax, npg = 1;
+        while (mlayout_steps(FMT, M, mslice_regions(kse, npg) * msl, false).bytes > budget) {
+            if (msl > 1) {
+                ++nsl;
+                msl = (lmax + nsl - 1) / nsl;
+            } else if (npg < kse) {
+                npg *= 2;
+            } else {
+                return Q4_ERR_SHAPE;
+            }
+        }
+        p.nsl = nsl;
+        p.msl = msl;
+        p.npg = npg;
+        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, true>(p, cus, nexperts, reserve, stream);
+    }
 }
 
 template <int FMT, int NMAT, int MODE, bool PURE>
@@ -371,35 +430,49 @@ inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st) return st;
-    // batched calls on the matrix cores; the expert call only on request
+    // batched calls on the matrix cores (also every batch the VALU kernel
+    // cannot stage whole); the expert call only on request
     // (Q4GEMV_MOE_MFMA=1: it measured slower than the VALU expert kernel at
     // the E=64, top-6, 1408 x 2048 shape), from M = 2 on, where its
     // activations leave room in LDS for the expert tables
     // (the SiLU-gated expert call always runs the VALU kernel)
-    const bool moe_fits = !mode_moe(MODE) ||
-                          (MODE == kModeMoe && moe_mfma_enabled() && M >= 2 &&
-                           mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds);
-    const int min_m = mode_moe(MODE) ? 2 : Q4_MFMA_MIN_M;
-    // (its staging covers whole 256-column steps; a call whose padded
-    // activations would not fit in LDS runs the VALU kernel)
-    const bool lds_fits =
-        mlayout(FMT, M, p.K, false).bytes <=
-        160 * 1024 - (mode_moe(MODE) ? kMfmaMoeStaticLds : kMfmaStaticLds);
-    if constexpr (MODE != kModeMoeSilu) {
-        if (M >= min_m && moe_fits && lds_fits && mfma_enabled()) {
-            const int nexp = mode_moe(MODE) ? npairs_max : 1;
-            switch (M) {
-                case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
-                case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
-                case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
-                case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
-                case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
-                case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
-                case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
-            }
-            return Q4_ERR_BATCH;
-        }
+    const bool vfits = valu_fits(M, p.K);
+    bool use_mfma;
+    if constexpr (mode_moe(MODE)) {
+        use_mfma = MODE == kModeMoe && moe_mfma_enabled() && M >= 2 &&
+                   (long long)M * mpadk(p.K) <= kMaxMK &&
+                   mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds;
+    } else {
+        use_mfma = M >= 2 && (!vfits || (M >= Q4_MFMA_MIN_M && mfma_enabled()));
     }
+    if constexpr (MODE != kModeMoeSilu) {
+    if (use_mfma) {
+        const int nexp = mode_moe(MODE) ? npairs_max : 1;
+        switch (M) {
+            case 2: return run_mfma_m<FMT, NMAT, MODE, PURE, 2>(p, cus, nexp, stream);
+            case 3: return run_mfma_m<FMT, NMAT, MODE, PURE, 3>(p, cus, nexp, stream);
+            case 4: return run_mfma_m<FMT, NMAT, MODE, PURE, 4>(p, cus, nexp, stream);
+            case 5: return run_mfma_m<FMT, NMAT, MODE, PURE, 5>(p, cus, nexp, stream);
+            case 6: return run_mfma_m<FMT, NMAT, MODE, PURE, 6>(p, cus, nexp, stream);
+            case 7: return run_mfma_m<FMT, NMAT, MODE, PURE, 7>(p, cus, nexp, stream);
+            case 8: return run_mfma_m<FMT, NMAT, MODE, PURE, 8>(p, cus, nexp, stream);
+        }
+        if constexpr (!mode_moe(MODE)) {
+            switch (M) {
+                case 9: return run_mfma_m<FMT, NMAT, MODE, PURE, 9>(p, cus, nexp, stream);
+                case 10: return run_mfma_m<FMT, NMAT, MODE, PURE, 10>(p, cus, nexp, stream);
+                case 11: return run_mfma_m<FMT, NMAT, MODE, PURE, 11>(p, cus, nexp, stream);
+                case 12: return run_mfma_m<FMT, NMAT, MODE, PURE, 12>(p, cus, nexp, stream);
+                case 13: return run_mfma_m<FMT, NMAT, MODE, PURE, 13>(p, cus, nexp, stream);
+                case 14: return run_mfma_m<FMT, NMAT, MODE, PURE, 14>(p, cus, nexp, stream);
+                case 15: return run_mfma_m<FMT, NMAT, MODE, PURE, 15>(p, cus, nexp, stream);
+                case 16: return run_mfma_m<FMT, NMAT, MODE, PURE, 16>(p, cus, nexp, stream);
+            }
+        }
+        return Q4_ERR_BATCH;
+    }
+    }
+    if (!vfits) return Q4_ERR_SHAPE;
     switch (M) {
         case 1: return run_m<FMT, NMAT, MODE, PURE, 1>(p, cus, npairs_max, stream);
         case 2: return run_m<FMT, NMAT, MODE, PURE, 2>(p, cus, npairs_max, stream);
@@ -510,9 +583,12 @@ inline GemvParams base_params(const void* w0, const void* w1, float* y0, float* 
     return p;
 }
 
+// Expert calls: M <= 8 (the decode batch), activations staged whole.
 inline int check_moe(int64_t M, int64_t top_k, int64_t E, int64_t N, int64_t K) {
+    if (M < 1 || M > 8) return Q4_ERR_BATCH;
     int st = check_dims(M, N, K, kFmtQ4_0);
     if (st) return st;
+    if (!valu_fits(M, K)) return Q4_ERR_SHAPE;
     if (E < 1 || E >= (1 << 20) || top_k < 1 || top_k > E || M * top_k > kMaxPairs)
         return Q4_ERR_SHAPE;
     if (E * N > INT32_MAX) return Q4_ERR_SHAPE;

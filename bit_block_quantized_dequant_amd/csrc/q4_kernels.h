@@ -98,6 +98,9 @@ struct GemvParams {
     int ntasks;     // dense calls: total tasks (expert call: computed in the kernel)
     int nwaves;     // waves in the grid
     int ks;         // batched kernel: waves that split one tile's K range
+    int nsl;        // batched kernel: K slices per wave-position group (1: whole rows)
+    int msl;        // batched kernel, sliced: staged steps per wave range and slice
+    int npg;        // batched kernel, sliced: groups of wave positions staged in turn
 };
 
 // Shared state of the expert call after the in-kernel dedupe.
@@ -143,12 +146,14 @@ struct XStage {
 constexpr int kMaxStageWaves = 8;
 static_assert(kBlock / kWave <= kMaxStageWaves && kBlock1 / kWave <= kMaxStageWaves,
               "staging scratch holds 8 waves");
-struct StageRed {
-    double ss[8][kMaxStageWaves];
-    float am[8][kMaxStageWaves];
-    float r[8];  // per token: the RMSNorm factor
-    int e[8];    // per token: the scale exponent
+template <int MT>
+struct StageRedT {
+    double ss[MT][kMaxStageWaves];
+    float am[MT][kMaxStageWaves];
+    float r[MT];  // per token: the RMSNorm factor
+    int e[MT];    // per token: the scale exponent
 };
+using StageRed = StageRedT<8>;
 
 // Exponent e with amax * 2^e in [2^target, 2^(target+1)), for amax >= 0;
 // a zero or non-finite amax leaves the token unscaled (e = 0).

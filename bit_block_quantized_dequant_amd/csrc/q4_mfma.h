@@ -58,8 +58,10 @@ namespace q4 {
 constexpr int kMBlock = 512;  // threads per workgroup
 constexpr int kMWaves = kMBlock / kWave;
 static_assert(kMWaves <= kMaxStageWaves, "staging scratch holds 8 waves");
-constexpr int kMaxMK = 32768;  // M * K limit of the library
+constexpr int kMaxMK = 32768;  // M * K of a call staged whole (register-held pieces)
 constexpr int kMPieces = (kMaxMK / 8 + kMBlock - 1) / kMBlock;  // staging pieces per thread
+constexpr int kMaxM = 16;  // token rows of the batched kernel: two 8-token A tiles
+__host__ __device__ constexpr int mtiles(int M) { return (M + 7) / 8; }
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -96,24 +98,30 @@ struct MLayout {
     int frag;  // A fragments: 2M rows x (K/8 + 1) pieces x 16 bytes (see fslot)
     int aux;   // Q4_K: Dmin A operand, (K/256) x 4 groups x 2M rows x 2 halves
                // Q4_0: block sums X, (K/32) blocks x sums_stride(M) tokens x fp32
-    int exps;  // e_m, 8 ints (padded to 64 bytes)
-    int part;  // partial sums, 2 buffers x 8 waves x 64 lanes x float2
+    int exps;  // e_m, 16 ints, then (K-sliced calls) the RMSNorm factors, 16 floats
+    int part;  // partial sums, 2 buffers x 8 waves x 64 lanes x float2 per A tile
     int wbuf;  // Q4_0: one tile-step of raw weight bytes per wave
     int bytes;
 };
 
-__host__ __device__ inline MLayout mlayout(int fmt, int M, int K0, bool pure) {
-    const int K = mpadk(K0);  // staged columns: whole steps
+// LDS map for M tokens and `steps` staged 256-column steps (K = 256 steps).
+__host__ __device__ inline MLayout mlayout_steps(int fmt, int M, int steps, bool pure) {
+    const int K = steps * 256;
     MLayout l;
     l.frag = 0;
     l.aux = pure ? 0 : (K / 8 + 1) * 2 * M * 16;
     l.exps = l.aux + (pure ? 0
                            : (fmt == kFmtQ4K ? (K / 256) * 4 * 2 * M * 4
                                              : (K / 32) * sums_stride(M) * 4));
-    l.part = l.exps + 64;
-    l.wbuf = l.part + 2 * kMWaves * 64 * 8;
+    l.part = l.exps + 128;
+    l.wbuf = l.part + 2 * kMWaves * 64 * 8 * mtiles(M);
     l.bytes = l.wbuf + (fmt == kFmtQ4_0 ? kMWaves * kQ40WaveBytes : 0);
     return l;
+}
+
+// The map of a call that stages its rows whole.
+__host__ __device__ inline MLayout mlayout(int fmt, int M, int K0, bool pure) {
+    return mlayout_steps(fmt, M, msteps(K0), pure);
 }
 
 // 16-byte slot of the A fragment of piece p, row i: rows of K/8 + 1 slots
@@ -161,9 +169,9 @@ __device__ __forceinline__ void mstage_issue(const GemvParams& p, MStageX& sx) {
     }
 }
 
-template <int FMT, int M, int MODE>
+template <int FMT, int M, int MODE, typename Red>
 __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLayout& ly,
-                                       StageRed& red, MStageX& sx) {
+                                       Red& red, MStageX& sx) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ppt = p.K >> 3;  // pieces per token
     const int np = M * ppt;
@@ -314,6 +322,199 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
 }
 
 // ---------------------------------------------------------------------------
+// K-sliced staging (calls whose activations do not fit in LDS at once).
+// Wave position sl of a tile group owns the steps [sl S / KS, (sl + 1) S / KS)
+// of a row, as in a call staged whole.  The positions form npg groups
+// staged in turn; for each group, nsl slices hold the s-th of nsl equal
+// sub-ranges of each of its positions' ranges, each position's in a region
+// of msl steps (local step region * msl + j).  A wave therefore meets its
+// own steps in the same order as in a call staged whole (the same
+// rounding, bit for bit); it idles in the other groups' slices (npg > 1
+// only where even one step per position does not fit in LDS).
+// ---------------------------------------------------------------------------
+struct MSlice {
+    int S, KS, npg, nsl, msl;
+    __device__ __forceinline__ int nslices() const { return npg * nsl; }
+    // sub-range [a, b) of wave position sl in slice `slice` and its region
+    // (empty when sl is not in the slice's group)
+    __device__ __forceinline__ void range(int sl, int slice, int& a, int& b, int& reg) const {
+        const int g = slice / nsl, s = slice - g * nsl;
+        const int p0 = g * KS / npg, p1 = (g + 1) * KS / npg;
+        a = b = reg = 0;
+        if (sl < p0 || sl >= p1) return;
+        reg = sl - p0;
+        const int s0 = sl * S / KS, L = (sl + 1) * S / KS - s0;
+        a = s0 + s * L / nsl;
+        b = s0 + (s + 1) * L / nsl;
+    }
+    // the wave position of region `reg` in slice `slice` (-1: none)
+    __device__ __forceinline__ int position(int reg, int slice) const {
+        const int g = slice / nsl;
+        const int p = g * KS / npg + reg;
+        return p < (g + 1) * KS / npg ? p : -1;
+    }
+};
+// Regions (positions) per group: the staged steps of a slice are regions * msl.
+__host__ __device__ inline int mslice_regions(int KS, int npg) { return (KS + npg - 1) / npg; }
+
+// Per-token factors from whole rows read from global memory: the RMSNorm
+// factor r_m (fp64 sum of squares) and the exponent e_m with
+// max_k |x_hat[m,k]| 2^e_m in [2^14, 2^15), into the exps region.
+template <int M, int MODE, typename Red>
+__device__ __forceinline__ void mstage_factors(const GemvParams& p, char* lds, const MLayout& ly,
+                                               Red& red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ppt = p.K >> 3;  // pieces of 8 per token
+    const int np = M * ppt;
+    int* ex = (int*)(lds + ly.exps);
+    float* rn = (float*)(lds + ly.exps) + 16;
+    auto piece = [&](int i, float (&v)[8]) {
+        const int m = i / ppt;
+        const float4* src = (const float4*)(p.x + (long long)m * p.K + 8 * (i - m * ppt));
+        const float4 a = src[0], b = src[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        return m;
+    };
+    if constexpr (MODE == kModeNorm) {
+        double ss[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) ss[m] = 0.0;
+        for (int i = tid; i < np; i += kMBlock) {
+            float v[8];
+            const int m = piece(i, v);
+            double t = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += (double)v[e] * (double)v[e];
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) ss[mm] += m == mm ? t : 0.0;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const double t = wave_sum_f64(ss[m]);
+            if (lane == kWave - 1) red.ss[m][wave] = t;
+        }
+        sync_lds();
+        if (tid < M) {
+            double t = 0.0;
+            for (int w = 0; w < kMWaves; ++w) t += red.ss[tid][w];
+            const float ms = (float)(t / (double)p.K);
+            rn[tid] = 1.0f / sqrtf(ms + p.eps);
+        }
+        sync_lds();
+    }
+    float am[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) am[m] = 0.f;
+    for (int i = tid; i < np; i += kMBlock) {
+        float v[8];
+        const int m = piece(i, v);
+        float t = 0.f;
+        if constexpr (MODE == kModeNorm) {
+            const float r = rn[m];
+            const float4* gs = (const float4*)(p.gamma + 8 * (i - m * ppt));
+            const float4 ga = gs[0], gb = gs[1];
+            const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf((v[e] * r) * g[e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(v[e]));
+        }
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], m == mm ? t : 0.f);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float t = wave_max_nonneg(am[m]);
+        if (lane == kWave - 1) red.am[m][wave] = t;
+    }
+    sync_lds();
+    if (tid < M) {
+        float t = 0.f;
+        for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red.am[tid][w]);
+        ex[tid] = xscale_exp(t, 14);
+    }
+    sync_lds();
+}
+
+// Stage slice s: the fragments (and sums) of every staged step of every
+// token, with the factors of mstage_factors; columns past K are zero.
+template <int FMT, int M, int MODE>
+__device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, const MLayout& ly,
+                                             const MSlice& sc, int s) {
+    const int tid = threadIdx.x;
+    const int kst = mslice_regions(sc.KS, sc.npg) * sc.msl * 256;  // staged columns
+    const int ppl = kst >> 3;              // staged pieces per token
+    const int np = M * ppl;
+    const int* ex = (const int*)(lds + ly.exps);
+    const float* rn = (const float*)(lds + ly.exps) + 16;
+    // (a 32-element group's 4 pieces are 4 consecutive threads, all active
+    // together: ppl and the block size are multiples of 4)
+    for (int i = tid; i < np; i += kMBlock) {
+        const int m = i / ppl;
+        const int pl = i - m * ppl;
+        const int ls = pl >> 5, pin = pl & 31;
+        const int rg = ls / sc.msl, j = ls - rg * sc.msl;
+        const int sl = sc.position(rg, s);
+        int a = 0, b = 0, reg = 0;
+        if (sl >= 0) sc.range(sl, s, a, b, reg);
+        const bool staged = j < b - a;  // (a region's unused tail is never read)
+        const int col = (a + j) * 256 + pin * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        if (staged && col < p.K) {
+            const float4* src = (const float4*)(p.x + (long long)m * p.K + col);
+            const float4 x0 = src[0], x1 = src[1];
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+            if constexpr (MODE == kModeNorm) {
+                const float r = rn[m];
+                const float4* gs = (const float4*)(p.gamma + col);
+                const float4 ga = gs[0], gb = gs[1];
+                const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (v[e] * r) * g[e];
+            }
+        }
+        const int e = ex[m];
+        const int ef = piece_is_high<FMT>(pin) ? e - 4 : e;
+        h8 hi, lo;
+        float part = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float xs = __builtin_ldexpf(v[slot_byte(t)], ef);
+            const _Float16 h = (_Float16)xs;
+            hi[t] = h;
+            lo[t] = (_Float16)(xs - (float)h);
+            part += __builtin_ldexpf(v[t], e);
+        }
+        part = dpp_add(part, 0);
+        part = dpp_add(part, 1);
+        if (staged) {
+            *(h8*)(lds + ly.frag + fslot(kst, 2 * m, pl) * 16) = hi;
+            *(h8*)(lds + ly.frag + fslot(kst, 2 * m + 1, pl) * 16) = lo;
+            if ((pl & 3) == 0) {
+                const int g32 = pl >> 2;  // local block / sub-block index
+                if constexpr (FMT == kFmtQ4_0) {
+                    ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
+                } else {
+                    const int sb = g32 >> 3, J = g32 & 7;
+                    const float xs = part * 0.03125f;
+                    const _Float16 h = (_Float16)xs;
+                    const _Float16 l = (_Float16)(xs - (float)h);
+                    _Float16* ap = (_Float16*)(lds + ly.aux);
+                    const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
+                    ap[base] = h;
+                    ap[base + 2] = l;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
 // Expert call: the in-kernel dedupe and, per unique expert u and token m,
@@ -324,19 +525,19 @@ struct MfmaMoe {
 };
 struct MfmaNoMoe {};
 
-template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD>
+template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD, bool SLICED>
 __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) {
-    static_assert(M >= 2 && M <= 8, "batched kernel");
+    static_assert(M >= 2 && M <= kMaxM, "batched kernel");
+    static_assert(!mode_moe(MODE) || (M <= 8 && !SLICED), "expert call: M <= 8, whole rows");
+    constexpr int NT = mtiles(M);  // A tiles of 8 tokens
     using St = MStep<FMT>;
     extern __shared__ float4 smem4[];
     char* lds = (char*)smem4;
-    __shared__ StageRed red;
-    const MLayout ly = mlayout(FMT, M, p.K, PURE);
+    __shared__ StageRedT<(M > 8 ? 16 : 8)> red;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = msteps(p.K);
-    const int kp = mpadk(p.K);
     // Q4_0: blocks of the row (a partial last step has fewer than 8), and
     // the largest byte offset of a 16-byte chunk inside the last step
     const int nblk = p.K >> 5;
@@ -348,6 +549,10 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     // (a wave without steps would skip the end-of-round reduction)
     int KS = p.ks;
     while (KS > S) KS >>= 1;
+    // staged steps: the whole row, or (K-sliced) KS regions of msl steps
+    const int staged_steps = SLICED ? mslice_regions(KS, p.npg) * p.msl : S;
+    const MLayout ly = mlayout_steps(FMT, M, staged_steps, PURE);
+    const int kst = staged_steps * 256;  // staged columns
     const int TG = kMWaves / KS;      // tiles per workgroup and round
     const int grp = wave / KS, sl = wave - grp * KS;
     const int jrow = lane & 15;  // tile row of this lane's B column and D values
@@ -478,10 +683,16 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         }
     };
 
-    // A fragment of piece pp for this lane (rows i >= 2M repeat row 2M-1)
-    const int i_lane = min(jrow, 2 * M - 1);
-    const char* arow = lds + ly.frag + fslot(kp, i_lane, 0) * 16;
-    auto afrag = [&](int pp) { return *(const h8*)(arow + pp * 16); };
+    // A fragment of piece pp for this lane in tile t (rows i >= 2M repeat
+    // row 2M-1)
+    int i_lane[NT];
+    const char* arow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        i_lane[t] = min(16 * t + jrow, 2 * M - 1);
+        arow[t] = lds + ly.frag + fslot(kst, i_lane[t], 0) * 16;
+    }
+    auto afrag = [&](int t, int pp) { return *(const h8*)(arow[t] + pp * 16); };
 
     // Q4_0: write the tile-step to this wave's LDS copy and read back, per
     // block pair k (36 bytes, words 0..8 at word 9k of row jrow): words
@@ -523,7 +734,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         __asm__ volatile("" ::: "memory");
     };
 
-    auto compute = [&](const WR& w, int st, float2& y) {
+    // step st of the row (for the masks of a partial last step), staged at
+    // local step stl (its fragments and sums)
+    auto compute = [&](const WR& w, int st, int stl, float2 (&y)[NT]) {
         if constexpr (FMT == kFmtQ4K) {
             // Lane group c holds, of half h (h = 0, 1), the 16 bytes
             // 16(c&1) .. of chunk g = 2h + c/2: low nibbles of sub-block
@@ -554,8 +767,13 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, a) *
                                                         __builtin_bit_cast(h2v, b));
             };
-            f4 acc0 = (f4)(0.f), acc1 = (f4)(0.f);
-            const int pbase = st * 32 + 8 * (int)qq + 2 * (c & 1);
+            f4 acc0[NT], acc1[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc0[t] = (f4)(0.f);
+                acc1[t] = (f4)(0.f);
+            }
+            const int pbase = stl * 32 + 8 * (int)qq + 2 * (c & 1);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
@@ -571,34 +789,45 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                                         pmul(d1 & 0x00F000F0u, scp[hh][1]),
                                         pmul(d18 & 0x00F000F0u, scp[hh][1])};
                     const int pp = pbase + 16 * hh + sidx;
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        afrag(pp), __builtin_bit_cast(h8, blo), acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        afrag(pp + 4), __builtin_bit_cast(h8, bhi), acc1, 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            afrag(t, pp), __builtin_bit_cast(h8, blo), acc0[t], 0, 0, 0);
+                        acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            afrag(t, pp + 4), __builtin_bit_cast(h8, bhi), acc1[t], 0, 0, 0);
+                    }
                 }
             }
             uint32_t scq, mp;
             q4k_scale_pairs(h1, h2, h3, q4k_sel(c), scq, mp);
             (void)scq;
-            const uint32_t am =
-                *(const uint32_t*)(lds + ly.aux + ((st * 4 + c) * 2 * M + i_lane) * 4);
-            const u32x4m amin = {am, 0u, 0u, 0u};
             const u32x4m bmin = {mp, 0u, 0u, 0u};
-            const f4 Dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(h8, amin), __builtin_bit_cast(h8, bmin), (f4)(0.f), 0, 0, 0);
             const float d = h_lo(w.v[0]), dmin32 = h_hi(w.v[0]) * 32.0f;
-            f4 t;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = __builtin_fmaf(-dmin32, Dm[r], d * (acc0[r] + acc1[r]));
-            y.x += t[0] + t[1];
-            y.y += t[2] + t[3];
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t am =
+                    *(const uint32_t*)(lds + ly.aux + ((stl * 4 + c) * 2 * M + i_lane[t]) * 4);
+                const u32x4m amin = {am, 0u, 0u, 0u};
+                const f4 Dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(h8, amin), __builtin_bit_cast(h8, bmin), (f4)(0.f), 0, 0,
+                    0);
+                f4 tt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tt[r] = __builtin_fmaf(-dmin32, Dm[r], d * (acc0[t][r] + acc1[t][r]));
+                y[t].x += tt[0] + tt[1];
+                y[t].y += tt[2] + tt[3];
+            }
         } else {
             WQ q;
             gather(w, st, q);
             const uint32_t hsel = (uint32_t)(c & 1);
             const uint32_t mask = c >= 2 ? 0x00F000F0u : 0x000F000Fu;
             constexpr int MP = sums_stride(M);
-            const float* xsum = (const float*)(lds + ly.aux) + min(2 * c, MP - 2);
+            const float* xsum[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                xsum[t] = (const float*)(lds + ly.aux) + min(8 * t + 2 * c, MP - 2);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t a0 = q.v[k][0], a1 = q.v[k][1], a2 = q.v[k][2];
@@ -612,18 +841,26 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 const float dB = blk0 + 1 < nblk ? h_hi(hsel ? a2 : z) : 0.f;
                 const u32x4m ba = {qa0 & mask, (qa0 >> 8) & mask, qa1 & mask, (qa1 >> 8) & mask};
                 const u32x4m bb = {b0 & mask, (b0 >> 8) & mask, b1 & mask, (b1 >> 8) & mask};
-                const int blk = blk0;
-                const f4 DA = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    afrag(blk * 4 + c), __builtin_bit_cast(h8, ba), (f4)(0.f), 0, 0, 0);
-                const f4 DB = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    afrag(blk * 4 + 4 + c), __builtin_bit_cast(h8, bb), (f4)(0.f), 0, 0, 0);
-                const float2 XA = *(const float2*)(xsum + blk * MP);
-                const float2 XB = *(const float2*)(xsum + (blk + 1) * MP);
-                // d (D - 8 X 2^-24): X holds sums of x 2^e, D carries 2^(e-24)
-                y.x = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.x, DA[0] + DA[1]), y.x);
-                y.y = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.y, DA[2] + DA[3]), y.y);
-                y.x = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.x, DB[0] + DB[1]), y.x);
-                y.y = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.y, DB[2] + DB[3]), y.y);
+                const int blk = stl * 8 + 2 * k;  // local block index of block A
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const f4 DA = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        afrag(t, blk * 4 + c), __builtin_bit_cast(h8, ba), (f4)(0.f), 0, 0, 0);
+                    const f4 DB = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        afrag(t, blk * 4 + 4 + c), __builtin_bit_cast(h8, bb), (f4)(0.f), 0, 0,
+                        0);
+                    const float2 XA = *(const float2*)(xsum[t] + blk * MP);
+                    const float2 XB = *(const float2*)(xsum[t] + (blk + 1) * MP);
+                    // d (D - 8 X 2^-24): X holds sums of x 2^e, D carries 2^(e-24)
+                    y[t].x = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.x, DA[0] + DA[1]),
+                                            y[t].x);
+                    y[t].y = __builtin_fmaf(dA, __builtin_fmaf(-0x1p-21f, XA.y, DA[2] + DA[3]),
+                                            y[t].y);
+                    y[t].x = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.x, DB[0] + DB[1]),
+                                            y[t].x);
+                    y[t].y = __builtin_fmaf(dB, __builtin_fmaf(-0x1p-21f, XB.y, DB[2] + DB[3]),
+                                            y[t].y);
+                }
             }
         }
     };
@@ -660,10 +897,11 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     };
 
     // End of round r: add the KS partial sums of the group's tile and write.
-    auto finish = [&](int r, float2 y, uint32_t cks, int buf) {
-        float2* part = (float2*)(lds + ly.part) + buf * kMWaves * 64;
-        if constexpr (PURE) y.x = __builtin_bit_cast(float, cks);
-        part[wave * 64 + lane] = y;
+    auto finish = [&](int r, float2 (&y)[NT], uint32_t cks, int buf) {
+        float2* part = (float2*)(lds + ly.part) + buf * kMWaves * 64 * NT;
+        if constexpr (PURE) y[0].x = __builtin_bit_cast(float, cks);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) part[(wave * 64 + lane) * NT + t] = y[t];
         __syncthreads();
         const int t = (r * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
         if (sl == 0 && t < ntiles) {
@@ -673,7 +911,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             if constexpr (PURE) {
                 uint32_t tot = cks;
                 for (int k = 1; k < KS; ++k)
-                    tot += __builtin_bit_cast(uint32_t, part[(wave + k) * 64 + lane].x);
+                    tot += __builtin_bit_cast(uint32_t, part[((wave + k) * 64 + lane) * NT].x);
                 tot += __shfl_xor(tot, 16, kWave);
                 tot += __shfl_xor(tot, 32, kWave);
                 if (c == 0 && row < p.N) {
@@ -691,45 +929,49 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                     }
                 }
             } else {
-                float2 tot = y;
-                for (int k = 1; k < KS; ++k) {
-                    const float2 o = part[(wave + k) * 64 + lane];
-                    tot.x += o.x;
-                    tot.y += o.y;
-                }
                 const int* ex = (const int*)(lds + ly.exps);
-                if constexpr (kPair) {
-                    // columns j and j + 8 hold row row0 + j of gate and of up
-                    const float ux = __shfl_xor(tot.x, 8, kWave);
-                    const float uy = __shfl_xor(tot.y, 8, kWave);
-                    const int prow = T.row0 + (jrow & 7);
-                    if (jrow < 8 && prow < p.N) {
 #pragma unroll
-                        for (int hm = 0; hm < 2; ++hm) {
-                            const int m = 2 * c + hm;
-                            if (m < M) {
-                                const int sm = 24 - ex[m];
-                                const float g = __builtin_ldexpf(hm ? tot.y : tot.x, sm);
-                                const float u = __builtin_ldexpf(hm ? uy : ux, sm);
-                                p.y0[(long long)m * p.N + prow] = silu_mul(g, u);
+                for (int t = 0; t < NT; ++t) {
+                    float2 tot = y[t];
+                    for (int k = 1; k < KS; ++k) {
+                        const float2 o = part[((wave + k) * 64 + lane) * NT + t];
+                        tot.x += o.x;
+                        tot.y += o.y;
+                    }
+                    if constexpr (kPair) {
+                        // columns j and j + 8 hold row row0 + j of gate and of up
+                        const float ux = __shfl_xor(tot.x, 8, kWave);
+                        const float uy = __shfl_xor(tot.y, 8, kWave);
+                        const int prow = T.row0 + (jrow & 7);
+                        if (jrow < 8 && prow < p.N) {
+#pragma unroll
+                            for (int hm = 0; hm < 2; ++hm) {
+                                const int m = 8 * t + 2 * c + hm;
+                                if (m < M) {
+                                    const int sm = 24 - ex[m];
+                                    const float g = __builtin_ldexpf(hm ? tot.y : tot.x, sm);
+                                    const float u = __builtin_ldexpf(hm ? uy : ux, sm);
+                                    p.y0[(long long)m * p.N + prow] = silu_mul(g, u);
+                                }
                             }
                         }
+                        continue;
                     }
-                    return;
-                }
-                float* yo = mt ? p.y1 : p.y0;
-                if (row < p.N) {
+                    float* yo = mt ? p.y1 : p.y0;
+                    if (row < p.N) {
 #pragma unroll
-                    for (int hm = 0; hm < 2; ++hm) {
-                        const int m = 2 * c + hm;
-                        if (m < M) {
-                            const float v = __builtin_ldexpf(hm ? tot.y : tot.x, 24 - ex[m]);
-                            if constexpr (kMoe) {
-                                // output [token, slot, row], if token m chose this expert
-                                const int sl2 = moe.uslot[T.u][m];
-                                if (sl2 >= 0) yo[((long long)m * p.top_k + sl2) * p.N + row] = v;
-                            } else {
-                                yo[(long long)m * p.N + row] = v;
+                        for (int hm = 0; hm < 2; ++hm) {
+                            const int m = 8 * t + 2 * c + hm;
+                            if (m < M) {
+                                const float v = __builtin_ldexpf(hm ? tot.y : tot.x, 24 - ex[m]);
+                                if constexpr (kMoe) {
+                                    // output [token, slot, row], if token m chose this expert
+                                    const int sl2 = moe.uslot[T.u][m];
+                                    if (sl2 >= 0)
+                                        yo[((long long)m * p.top_k + sl2) * p.N + row] = v;
+                                } else {
+                                    yo[(long long)m * p.N + row] = v;
+                                }
                             }
                         }
                     }
@@ -738,6 +980,49 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         }
     };
 
+    if constexpr (SLICED) {
+        // ---- K-sliced: per round, the slices one after another; in each,
+        // the wave computes its sub-range (the first step's loads issued
+        // ahead of the staging).  Every wave meets the same barriers: two
+        // per slice (none for a pure read) and finish()'s one per round. ----
+        const MSlice sc{S, KS, p.npg, p.nsl, p.msl};
+        if constexpr (!PURE) mstage_factors<M, mode_norm(MODE) ? kModeNorm : kModeDense>(p, lds, ly, red);
+        int buf = 0;
+        for (int r = 0; r < nrounds; ++r) {
+            float2 y[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) y[t] = make_float2(0.f, 0.f);
+            uint32_t cks = 0;
+            for (int s = 0; s < sc.nslices(); ++s) {
+                int a, b, reg;
+                sc.range(sl, s, a, b, reg);
+                const int lbase = reg * sc.msl - a;  // local step of step st: st + lbase
+                WR wa, wb;
+                if (a < b) load(r, a, wa);
+                if constexpr (!PURE) {
+                    sync_lds();  // every wave is done with the previous slice
+                    mstage_slice<FMT, M, mode_norm(MODE) ? kModeNorm : kModeDense>(p, lds, ly,
+                                                                                 sc, s);
+                    sync_lds();
+                }
+                for (int st = a; st < b; st += 2) {
+                    const bool hb = st + 1 < b;
+                    if (hb) load(r, st + 1, wb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (PURE) cks += checksum(wa, st);
+                    else compute(wa, st, st + lbase, y);
+                    if (!hb) break;
+                    if (st + 2 < b) load(r, st + 2, wa);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (PURE) cks += checksum(wb, st + 1);
+                    else compute(wb, st + 1, st + 1 + lbase, y);
+                }
+            }
+            finish(r, y, cks, buf);
+            buf ^= 1;
+        }
+        return;
+    } else {
     // Ring of PD steps in flight.  The wave's steps, round after round, are
     // (r, st0) .. (r, st1 - 1); slot j of the ring is consumed and reloaded
     // in place, PD steps ahead (past the last round the tile index clamps,
@@ -760,7 +1045,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
 
     const int n = nrounds * (st1 - st0);
     int cs = st0, cr = 0, buf = 0;
-    float2 y = make_float2(0.f, 0.f);
+    float2 y[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = make_float2(0.f, 0.f);
     uint32_t cks = 0;
     for (int base = 0; base < n; base += PD) {
 #pragma unroll
@@ -770,7 +1057,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 if constexpr (PURE) {
                     cks += checksum(w[j], cs);
                 } else {
-                    compute(w[j], cs, y);
+                    compute(w[j], cs, cs, y);
                 }
             }
             load(lr, ls, w[j]);
@@ -783,10 +1070,12 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 finish(cr, y, cks, buf);
                 ++cr;
                 buf ^= 1;
-                y = make_float2(0.f, 0.f);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) y[t] = make_float2(0.f, 0.f);
                 cks = 0;
             }
         }
+    }
     }
 }
 

@@ -9,7 +9,7 @@ const char* q4_strerror(int status) {
         case Q4_OK: return "ok";
         case Q4_ERR_NULL: return "a required pointer is NULL";
         case Q4_ERR_SHAPE: return "N, K, E, top_k or M*K outside the supported limits";
-        case Q4_ERR_BATCH: return "batch M outside [1, 8]";
+        case Q4_ERR_BATCH: return "batch M outside [1, 16] (dense calls) or [1, 8] (expert calls, router)";
         case Q4_ERR_ALIGN: return "pointer not aligned (weights and x: 16 bytes; others: 4)";
         case Q4_ERR_ARG: return "invalid argument";
         case Q4_ERR_HIP: return "the HIP runtime refused the launch";

@@ -47,7 +47,8 @@
  *       (random weights of the formats' usual distributions give about 3.9
  *       for Q4_0 and 1.3 for Q4_K; a token concentrated on weights whose
  *       two parts cancel can exceed it);
- *   (2) batched dense calls with M >= 3 (the matrix-core path) carry each
+ *   (2) batched dense calls with M >= 3, and any batch the VALU kernel
+ *       cannot stage whole (the matrix-core path), carry each
  *       x as two f16 parts of x * 2^e, which represents elements down to
  *       2^-38 * max_k |x[m,k]| to 22 bits and smaller ones with an absolute
  *       error up to 2^-39 * max_k |x[m,k]|; the bound holds while
@@ -71,9 +72,14 @@
  *     validation error nothing is launched and a status > 0 is returned.
  *     Q4_ERR_HIP means the launch itself failed; kernel faults surface, as
  *     usual for HIP, on a later synchronization.
- *   - Limits: 1 <= M <= 8 (Q4_ERR_BATCH); K > 0 with K % 32 == 0 for Q4_K
- *     and K % 64 == 0 for Q4_0 (an even block count keeps every Q4_0 row
- *     4-byte aligned), M * ceil(K/64) * 64 <= Q4_MAX_MK, 1 <= N < 2^31
+ *   - Limits: 1 <= M <= Q4_MAX_M for the dense calls, 1 <= M <= 8 for the
+ *     expert calls and the router (Q4_ERR_BATCH); 0 < K <= Q4_MAX_K with
+ *     K % 32 == 0 for Q4_K and K % 64 == 0 for Q4_0 (an even block count
+ *     keeps every Q4_0 row 4-byte aligned); a single token (M = 1) and the
+ *     expert calls: M * ceil(K/64) * 64 <= Q4_MAX_MK (their activations are
+ *     staged whole in LDS); dense batches of M >= 2 have no M * K limit
+ *     (the matrix-core kernel stages K in slices when the rows do not fit
+ *     at once, with the same results bit for bit); 1 <= N < 2^31
  *     (Q4_ERR_SHAPE).  Weight and x
  *     pointers 16-byte aligned, all other pointers 4-byte aligned
  *     (Q4_ERR_ALIGN).  Values out of range are refused, never clamped.
@@ -106,16 +112,20 @@ enum {
     Q4_OK = 0,
     Q4_ERR_NULL = 1,   /* a required pointer is NULL */
     Q4_ERR_SHAPE = 2,  /* N, K, E, top_k or M*K outside the documented limits */
-    Q4_ERR_BATCH = 3,  /* M outside [1, 8] */
+    Q4_ERR_BATCH = 3,  /* M outside [1, 16] (dense calls) or [1, 8] (experts, router) */
     Q4_ERR_ALIGN = 4,  /* a pointer is not aligned as documented */
     Q4_ERR_ARG = 5,    /* another argument is invalid (eps, kernel id) */
     Q4_ERR_HIP = 6     /* the HIP runtime refused the launch */
 };
 
-/* Largest M * K accepted (K rounded up to a multiple of 64): the
- * activations of one call are staged whole in the 160 KB LDS of a compute
- * unit. */
+/* Largest M * K (K rounded up to a multiple of 64) of a call whose
+ * activations are staged whole in the 160 KB LDS of a compute unit: single
+ * tokens and the expert calls. */
 #define Q4_MAX_MK 32768
+
+/* Largest batch M of the dense calls, and largest K of any call. */
+#define Q4_MAX_M 16
+#define Q4_MAX_K (1 << 20)
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* q4_strerror(int status);

@@ -455,3 +455,79 @@ def down_check(N, K, experts, E, npairs_max, cus=256, wgc=4, RR=1):
         assert off % 4 == 0
         n += 1
     return n
+
+
+# ---------------------------------------------------------------------------
+# K-sliced staging of the batched kernel (run_mfma_m() in q4_host.h,
+# MSlice / mstage_slice in q4_mfma.h).
+# ---------------------------------------------------------------------------
+LDS_TOTAL = 160 * 1024
+
+
+def mlayout_steps(fmt, M, steps, pure=False):
+    K = steps * 256
+    ntile = (M + 7) // 8
+    aux = 0 if pure else (K // 8 + 1) * 2 * M * 16
+    aux_bytes = 0 if pure else ((K // 256) * 4 * 2 * M * 4 if fmt == "q4k"
+                                else (K // 32) * sums_stride(M) * 4)
+    exps = aux + aux_bytes
+    part = exps + 128
+    wbuf = part + 2 * 8 * 64 * 8 * ntile
+    return wbuf + (8 * Q40_WAVE_BYTES if fmt == "q4_0" else 0)
+
+
+def slice_plan(fmt, M, N, K, nmat=1, cus=256):
+    """(whole, KS, npg, nsl, msl, budget) as run_mfma_m chooses them."""
+    reserve = 2048 if M > 8 else 1024
+    budget = LDS_TOTAL - reserve
+    S = (K + 255) // 256
+    ntiles = nmat * ((N + 15) // 16)
+    ks = mfma_ks(ntiles, S, cus)
+    whole = M * S * 256 <= 32768 and mlayout_steps(fmt, M, S) <= budget
+    if whole:
+        return True, ks, 1, 1, S, budget
+    kse = ks
+    while kse > S:
+        kse //= 2
+    lmax = -(-S // kse)
+    nsl, msl, npg = 1, lmax, 1
+    while mlayout_steps(fmt, M, -(-kse // npg) * msl) > budget:
+        if msl > 1:
+            nsl += 1
+            msl = -(-lmax // nsl)
+        else:
+            assert npg < kse, "no slice fits"
+            npg *= 2
+    return False, kse, npg, nsl, msl, budget
+
+
+def slice_ranges(S, KS, npg, nsl, sl, slice_):
+    """(a, b, region) of wave position sl in a slice (MSlice::range)."""
+    g, s = divmod(slice_, nsl)
+    p0, p1 = g * KS // npg, (g + 1) * KS // npg
+    if not p0 <= sl < p1:
+        return 0, 0, 0
+    s0 = sl * S // KS
+    L = (sl + 1) * S // KS - s0
+    return s0 + s * L // nsl, s0 + (s + 1) * L // nsl, sl - p0
+
+
+def slice_check(fmt, M, N, K, nmat=1, cus=256):
+    """Every wave position's steps are covered once, in order, across the
+    slices; each sub-range fits its region of msl local steps, and regions
+    stay inside the staged steps; the staged layout fits the LDS budget."""
+    whole, KS, npg, nsl, msl, budget = slice_plan(fmt, M, N, K, nmat, cus)
+    S = (K + 255) // 256
+    if whole:
+        assert mlayout_steps(fmt, M, S) <= budget
+        return whole
+    regions = -(-KS // npg)
+    assert mlayout_steps(fmt, M, regions * msl) <= budget
+    for sl in range(KS):
+        seen = []
+        for sc in range(npg * nsl):
+            a, b, reg = slice_ranges(S, KS, npg, nsl, sl, sc)
+            assert 0 <= b - a <= msl and reg < regions, (sl, sc, a, b, msl)
+            seen += list(range(a, b))
+        assert seen == list(range(sl * S // KS, (sl + 1) * S // KS)), (sl, seen)
+    return whole

@@ -214,3 +214,22 @@ def test_down_lane_groups():
     assert A.choose_lg_waste(22) == 8
     assert A.choose_lg_waste(32) == 32 and A.choose_lg_waste(64) == 64
     assert A.choose_lg_waste(56) == 64 and A.choose_lg_waste(1) == 4
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q4_0"])
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (16, 14336, 4096), (4, 4096, 14336),
+                                   (8, 4096, 14336), (9, 777, 2048), (16, 40, 32768),
+                                   (3, 4096, 65536), (2, 4096, 16448), (12, 300, 3616),
+                                   (16, 1, 256), (5, 513, 1 << 20)])
+def test_slice_plans(fmt, M, N, K):
+    if fmt == "q4_0" and K % 64:
+        pytest.skip("Q4_0 rows take K % 64 == 0")
+    A.slice_check(fmt, M, N, K)
+
+
+def test_slicing_keeps_small_batches_whole():
+    # the workloads' batches stage whole (no change to their kernels)
+    for fmt, M, N, K in (("q4_0", 8, 4096, 4096), ("q4k", 8, 14336, 4096),
+                         ("q4k", 4, 18944, 3584), ("q4_0", 3, 4096, 4096)):
+        assert A.slice_plan(fmt, M, N, K)[0], (fmt, M, N, K)
+    assert not A.slice_plan("q4_0", 16, 4096, 4096)[0]

@@ -64,14 +64,15 @@ def L():
     ((A, None, A, 1, 16, 256, None), NULL),
     ((A, A, None, 1, 16, 256, None), NULL),
     ((A, A, A, 0, 16, 256, None), BATCH),
-    ((A, A, A, 9, 16, 256, None), BATCH),
+    ((A, A, A, 17, 16, 256, None), BATCH),
     ((A, A, A, -1, 16, 256, None), BATCH),
     ((A, A, A, 1, 0, 256, None), SHAPE),
     ((A, A, A, 1, 2 ** 31, 256, None), SHAPE),
     ((A, A, A, 1, 16, 0, None), SHAPE),
     ((A, A, A, 1, 16, 272, None), SHAPE),  # not a multiple of 32
     ((A, A, A, 1, 16, -256, None), SHAPE),
-    ((A, A, A, 2, 16, 32768, None), SHAPE),  # M*K over the LDS limit
+    ((A, A, A, 1, 16, 32832, None), SHAPE),  # one token over the VALU staging limit
+    ((A, A, A, 2, 16, (1 << 20) + 256, None), SHAPE),  # over Q4_MAX_K
     ((A, MIS, A, 1, 16, 256, None), ALIGN),
     ((A, A + 4, A, 1, 16, 256, None), ALIGN),
     ((A, A, A + 8, 1, 16, 256, None), ALIGN),
@@ -95,10 +96,13 @@ def test_k_granularity(q4lib):
         assert L().dequant_q4_0(A, MIS, 16, K, None) == SHAPE, K
     for K in (64, 1408, 14336):
         assert L().q4_0_gemv(A, MIS, A, 1, 16, K, None) == ALIGN, K
-    # the padded staging counts whole 64-column units: M * ceil(K/64) * 64
-    # (3 * 10912 = 32736 fits, but 3 * 10944 does not)
-    assert L().q4k_gemv(A, MIS, A, 3, 16, 10912, None) == SHAPE
-    assert L().q4k_gemv(A, MIS, A, 3, 16, 10880, None) == ALIGN
+    # a single token is staged whole: ceil(K/64) * 64 <= 32768; batches
+    # stage K in slices when needed (no M * K limit)
+    assert L().q4k_gemv(A, MIS, A, 1, 16, 32800, None) == SHAPE
+    assert L().q4k_gemv(A, MIS, A, 1, 16, 32768, None) == ALIGN
+    for M in (2, 3, 16):
+        assert L().q4k_gemv(A, MIS, A, M, 16, 65536, None) == ALIGN, M
+    assert L().q4_0_gemv(A, MIS, A, 16, 16, 14336, None) == ALIGN
 
 
 def test_rmsnorm_validation(q4lib):
@@ -108,7 +112,7 @@ def test_rmsnorm_validation(q4lib):
     assert f(A, A, A, A, -1.0, 1, 16, 256, None) == ARG
     assert f(A, A, A, A, float("nan"), 1, 16, 256, None) == ARG
     assert f(A, A, A, A, float("inf"), 1, 16, 256, None) == ARG
-    assert f(A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, 1e-5, 17, 16, 256, None) == BATCH
 
 
 def test_gate_up_validation(q4lib):
@@ -128,7 +132,7 @@ def test_rmsnorm_gate_up_validation(q4lib):
     assert f(A, A + 2, A, A, A, A, 1e-5, 1, 16, 256, None) == ALIGN
     assert f(A, A, A, A, A, A, -1.0, 1, 16, 256, None) == ARG
     assert f(A, A, A, A, A, A, float("nan"), 1, 16, 256, None) == ARG
-    assert f(A, A, A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, A, A, 1e-5, 17, 16, 256, None) == BATCH
     assert f(A, A, A, A, A, A, 1e-5, 1, 16, 100, None) == SHAPE
 
 
@@ -139,7 +143,7 @@ def test_rmsnorm_gate_up_silu_validation(q4lib):
     assert f(A + 2, A, A, A, A, 1e-5, 1, 16, 256, None) == ALIGN
     assert f(A, A, A, A, A + 4, 1e-5, 1, 16, 256, None) == ALIGN
     assert f(A, A, A, A, A, -1.0, 1, 16, 256, None) == ARG
-    assert f(A, A, A, A, A, 1e-5, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, A, 1e-5, 17, 16, 256, None) == BATCH
     assert f(A, A, A, A, A, 1e-5, 1, 16, 100, None) == SHAPE
 
 
@@ -152,7 +156,7 @@ def test_gate_up_silu_validation(q4lib):
     assert f(A, A + 4, A, A, 1, 16, 256, None) == ALIGN
     assert f(A, A, A, A + 8, 1, 16, 256, None) == ALIGN
     assert f(A, A, A, A, 1, 16, 100, None) == SHAPE
-    assert f(A, A, A, A, 9, 16, 256, None) == BATCH
+    assert f(A, A, A, A, 17, 16, 256, None) == BATCH
     assert f(A, A, A, A, 0, 16, 256, None) == BATCH
 
 
