@@ -66,6 +66,13 @@ class Oracle:
         L.oracle_moe_q4_0_down.argtypes = [_u8p, _f32p, _i32p, _i64, _i64, _i64, _i64, _i64,
                                            _f64p, _f64p, _int]
         L.oracle_moe_q4_0_down.restype = None
+        L.oracle_dequant_q4_0_soa.argtypes = [_u8p, _u8p, _i64, _i64, _f32p]
+        L.oracle_dequant_q4_0_soa.restype = None
+        L.oracle_q4_0_to_soa.argtypes = [_u8p, _i64, _i64, _u8p, _u8p]
+        L.oracle_q4_0_to_soa.restype = None
+        L.oracle_q4_0_soa_gemv.argtypes = [_u8p, _u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p,
+                                           _int]
+        L.oracle_q4_0_soa_gemv.restype = None
         L.oracle_silu_mul.argtypes = [_f64p, _f64p, _i64, _f64p]
         L.oracle_silu_mul.restype = None
         L.oracle_topk_softmax.argtypes = [_f64p, _i64, _i64, _i64, _int, _i32p, _f64p]
@@ -101,6 +108,38 @@ class Oracle:
         out = np.empty((N, K), dtype=np.float32)
         self.L.oracle_dequant_q4k(_p(w, _u8p), N, K, _p(out, _f32p))
         return out
+
+    def dequant_q4_0_soa(self, scales, quants, N: int, K: int) -> np.ndarray:
+        sc = _c(scales, np.uint8)
+        qs = _c(quants, np.uint8)
+        nb = N * (K // 32)
+        assert sc.size == 2 * nb and qs.size == 16 * nb
+        out = np.empty((N, K), dtype=np.float32)
+        self.L.oracle_dequant_q4_0_soa(_p(sc, _u8p), _p(qs, _u8p), N, K, _p(out, _f32p))
+        return out
+
+    def q4_0_to_soa(self, w, N: int, K: int):
+        """(scales uint8 [N, K/32*2], quants uint8 [N, K/32*16]) of Q4_0 rows."""
+        w = _c(w, np.uint8)
+        nb = K // 32
+        assert w.size == N * nb * 18
+        sc = np.empty((N, nb * 2), dtype=np.uint8)
+        qs = np.empty((N, nb * 16), dtype=np.uint8)
+        self.L.oracle_q4_0_to_soa(_p(w, _u8p), N, K, _p(sc, _u8p), _p(qs, _u8p))
+        return sc, qs
+
+    def q4_0_soa_gemv(self, scales, quants, x, N: int, K: int, nthreads: int = 1):
+        """Returns (y, absdot), each float64 [M, N]."""
+        sc = _c(scales, np.uint8)
+        qs = _c(quants, np.uint8)
+        x = _c(np.atleast_2d(x), np.float32)
+        M = x.shape[0]
+        assert x.shape[1] == K
+        y = np.empty((M, N), dtype=np.float64)
+        a = np.empty((M, N), dtype=np.float64)
+        self.L.oracle_q4_0_soa_gemv(_p(sc, _u8p), _p(qs, _u8p), _p(x, _f32p), M, N, K,
+                                    _p(y, _f64p), _p(a, _f64p), int(nthreads))
+        return y, a
 
     def _gemv(self, fname, w, x, N, K, nthreads):
         w = _c(w, np.uint8)

@@ -131,6 +131,41 @@ void oracle_dequant_q4_0(const uint8_t* w, int64_t N, int64_t K, float* out)
                                out + n * K + b * Q4_0_BLOCK_ELEMS);
 }
 
+/* ------------------------------------------------------------------------
+ * Q4_0 in split arrays ([IL] GEMV_F16S: `scales: array<f16>` and `quants:
+ * array<vec4<u32>>`, one f16 scale and one 16-byte vector per block of 32
+ * weights).  Row n holds nb = K/32 blocks: scale of block b at
+ * scales[n*nb + b], its 16 nibble bytes at quants[(n*nb + b)*16 ..]; the
+ * nibbles mean what they mean in an 18-byte block (q4_lo / q4_hi: the low
+ * nibble of byte j is element j, the high nibble element j+16, minus 8).
+ * ---------------------------------------------------------------------- */
+void oracle_dequant_q4_0_soa(const uint8_t* scales, const uint8_t* quants, int64_t N,
+                             int64_t K, float* out)
+{
+    int64_t nb = K / Q4_0_BLOCK_ELEMS;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            double d = f16_value(le16(scales + 2 * (n * nb + b)));
+            const uint8_t* q = quants + 16 * (n * nb + b);
+            float* o = out + n * K + b * Q4_0_BLOCK_ELEMS;
+            for (int j = 0; j < 32; ++j) {
+                int v = j < 16 ? (q[j] & 0x0F) : (q[j - 16] >> 4);
+                o[j] = (float)(d * (double)(v - 8));
+            }
+        }
+}
+
+/* The split-array form of N rows of 18-byte Q4_0 blocks: a byte copy. */
+void oracle_q4_0_to_soa(const uint8_t* w, int64_t N, int64_t K, uint8_t* scales,
+                        uint8_t* quants)
+{
+    int64_t nblk = N * (K / Q4_0_BLOCK_ELEMS);
+    for (int64_t i = 0; i < nblk; ++i) {
+        memcpy(scales + 2 * i, w + Q4_0_BLOCK_BYTES * i, 2);
+        memcpy(quants + 16 * i, w + Q4_0_BLOCK_BYTES * i + 2, 16);
+    }
+}
+
 /* Q4_K rows whose K is not a multiple of 256 ([TG] PHASE 3 sizes a row by
  * ceiling division, (K + 255) / 256 super-blocks, while the format defines
  * whole super-blocks only).  The reading taken here: a row is
@@ -161,8 +196,9 @@ void oracle_dequant_q4k(const uint8_t* w, int64_t N, int64_t K, float* out)
  * product of two floats is exact in double.
  * ---------------------------------------------------------------------- */
 typedef struct {
-    int fmt; /* 0 = Q4_0, 1 = Q4_K */
+    int fmt; /* 0 = Q4_0, 1 = Q4_K, 2 = Q4_0 split arrays (w: scales, w2: quants) */
     const uint8_t* w;
+    const uint8_t* w2;
     const float* x;
     int64_t M, N, K;
     double* y;
@@ -179,8 +215,11 @@ static void* gemv_worker(void* arg)
     for (int64_t n = j->row0; n < j->row1; ++n) {
         if (j->fmt == 0)
             oracle_dequant_q4_0(j->w + n * row_bytes, 1, j->K, row);
-        else
+        else if (j->fmt == 1)
             oracle_dequant_q4k(j->w + n * row_bytes, 1, j->K, row);
+        else
+            oracle_dequant_q4_0_soa(j->w + n * (j->K / Q4_0_BLOCK_ELEMS) * 2,
+                                    j->w2 + n * (j->K / Q4_0_BLOCK_ELEMS) * 16, 1, j->K, row);
         for (int64_t m = 0; m < j->M; ++m) {
             const float* xm = j->x + m * j->K;
             double acc = 0.0, aacc = 0.0;
@@ -197,21 +236,21 @@ static void* gemv_worker(void* arg)
     return NULL;
 }
 
-static void gemv_run(int fmt, const uint8_t* w, const float* x, int64_t M, int64_t N,
-                     int64_t K, double* y, double* absdot, int nthreads)
+static void gemv_run(int fmt, const uint8_t* w, const uint8_t* w2, const float* x, int64_t M,
+                     int64_t N, int64_t K, double* y, double* absdot, int nthreads)
 {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > N) nthreads = (int)N;
     if (nthreads <= 1) {
-        gemv_job j = {fmt, w, x, M, N, K, y, absdot, 0, N};
+        gemv_job j = {fmt, w, w2, x, M, N, K, y, absdot, 0, N};
         gemv_worker(&j);
         return;
     }
     pthread_t tid[256];
     gemv_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
-        gemv_job j = {fmt, w, x, M, N, K, y, absdot,
+        gemv_job j = {fmt, w, w2, x, M, N, K, y, absdot,
                       N * t / nthreads, N * (t + 1) / nthreads};
         jobs[t] = j;
         pthread_create(&tid[t], NULL, gemv_worker, &jobs[t]);
@@ -222,13 +261,20 @@ static void gemv_run(int fmt, const uint8_t* w, const float* x, int64_t M, int64
 void oracle_q4_0_gemv(const uint8_t* w, const float* x, int64_t M, int64_t N, int64_t K,
                       double* y, double* absdot, int nthreads)
 {
-    gemv_run(0, w, x, M, N, K, y, absdot, nthreads);
+    gemv_run(0, w, NULL, x, M, N, K, y, absdot, nthreads);
 }
 
 void oracle_q4k_gemv(const uint8_t* w, const float* x, int64_t M, int64_t N, int64_t K,
                      double* y, double* absdot, int nthreads)
 {
-    gemv_run(1, w, x, M, N, K, y, absdot, nthreads);
+    gemv_run(1, w, NULL, x, M, N, K, y, absdot, nthreads);
+}
+
+void oracle_q4_0_soa_gemv(const uint8_t* scales, const uint8_t* quants, const float* x,
+                          int64_t M, int64_t N, int64_t K, double* y, double* absdot,
+                          int nthreads)
+{
+    gemv_run(2, scales, quants, x, M, N, K, y, absdot, nthreads);
 }
 
 /* ------------------------------------------------------------------------

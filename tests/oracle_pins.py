@@ -583,8 +583,50 @@ def pin_moe_down(o):
             assert np.allclose(y[m, s], want, rtol=1e-12, atol=1e-12), (m, s)
 
 
+def brute_weight_q4_0_soa(scales_row, quants_row, e):
+    """Element e of a split-array Q4_0 row, gathered bit by bit: the scale
+    from the f16 array, the nibble from the block's 16 bytes."""
+    b, j = divmod(e, 32)
+    q = _bits(quants_row, 8 * (16 * b + j % 16) + 4 * (j // 16), 4)
+    return _half(scales_row, 2 * b) * (q - 8)
+
+
+def pin_q4_0_soa(o):
+    """Split arrays ([IL] GEMV_F16S scales / quants): the bit-gathering
+    evaluator with exact rationals (odd block counts too); the repack is the
+    byte split of each 18-byte block (scale bytes, then nibble bytes); the
+    split form of a row decodes to the 18-byte form's values bit for bit,
+    and its GEMV equals numpy's float64 matmul of those values."""
+    rng = synth.make_rng(47)
+    for K in (32, 96, 256):
+        N, M = 3, 2
+        w = synth.q4_0_matrix(rng, N, K)
+        sc, qs = o.q4_0_to_soa(w, N, K)
+        blk = w.reshape(N, K // 32, 18)
+        assert np.array_equal(sc, blk[:, :, 0:2].reshape(N, -1)), K
+        assert np.array_equal(qs, blk[:, :, 2:18].reshape(N, -1)), K
+        deq = o.dequant_q4_0_soa(sc, qs, N, K)
+        assert np.array_equal(deq.view(np.uint32), o.dequant_q4_0(w, N, K).view(np.uint32)), K
+        x = synth.activations(rng, M, K)
+        y, a = o.q4_0_soa_gemv(sc, qs, x, N, K)
+        for n in range(N):
+            wf = [_to_f32(brute_weight_q4_0_soa(sc[n], qs[n], e)) for e in range(K)]
+            assert np.array_equal(np.array(wf, np.float32), deq[n]), (K, n)
+            for m in range(M):
+                exact = sum(Fraction(float(wk)) * Fraction(float(xk)) for wk, xk in zip(wf, x[m]))
+                aex = sum(abs(Fraction(float(wk)) * Fraction(float(xk)))
+                          for wk, xk in zip(wf, x[m]))
+                tol = K * 2.0 ** -52 * float(aex)
+                assert abs(y[m, n] - float(exact)) <= tol, (K, n, m)
+                assert abs(a[m, n] - float(aex)) <= tol, (K, n, m)
+        ref = x.astype(np.float64) @ deq.astype(np.float64).T
+        aref = np.abs(x.astype(np.float64)) @ np.abs(deq.astype(np.float64)).T
+        assert np.all(np.abs(y - ref) <= 1e-12 * aref), K
+
+
 # fast pins first: the mutant test stops at the first failing pin
 ALL_PINS = [pin_q4_0_golden, pin_q4k_golden, pin_checksum, pin_silu, pin_topk_softmax,
             pin_router, pin_gemv_onehot_and_scaling, pin_element_order, pin_identities, pin_q4k_scale_roundtrip, pin_gemv_vs_numpy,
-            pin_rmsnorm, pin_composites, pin_q4k_tail, pin_moe_down, pin_f16_decode,
+            pin_rmsnorm, pin_composites, pin_q4k_tail, pin_moe_down, pin_q4_0_soa,
+            pin_f16_decode,
             pin_bruteforce]

@@ -68,6 +68,13 @@ MUTANTS = {
         "h + p * K, 1, N, K, yp", "h + (p / top_k) * K, 1, N, K, yp"),
     "down ignores the expert id": ("oracle_q4_0_gemv(wd + e * mat_bytes", "oracle_q4_0_gemv(wd"),
     "down invalid id not NaN": ("yp[r] = NAN;", "yp[r] = 0.0;"),
+    "soa offset 8 -> 0": ("(float)(d * (double)(v - 8))", "(float)(d * (double)v)"),
+    "soa high nibble from the next byte": ("(q[j - 16] >> 4)", "(q[j - 15 < 16 ? j - 15 : 15] >> 4)"),
+    "soa scale of the row's first block": ("le16(scales + 2 * (n * nb + b))",
+                                           "le16(scales + 2 * (n * nb))"),
+    "soa repack takes the scale from the nibbles": (
+        "memcpy(scales + 2 * i, w + Q4_0_BLOCK_BYTES * i, 2);",
+        "memcpy(scales + 2 * i, w + Q4_0_BLOCK_BYTES * i + 2, 2);"),
     "silu without g": ("double s = g[i] / (1.0 + exp(-g[i]));",
                        "double s = 1.0 / (1.0 + exp(-g[i]));"),
 }
