@@ -23,6 +23,7 @@ __all__ = [
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv",
     "fused_gate_up_silu_q4k_gemv", "fused_rmsnorm_gate_up_silu_q4k_gemv",
     "moe_q4_gemv", "moe_q4_gemv_silu", "moe_q4_gemv_down", "moe_router_q4_0", "dequant_q4k",
+    "q4_0_gemv_soa", "q4_0_repack_soa",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "Q4_READ_MOE_DOWN", "LIB_PATH", "q4_0_row_bytes",
     "q4k_row_bytes",
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "moe_router_q4_0": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp],
             "moe_q4_gemv": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp],
             "dequant_q4k": [_vp, _vp, _i64, _i64, _vp],
+            "q4_0_gemv_soa": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+            "q4_0_repack_soa": [_vp, _vp, _vp, _i64, _i64, _vp],
             "dequant_q4_0": [_vp, _vp, _i64, _i64, _vp],
             "q4_pure_read": [_vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                              _vp],
@@ -304,6 +307,23 @@ def moe_router_q4_0(ids, weights, w_router, x, M, E, K, top_k, normalize, stream
                                   (x, "x", _sz(M * K, 4), F32))
     _ok(lib().moe_router_q4_0(pi, pw, pr, px, M, E, K, top_k, int(normalize),
                               _stream(stream, dev)), "moe_router_q4_0")
+
+
+def q4_0_repack_soa(scales, quants, w, N, K, stream=None):
+    """Split N rows of 18-byte Q4_0 blocks into f16 scales [N, K/32] and
+    16-byte nibble blocks [N, K/32, 16] (byte copies)."""
+    nb = N * (K // 32)
+    (ps, pq, pw), dev = _ptrs((scales, "scales", 2 * nb, U8), (quants, "quants", 16 * nb, U8),
+                              (w, "w", 18 * nb, U8))
+    _ok(lib().q4_0_repack_soa(ps, pq, pw, N, K, _stream(stream, dev)), "q4_0_repack_soa")
+
+
+def q4_0_gemv_soa(y, scales, quants, x, M, N, K, stream=None):
+    """y[M, N] = X . W^T over split-array Q4_0 (scales, quants)."""
+    nb = N * (K // 32)
+    (py, ps, pq, px), dev = _ptrs((y, "y", _sz(M * N, 4), F32), (scales, "scales", 2 * nb, U8),
+                                  (quants, "quants", 16 * nb, U8), (x, "x", _sz(M * K, 4), F32))
+    _ok(lib().q4_0_gemv_soa(py, ps, pq, px, M, N, K, _stream(stream, dev)), "q4_0_gemv_soa")
 
 
 def dequant_q4k(out, w, N, K, stream=None):

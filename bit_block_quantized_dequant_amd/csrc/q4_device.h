@@ -35,6 +35,10 @@ namespace q4 {
 constexpr int kWave = 64;
 constexpr int kFmtQ4_0 = 0;
 constexpr int kFmtQ4K = 1;
+// Q4_0 in split arrays (inferencelayer 0.2.13, kernel_lab.rs, GEMV_F16S:
+// `scales: array<f16>`, `quants: array<vec4<u32>>`): an f16 scale per block
+// in one array, the block's 16 nibble bytes in another.
+constexpr int kFmtQ4_0S = 2;
 
 constexpr int kUnitElems = 64;      // weights per lane unit
 constexpr int kQ4KBytes = 144;      // Q4_K super-block
@@ -118,6 +122,21 @@ __device__ __forceinline__ void load_unit_at(const uint8_t* base, uint32_t ho, u
         r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
         r[8] = ldg4(p + 32);
     }
+}
+
+// Split-array Q4_0 unit: blocks A and B's 16 nibble bytes (words 0-3, 4-7;
+// both 16-byte aligned) and their f16 scales (2-byte aligned) packed into
+// word 8 (A low, B high).
+__device__ __forceinline__ void load_unit_soa(const uint8_t* qbase, uint32_t qa, uint32_t qb,
+                                              const uint8_t* sbase, uint32_t sa, uint32_t sb,
+                                              uint32_t (&r)[kUnitWords]) {
+    const u32x4 a = ldg16(qbase + qa);
+    const u32x4 b = ldg16(qbase + qb);
+    const uint32_t da = *(const uint16_t*)__builtin_assume_aligned(sbase + sa, 2);
+    const uint32_t db = *(const uint16_t*)__builtin_assume_aligned(sbase + sb, 2);
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    r[8] = da | (db << 16);
 }
 
 // Unit u of a row: the super-block (Q4_K) or block pair (Q4_0) it lives in.
@@ -241,16 +260,26 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
             }
         }
     } else {
-        // block A = bytes 0..17 (d in w0.lo, nibbles shifted by two bytes),
-        // block B = bytes 18..35 (d in w4.hi, nibbles in w5..w8)
+        // 18-byte blocks: block A = bytes 0..17 (d in w0.lo, nibbles
+        // shifted by two bytes), block B = bytes 18..35 (d in w4.hi,
+        // nibbles in w5..w8).  Split arrays: nibbles in w0..w3 and w4..w7,
+        // scales in w8.
+        constexpr bool kSoa = FMT == kFmtQ4_0S;
         uint32_t qa[NR][4];
         float a0[NR][M], a1[NR][M], b0[NR][M], b1[NR][M];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            qa[r][0] = __builtin_amdgcn_alignbit(w[r][1], w[r][0], 16);
-            qa[r][1] = __builtin_amdgcn_alignbit(w[r][2], w[r][1], 16);
-            qa[r][2] = __builtin_amdgcn_alignbit(w[r][3], w[r][2], 16);
-            qa[r][3] = __builtin_amdgcn_alignbit(w[r][4], w[r][3], 16);
+            if constexpr (kSoa) {
+                qa[r][0] = w[r][0];
+                qa[r][1] = w[r][1];
+                qa[r][2] = w[r][2];
+                qa[r][3] = w[r][3];
+            } else {
+                qa[r][0] = __builtin_amdgcn_alignbit(w[r][1], w[r][0], 16);
+                qa[r][1] = __builtin_amdgcn_alignbit(w[r][2], w[r][1], 16);
+                qa[r][2] = __builtin_amdgcn_alignbit(w[r][3], w[r][2], 16);
+                qa[r][3] = __builtin_amdgcn_alignbit(w[r][4], w[r][3], 16);
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const float2 X8 = xs[m * k64 + u];  // (-8 * X_A, -8 * X_B)
@@ -272,7 +301,7 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
                     if (i < 4)
                         nib_dot(qa[r][i], xlo, xhi, a0[r][m], a1[r][m]);
                     else
-                        nib_dot(w[r][1 + i], xlo, xhi, b0[r][m], b1[r][m]);
+                        nib_dot(w[r][kSoa ? i : 1 + i], xlo, xhi, b0[r][m], b1[r][m]);
                 }
             }
             if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
@@ -281,8 +310,10 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&w)[NR][kUnitWords], in
         for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                float a = __builtin_fmaf(h_lo(w[r][0]), a0[r][m] + a1[r][m], acc[r][m]);
-                a = __builtin_fmaf(h_hi(w[r][4]), b0[r][m] + b1[r][m], a);
+                const float dA = h_lo(w[r][kSoa ? 8 : 0]);
+                const float dB = h_hi(w[r][kSoa ? 8 : 4]);
+                float a = __builtin_fmaf(dA, a0[r][m] + a1[r][m], acc[r][m]);
+                a = __builtin_fmaf(dB, b0[r][m] + b1[r][m], a);
                 acc[r][m] = act ? a : acc[r][m];
             }
     }

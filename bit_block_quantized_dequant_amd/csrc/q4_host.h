@@ -42,9 +42,11 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 // K granularity of a format: a Q4_K row may end inside its last super-block
 // at any multiple of 32 (the rest of that super-block is padding); a Q4_0
 // row must hold an even number of 18-byte blocks, so that every row starts
-// on a 4-byte boundary for the kernels' word loads.
+// on a 4-byte boundary for the kernels' word loads; split-array Q4_0 rows
+// take any whole number of blocks (their nibble blocks are 16-byte aligned
+// and their scales are loaded 16 bits at a time).
 inline bool k_ok(int64_t K, int fmt) {
-    return K > 0 && K <= INT32_MAX && K % (fmt == kFmtQ4K ? 32 : 64) == 0;
+    return K > 0 && K <= INT32_MAX && K % (fmt == kFmtQ4_0 ? 64 : 32) == 0;
 }
 
 // Staged columns of a call: K rounded up to whole 64-weight units.
@@ -65,9 +67,13 @@ inline bool valu_fits(int64_t M, int64_t K) {
     return M <= 8 && M * k_units(K) * kUnitElems <= Q4_MAX_MK;
 }
 
-// Bytes of one weight row: ceil(K/256) super-blocks (Q4_K), K/32 blocks (Q4_0).
+// Bytes of one weight row: ceil(K/256) super-blocks (Q4_K), K/32 blocks
+// (Q4_0), K/32 nibble blocks of 16 bytes (split-array Q4_0; its scales are
+// a second array of K/32 f16 per row).
 inline long long row_bytes_of(int64_t K, int fmt) {
-    return fmt == kFmtQ4K ? (long long)((K + 255) / 256) * kQ4KBytes : (long long)(K / 32) * 18;
+    return fmt == kFmtQ4K    ? (long long)((K + 255) / 256) * kQ4KBytes
+           : fmt == kFmtQ4_0 ? (long long)(K / 32) * 18
+                             : (long long)(K / 32) * 16;
 }
 
 // ---------------------------------------------------------------------------
@@ -443,9 +449,10 @@ inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
                    (long long)M * mpadk(p.K) <= kMaxMK &&
                    mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds;
     } else {
-        use_mfma = M >= 2 && (!vfits || (M >= Q4_MFMA_MIN_M && mfma_enabled()));
+        use_mfma = FMT != kFmtQ4_0S &&
+                   M >= 2 && (!vfits || (M >= Q4_MFMA_MIN_M && mfma_enabled()));
     }
-    if constexpr (MODE != kModeMoeSilu) {
+    if constexpr (MODE != kModeMoeSilu && FMT != kFmtQ4_0S) {
     if (use_mfma) {
         const int nexp = mode_moe(MODE) ? npairs_max : 1;
         switch (M) {

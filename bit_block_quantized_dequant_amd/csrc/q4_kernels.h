@@ -90,6 +90,7 @@ struct GemvParams {
     int top_k;
     int E;
     long long row_bytes;
+    const uint8_t* sc;  // split-array Q4_0: the f16 scales (w0: the nibble blocks)
     int upr;        // units per row = ceil(K / 64) (the last one half used when K % 64 == 32)
     int lg;         // lanes per row group (power of two, <= 64)
     int upl;        // units per lane per row = ceil(upr / lg)
@@ -230,7 +231,7 @@ __device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i
     s = dpp_add(s, 0);
     s = dpp_add(s, 1);
     s = dpp_add(s, 2);
-    if (store && (c & 7) == 7) xsum[m * 2 * p.upr + (c >> 3)] = (FMT == kFmtQ4_0) ? -8.0f * s : s;
+    if (store && (c & 7) == 7) xsum[m * 2 * p.upr + (c >> 3)] = (FMT != kFmtQ4K) ? -8.0f * s : s;
     if constexpr (!DEFER) {
         const float sc = elem_is_high<FMT>(4 * c) ? 0x1p20f : 0x1p24f;
         v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
@@ -528,8 +529,11 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // task's first row) plus a 32-bit per-lane offset (row inside the task,
     // unit inside the row), so that the loads take the scalar-base form.
     auto unit_off = [&](int u) -> uint32_t {
-        return FMT == kFmtQ4K ? (uint32_t)(u >> 2) * kQ4KBytes : (uint32_t)u * kQ4_0PairBytes;
+        return FMT == kFmtQ4K    ? (uint32_t)(u >> 2) * kQ4KBytes
+               : FMT == kFmtQ4_0 ? (uint32_t)u * kQ4_0PairBytes
+                                 : (uint32_t)u * 32u;
     };
+    const int nblk = p.K >> 5;  // split-array Q4_0: blocks per row
     const uint32_t uoff_lane = unit_off(li);
     const uint32_t uoff_last = unit_off(u_last);
     const uint32_t pass_stride = unit_off(p.lg);
@@ -558,10 +562,23 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         for (int r = 0; r < RR; ++r) {
             const uint32_t lr = (uint32_t)min(gi * RR + r + (R0 - R0c), lrow_max);
             const uint32_t ro = lr * rb;
+            if constexpr (FMT == kFmtQ4_0S) {
+                // blocks 2u and 2u + 1 of the row (block B clamped to the
+                // row's last block when K % 64 == 32: its activations are 0)
+                static_assert(NMAT == 1, "split-array Q4_0: single matrix");
+                const int uu = in_row ? u : u_last;
+                const uint32_t bA = 2u * (uint32_t)uu;
+                const uint32_t bB = (uint32_t)min(2 * uu + 1, nblk - 1);
+                const uint32_t srb = 2u * (uint32_t)nblk;
+                const uint8_t* sb = p.sc + (ubase + R0c) * (long long)srb;
+                load_unit_soa(p.w0 + sbase, ro + 16u * bA, ro + 16u * bB, sb, lr * srb + 2u * bA,
+                              lr * srb + 2u * bB, dst[r]);
+            } else {
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                const uint8_t* b = (mt == 0 ? p.w0 : p.w1) + sbase;
-                load_unit_at<FMT>(b, ro + uoff, ro + qoff, dst[mt * RR + r]);
+                for (int mt = 0; mt < NMAT; ++mt) {
+                    const uint8_t* b = (mt == 0 ? p.w0 : p.w1) + sbase;
+                    load_unit_at<FMT>(b, ro + uoff, ro + qoff, dst[mt * RR + r]);
+                }
             }
         }
     };
@@ -962,6 +979,25 @@ __global__ __launch_bounds__(256) void dequant_kernel(float* __restrict__ out,
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Repack of 18-byte Q4_0 blocks into split arrays: one thread per block,
+// nine 16-bit loads (the blocks are 2-byte aligned), one 16-bit and one
+// 16-byte store.
+// ---------------------------------------------------------------------------
+static __global__ __launch_bounds__(256) void repack_q4_0_soa_kernel(
+    uint16_t* __restrict__ scales, u32x4* __restrict__ quants, const uint8_t* __restrict__ w,
+    long long nblocks) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nblocks) return;
+    const uint16_t* b = (const uint16_t*)__builtin_assume_aligned(w + 18 * i, 2);
+    uint32_t h[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) h[k] = b[k];
+    scales[i] = (uint16_t)h[0];
+    quants[i] = u32x4{h[1] | (h[2] << 16), h[3] | (h[4] << 16), h[5] | (h[6] << 16),
+                      h[7] | (h[8] << 16)};
 }
 
 }  // namespace q4

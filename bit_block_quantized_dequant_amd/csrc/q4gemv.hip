@@ -1,4 +1,5 @@
-// q4gemv.hip -- libq4gemv entry points: status text, version, the expert router and the dequantization calls
+// q4gemv.hip -- libq4gemv entry points: status text, version, the expert router, the
+// dequantization calls and the split-array repack
 // (declared in include/q4gemv.h; validation and launch planning in q4_host.h).
 #include "q4_host.h"
 
@@ -67,6 +68,20 @@ int dequant_q4_0(float* out, const void* w, int64_t N, int64_t K, void* stream) 
     hipLaunchKernelGGL(dequant_kernel<kFmtQ4_0>, dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)stream, out, (const uint8_t*)w, nunits, (int)upr, (int)K,
                        row_bytes_of(K, kFmtQ4_0));
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+int q4_0_repack_soa(void* scales, void* quants, const void* w, int64_t N, int64_t K,
+                    void* stream) {
+    if (!scales || !quants || !w) return Q4_ERR_NULL;
+    if (!k_ok(K, kFmtQ4_0S) || K > Q4_MAX_K || N < 1 || N > INT32_MAX) return Q4_ERR_SHAPE;
+    if (!aligned(w, 2) || !aligned(scales, 2) || !aligned(quants, 16)) return Q4_ERR_ALIGN;
+    const long long nblocks = (long long)N * (K / 32);
+    const long long blocks = (nblocks + 255) / 256;
+    if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
+    hipLaunchKernelGGL(repack_q4_0_soa_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, (uint16_t*)scales, (u32x4*)quants,
+                       (const uint8_t*)w, nblocks);
     return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
 }
 

@@ -290,6 +290,28 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
                     void* stream);
 
 /*
+ * Q4_0 in split arrays (inferencelayer 0.2.13, kernel_lab.rs, GEMV_F16S:
+ * `scales: array<f16>`, `quants: array<vec4<u32>>`): row n's block b has
+ * its f16 scale at scales[n * K/32 + b] and its 16 nibble bytes at
+ * quants + (n * K/32 + b) * 16, the nibbles meaning what they mean in an
+ * 18-byte Q4_0 block.  Every nibble block is 16-byte aligned, so K may be
+ * any multiple of 32 (an odd block count too).
+ *
+ * q4_0_repack_soa: the split form of N rows of 18-byte Q4_0 blocks (a byte
+ * copy; scales: N * K/32 * 2 bytes, 2-byte aligned; quants: N * K/32 * 16
+ * bytes, 16-byte aligned; w 2-byte aligned).
+ * q4_0_gemv_soa: y[M, N] = X[M, K] . W^T over the split form, the weights
+ * read once for all M; the results are those of q4_0_gemv on the 18-byte
+ * form within the same bound.  Limits: 1 <= M <= 8 (Q4_ERR_BATCH),
+ * M * ceil(K/64) * 64 <= Q4_MAX_MK (Q4_ERR_SHAPE; the VALU kernel runs
+ * every batch); alignment: quants and x 16 bytes, scales 2, y 4.
+ */
+int q4_0_repack_soa(void* scales, void* quants, const void* w, int64_t N, int64_t K,
+                    void* stream);
+int q4_0_gemv_soa(float* y, const void* scales, const void* quants, const float* x,
+                  int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Dequantize N rows of Q4_K to fp32 out[N, K], bit-exact: every weight is
  * the correctly rounded fp32 value of d*sc*q - dmin*m.
  * (trueno-gpu 0.4.11, fused.rs, FusedRmsNormQ4KGemvKernel PHASE 3.)

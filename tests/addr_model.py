@@ -57,7 +57,7 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
 
 
 def unit_off(fmt, u):
-    return (u >> 2) * Q4K_BYTES if fmt == "q4k" else u * Q40_PAIR
+    return (u >> 2) * Q4K_BYTES if fmt == "q4k" else (u * 32 if fmt == "q4_0s" else u * Q40_PAIR)
 
 
 def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
@@ -114,6 +114,18 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
                     lr = min(gi * RR + r + (R0 - R0c), lrow_max) & U32
                     ro = (lr * rb) & U32
                     sbase = (ubase + R0c) * rb
+                    if fmt == "q4_0s":
+                        # split arrays: nibble blocks 2u and min(2u+1, nb-1)
+                        # (offsets into the quants), and their f16 scales
+                        # (yielded as matrix 1: offsets into the scales)
+                        nb = K // 32
+                        uu = u if in_row else u_last
+                        for blk in (2 * uu, min(2 * uu + 1, nb - 1)):
+                            qo = (ubase + R0c) * nb * 16 + ((lr * nb * 16 + 16 * blk) & U32)
+                            so = (ubase + R0c) * nb * 2 + ((lr * nb * 2 + 2 * blk) & U32)
+                            yield 0, qo, 16
+                            yield 1, so, 2
+                        continue
                     for mt in range(nmat):
                         if fmt == "q4k":
                             yield mt, sbase + ((ro + uoff) & U32), 16
@@ -132,12 +144,18 @@ def loads(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
 
 def check(fmt, M, N, K, RR, nmat, moe_experts=None, E=1, **kw):
     rows_total = (E if moe_experts is not None else 1) * N
-    rb = row_bytes(fmt, K)
-    limit = rows_total * rb
+    if fmt == "q4_0s":
+        limits = [rows_total * (K // 32) * 16, rows_total * (K // 32) * 2]
+        aligns = [16, 2]
+    else:
+        rb = row_bytes(fmt, K)
+        limits, aligns = [rows_total * rb] * 2, [4, 4]
     n = 0
     for mt, off, nb in loads(fmt, M, N, K, RR, nmat, moe_experts, E, **kw):
+        limit = limits[mt] if fmt == "q4_0s" else limits[0]
         assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
-        assert off % 4 == 0, ("word loads need 4-byte alignment", fmt, K, off)
+        a = aligns[mt] if fmt == "q4_0s" else 4
+        assert off % a == 0, ("word loads need %d-byte alignment" % a, fmt, K, off)
         n += 1
     return n
 

@@ -233,3 +233,13 @@ def test_slicing_keeps_small_batches_whole():
                          ("q4k", 4, 18944, 3584), ("q4_0", 3, 4096, 4096)):
         assert A.slice_plan(fmt, M, N, K)[0], (fmt, M, N, K)
     assert not A.slice_plan("q4_0", 16, 4096, 4096)[0]
+
+
+@pytest.mark.parametrize("K", [32, 96, 1408, 2080, 4096])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_soa_loads_in_bounds(M, K):
+    """Split-array Q4_0: nibble blocks 16-byte aligned, scales 2-byte aligned,
+    an odd block count's last unit clamped to the row's last block."""
+    if M * ((K + 63) // 64) * 64 > 32768:
+        pytest.skip("over the staging limit")
+    assert A.check("q4_0s", M, 301, K, RR=2, nmat=1, cus=8) > 0

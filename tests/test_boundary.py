@@ -294,3 +294,20 @@ def test_binding_raises_q4error(q4lib):
     with pytest.raises(q4.Q4Error) as ei:
         q4._ok(L().q4k_gemv(None, A, A, 1, 16, 256, None), "q4k_gemv")
     assert ei.value.status == NULL
+
+
+def test_soa_validation(q4lib):
+    g = L().q4_0_gemv_soa
+    assert g(None, A, A, A, 1, 16, 96, None) == NULL
+    assert g(A, None, A, A, 1, 16, 96, None) == NULL
+    assert g(A, A, A, A, 9, 16, 96, None) == BATCH       # the VALU kernel: M <= 8
+    assert g(A, A, A, A, 1, 16, 48, None) == SHAPE       # K % 32
+    assert g(A, A, A, A, 1, 16, 32800, None) == SHAPE    # staging limit
+    assert g(A, A + 1, A, A, 1, 16, 96, None) == ALIGN   # scales: 2 bytes
+    assert g(A, A, A + 8, A, 1, 16, 96, None) == ALIGN   # quants: 16 bytes
+    assert g(A + 2, A + 2, A, A + 4, 1, 16, 2080, None) == ALIGN  # odd block count passes
+    r = L().q4_0_repack_soa
+    assert r(None, A, A, 16, 96, None) == NULL
+    assert r(A, A, A, 16, 48, None) == SHAPE
+    assert r(A, A + 8, A, 16, 96, None) == ALIGN
+    assert r(A, A, A + 1, 16, 96, None) == ALIGN
