@@ -198,15 +198,24 @@ def check(status, what):
 # ---------------------------------------------------------------------------
 # workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
 # ---------------------------------------------------------------------------
-def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False):
+def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False, soa=False):
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
     from bit_block_quantized_dequant_amd import synth
 
     L = q4.lib()
-    d = synth.down_inputs(M, distinct) if index == 6 else \
-        synth.workload_inputs(index, M=M, distinct=distinct)
+    if index == 6:
+        d = synth.down_inputs(M, distinct)
+    elif index == 7:
+        # the dense down-projection after workload 4's gate+up pair: Q4_K,
+        # 4096 rows x 14336, x ~ N(0, 1), its own seed
+        rng7 = synth.make_rng(synth.SEED_BASE + 7)
+        N7, K7 = synth.DENSE_DOWN["N"], synth.DENSE_DOWN["K"]
+        d = dict(N=N7, K=K7, w=synth.q4k_matrix(rng7, N7, K7),
+                 x=synth.activations(rng7, M, K7))
+    else:
+        d = synth.workload_inputs(index, M=M, distinct=distinct)
     N, K = d["N"], d["K"]
     keep = []
 
@@ -218,7 +227,26 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
     x = T(d["h"] if index == 6 else d["x"])
     notes = {}
     rot = None
-    if index in (1, 2):
+    if index in (1, 2) and soa:
+        # split arrays, one copy = [nibble blocks | f16 scales]
+        sc, qs = synth.q4_0_soa_split(d["w"])
+        qbytes = qs.nbytes
+        rot = Rotation(torch, dev, np.concatenate([qs.reshape(-1), sc.reshape(-1)]))
+        y = torch.empty(M, N, device=dev)
+        cks = torch.empty(N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+
+        def launch(i, stream):
+            p = rot.ptr(i)
+            check(L.q4_0_gemv_soa(y.data_ptr(), p + qbytes, p, x.data_ptr(), M, N, K, stream),
+                  "q4_0_gemv_soa")
+
+        def ceil_launch(i, stream):  # (no mirror of its own: the 18-byte call's addressing)
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4_0_GEMV, rot.ptr(i), None, None,
+                                 M, 0, 0, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+        outs, couts = [y], [cks]
+    elif index in (1, 2):
         rot = Rotation(torch, dev, d["w"])
         y = torch.empty(M, N, device=dev)
         cks = torch.empty(N, dtype=torch.int32, device=dev)
@@ -230,6 +258,20 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
 
         def ceil_launch(i, stream):
             check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4_0_GEMV, rot.ptr(i), None, None,
+                                 M, 0, 0, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+        outs, couts = [y], [cks]
+    elif index == 7:
+        rot = Rotation(torch, dev, d["w"])
+        y = torch.empty(M, N, device=dev)
+        cks = torch.empty(N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+
+        def launch(i, stream):
+            check(L.q4k_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K, stream), "q4k_gemv")
+
+        def ceil_launch(i, stream):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4K_GEMV, rot.ptr(i), None, None,
                                  M, 0, 0, N, K, stream), "q4_pure_read")
         keep += [rot, y, cks]
         outs, couts = [y], [cks]
@@ -356,14 +398,16 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False)
     return wbytes, launch, ceil_launch, notes, keep, outs, couts, (stream_launch, [scks])
 
 
-def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False, norm=False):
+def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False, norm=False,
+            soa=False):
     (wbytes, launch, ceil_launch, notes, keep, outs, couts,
-     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu, norm)
+     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu, norm, soa)
     wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
     cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
     swall, sdurs, scnts = time_launches(torch, stream_launch, warmup, steps, souts)
     st, cst, sst = stats(durs, cnts), stats(cdurs, ccnts), stats(sdurs, scnts)
-    res = dict(index=index, M=M, distinct=distinct, silu=silu, norm=norm, weight_bytes=wbytes,
+    res = dict(index=index, M=M, distinct=distinct, silu=silu, norm=norm, soa=soa,
+               weight_bytes=wbytes,
                wall_s=wall,
                steps=steps,
                value_gbs=wbytes * steps / wall / 1e9,
@@ -655,7 +699,8 @@ def write_report(path, rows, headline, router=None):
     names = {1: "q4_0_gemv K=512 N=256", 2: "q4_0_gemv K=4096 N=4096",
              3: "fused_rmsnorm_q4k_gemv K=3584 N=18944", 4: "fused_gate_up_q4k_gemv K=4096 N=14336x2",
              5: "moe_q4_gemv E=64 top6 N=1408 K=2048",
-             6: "moe_q4_gemv_down E=64 top6 N=2048 K=1408"}
+             6: "moe_q4_gemv_down E=64 top6 N=2048 K=1408",
+             7: "q4k_gemv (dense down-projection) K=14336 N=4096"}
     lines = ["| workload | M | weight MB | kernel us (median) | GB/s (mean dur) | % of 8 TB/s | "
              "ceiling GB/s | % of ceiling | stream GB/s | % of stream | spread |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -666,6 +711,8 @@ def write_report(path, rows, headline, router=None):
                 "moe_q4_gemv", "moe_q4_gemv_silu")
         if r.get("norm"):
             name = name.replace("fused_gate_up", "fused_rmsnorm_gate_up")
+        if r.get("soa"):
+            name = name.replace("q4_0_gemv", "q4_0_gemv_soa")
         if r["index"] in (5, 6):
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
@@ -718,22 +765,25 @@ def main():
     rows = []
     if args.all:
         # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output,
-        #  RMSNorm feeding the pair)
-        for index, Ms, dist, silu, norm in ((1, (1,), 0, 0, 0), (2, (1, 2, 4, 8), 0, 0, 0),
-                                            (3, (1,), 0, 0, 0), (4, (1, 2, 4, 8), 0, 0, 0),
-                                            (4, (1, 4), 0, 1, 0), (4, (1, 4), 0, 0, 1),
-                                            (4, (1, 4), 0, 1, 1),
-                                            (5, (4,), 0, 0, 0), (5, (4,), 1, 0, 0),
-                                            (5, (4,), 0, 1, 0), (6, (4,), 0, 0, 0),
-                                            (6, (1, 8), 0, 0, 0)):
+        #  RMSNorm feeding the pair, split-array Q4_0); 6 is the expert
+        # down-projection, 7 the dense down-projection (4096 x 14336)
+        for index, Ms, dist, silu, norm, soa in (
+                (1, (1,), 0, 0, 0, 0), (2, (1, 2, 4, 8, 16), 0, 0, 0, 0),
+                (2, (1, 2, 4, 8), 0, 0, 0, 1),
+                (3, (1,), 0, 0, 0, 0), (4, (1, 2, 4, 8, 16), 0, 0, 0, 0),
+                (4, (1, 4), 0, 1, 0, 0), (4, (1, 4), 0, 0, 1, 0),
+                (4, (1, 4), 0, 1, 1, 0),
+                (5, (4,), 0, 0, 0, 0), (5, (4,), 1, 0, 0, 0),
+                (5, (4,), 0, 1, 0, 0), (6, (1, 4, 8), 0, 0, 0, 0),
+                (7, (1, 4), 0, 0, 0, 0)):
             for M in Ms:
                 r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu),
-                            bool(norm))
+                            bool(norm), bool(soa))
                 rows.append(r)
-                print("workload %d%s%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
+                print("workload %d%s%s%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
                       "ceiling, %.1f%% of stream)"
                       % (index, " distinct" if dist else "", " silu" if silu else "",
-                         " norm" if norm else "", M,
+                         " norm" if norm else "", " soa" if soa else "", M,
                          r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
                          100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
                          100 * r["frac_of_stream"]), file=sys.stderr, flush=True)

@@ -241,6 +241,9 @@ inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npa
 #ifndef Q4_RR_PAIR
 #define Q4_RR_PAIR 1  // rows per lane per step and matrix, two-matrix calls
 #endif
+#ifndef Q4_RR_MOE
+#define Q4_RR_MOE 1  // rows per lane per step and matrix, expert calls
+#endif
 #ifndef Q4_PREFETCH
 #define Q4_PREFETCH 1  // steps of weight loads in flight ahead of the computed one
 #endif
@@ -257,7 +260,7 @@ inline bool xr_enabled() {
 
 template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
 inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
-    constexpr int RR = NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR;
+    constexpr int RR = mode_moe(MODE) ? Q4_RR_MOE : (NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR);
     // Workgroup shape (measured): single-token and expert calls run 256-thread
     // groups; dense single-token calls at most two per CU (four were 4 %
     // slower), expert calls up to four (their 136 VGPRs allow three: 12
@@ -449,10 +452,9 @@ inline int run(GemvParams& p, int M, int npairs_max, void* stream) {
                    (long long)M * mpadk(p.K) <= kMaxMK &&
                    mlayout(FMT, M, p.K, false).bytes <= 160 * 1024 - kMfmaMoeStaticLds;
     } else {
-        use_mfma = FMT != kFmtQ4_0S &&
-                   M >= 2 && (!vfits || (M >= Q4_MFMA_MIN_M && mfma_enabled()));
+        use_mfma = M >= 2 && (!vfits || (M >= Q4_MFMA_MIN_M && mfma_enabled()));
     }
-    if constexpr (MODE != kModeMoeSilu && FMT != kFmtQ4_0S) {
+    if constexpr (MODE != kModeMoeSilu) {
     if (use_mfma) {
         const int nexp = mode_moe(MODE) ? npairs_max : 1;
         switch (M) {

@@ -115,7 +115,7 @@ __host__ __device__ inline MLayout mlayout_steps(int fmt, int M, int steps, bool
                                              : (K / 32) * sums_stride(M) * 4));
     l.part = l.exps + 128;
     l.wbuf = l.part + 2 * kMWaves * 64 * 8 * mtiles(M);
-    l.bytes = l.wbuf + (fmt == kFmtQ4_0 ? kMWaves * kQ40WaveBytes : 0);
+    l.bytes = l.wbuf + (fmt != kFmtQ4K ? kMWaves * kQ40WaveBytes : 0);
     return l;
 }
 
@@ -280,7 +280,7 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
             *(h8*)(lds + ly.frag + fslot(kp, 2 * m + 1, pp) * 16) = lo;
             if ((pp & 3) == 0) {
                 const int g32 = pp >> 2;  // Q4_0 block / Q4_K sub-block index
-                if constexpr (FMT == kFmtQ4_0) {
+                if constexpr (FMT != kFmtQ4K) {
                     ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
                 } else {
                     // Dmin A operand: group c = J/2 of super-block sb holds
@@ -308,7 +308,7 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         *(h8*)(lds + ly.frag + fslot(kp, 2 * m + 1, pp) * 16) = z;
         if ((pp & 3) == 0) {
             const int g32 = pp >> 2;
-            if constexpr (FMT == kFmtQ4_0) {
+            if constexpr (FMT != kFmtQ4K) {
                 ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = 0.f;
             } else {
                 const int sb = g32 >> 3, J = g32 & 7;
@@ -497,7 +497,7 @@ __device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, con
             *(h8*)(lds + ly.frag + fslot(kst, 2 * m + 1, pl) * 16) = lo;
             if ((pl & 3) == 0) {
                 const int g32 = pl >> 2;  // local block / sub-block index
-                if constexpr (FMT == kFmtQ4_0) {
+                if constexpr (FMT != kFmtQ4K) {
                     ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
                 } else {
                     const int sb = g32 >> 3, J = g32 & 7;
@@ -662,6 +662,24 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
             w.v[0] = h.x; w.v[1] = h.y; w.v[2] = h.z; w.v[3] = h.w;
             w.v[4] = q0.x; w.v[5] = q0.y; w.v[6] = q0.z; w.v[7] = q0.w;
             w.v[8] = q1.x; w.v[9] = q1.y; w.v[10] = q1.z; w.v[11] = q1.w;
+        } else if constexpr (FMT == kFmtQ4_0S) {
+            // split arrays: chunks lane and lane + 64 of the tile-step's 16
+            // rows x 8 nibble blocks (row ch / 8, block ch % 8; blocks past
+            // the row's end re-read its last block, whose scale is masked),
+            // and the same rows' 8 f16 scales each, two per lane
+            const uint32_t nb = (uint32_t)nblk;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int ch = lane + kWave * k;
+                const uint32_t ro = (uint32_t)min(ch >> 3, p.N - 1 - row0);
+                const uint32_t gb = (uint32_t)min(st * 8 + (ch & 7), nblk - 1);
+                const uint32_t qo = idle ? 0u : ro * rb + 16u * gb;
+                const u32x4 v = ldg16(base + qo);
+                w.v[4 * k] = v.x; w.v[4 * k + 1] = v.y; w.v[4 * k + 2] = v.z; w.v[4 * k + 3] = v.w;
+                const uint8_t* sb = p.sc + (T.ebase + row0) * (long long)(2u * nb);
+                const uint32_t so2 = idle ? 0u : ro * 2u * nb + 2u * gb;
+                w.v[8 + k] = *(const uint16_t*)__builtin_assume_aligned(sb + so2, 2);
+            }
         } else {
             // chunks lane, lane + 64, lane + 128 (clamped) of the tile-step:
             // chunk ch is bytes 16 (ch % 9) .. of the step's 144 bytes of
@@ -705,6 +723,34 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     };
     char* wb = lds + ly.wbuf + wave * kQ40WaveBytes;
     auto gather = [&](const WR& w, int st, WQ& q) {
+        if constexpr (FMT == kFmtQ4_0S) {
+            // split arrays: the copy holds the 16 rows' nibble blocks (row r,
+            // block b at 16 (8r + b)), then their scales (at 2048 + 2 (8r + b));
+            // per block pair k this lane reads its 8 bytes of blocks 2k and
+            // 2k + 1 (bytes 8 (c & 1) ..) and the pair's two scales
+            (void)st;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int ch = lane + kWave * k;
+                *(u32x4*)(wb + ch * 16) =
+                    u32x4{w.v[4 * k], w.v[4 * k + 1], w.v[4 * k + 2], w.v[4 * k + 3]};
+                *(uint16_t*)(wb + 2048 + ch * 2) = (uint16_t)w.v[8 + k];
+            }
+            __asm__ volatile("" ::: "memory");
+            const int hh = c & 1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t* pa = (const uint32_t*)(wb + jrow * 128 + 32 * k + 8 * hh);
+                q.v[k][0] = pa[0];
+                q.v[k][1] = pa[1];
+                q.v[k][2] = pa[4];
+                q.v[k][3] = pa[5];
+                q.v[k][4] = *(const uint32_t*)(wb + 2048 + jrow * 16 + 4 * k);
+                q.v[k][5] = 0u;
+            }
+            __asm__ volatile("" ::: "memory");
+            return;
+        }
         const bool part = st == S - 1;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -830,15 +876,30 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                 xsum[t] = (const float*)(lds + ly.aux) + min(8 * t + 2 * c, MP - 2);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint32_t a0 = q.v[k][0], a1 = q.v[k][1], a2 = q.v[k][2];
-                const uint32_t b0 = q.v[k][3], b1 = q.v[k][4], z = q.v[k][5];
-                const uint32_t qa0 = __builtin_amdgcn_alignbit(a1, a0, 16);
-                const uint32_t qa1 = __builtin_amdgcn_alignbit(a2, a1, 16);
+                uint32_t qa0, qa1, b0, b1;
+                float dA, dB;
                 const int blk0 = st * 8 + 2 * k;  // block index of block A in the row
+                if constexpr (FMT == kFmtQ4_0S) {
+                    qa0 = q.v[k][0];
+                    qa1 = q.v[k][1];
+                    b0 = q.v[k][2];
+                    b1 = q.v[k][3];
+                    dA = h_lo(q.v[k][4]);
+                    dB = h_hi(q.v[k][4]);
+                } else {
+                    const uint32_t a0 = q.v[k][0], a1 = q.v[k][1], a2 = q.v[k][2];
+                    const uint32_t z = q.v[k][5];
+                    b0 = q.v[k][3];
+                    b1 = q.v[k][4];
+                    qa0 = __builtin_amdgcn_alignbit(a1, a0, 16);
+                    qa1 = __builtin_amdgcn_alignbit(a2, a1, 16);
+                    dA = h_lo(hsel ? z : a0);
+                    dB = h_hi(hsel ? a2 : z);
+                }
                 // blocks past the row's end (partial last step) hold other
                 // bytes: their scales are masked (their activations are 0)
-                const float dA = blk0 < nblk ? h_lo(hsel ? z : a0) : 0.f;
-                const float dB = blk0 + 1 < nblk ? h_hi(hsel ? a2 : z) : 0.f;
+                dA = blk0 < nblk ? dA : 0.f;
+                dB = blk0 + 1 < nblk ? dB : 0.f;
                 const u32x4m ba = {qa0 & mask, (qa0 >> 8) & mask, qa1 & mask, (qa1 >> 8) & mask};
                 const u32x4m bb = {b0 & mask, (b0 >> 8) & mask, b1 & mask, (b1 >> 8) & mask};
                 const int blk = stl * 8 + 2 * k;  // local block index of block A

@@ -44,8 +44,6 @@ int q4_0_gemv_soa(float* y, const void* scales, const void* quants, const float*
     if (!y || !scales || !quants || !x) return Q4_ERR_NULL;
     int st = check_dims(M, N, K, kFmtQ4_0S);
     if (st) return st;
-    if (M > 8) return Q4_ERR_BATCH;
-    if (!valu_fits(M, K)) return Q4_ERR_SHAPE;
     if (!aligned(quants, 16) || !aligned(scales, 2) || !aligned(x, 16) || !aligned(y, 4))
         return Q4_ERR_ALIGN;
     GemvParams p = base_params(quants, quants, y, y, x, N, K, kFmtQ4_0S);

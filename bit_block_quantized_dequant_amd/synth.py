@@ -101,6 +101,16 @@ def q4k_row_bytes(K: int) -> int:
     return ((K + 255) // 256) * 144
 
 
+def q4_0_soa_split(w: np.ndarray):
+    """The split-array form of 18-byte Q4_0 rows: (f16 scale bytes
+    [rows, K/32*2], nibble bytes [rows, K/32*16]) -- a byte split, no
+    arithmetic."""
+    rows = w.shape[0]
+    blk = np.ascontiguousarray(w).reshape(rows, -1, 18)
+    return (np.ascontiguousarray(blk[:, :, 0:2]).reshape(rows, -1),
+            np.ascontiguousarray(blk[:, :, 2:18]).reshape(rows, -1))
+
+
 def pair_activations(rng, M: int, top_k: int, K: int, sigma: float = 1.0) -> np.ndarray:
     """Inputs of the expert down-projection, fp32 [M, top_k, K]: one row per
     (token, slot) pair."""

@@ -302,9 +302,9 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
  * bytes, 16-byte aligned; w 2-byte aligned).
  * q4_0_gemv_soa: y[M, N] = X[M, K] . W^T over the split form, the weights
  * read once for all M; the results are those of q4_0_gemv on the 18-byte
- * form within the same bound.  Limits: 1 <= M <= 8 (Q4_ERR_BATCH),
- * M * ceil(K/64) * 64 <= Q4_MAX_MK (Q4_ERR_SHAPE; the VALU kernel runs
- * every batch); alignment: quants and x 16 bytes, scales 2, y 4.
+ * form within the same bound (bit for bit at M <= 2, where both run the
+ * VALU kernel).  Limits as q4_0_gemv's, with K % 32 == 0; alignment:
+ * quants and x 16 bytes, scales 2, y 4.
  */
 int q4_0_repack_soa(void* scales, void* quants, const void* w, int64_t N, int64_t K,
                     void* stream);

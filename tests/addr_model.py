@@ -180,7 +180,7 @@ def mlayout(fmt, M, K, pure=False):
     exps = aux + aux_bytes
     part = exps + 64
     wbuf = part + 2 * 8 * 64 * 8
-    nbytes = wbuf + (8 * Q40_WAVE_BYTES if fmt == "q4_0" else 0)
+    nbytes = wbuf + (8 * Q40_WAVE_BYTES if fmt != "q4k" else 0)
     return dict(frag=0, aux=aux, exps=exps, part=part, wbuf=wbuf, bytes=nbytes)
 
 
@@ -262,6 +262,19 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, pair=False):
                         yield mt, base + off, 16
                         yield mt, base + off + co + 16, 16
                         yield mt, base + off + co + 80, 16
+                    elif fmt == "q4_0s":
+                        # split arrays: nibble chunks lane, lane + 64 (row ch // 8,
+                        # block ch % 8, clamped to the row's last block) as
+                        # matrix 0, their f16 scales as matrix 1
+                        nb = K // 32
+                        for k in range(2):
+                            ch = lane + 64 * k
+                            ro = min(ch >> 3, N - 1 - row0)
+                            gb = min(st * 8 + (ch & 7), nb - 1)
+                            qo = 0 if idle else (ro * nb * 16 + 16 * gb) & U32
+                            so = 0 if idle else (ro * nb * 2 + 2 * gb) & U32
+                            yield 0, (ebase + row0) * nb * 16 + qo, 16
+                            yield 1, (ebase + row0) * nb * 2 + so, 2
                     else:
                         # a partial last step clamps its chunk columns to
                         # the row's last 16 bytes
@@ -278,13 +291,18 @@ def mfma_loads(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, pair=False):
 
 def mfma_check(fmt, M, N, K, nmat, cus=256, experts=None, umax=1, E=1, pair=False):
     pl = mfma_plan(fmt, M, K, N, nmat, cus, pair=pair)
-    assert pl["lds"] <= LDS_CAP, (fmt, M, K, pl["lds"])
-    rb = row_bytes(fmt, K)
-    limit = (E if experts is not None else 1) * N * rb
+    assert pl["lds"] <= LDS_CAP or M * K > 32768, (fmt, M, K, pl["lds"])
+    rows = (E if experts is not None else 1) * N
+    if fmt == "q4_0s":
+        limits, aligns = [rows * (K // 32) * 16, rows * (K // 32) * 2], [16, 2]
+    else:
+        limits, aligns = [rows * row_bytes(fmt, K)] * 2, [4, 4]
     n = 0
     for mt, off, nb in mfma_loads(fmt, M, N, K, nmat, cus, experts, umax, pair):
-        assert 0 <= off and off + nb <= limit, (fmt, M, N, K, mt, off, nb, limit)
-        assert off % 4 == 0, ("word loads need 4-byte alignment", fmt, K, off)
+        lim = limits[mt] if fmt == "q4_0s" else limits[0]
+        assert 0 <= off and off + nb <= lim, (fmt, M, N, K, mt, off, nb, lim)
+        a = aligns[mt] if fmt == "q4_0s" else 4
+        assert off % a == 0, ("loads need %d-byte alignment" % a, fmt, K, off)
         n += 1
     return n
 
@@ -491,7 +509,7 @@ def mlayout_steps(fmt, M, steps, pure=False):
     exps = aux + aux_bytes
     part = exps + 128
     wbuf = part + 2 * 8 * 64 * 8 * ntile
-    return wbuf + (8 * Q40_WAVE_BYTES if fmt == "q4_0" else 0)
+    return wbuf + (8 * Q40_WAVE_BYTES if fmt != "q4k" else 0)
 
 
 def slice_plan(fmt, M, N, K, nmat=1, cus=256):

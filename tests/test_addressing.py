@@ -243,3 +243,9 @@ def test_soa_loads_in_bounds(M, K):
     if M * ((K + 63) // 64) * 64 > 32768:
         pytest.skip("over the staging limit")
     assert A.check("q4_0s", M, 301, K, RR=2, nmat=1, cus=8) > 0
+
+
+@pytest.mark.parametrize("K", [32, 96, 1408, 2080, 4096])
+@pytest.mark.parametrize("M", [3, 8])
+def test_soa_batched_loads_in_bounds(M, K):
+    assert A.mfma_check("q4_0s", M, 301, K, 1, cus=8) > 0

@@ -300,7 +300,7 @@ def test_soa_validation(q4lib):
     g = L().q4_0_gemv_soa
     assert g(None, A, A, A, 1, 16, 96, None) == NULL
     assert g(A, None, A, A, 1, 16, 96, None) == NULL
-    assert g(A, A, A, A, 9, 16, 96, None) == BATCH       # the VALU kernel: M <= 8
+    assert g(A, A, A, A, 17, 16, 96, None) == BATCH
     assert g(A, A, A, A, 1, 16, 48, None) == SHAPE       # K % 32
     assert g(A, A, A, A, 1, 16, 32800, None) == SHAPE    # staging limit
     assert g(A, A + 1, A, A, 1, 16, 96, None) == ALIGN   # scales: 2 bytes

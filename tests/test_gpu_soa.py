@@ -3,7 +3,8 @@ against the CPU oracle through the C ABI: the repack is bit-exact against
 the oracle's byte split, and the GEMV is within 1e-4 * sum_k |w x| for odd
 and even block counts and every batch M = 1..8.  At M = 1, 2 both layouts
 run the same VALU arithmetic in the same order, so the split form's result
-equals q4_0_gemv's bit for bit."""
+equals q4_0_gemv's bit for bit; at M >= 3 both run the matrix-core kernel
+with the same K split and step order, so they agree bit for bit too."""
 import numpy as np
 import pytest
 
@@ -34,11 +35,13 @@ def test_repack_bitexact(dev, orc, K):
     assert np.array_equal(host(qs), want_qs.reshape(-1)), K
 
 
-@pytest.mark.parametrize("K", [32, 96, 1408, 2080, 4096])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("K", [32, 96, 1408, 2080, 4096, 14336])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 13, 16])
 def test_soa_gemv(dev, orc, M, K):
+    """M >= 3 on the matrix cores (K-sliced where needed; a partial last
+    step at K = 32, 96, 1408, 2080)."""
     import bit_block_quantized_dequant_amd as q4
-    if M * ((K + 63) // 64) * 64 > 32768:
+    if M == 1 and K > 32768:
         pytest.skip("over the staging limit")
     rng = synth.make_rng(5100 + 10 * K + M)
     N = 301
@@ -51,10 +54,14 @@ def test_soa_gemv(dev, orc, M, K):
     ref, ab = orc.q4_0_soa_gemv(hsc, hqs, x, N, K, NT)
     got = host(y)
     assert_bound(got, ref, ab, "q4_0_gemv_soa M=%d K=%d" % (M, K))
-    if M <= 2 and K % 64 == 0:
+    if M <= 2 and K % 64 == 0 and M * K <= 32768:
         y2 = empty((M, N), dev)
         q4.q4_0_gemv(y2, T(w, dev), T(x, dev), M, N, K)
         assert_bits(got, host(y2), "split arrays vs 18-byte blocks M=%d K=%d" % (M, K))
+    if M >= 3 and K % 64 == 0:
+        y3 = empty((M, N), dev)
+        q4.q4_0_gemv(y3, T(w, dev), T(x, dev), M, N, K)
+        assert_bits(got, host(y3), "split arrays vs 18-byte blocks M=%d K=%d" % (M, K))
 
 
 def test_soa_workload2_shape(dev, orc):
