@@ -517,11 +517,10 @@ __device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, con
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-// Expert call: the in-kernel dedupe and, per unique expert u and token m,
-// the slot s with ids[m][s] = expert u (-1: token m did not choose u).
+// Expert call: the in-kernel dedupe (per unique expert, the (token, slot)
+// pairs that chose it; a token may list one expert in several slots).
 struct MfmaMoe {
     MoeShared d;
-    signed char uslot[kMaxPairs][8];
 };
 struct MfmaNoMoe {};
 
@@ -573,13 +572,6 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     if constexpr (kMoe) {
         moe_dedupe<M>(p, moe.d);
         __syncthreads();
-        if ((int)threadIdx.x < moe.d.nu) {
-            const int u = threadIdx.x;
-            const unsigned long long pairs = moe.d.upairs[u];
-            for (int m = 0; m < 8; ++m) moe.uslot[u][m] = -1;
-            for (int pr = 0; pr < M * p.top_k; ++pr)
-                if ((pairs >> pr) & 1ull) moe.uslot[u][pr / p.top_k] = (signed char)(pr % p.top_k);
-        }
         // outputs of pairs with an invalid id: NaN (or all-ones checksums)
         if (moe.d.invalid) {
             const int P = M * p.top_k;
@@ -1026,10 +1018,15 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                             if (m < M) {
                                 const float v = __builtin_ldexpf(hm ? tot.y : tot.x, 24 - ex[m]);
                                 if constexpr (kMoe) {
-                                    // output [token, slot, row], if token m chose this expert
-                                    const int sl2 = moe.uslot[T.u][m];
-                                    if (sl2 >= 0)
-                                        yo[((long long)m * p.top_k + sl2) * p.N + row] = v;
+                                    // output [token, slot, row] for every slot in which
+                                    // token m chose this expert
+                                    unsigned long long pm = moe.d.upairs[T.u];
+                                    while (pm) {
+                                        const int pr = __builtin_ctzll(pm);
+                                        pm &= pm - 1ull;
+                                        if (pr / p.top_k == m)
+                                            yo[(long long)pr * p.N + row] = v;
+                                    }
                                 } else {
                                     yo[(long long)m * p.N + row] = v;
                                 }

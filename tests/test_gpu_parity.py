@@ -160,6 +160,13 @@ def test_workload5_moe_all_distinct_and_repeats(dev, orc):
     g, u, rg, ru, ag, au = _moe_case(dev, orc, d, same, "shared experts")
     assert_bound(g, rg, ag, "shared gate")
     assert_bound(u, ru, au, "shared up")
+    # a token lists one expert in two slots: both slots are written
+    dup = same.copy()
+    dup[:, 1] = dup[:, 0]
+    dup[2, 4] = dup[2, 5]
+    g, u, rg, ru, ag, au = _moe_case(dev, orc, d, dup, "repeated within a token")
+    assert_bound(g, rg, ag, "repeated gate")
+    assert_bound(u, ru, au, "repeated up")
 
 
 def test_moe_invalid_ids_give_nan(dev, orc):
@@ -562,7 +569,8 @@ def test_graph_replay_matches_eager(dev):
 
 def test_moe_matrix_core_path_in_child_process():
     """The matrix-core expert path (opt-in, Q4GEMV_MOE_MFMA=1; the switch is
-    read once per process) against the oracle, in one child process."""
+    read once per process) against the oracle, in one child process; some
+    tokens list one expert in two slots, and both slots must be written."""
     import subprocess
     import sys
     code = (
@@ -580,6 +588,7 @@ def test_moe_matrix_core_path_in_child_process():
         "    x = synth.activations(rng, M, K)\n"
         "    ids = synth.expert_ids(rng, M, top_k, E)\n"
         "    if seed == 1: ids[1, 0] = -3\n"
+        "    if seed in (0, 2): ids[1, 0] = ids[1, 2]  # one expert in two slots of a token\n"
         "    g = torch.full((M, top_k, N), float('nan'), device=dev)\n"
         "    u = torch.full((M, top_k, N), float('nan'), device=dev)\n"
         "    q4.moe_q4_gemv(g, u, T(wg), T(wu), T(x), T(ids), M, top_k, E, N, K)\n"
