@@ -198,7 +198,8 @@ def check(status, what):
 # ---------------------------------------------------------------------------
 # workloads: each returns (weight bytes per call, launch(i), ceiling launch(i), notes)
 # ---------------------------------------------------------------------------
-def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False, soa=False):
+def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False, soa=False,
+                   splitk=False):
     import numpy as np
 
     import bit_block_quantized_dequant_amd as q4
@@ -246,6 +247,25 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False,
                                  M, 0, 0, N, K, stream), "q4_pure_read")
         keep += [rot, y, cks]
         outs, couts = [y], [cks]
+    elif index in (1, 2) and splitk:
+        rot = Rotation(torch, dev, d["w"])
+        y = torch.empty(M, N, device=dev)
+        cks = torch.empty(N, dtype=torch.int32, device=dev)
+        wbytes = rot.nbytes
+        need = q4.splitk_workspace_bytes(q4.Q4_FORMAT_Q4_0, M, N, K)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        notes = dict(splitk_workspace_bytes=need)
+        keep.append(ws)
+
+        def launch(i, stream):
+            check(L.q4_0_gemv_splitk(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K,
+                                     ws.data_ptr(), need, stream), "q4_0_gemv_splitk")
+
+        def ceil_launch(i, stream):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_Q4_0_GEMV, rot.ptr(i), None, None,
+                                 M, 0, 0, N, K, stream), "q4_pure_read")
+        keep += [rot, y, cks]
+        outs, couts = [y], [cks]
     elif index in (1, 2):
         rot = Rotation(torch, dev, d["w"])
         y = torch.empty(M, N, device=dev)
@@ -266,8 +286,15 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False,
         y = torch.empty(M, N, device=dev)
         cks = torch.empty(N, dtype=torch.int32, device=dev)
         wbytes = rot.nbytes
+        need = q4.splitk_workspace_bytes(q4.Q4_FORMAT_Q4K, M, N, K) if splitk else 0
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        keep.append(ws)
 
         def launch(i, stream):
+            if splitk:
+                check(L.q4k_gemv_splitk(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K,
+                                        ws.data_ptr(), need, stream), "q4k_gemv_splitk")
+                return
             check(L.q4k_gemv(y.data_ptr(), rot.ptr(i), x.data_ptr(), M, N, K, stream), "q4k_gemv")
 
         def ceil_launch(i, stream):
@@ -399,14 +426,15 @@ def setup_workload(torch, dev, index, M, distinct=False, silu=False, norm=False,
 
 
 def measure(torch, dev, index, M, warmup, steps, distinct=False, silu=False, norm=False,
-            soa=False):
+            soa=False, splitk=False):
     (wbytes, launch, ceil_launch, notes, keep, outs, couts,
-     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu, norm, soa)
+     (stream_launch, souts)) = setup_workload(torch, dev, index, M, distinct, silu, norm, soa,
+                                              splitk)
     wall, durs, cnts = time_launches(torch, launch, warmup, steps, outs)
     cwall, cdurs, ccnts = time_launches(torch, ceil_launch, warmup, steps, couts)
     swall, sdurs, scnts = time_launches(torch, stream_launch, warmup, steps, souts)
     st, cst, sst = stats(durs, cnts), stats(cdurs, ccnts), stats(sdurs, scnts)
-    res = dict(index=index, M=M, distinct=distinct, silu=silu, norm=norm, soa=soa,
+    res = dict(index=index, M=M, distinct=distinct, silu=silu, norm=norm, soa=soa, splitk=splitk,
                weight_bytes=wbytes,
                wall_s=wall,
                steps=steps,
@@ -713,6 +741,9 @@ def write_report(path, rows, headline, router=None):
             name = name.replace("fused_gate_up", "fused_rmsnorm_gate_up")
         if r.get("soa"):
             name = name.replace("q4_0_gemv", "q4_0_gemv_soa")
+        if r.get("splitk"):
+            name = name.replace("q4_0_gemv", "q4_0_gemv_splitk").replace("q4k_gemv",
+                                                                        "q4k_gemv_splitk")
         if r["index"] in (5, 6):
             name += " (%s, %d experts)" % ("all distinct" if r["distinct"] else "seeded ids",
                                            r["unique_experts"])
@@ -767,23 +798,25 @@ def main():
         # (workload, batch sizes, all-distinct expert ids, SiLU-gated single output,
         #  RMSNorm feeding the pair, split-array Q4_0); 6 is the expert
         # down-projection, 7 the dense down-projection (4096 x 14336)
-        for index, Ms, dist, silu, norm, soa in (
-                (1, (1,), 0, 0, 0, 0), (2, (1, 2, 4, 8, 16), 0, 0, 0, 0),
-                (2, (1, 2, 4, 8), 0, 0, 0, 1),
-                (3, (1,), 0, 0, 0, 0), (4, (1, 2, 4, 8, 16), 0, 0, 0, 0),
-                (4, (1, 4), 0, 1, 0, 0), (4, (1, 4), 0, 0, 1, 0),
-                (4, (1, 4), 0, 1, 1, 0),
-                (5, (4,), 0, 0, 0, 0), (5, (4,), 1, 0, 0, 0),
-                (5, (4,), 0, 1, 0, 0), (6, (1, 4, 8), 0, 0, 0, 0),
-                (7, (1, 4), 0, 0, 0, 0)):
+        # (index, Ms, all-distinct ids, SiLU, RMSNorm, split arrays, split-K)
+        for index, Ms, dist, silu, norm, soa, sk in (
+                (1, (1,), 0, 0, 0, 0, 0), (2, (1, 2, 4, 8, 16), 0, 0, 0, 0, 0),
+                (2, (4, 8, 16), 0, 0, 0, 0, 1), (2, (1, 2, 4, 8), 0, 0, 0, 1, 0),
+                (3, (1,), 0, 0, 0, 0, 0), (4, (1, 2, 4, 8, 16), 0, 0, 0, 0, 0),
+                (4, (1, 4), 0, 1, 0, 0, 0), (4, (1, 4), 0, 0, 1, 0, 0),
+                (4, (1, 4), 0, 1, 1, 0, 0),
+                (5, (4,), 0, 0, 0, 0, 0), (5, (4,), 1, 0, 0, 0, 0),
+                (5, (4,), 0, 1, 0, 0, 0), (6, (1, 4, 8), 0, 0, 0, 0, 0),
+                (7, (1, 4), 0, 0, 0, 0, 0), (7, (4,), 0, 0, 0, 0, 1)):
             for M in Ms:
                 r = measure(torch, dev, index, M, args.warmup, args.steps, bool(dist), bool(silu),
-                            bool(norm), bool(soa))
+                            bool(norm), bool(soa), bool(sk))
                 rows.append(r)
-                print("workload %d%s%s%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% of "
-                      "ceiling, %.1f%% of stream)"
+                print("workload %d%s%s%s%s%s M=%d: %.2f us, %.0f GB/s (%.1f%% of peak, %.1f%% "
+                      "of ceiling, %.1f%% of stream)"
                       % (index, " distinct" if dist else "", " silu" if silu else "",
-                         " norm" if norm else "", " soa" if soa else "", M,
+                         " norm" if norm else "", " soa" if soa else "",
+                         " splitk" if sk else "", M,
                          r["kernel"]["median_ms"] * 1e3, r["kernel_gbs"],
                          100 * r["frac_of_peak"], 100 * r["frac_of_ceiling"],
                          100 * r["frac_of_stream"]), file=sys.stderr, flush=True)

@@ -23,7 +23,8 @@ __all__ = [
     "fused_rmsnorm_q4k_gemv", "fused_gate_up_q4k_gemv", "fused_rmsnorm_gate_up_q4k_gemv",
     "fused_gate_up_silu_q4k_gemv", "fused_rmsnorm_gate_up_silu_q4k_gemv",
     "moe_q4_gemv", "moe_q4_gemv_silu", "moe_q4_gemv_down", "moe_router_q4_0", "dequant_q4k",
-    "q4_0_gemv_soa", "q4_0_repack_soa",
+    "q4_0_gemv_soa", "q4_0_repack_soa", "q4_0_gemv_splitk", "q4k_gemv_splitk",
+    "splitk_workspace_bytes", "Q4_FORMAT_Q4_0", "Q4_FORMAT_Q4K",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "Q4_READ_MOE_DOWN", "LIB_PATH", "q4_0_row_bytes",
     "q4k_row_bytes",
@@ -39,6 +40,8 @@ Q4_READ_GATE_UP = 2
 Q4_READ_MOE = 3
 Q4_READ_STREAM = 4
 Q4_READ_MOE_DOWN = 5
+Q4_FORMAT_Q4_0 = 0
+Q4_FORMAT_Q4K = 1
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_BATCH", 4: "Q4_ERR_ALIGN",
           5: "Q4_ERR_ARG", 6: "Q4_ERR_HIP"}
@@ -85,6 +88,9 @@ def lib() -> ctypes.CDLL:
             "dequant_q4k": [_vp, _vp, _i64, _i64, _vp],
             "q4_0_gemv_soa": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
             "q4_0_repack_soa": [_vp, _vp, _vp, _i64, _i64, _vp],
+            "q4_splitk_workspace": [ctypes.c_int, _i64, _i64, _i64, _vp],
+            "q4_0_gemv_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
+            "q4k_gemv_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
             "dequant_q4_0": [_vp, _vp, _i64, _i64, _vp],
             "q4_pure_read": [_vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                              _vp],
@@ -324,6 +330,37 @@ def q4_0_gemv_soa(y, scales, quants, x, M, N, K, stream=None):
     (py, ps, pq, px), dev = _ptrs((y, "y", _sz(M * N, 4), F32), (scales, "scales", 2 * nb, U8),
                                   (quants, "quants", 16 * nb, U8), (x, "x", _sz(M * K, 4), F32))
     _ok(lib().q4_0_gemv_soa(py, ps, pq, px, M, N, K, _stream(stream, dev)), "q4_0_gemv_soa")
+
+
+def splitk_workspace_bytes(fmt, M, N, K) -> int:
+    """Workspace bytes the split-K calls need for this shape on the current
+    device (0: the call does not split)."""
+    b = ctypes.c_int64(0)
+    _ok(lib().q4_splitk_workspace(int(fmt), M, N, K, ctypes.byref(b)), "q4_splitk_workspace")
+    return int(b.value)
+
+
+def _splitk(name, fmt, y, w, x, M, N, K, workspace, stream):
+    rb = q4_0_row_bytes(K) if fmt == Q4_FORMAT_Q4_0 else q4k_row_bytes(K)
+    need = splitk_workspace_bytes(fmt, M, N, K)
+    specs = [(y, "y", _sz(M * N, 4), F32), (w, "w", _sz(N, rb), U8), (x, "x", _sz(M * K, 4), F32)]
+    if need:
+        specs.append((workspace, "workspace", need, U8))
+    ptrs, dev = _ptrs(*specs)
+    pws = ptrs[3] if need else None
+    _ok(getattr(lib(), name)(ptrs[0], ptrs[1], ptrs[2], M, N, K, pws, need,
+                             _stream(stream, dev)), name)
+
+
+def q4_0_gemv_splitk(y, w, x, M, N, K, workspace, stream=None):
+    """q4_0_gemv with K split over workgroups (workspace: zero-filled device
+    bytes of at least splitk_workspace_bytes(Q4_FORMAT_Q4_0, M, N, K))."""
+    _splitk("q4_0_gemv_splitk", Q4_FORMAT_Q4_0, y, w, x, M, N, K, workspace, stream)
+
+
+def q4k_gemv_splitk(y, w, x, M, N, K, workspace, stream=None):
+    """q4k_gemv with K split over workgroups (workspace as q4_0_gemv_splitk's)."""
+    _splitk("q4k_gemv_splitk", Q4_FORMAT_Q4K, y, w, x, M, N, K, workspace, stream)
 
 
 def dequant_q4k(out, w, N, K, stream=None):

@@ -352,8 +352,9 @@ inline bool moe_mfma_enabled() {
     return on;
 }
 
-template <int FMT, int NMAT, int MODE, bool PURE, int M, bool SLICED>
+template <int FMT, int NMAT, int MODE, bool PURE, int M, int STG>
 inline int run_mfma_launch(GemvParams& p, int cus, int nexperts, int reserve, void* stream) {
+    constexpr bool SLICED = STG == kStgSliced;
     constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
@@ -368,12 +369,12 @@ inline int run_mfma_launch(GemvParams& p, int cus, int nexperts, int reserve, vo
     if (call_lds > 64 * 1024) {  // the occupancy query needs the raised limit
         static std::atomic<int> big_lds_mirror[kMaxDevices];
         int st = allow_big_lds(
-            (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, SLICED>, big_lds_mirror,
+            (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, STG>, big_lds_mirror,
             reserve);
         if (st) return st;
     }
     const int res = resident_per_cu(
-        (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, SLICED>, kMBlock, call_lds,
+        (const void*)mfma_gemv_kernel<FMT, M, NMAT, MODE, false, PD, STG>, kMBlock, call_lds,
         resident);
     if (wgc > res) wgc = res;
     const long long ntiles_run =
@@ -384,7 +385,7 @@ inline int run_mfma_launch(GemvParams& p, int cus, int nexperts, int reserve, vo
     long long blocks = (long long)cus * wgc;
     const long long need = (ntiles_run + TG - 1) / TG;
     if (blocks > need) blocks = need;
-    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD, SLICED>, p, (int)blocks, lds,
+    return launch(mfma_gemv_kernel<FMT, M, NMAT, MODE, PURE, PD, STG>, p, (int)blocks, lds,
                   stream, big_lds_done, kMBlock, reserve);
 }
 
@@ -406,8 +407,8 @@ inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
     const bool whole = (long long)M * mpadk(p.K) <= kMaxMK &&
                        mlayout(FMT, M, p.K, false).bytes <= budget;
     if (whole || mode_moe(MODE))  // (expert calls are only sent here whole)
-        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, false>(p, cus, nexperts, reserve,
-                                                                stream);
+        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, kStgWhole>(p, cus, nexperts, reserve,
+                                                                    stream);
     if constexpr (mode_moe(MODE)) {
         return Q4_ERR_SHAPE;
     } else {
@@ -430,7 +431,8 @@ inline int run_mfma_m(GemvParams& p, int cus, int nexperts, void* stream) {
         p.nsl = nsl;
         p.msl = msl;
         p.npg = npg;
-        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, true>(p, cus, nexperts, reserve, stream);
+        return run_mfma_launch<FMT, NMAT, MODE, PURE, M, kStgSliced>(p, cus, nexperts, reserve,
+                                                                     stream);
     }
 }
 
@@ -573,6 +575,108 @@ inline int run_down(GemvParams& p, int M, int npairs_max, void* stream) {
         case 6: return run_down_m<6, PURE>(p, cus, npairs_max, stream);
         case 7: return run_down_m<7, PURE>(p, cus, npairs_max, stream);
         case 8: return run_down_m<8, PURE>(p, cus, npairs_max, stream);
+    }
+    return Q4_ERR_BATCH;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K batched GEMV (caller workspace): the partial-sum kernel, then the
+// merge kernel, on the caller's stream.  The plan depends on N, K and the CU
+// count only (not on M), so every batch of one shape splits alike and a
+// token's row does not depend on the batch.
+// ---------------------------------------------------------------------------
+struct SplitKPlan {
+    int kp = 1;       // K parts
+    int msl = 0;      // steps per part (staged at once)
+    int ngroups = 0;  // tile groups (8 tiles of 16 rows)
+    long long part_bytes = 0, exp_bytes = 0, total = 0;
+};
+
+inline long long align256(long long v) { return (v + 255) / 256 * 256; }
+
+inline SplitKPlan splitk_plan(int fmt, int64_t M, int64_t N, int64_t K, int cus) {
+    SplitKPlan pl;
+    const int S = msteps((int)K);
+    const long long ntiles = (N + 15) / 16;
+    pl.ngroups = (int)((ntiles + kMWaves - 1) / kMWaves);
+    static const int forced = env_int("Q4GEMV_SPLITK_KP", 0);
+    // about one workgroup per CU (measured: the batched Q4_0 workload at
+    // M = 4 / 8 / 16 ran 13.9 / 15.4 / 19.0 us with 8 parts, 19.5 / 21.4 /
+    // 25.4 us with 16, 15.2 / 16.5 / 20.9 us with 4)
+    long long kp = forced > 0 ? forced : ((long long)cus + pl.ngroups - 1) / pl.ngroups;
+    if (kp > S) kp = S;
+    if (kp < 1) kp = 1;
+    // the largest batch's staging of one part must fit in LDS
+    for (;;) {
+        const int msl = (int)((S + kp - 1) / kp);
+        if (mlayout_steps(fmt, kMaxM, msl, false).bytes <= 160 * 1024 - kMfmaBigStaticLds ||
+            kp >= S)
+            break;
+        ++kp;
+    }
+    pl.kp = (int)kp;
+    pl.msl = (int)((S + kp - 1) / kp);
+    pl.part_bytes = align256(kp * M * N * 4);
+    pl.exp_bytes = align256(kp * M * 4);
+    pl.total = pl.exp_bytes + pl.part_bytes;
+    return pl;
+}
+
+template <int FMT, int M>
+inline int run_splitk_m(GemvParams& p, const SplitKPlan& pl, int cus, void* stream) {
+    constexpr int PD = FMT == kFmtQ4K ? Q4_MFMA_PD_Q4K : Q4_MFMA_PD_Q4_0;
+    constexpr int reserve = M > 8 ? kMfmaBigStaticLds : kMfmaStaticLds;
+    static std::atomic<int> big_lds_done[kMaxDevices];
+    (void)cus;
+    p.ks = 1;
+    p.kp = pl.kp;
+    p.msl = pl.msl;
+    p.nsl = 1;
+    p.npg = 1;
+    const size_t lds = (size_t)mlayout_steps(FMT, M, pl.msl, false).bytes;
+    const long long blocks = (long long)pl.ngroups * pl.kp;
+    if (blocks > INT32_MAX) return Q4_ERR_SHAPE;
+    int st = launch(mfma_gemv_kernel<FMT, M, 1, kModeDense, false, PD, kStgSplitK>, p,
+                    (int)blocks, lds, stream, big_lds_done, kMBlock, reserve);
+    if (st) return st;
+    const long long outs = (long long)M * p.N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, p.y0, (const float*)p.part, (const int*)p.pexp,
+                       pl.kp, M, p.N);
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ERR_HIP;
+}
+
+// The split-K call: workspace laid out as [exponents | partials].
+template <int FMT>
+inline int run_splitk(GemvParams& p, int M, void* ws, int64_t ws_bytes, void* stream) {
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st) return st;
+    const SplitKPlan pl = splitk_plan(FMT, M, p.N, p.K, cus);
+    // single tokens and pairs run the VALU kernel, and a plan of one part
+    // is the ordinary call: the workspace is not used
+    if (M < Q4_MFMA_MIN_M || pl.kp == 1) return run<FMT, 1, kModeDense, false>(p, M, 0, stream);
+    if (!ws) return Q4_ERR_NULL;
+    if (ws_bytes < pl.total) return Q4_ERR_SHAPE;
+    if (!aligned(ws, 256)) return Q4_ERR_ALIGN;
+    uint8_t* b = (uint8_t*)ws;
+    p.pexp = (int*)b;
+    p.part = (float*)(b + pl.exp_bytes);
+    switch (M) {
+        case 3: return run_splitk_m<FMT, 3>(p, pl, cus, stream);
+        case 4: return run_splitk_m<FMT, 4>(p, pl, cus, stream);
+        case 5: return run_splitk_m<FMT, 5>(p, pl, cus, stream);
+        case 6: return run_splitk_m<FMT, 6>(p, pl, cus, stream);
+        case 7: return run_splitk_m<FMT, 7>(p, pl, cus, stream);
+        case 8: return run_splitk_m<FMT, 8>(p, pl, cus, stream);
+        case 9: return run_splitk_m<FMT, 9>(p, pl, cus, stream);
+        case 10: return run_splitk_m<FMT, 10>(p, pl, cus, stream);
+        case 11: return run_splitk_m<FMT, 11>(p, pl, cus, stream);
+        case 12: return run_splitk_m<FMT, 12>(p, pl, cus, stream);
+        case 13: return run_splitk_m<FMT, 13>(p, pl, cus, stream);
+        case 14: return run_splitk_m<FMT, 14>(p, pl, cus, stream);
+        case 15: return run_splitk_m<FMT, 15>(p, pl, cus, stream);
+        case 16: return run_splitk_m<FMT, 16>(p, pl, cus, stream);
     }
     return Q4_ERR_BATCH;
 }

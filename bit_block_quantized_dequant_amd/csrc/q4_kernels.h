@@ -102,6 +102,9 @@ struct GemvParams {
     int nsl;        // batched kernel: K slices per wave-position group (1: whole rows)
     int msl;        // batched kernel, sliced: staged steps per wave range and slice
     int npg;        // batched kernel, sliced: groups of wave positions staged in turn
+    int kp;         // batched kernel, split-K: K parts (one workgroup per tile group and part)
+    float* part;    // split-K workspace: partial sums [kp][M][N] (scaled by 2^(e-24))
+    int* pexp;      // split-K workspace: each part's token exponents [kp][M]
 };
 
 // Shared state of the expert call after the in-kernel dedupe.

@@ -514,6 +514,64 @@ __device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, con
     }
 }
 
+// Split-K: the exponents of one K part, from its columns [c0, c1) only
+// (max_k |x[m,k]| 2^e_m in [2^14, 2^15) over the part; a part whose
+// columns are all zero gets kNoExp, which the merge ignores).
+constexpr int kNoExp = 1 << 20;
+template <int M, typename Red>
+__device__ __forceinline__ void mstage_part_factors(const GemvParams& p, char* lds,
+                                                    const MLayout& ly, Red& red, int c0, int c1) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ppr = (min(c1, p.K) - c0) >> 3;  // pieces of 8 per token in the part
+    const int np = M * ppr;
+    int* ex = (int*)(lds + ly.exps);
+    float am[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) am[m] = 0.f;
+    for (int i = tid; i < np; i += kMBlock) {
+        const int m = i / ppr;
+        const float4* src = (const float4*)(p.x + (long long)m * p.K + c0 + 8 * (i - m * ppr));
+        const float4 a = src[0], b = src[1];
+        const float t = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                              fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], m == mm ? t : 0.f);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float t = wave_max_nonneg(am[m]);
+        if (lane == kWave - 1) red.am[m][wave] = t;
+    }
+    sync_lds();
+    if (tid < M) {
+        float t = 0.f;
+        for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red.am[tid][w]);
+        ex[tid] = t > 0.f ? xscale_exp(t, 14) : kNoExp;
+    }
+    sync_lds();
+}
+
+// The merge of split-K partial sums: y[m, row] = sum over parts q (in
+// order) of part[q][m][row] brought to the common scale 2^(24 - e*), e* the
+// smallest exponent of the token's parts (the part of largest magnitude);
+// parts with no nonzero column are skipped.
+static __global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    float* __restrict__ y, const float* __restrict__ part, const int* __restrict__ pexp, int kp,
+    int M, int N) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long long)M * N) return;
+    const int m = (int)(i / N), row = (int)(i - (long long)m * N);
+    int emin = kNoExp;
+    for (int q = 0; q < kp; ++q) emin = min(emin, pexp[q * M + m]);
+    float sum = 0.f;
+    for (int q = 0; q < kp; ++q) {
+        const int eq = pexp[q * M + m];
+        const float v = part[((long long)q * M + m) * N + row];
+        sum += eq == kNoExp ? 0.f : __builtin_ldexpf(v, emin - eq);
+    }
+    y[i] = emin == kNoExp ? 0.f : __builtin_ldexpf(sum, 24 - emin);
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
@@ -524,10 +582,21 @@ struct MfmaMoe {
 };
 struct MfmaNoMoe {};
 
-template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD, bool SLICED>
+// Staging of the batched kernel: whole rows, K slices, or (split-K) one K
+// part per workgroup with partial sums merged by the last workgroup to
+// finish its tile group.
+constexpr int kStgWhole = 0;
+constexpr int kStgSliced = 1;
+constexpr int kStgSplitK = 2;
+
+template <int FMT, int M, int NMAT, int MODE, bool PURE, int PD, int STG>
 __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) {
+    constexpr bool SLICED = STG == kStgSliced;
+    constexpr bool SPLITK = STG == kStgSplitK;
     static_assert(M >= 2 && M <= kMaxM, "batched kernel");
-    static_assert(!mode_moe(MODE) || (M <= 8 && !SLICED), "expert call: M <= 8, whole rows");
+    static_assert(!mode_moe(MODE) || (M <= 8 && STG == kStgWhole), "expert call: M <= 8, whole rows");
+    static_assert(!SPLITK || (MODE == kModeDense && NMAT == 1 && !PURE),
+                  "split-K: single-matrix GEMV");
     constexpr int NT = mtiles(M);  // A tiles of 8 tokens
     using St = MStep<FMT>;
     extern __shared__ float4 smem4[];
@@ -548,8 +617,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     // (a wave without steps would skip the end-of-round reduction)
     int KS = p.ks;
     while (KS > S) KS >>= 1;
-    // staged steps: the whole row, or (K-sliced) KS regions of msl steps
-    const int staged_steps = SLICED ? mslice_regions(KS, p.npg) * p.msl : S;
+    // staged steps: the whole row, (K-sliced) KS regions of msl steps, or
+    // (split-K, KS = 1) one part of msl steps
+    const int staged_steps = SLICED ? mslice_regions(KS, p.npg) * p.msl : (SPLITK ? p.msl : S);
     const MLayout ly = mlayout_steps(FMT, M, staged_steps, PURE);
     const int kst = staged_steps * 256;  // staged columns
     const int TG = kMWaves / KS;      // tiles per workgroup and round
@@ -635,8 +705,10 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     // one cache line per instruction) and stay unconditional.
     auto load = [&](int r, int st, WR& w) {
         const int rr = min(r, nrounds - 1);
-        const int traw = (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
-        const bool idle = r >= nrounds || traw >= ntiles;  // wave-uniform
+        // (split-K: workgroup b serves tile group b / kp, one tile per wave)
+        const int traw = SPLITK ? ((int)blockIdx.x / p.kp) * TG + grp
+                                : (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
+        const bool idle = SPLITK ? traw >= ntiles : (r >= nrounds || traw >= ntiles);
         const Tile T = tile_at(min(traw, ntiles - 1));
         const int row0 = T.row0;
         const bool up = kPair ? jrow >= 8 : T.mt != 0;
@@ -1038,7 +1110,53 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         }
     };
 
-    if constexpr (SLICED) {
+    if constexpr (SPLITK) {
+        // ---- split-K: this workgroup's tile group and K part; each wave
+        // one tile (KS = 1) over the part's steps; partial sums in the
+        // part's own scale to the workspace (a second kernel merges them:
+        // the kernel boundary makes every part visible, with no device-scope
+        // fence, which on this part writes back a whole L2) ----
+        const int g = blockIdx.x / p.kp, kp = blockIdx.x - g * p.kp;
+        const MSlice sc{S, 1, 1, p.kp, p.msl};
+        int a, b, reg;
+        sc.range(0, kp, a, b, reg);
+        WR wa, wb;
+        if (a < b) load(0, a, wa);
+        mstage_part_factors<M>(p, lds, ly, red, a * 256, b * 256);
+        mstage_slice<FMT, M, kModeDense>(p, lds, ly, sc, kp);
+        sync_lds();
+        float2 y[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) y[t] = make_float2(0.f, 0.f);
+        for (int st = a; st < b; st += 2) {
+            const bool hb = st + 1 < b;
+            if (hb) load(0, st + 1, wb);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wa, st, st - a, y);
+            if (!hb) break;
+            if (st + 2 < b) load(0, st + 2, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wb, st + 1, st + 1 - a, y);
+        }
+        // partial sums of this wave's tile (lane group c: tokens 8t + 2c + hm)
+        const int t_wave = g * TG + grp;
+        const int* ex = (const int*)(lds + ly.exps);
+        if (t_wave < ntiles) {
+            const int row = (t_wave << 4) + jrow;
+            if (row < p.N) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int hm = 0; hm < 2; ++hm) {
+                        const int m = 8 * t + 2 * c + hm;
+                        if (m < M)
+                            p.part[((long long)kp * M + m) * p.N + row] = hm ? y[t].y : y[t].x;
+                    }
+            }
+        }
+        if ((int)threadIdx.x < M) p.pexp[kp * M + threadIdx.x] = ex[threadIdx.x];
+        return;  // (splitk_reduce_kernel, launched next on the stream, merges the parts)
+    } else if constexpr (SLICED) {
         // ---- K-sliced: per round, the slices one after another; in each,
         // the wave computes its sub-range (the first step's loads issued
         // ahead of the staging).  Every wave meets the same barriers: two

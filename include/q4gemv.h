@@ -290,6 +290,39 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
                     void* stream);
 
 /*
+ * Split-K batched GEMV with a caller workspace: y[M, N] = X[M, K] . W^T,
+ * as q4_0_gemv / q4k_gemv, for batches whose activations cost more to stage
+ * in every workgroup than the weights they meet there (few output rows, long
+ * K).  A workgroup serves 8 tiles of 16 rows and one of kp parts of K: it
+ * stages only that part of X, scaled per token by a power of two of its
+ * own, and writes its partial sums to the workspace; a second kernel on the
+ * same stream adds the kp partials in a fixed order, each brought to a
+ * common scale, and writes y.  kp depends on N, K and the device only, so a
+ * token's row does not depend on the batch.  Same bound as the two calls.
+ *   q4_splitk_workspace: *bytes = the workspace these calls need for this
+ *     shape on the current device (0 if the call would not split: M <= 2,
+ *     which runs the VALU kernel, or a plan of one part, which runs the
+ *     ordinary call).  format: Q4_FORMAT_Q4_0 or Q4_FORMAT_Q4K (Q4_ERR_ARG).
+ *   workspace: device memory of at least that many bytes, 256-byte aligned,
+ *     any content (it holds nothing between calls); calls that share a
+ *     workspace must not overlap.  A smaller workspace: Q4_ERR_SHAPE; NULL
+ *     where one is needed: Q4_ERR_NULL.  Other limits and alignment as
+ *     q4_0_gemv / q4k_gemv.
+ * It pays where staging dominates: 16 tokens, or long K (on MI355X, 4 x
+ * 14336 against 4096 rows: 19 against 30 us; 16 x 4096 against 4096 rows:
+ * 19 against 31 us); at 4 or 8 tokens of K = 4096 the ordinary call is
+ * faster.  (The pages' kernels stage x once per workgroup; splitting K over
+ * workgroups is this library's answer to the staging cost of batches on a
+ * 256-CU part.)
+ */
+enum { Q4_FORMAT_Q4_0 = 0, Q4_FORMAT_Q4K = 1 };
+int q4_splitk_workspace(int format, int64_t M, int64_t N, int64_t K, int64_t* bytes);
+int q4_0_gemv_splitk(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+int q4k_gemv_splitk(float* y, const void* w, const float* x, int64_t M, int64_t N, int64_t K,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Q4_0 in split arrays (inferencelayer 0.2.13, kernel_lab.rs, GEMV_F16S:
  * `scales: array<f16>`, `quants: array<vec4<u32>>`): row n's block b has
  * its f16 scale at scales[n * K/32 + b] and its 16 nibble bytes at

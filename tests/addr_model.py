@@ -567,3 +567,49 @@ def slice_check(fmt, M, N, K, nmat=1, cus=256):
             seen += list(range(a, b))
         assert seen == list(range(sl * S // KS, (sl + 1) * S // KS)), (sl, seen)
     return whole
+
+
+# ---------------------------------------------------------------------------
+# Split-K batched GEMV (splitk_plan() in q4_host.h, the kStgSplitK path of
+# q4_mfma.h): workgroup b serves tile group b // kp and K part b % kp.
+# ---------------------------------------------------------------------------
+def splitk_plan(fmt, M, N, K, cus=256):
+    S = (K + 255) // 256
+    ntiles = (N + 15) // 16
+    ngroups = -(-ntiles // 8)
+    kp = min(S, max(1, -(-cus // ngroups)))
+    while True:
+        msl = -(-S // kp)
+        if mlayout_steps(fmt, 16, msl) <= LDS_TOTAL - 2048 or kp >= S:
+            break
+        kp += 1
+    msl = -(-S // kp)
+    return dict(kp=kp, msl=msl, ngroups=ngroups, S=S)
+
+
+def splitk_check(fmt, M, N, K, cus=256):
+    """Parts cover every step once; a part fits its staged steps and LDS;
+    every partial and exponent index is inside its region; the plan does
+    not depend on M."""
+    pl = splitk_plan(fmt, M, N, K, cus)
+    for M2 in (3, 8, 16):
+        assert splitk_plan(fmt, M2, N, K, cus) == pl
+    S, kp, msl, G = pl["S"], pl["kp"], pl["msl"], pl["ngroups"]
+    assert mlayout_steps(fmt, M, msl) <= LDS_TOTAL - (2048 if M > 8 else 1024)
+    steps = []
+    for q in range(kp):
+        a, b, _ = slice_ranges(S, 1, 1, kp, 0, q)
+        assert b - a <= msl
+        steps += list(range(a, b))
+    assert steps == list(range(S))
+    for b in range(G * kp):
+        g, q = divmod(b, kp)
+        assert g < G
+        for grp in range(8):
+            t = g * 8 + grp
+            for jrow in range(16):
+                row = t * 16 + jrow
+                if t < (N + 15) // 16 and row < N:
+                    for m in range(M):
+                        assert 0 <= (q * M + m) * N + row < kp * M * N
+    return pl

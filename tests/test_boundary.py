@@ -311,3 +311,16 @@ def test_soa_validation(q4lib):
     assert r(A, A, A, 16, 48, None) == SHAPE
     assert r(A, A + 8, A, 16, 96, None) == ALIGN
     assert r(A, A, A + 1, 16, 96, None) == ALIGN
+
+
+def test_splitk_validation(q4lib):
+    b = ctypes.c_int64(0)
+    assert L().q4_splitk_workspace(7, 8, 16, 256, ctypes.byref(b)) == ARG
+    assert L().q4_splitk_workspace(0, 17, 16, 256, ctypes.byref(b)) == BATCH
+    assert L().q4_splitk_workspace(0, 8, 16, 96, ctypes.byref(b)) == SHAPE
+    assert L().q4_splitk_workspace(0, 8, 16, 256, None) == NULL
+    f = L().q4_0_gemv_splitk
+    assert f(None, A, A, 8, 16, 256, A, 1 << 20, None) == NULL
+    assert f(A, A, A, 17, 16, 256, A, 1 << 20, None) == BATCH
+    assert f(A, MIS, A, 8, 16, 256, A, 1 << 20, None) == ALIGN
+    assert L().q4k_gemv_splitk(A, A, A, 8, 16, 48, A, 1 << 20, None) == SHAPE
