@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "q4_splitk_workspace": [ctypes.c_int, _i64, _i64, _i64, _vp],
             "q4_0_gemv_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
             "q4k_gemv_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
+            "q4_0_gemv_splitk_noalloc": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
             "dequant_q4_0": [_vp, _vp, _i64, _i64, _vp],
             "q4_pure_read": [_vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                              _vp],
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        L.q4_noalloc_scratch_bytes.argtypes = []
+        L.q4_noalloc_scratch_bytes.restype = ctypes.c_longlong
         _LIB = L
     return _LIB
 

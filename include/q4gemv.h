@@ -323,6 +323,22 @@ int q4k_gemv_splitk(float* y, const void* w, const float* x, int64_t M, int64_t 
                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it):
+ * q4_0_gemv_splitk_noalloc is q4_0_gemv_splitk with the library's own
+ * workspace, a device array of q4_noalloc_scratch_bytes() bytes (8 MiB) per
+ * GPU, held until the process ends; it allocates nothing.  A shape whose
+ * workspace (q4_splitk_workspace) exceeds it: Q4_ERR_SHAPE, before any
+ * launch (16 tokens of 4096 rows at K = 4096 need 2 MiB; very long K needs
+ * more parts and can exceed it).  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (different streams, or host threads) race and must not
+ * be made.  Results equal q4_0_gemv_splitk's bit for bit.
+ */
+long long q4_noalloc_scratch_bytes(void);
+int q4_0_gemv_splitk_noalloc(float* y, const void* w, const float* x, int64_t M, int64_t N,
+                             int64_t K, void* stream);
+
+/*
  * Q4_0 in split arrays (inferencelayer 0.2.13, kernel_lab.rs, GEMV_F16S:
  * `scales: array<f16>`, `quants: array<vec4<u32>>`): row n's block b has
  * its f16 scale at scales[n * K/32 + b] and its 16 nibble bytes at
