@@ -604,6 +604,10 @@ inline SplitKPlan splitk_plan(int fmt, int64_t M, int64_t N, int64_t K, int cus)
     // M = 4 / 8 / 16 ran 13.9 / 15.4 / 19.0 us with 8 parts, 19.5 / 21.4 /
     // 25.4 us with 16, 15.2 / 16.5 / 20.9 us with 4)
     long long kp = forced > 0 ? forced : ((long long)cus + pl.ngroups - 1) / pl.ngroups;
+    // parts of at most kSplitKOneSteps steps are staged in one pass (up to
+    // 64 parts; longer rows keep longer parts)
+    const long long kone = (S + kSplitKOneSteps - 1) / kSplitKOneSteps;
+    if (forced <= 0 && kone <= 64 && kp < kone) kp = kone;
     if (kp > S) kp = S;
     if (kp < 1) kp = 1;
     // the largest batch's staging of one part must fit in LDS

@@ -610,6 +610,8 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     int osh[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) osh[m] = (FMT == kFmtQ4K ? 24 : 0) - xe[m];
+    // the pair bits of one token: top_k consecutive bits (M * top_k <= 64)
+    const unsigned long long tkmask = p.top_k >= 64 ? ~0ull : ((1ull << p.top_k) - 1ull);
 
     if constexpr (mode_moe(MODE)) {
         // rows of pairs with an invalid id: NaN (or an all-ones checksum)
@@ -705,6 +707,16 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         // ---- end of a task: reduce over the row group; its last lane writes ----
         const int r0 = group_row(c);
         const bool last_lane = li == p.lg - 1;
+        // expert call: only the tokens that chose the task's expert have
+        // totals to reduce and write (wave-uniform), and token m's pairs are
+        // bits m * top_k .. of the expert's pair mask
+        unsigned int tsel = ~0u;
+        unsigned long long upairs = 0ull;
+        if constexpr (mode_moe(MODE)) {
+            tsel = moe.utok[c.ue];
+            upairs = moe.upairs[c.ue];
+        }
+        auto token_pairs = [&](int m) { return upairs & (tkmask << (m * p.top_k)); };
         if constexpr (mode_silu(MODE) && !PURE) {
             // one output, h = silu(gate) * up: row r's gate total is q = r,
             // its up total q = RR + r, both in this lane
@@ -715,6 +727,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                 const bool wr = last_lane && row < p.N;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
+                    if (!((tsel >> m) & 1u)) continue;
                     const float g = __builtin_ldexpf(group_total(acc[r][m], p.lg), osh[m]);
                     const float u = __builtin_ldexpf(group_total(acc[RR + r][m], p.lg), osh[m]);
                     acc[r][m] = 0.f;
@@ -722,11 +735,11 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                     if (wr) {
                         const float h = silu_mul(g, u);
                         if constexpr (mode_moe(MODE)) {
-                            unsigned long long pm = moe.upairs[c.ue];
+                            unsigned long long pm = token_pairs(m);
                             while (pm) {
                                 const int pr = __builtin_ctzll(pm);
                                 pm &= pm - 1ull;
-                                if (pr / p.top_k == m) p.y0[(long long)pr * p.N + row] = h;
+                                p.y0[(long long)pr * p.N + row] = h;
                             }
                         } else {
                             p.y0[(long long)m * p.N + row] = h;
@@ -763,15 +776,16 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                     float* y = mt == 0 ? p.y0 : p.y1;
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
+                        if (!((tsel >> m) & 1u)) continue;
                         const float v = __builtin_ldexpf(group_total(acc[q][m], p.lg), osh[m]);
                         acc[q][m] = 0.f;
                         if (wr) {
                             if constexpr (mode_moe(MODE)) {
-                                unsigned long long pm = moe.upairs[c.ue];
+                                unsigned long long pm = token_pairs(m);
                                 while (pm) {
                                     const int pr = __builtin_ctzll(pm);
                                     pm &= pm - 1ull;
-                                    if (pr / p.top_k == m) y[(long long)pr * p.N + row] = v;
+                                    y[(long long)pr * p.N + row] = v;
                                 }
                             } else {
                                 y[(long long)m * p.N + row] = v;

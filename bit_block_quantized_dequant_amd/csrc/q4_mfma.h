@@ -140,14 +140,68 @@ __device__ __forceinline__ bool piece_is_high(int pp) {
     return FMT == kFmtQ4K ? ((pp >> 2) & 1) : ((pp >> 1) & 1);
 }
 
+// Per-token largest magnitude of a workgroup's staged pieces, each wave's
+// into red.am[m][wave] (0 for tokens it holds no piece of): piece slot k of
+// thread tid is piece tid + k * kMBlock of np, of token um[k] (ppt pieces
+// per token), with largest magnitude mag(k) (0 for a slot past np).  When
+// ppt is a multiple of 64 every slot of a wave lies inside one token, and a
+// thread's tokens do not decrease with k: one wave reduction per slot and a
+// running maximum over the slots.  Otherwise each token is selected from
+// every slot and reduced.  A maximum is exact in any order, so both give the
+// same values.
+template <int M, int P, typename Red, typename Mag>
+__device__ __forceinline__ void piece_maxima(Red& red, const int (&um)[P], int np, int ppt,
+                                             Mag mag) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (ppt % kWave == 0) {
+        if (lane < M) red.am[lane][wave] = 0.f;
+        const int w0 = tid - lane;
+        float cur = 0.f;
+        int cu = -1;
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            if (w0 + k * kMBlock >= np) break;  // (wave-uniform: no piece of this wave)
+            const float r = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_max_nonneg(mag(k))),
+                                                 kWave - 1));
+            const int u = __builtin_amdgcn_readfirstlane(um[k]);
+            if (u != cu) {
+                if (cu >= 0 && lane == 0) red.am[cu][wave] = cur;
+                cu = u;
+                cur = r;
+            } else {
+                cur = fmaxf(cur, r);
+            }
+        }
+        if (cu >= 0 && lane == 0) red.am[cu][wave] = cur;
+    } else {
+        float am[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) am[m] = 0.f;
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const float t = mag(k);
+#pragma unroll
+            for (int m = 0; m < M; ++m) am[m] = fmaxf(am[m], um[k] == m ? t : 0.f);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float t = wave_max_nonneg(am[m]);  // am >= 0: largest |x|
+            if (lane == kWave - 1) red.am[m][wave] = t;
+        }
+    }
+}
+
 // The activation pieces of one thread (8 consecutive elements each) and
 // their tokens, loaded by mstage_issue before the first weight loads: loads
 // complete in issue order, so activations loaded after the weights would
 // wait for the weights' HBM latency before the staging could start.
-struct MStageX {
-    float v[kMPieces][8];
-    int um[kMPieces];
+template <int P>
+struct MStageXT {
+    float v[P][8];
+    int um[P];
 };
+using MStageX = MStageXT<kMPieces>;
 
 template <int M>
 __device__ __forceinline__ void mstage_issue(const GemvParams& p, MStageX& sx) {
@@ -227,23 +281,12 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
     // (any finite magnitude: the scale is applied with ldexp, not a
     // constructed power of two)
     {
-        float am[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) am[m] = 0.f;
-#pragma unroll
-        for (int k = 0; k < kMPieces; ++k) {
+        piece_maxima<M, kMPieces>(red, um, np, ppt, [&](int k) {
             float t = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(v[k][e]));
-            t = valid(k) ? t : 0.f;
-#pragma unroll
-            for (int m = 0; m < M; ++m) am[m] = fmaxf(am[m], um[k] == m ? t : 0.f);
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float t = wave_max_nonneg(am[m]);  // am >= 0: largest |x|
-            if (lane == kWave - 1) red.am[m][wave] = t;
-        }
+            return valid(k) ? t : 0.f;
+        });
         sync_lds();
         if (tid < M) {
             float t = 0.f;
@@ -551,6 +594,117 @@ __device__ __forceinline__ void mstage_part_factors(const GemvParams& p, char* l
     sync_lds();
 }
 
+// Split-K staging in one pass, for a part of at most kSplitKOneSteps steps:
+// its M * ppt <= 128 M pieces fit in P = ceil(M / 4) pieces per thread,
+// a count fixed at compile time so that the loads stay unconditional (a
+// load under a branch is merged into its register by a copy, which waits
+// for every load in flight).  Piece pp of token m covers columns c0 + 8 pp
+// .. of the row; pieces past K (in the row's partial last step) are loaded
+// clamped and staged as zeros.  The loads go out before the weight loads
+// (mstage_issue's reason).
+constexpr int kSplitKOneSteps = 4;
+template <int M>
+__host__ __device__ constexpr int part_pieces() { return (M + 3) / 4; }
+
+template <int M, int P>
+__device__ __forceinline__ void mstage_part_issue(const GemvParams& p, int c0, int ppt,
+                                                  MStageXT<P>& sx) {
+    const int tid = threadIdx.x;
+    const int np = M * ppt;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const int pc = min(tid + k * kMBlock, np - 1);
+        int m = 0;
+#pragma unroll
+        for (int mm = 1; mm < M; ++mm) m += pc >= mm * ppt;
+        sx.um[k] = m;
+        const int col = min(c0 + 8 * (pc - m * ppt), p.K - 8);
+        const float4* src = (const float4*)(p.x + (long long)m * p.K + col);
+        const float4 a = src[0], b = src[1];
+        sx.v[k][0] = a.x; sx.v[k][1] = a.y; sx.v[k][2] = a.z; sx.v[k][3] = a.w;
+        sx.v[k][4] = b.x; sx.v[k][5] = b.y; sx.v[k][6] = b.z; sx.v[k][7] = b.w;
+    }
+}
+
+// The part's exponents (kNoExp for a token with no nonzero element in the
+// part) and its fragments and sums, in the layout of mstage_slice (region
+// width kst columns, local piece and group indices).
+template <int FMT, int M, int P, typename Red>
+__device__ __forceinline__ void mstage_part_finish(const GemvParams& p, char* lds,
+                                                   const MLayout& ly, Red& red, MStageXT<P>& sx,
+                                                   int c0, int ppt, int kst) {
+    const int tid = threadIdx.x;
+    const int np = M * ppt;
+    float (&v)[P][8] = sx.v;
+    const int (&um)[P] = sx.um;
+    auto valid = [&](int k) { return tid + k * kMBlock < np; };
+    int* ex = (int*)(lds + ly.exps);
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const int pc = min(tid + k * kMBlock, np - 1);
+        if (c0 + 8 * (pc - um[k] * ppt) >= p.K) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+        }
+    }
+    {
+        piece_maxima<M, P>(red, um, np, ppt, [&](int k) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(v[k][e]));
+            return valid(k) ? t : 0.f;
+        });
+        sync_lds();
+        if (tid < M) {
+            float t = 0.f;
+            for (int w = 0; w < kMWaves; ++w) t = fmaxf(t, red.am[tid][w]);
+            ex[tid] = t > 0.f ? xscale_exp(t, 14) : kNoExp;
+        }
+        sync_lds();
+    }
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const int pc = min(tid + k * kMBlock, np - 1);
+        const int m = um[k];
+        const int pp = pc - m * ppt;
+        const int e = ex[m];
+        const int ef = piece_is_high<FMT>(pp) ? e - 4 : e;
+        h8 hi, lo;
+        float part = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float xs = __builtin_ldexpf(v[k][slot_byte(t)], ef);
+            const _Float16 h = (_Float16)xs;
+            hi[t] = h;
+            lo[t] = (_Float16)(xs - (float)h);
+            part += __builtin_ldexpf(v[k][t], e);
+        }
+        // the 4 pieces of one 32-element group are 4 consecutive threads
+        // (ppt is a multiple of 32)
+        part = dpp_add(part, 0);
+        part = dpp_add(part, 1);
+        if (valid(k)) {
+            *(h8*)(lds + ly.frag + fslot(kst, 2 * m, pp) * 16) = hi;
+            *(h8*)(lds + ly.frag + fslot(kst, 2 * m + 1, pp) * 16) = lo;
+            if ((pp & 3) == 0) {
+                const int g32 = pp >> 2;
+                if constexpr (FMT != kFmtQ4K) {
+                    ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
+                } else {
+                    const int sb = g32 >> 3, J = g32 & 7;
+                    const float xs = part * 0.03125f;
+                    const _Float16 h = (_Float16)xs;
+                    const _Float16 l = (_Float16)(xs - (float)h);
+                    _Float16* a = (_Float16*)(lds + ly.aux);
+                    const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
+                    a[base] = h;
+                    a[base + 2] = l;
+                }
+            }
+        }
+    }
+}
+
 // The merge of split-K partial sums: y[m, row] = sum over parts q (in
 // order) of part[q][m][row] brought to the common scale 2^(24 - e*), e* the
 // smallest exponent of the token's parts (the part of largest magnitude);
@@ -561,13 +715,52 @@ static __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (long long)M * N) return;
     const int m = (int)(i / N), row = (int)(i - (long long)m * N);
+    const int* pe = pexp + m;
+    const float* pp = part + (long long)m * N + row;
+    const long long qs = (long long)M * N;  // part stride
+    // parts in chunks of 8 whose loads all go out before their use; with
+    // at most 8 parts, exponents and partials in one round trip
+    constexpr int U = 8;
+    if (kp <= U) {
+        int e[U];
+        float v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool ok = j < kp;
+            e[j] = ok ? pe[j * M] : kNoExp;
+            v[j] = ok ? pp[j * qs] : 0.f;
+        }
+        int emin = kNoExp;
+#pragma unroll
+        for (int j = 0; j < U; ++j) emin = min(emin, e[j]);
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            if (e[j] != kNoExp) sum += __builtin_ldexpf(v[j], emin - e[j]);
+        y[i] = emin == kNoExp ? 0.f : __builtin_ldexpf(sum, 24 - emin);
+        return;
+    }
     int emin = kNoExp;
-    for (int q = 0; q < kp; ++q) emin = min(emin, pexp[q * M + m]);
+    for (int q0 = 0; q0 < kp; q0 += U) {
+        int e[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) e[j] = q0 + j < kp ? pe[(q0 + j) * M] : kNoExp;
+#pragma unroll
+        for (int j = 0; j < U; ++j) emin = min(emin, e[j]);
+    }
     float sum = 0.f;
-    for (int q = 0; q < kp; ++q) {
-        const int eq = pexp[q * M + m];
-        const float v = part[((long long)q * M + m) * N + row];
-        sum += eq == kNoExp ? 0.f : __builtin_ldexpf(v, emin - eq);
+    for (int q0 = 0; q0 < kp; q0 += U) {
+        int e[U];
+        float v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool ok = q0 + j < kp;
+            e[j] = ok ? pe[(q0 + j) * M] : kNoExp;
+            v[j] = ok ? pp[(q0 + j) * qs] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            if (e[j] != kNoExp) sum += __builtin_ldexpf(v[j], emin - e[j]);
     }
     y[i] = emin == kNoExp ? 0.f : __builtin_ldexpf(sum, 24 - emin);
 }
@@ -708,7 +901,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         // (split-K: workgroup b serves tile group b / kp, one tile per wave)
         const int traw = SPLITK ? ((int)blockIdx.x / p.kp) * TG + grp
                                 : (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
-        const bool idle = SPLITK ? traw >= ntiles : (r >= nrounds || traw >= ntiles);
+        const bool idle = SPLITK ? (r > 0 || traw >= ntiles) : (r >= nrounds || traw >= ntiles);
         const Tile T = tile_at(min(traw, ntiles - 1));
         const int row0 = T.row0;
         const bool up = kPair ? jrow >= 8 : T.mt != 0;
@@ -1092,12 +1285,15 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
                                 if constexpr (kMoe) {
                                     // output [token, slot, row] for every slot in which
                                     // token m chose this expert
-                                    unsigned long long pm = moe.d.upairs[T.u];
+                                    // (token m's pairs: bits m * top_k .. of the mask)
+                                    const unsigned long long tk =
+                                        p.top_k >= 64 ? ~0ull : ((1ull << p.top_k) - 1ull);
+                                    unsigned long long pm =
+                                        moe.d.upairs[T.u] & (tk << (m * p.top_k));
                                     while (pm) {
                                         const int pr = __builtin_ctzll(pm);
                                         pm &= pm - 1ull;
-                                        if (pr / p.top_k == m)
-                                            yo[(long long)pr * p.N + row] = v;
+                                        yo[(long long)pr * p.N + row] = v;
                                     }
                                 } else {
                                     yo[(long long)m * p.N + row] = v;
@@ -1120,24 +1316,45 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         const MSlice sc{S, 1, 1, p.kp, p.msl};
         int a, b, reg;
         sc.range(0, kp, a, b, reg);
+        // one pass over the part's activations (parts of at most
+        // kSplitKOneSteps steps; the call-uniform choice), else two passes
+        // from global memory
+        const int ppt = (b - a) * 32;
+        const bool one = p.msl <= kSplitKOneSteps;
+        constexpr int PP = part_pieces<M>();
+        MStageXT<PP> sx;
+        if (one) mstage_part_issue<M, PP>(p, a * 256, ppt, sx);
+        __builtin_amdgcn_sched_barrier(0);  // the activation loads go out first
+        // two steps of weights in flight, the first two before the staging;
+        // every load is unconditional (a step past the part is an idle load
+        // of one cache line) and the loop is counted, so that no load is
+        // merged into its registers by a copy that would wait for it
         WR wa, wb;
-        if (a < b) load(0, a, wa);
-        mstage_part_factors<M>(p, lds, ly, red, a * 256, b * 256);
-        mstage_slice<FMT, M, kModeDense>(p, lds, ly, sc, kp);
+        auto sk_load = [&](int st, WR& w) { load(st < b ? 0 : 1, min(st, b - 1), w); };
+        sk_load(a, wa);
+        sk_load(a + 1, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (one) {
+            mstage_part_finish<FMT, M, PP>(p, lds, ly, red, sx, a * 256, ppt, p.msl * 256);
+        } else {
+            mstage_part_factors<M>(p, lds, ly, red, a * 256, b * 256);
+            mstage_slice<FMT, M, kModeDense>(p, lds, ly, sc, kp);
+        }
         sync_lds();
         float2 y[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) y[t] = make_float2(0.f, 0.f);
-        for (int st = a; st < b; st += 2) {
-            const bool hb = st + 1 < b;
-            if (hb) load(0, st + 1, wb);
-            __builtin_amdgcn_sched_barrier(0);
+        const int nst = b - a;  // >= 1: parts are never empty (kp <= S)
+        for (int i = 0; i < (nst >> 1); ++i) {
+            const int st = a + 2 * i;
             compute(wa, st, st - a, y);
-            if (!hb) break;
-            if (st + 2 < b) load(0, st + 2, wa);
+            sk_load(st + 2, wa);
             __builtin_amdgcn_sched_barrier(0);
             compute(wb, st + 1, st + 1 - a, y);
+            sk_load(st + 3, wb);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (nst & 1) compute(wa, b - 1, nst - 1, y);
         // partial sums of this wave's tile (lane group c: tokens 8t + 2c + hm)
         const int t_wave = g * TG + grp;
         const int* ex = (const int*)(lds + ly.exps);

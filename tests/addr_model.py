@@ -573,11 +573,18 @@ def slice_check(fmt, M, N, K, nmat=1, cus=256):
 # Split-K batched GEMV (splitk_plan() in q4_host.h, the kStgSplitK path of
 # q4_mfma.h): workgroup b serves tile group b // kp and K part b % kp.
 # ---------------------------------------------------------------------------
+SPLITK_ONE_STEPS = 4  # kSplitKOneSteps
+
+
 def splitk_plan(fmt, M, N, K, cus=256):
     S = (K + 255) // 256
     ntiles = (N + 15) // 16
     ngroups = -(-ntiles // 8)
-    kp = min(S, max(1, -(-cus // ngroups)))
+    kp = max(1, -(-cus // ngroups))
+    kone = -(-S // SPLITK_ONE_STEPS)  # parts short enough for one-pass staging
+    if kone <= 64 and kp < kone:
+        kp = kone
+    kp = min(S, kp)
     while True:
         msl = -(-S // kp)
         if mlayout_steps(fmt, 16, msl) <= LDS_TOTAL - 2048 or kp >= S:
@@ -597,10 +604,23 @@ def splitk_check(fmt, M, N, K, cus=256):
     S, kp, msl, G = pl["S"], pl["kp"], pl["msl"], pl["ngroups"]
     assert mlayout_steps(fmt, M, msl) <= LDS_TOTAL - (2048 if M > 8 else 1024)
     steps = []
+    PP = (M + 3) // 4  # part_pieces<M>()
     for q in range(kp):
         a, b, _ = slice_ranges(S, 1, 1, kp, 0, q)
-        assert b - a <= msl
+        assert 1 <= b - a <= msl
         steps += list(range(a, b))
+        if msl <= SPLITK_ONE_STEPS:
+            # one-pass staging: the part's pieces fit PP per thread, and each
+            # thread's (clamped) activation loads stay inside the row
+            ppt = (b - a) * 32
+            np_ = M * ppt
+            assert np_ <= 512 * PP
+            for tid in range(0, 512, 7):
+                for k in range(PP):
+                    pc = min(tid + 512 * k, np_ - 1)
+                    m = pc // ppt
+                    col = min(a * 256 + 8 * (pc - m * ppt), K - 8)
+                    assert 0 <= m < M and 0 <= col and col + 8 <= K
     assert steps == list(range(S))
     for b in range(G * kp):
         g, q = divmod(b, kp)

@@ -254,7 +254,8 @@ def test_soa_batched_loads_in_bounds(M, K):
 @pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 8, 4096, 4096), ("q4_0", 16, 4096, 4096),
                                        ("q4k", 4, 4096, 14336), ("q4_0", 5, 777, 1408),
                                        ("q4k", 6, 513, 2080), ("q4k", 8, 33, 32768),
-                                       ("q4_0", 12, 16, 4096)])
+                                       ("q4_0", 12, 16, 4096), ("q4_0", 3, 4096, 4096),
+                                       ("q4k", 16, 4096, 14336), ("q4_0", 7, 256, 1 << 20)])
 def test_splitk_plans(fmt, M, N, K):
     pl = A.splitk_check(fmt, M, N, K)
     assert pl["kp"] >= 1
