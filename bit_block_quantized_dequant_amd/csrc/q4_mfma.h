@@ -775,6 +775,22 @@ struct MfmaMoe {
 };
 struct MfmaNoMoe {};
 
+// Split-K: the tile group g and K part q of workgroup b of T.  Workgroups
+// are dispatched to the 8 XCDs in turn (b % 8), each with its own L2; the
+// roles are dealt so that XCD x takes a contiguous run of (group, part)
+// pairs, i.e. the consecutive parts of a group mostly share one L2 (the
+// 144-byte blocks of a row do not end on cache lines, so two parts that
+// meet inside a line would each fetch it).  A bijection for any T: XCD x
+// holds T / 8 workgroups, one more when x < T % 8.
+constexpr int kXcds = 8;
+__host__ __device__ inline void splitk_role(int b, int T, int kp, int& g, int& q) {
+    const int per = T / kXcds, rem = T - per * kXcds;
+    const int x = b % kXcds, i = b / kXcds;
+    const int L = x * per + (x < rem ? x : rem) + i;
+    g = L / kp;
+    q = L - g * kp;
+}
+
 // Staging of the batched kernel: whole rows, K slices, or (split-K) one K
 // part per workgroup with partial sums merged by the last workgroup to
 // finish its tile group.
@@ -899,7 +915,9 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     auto load = [&](int r, int st, WR& w) {
         const int rr = min(r, nrounds - 1);
         // (split-K: workgroup b serves tile group b / kp, one tile per wave)
-        const int traw = SPLITK ? ((int)blockIdx.x / p.kp) * TG + grp
+        int sg = 0, sq = 0;
+        if constexpr (SPLITK) splitk_role((int)blockIdx.x, (int)gridDim.x, p.kp, sg, sq);
+        const int traw = SPLITK ? sg * TG + grp
                                 : (rr * (int)gridDim.x + (int)blockIdx.x) * TG + grp;
         const bool idle = SPLITK ? (r > 0 || traw >= ntiles) : (r >= nrounds || traw >= ntiles);
         const Tile T = tile_at(min(traw, ntiles - 1));
@@ -1312,7 +1330,8 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
         // part's own scale to the workspace (a second kernel merges them:
         // the kernel boundary makes every part visible, with no device-scope
         // fence, which on this part writes back a whole L2) ----
-        const int g = blockIdx.x / p.kp, kp = blockIdx.x - g * p.kp;
+        int g, kp;
+        splitk_role((int)blockIdx.x, (int)gridDim.x, p.kp, g, kp);
         const MSlice sc{S, 1, 1, p.kp, p.msl};
         int a, b, reg;
         sc.range(0, kp, a, b, reg);

@@ -594,6 +594,15 @@ def splitk_plan(fmt, M, N, K, cus=256):
     return dict(kp=kp, msl=msl, ngroups=ngroups, S=S)
 
 
+def splitk_role(b, T, kp, xcds=8):
+    """(group, part) of split-K workgroup b of T (splitk_role() in q4_mfma.h):
+    XCD b % 8 takes a contiguous run of the (group, part) pairs."""
+    per, rem = divmod(T, xcds)
+    x, i = b % xcds, b // xcds
+    L = x * per + min(x, rem) + i
+    return divmod(L, kp)
+
+
 def splitk_check(fmt, M, N, K, cus=256):
     """Parts cover every step once; a part fits its staged steps and LDS;
     every partial and exponent index is inside its region; the plan does
@@ -622,8 +631,10 @@ def splitk_check(fmt, M, N, K, cus=256):
                     col = min(a * 256 + 8 * (pc - m * ppt), K - 8)
                     assert 0 <= m < M and 0 <= col and col + 8 <= K
     assert steps == list(range(S))
+    roles = [splitk_role(b, G * kp, kp) for b in range(G * kp)]
+    assert sorted(roles) == [divmod(L, kp) for L in range(G * kp)]  # a bijection
     for b in range(G * kp):
-        g, q = divmod(b, kp)
+        g, q = roles[b]
         assert g < G
         for grp in range(8):
             t = g * 8 + grp
