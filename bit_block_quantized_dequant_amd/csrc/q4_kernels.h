@@ -194,8 +194,10 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+// (bs: the kernel's block size, a compile-time constant of every caller, so
+// that no load of the dispatch's block size precedes these loads)
 template <int MODE, int NX = kXReg>
-__device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage<NX>& st) {
+__device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage<NX>& st, int bs) {
     const int kq = p.K >> 2;
     const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
@@ -203,7 +205,7 @@ __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
         // unconditional (clamped) loads keep the load-counter waits exact
-        const int i = min((int)threadIdx.x + k * (int)blockDim.x, total - 1);
+        const int i = min((int)threadIdx.x + k * bs, total - 1);
         st.x[k] = x4[i];
         if constexpr (mode_norm(MODE)) st.g[k] = g4[i % kq];
     }
@@ -269,11 +271,10 @@ __device__ __forceinline__ void stage_pad(const GemvParams& p, float4* xl, float
 template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg, bool DEFER = false>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
                                                float4* xl, float* xsum, StageRed& red,
-                                               int (&xe)[M]) {
+                                               int (&xe)[M], int bs) {
     static_assert(!DEFER || (M == 1 && !mode_norm(MODE)), "deferred scaling: one token, no norm");
     const int tid = threadIdx.x;
-    const int bs = blockDim.x;
-    const int kq = p.K >> 2;
+        const int kq = p.K >> 2;
     const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
     const float4* g4 = (const float4*)p.gamma;
@@ -409,15 +410,27 @@ __device__ __forceinline__ int stage_x_exponent(const StageRed& red, int nwaves)
     return __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
 }
 
-// In-kernel dedupe of the expert ids (wave 0); everyone reads it after the
-// barrier that follows.
+// The expert id of pair (threadIdx.x mod 64), for moe_dedupe; issued ahead
+// of other loads so that the dedupe waits for it alone.
 template <int M>
-__device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
-    const int tid = threadIdx.x;
-    if (tid < kWave) {
+__device__ __forceinline__ int moe_load_id(const GemvParams& p) {
+    // every wave, unconditionally (clamped): a load under a branch would be
+    // merged into its register by a copy that waits for all loads in flight
+    return p.ids[min((int)threadIdx.x & (kWave - 1), M * p.top_k - 1)];
+}
+
+// In-kernel dedupe of the expert ids (wave 0, from moe_load_id); everyone
+// reads it after the barrier that follows.
+template <int M>
+__device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh, int e_loaded) {
+    // every wave computes it (its own copy of the ids, so that their load is
+    // used unconditionally and stays where it was issued); wave 0 writes it
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool w0 = threadIdx.x < kWave;
+    {
         const int P = M * p.top_k;
-        const bool in = tid < P;
-        const int e = in ? p.ids[tid] : -1;
+        const bool in = lane < P;
+        const int e = in ? e_loaded : -1;
         const bool ok = in && e >= 0 && e < p.E;
         // (pair t's id and validity are read with v_readlane into scalar
         // registers: t is uniform, so no LDS permute round trip per pair)
@@ -430,7 +443,7 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
         for (int t = 0; t < P; ++t) {
             const int et = __builtin_amdgcn_readlane(eo, t);
             const bool same = ok && et == e;
-            if (t < tid && same) first = false;
+            if (t < lane && same) first = false;
             if (same) {
                 pairs |= 1ull << t;
                 toks |= 1u << (t / p.top_k);
@@ -438,13 +451,13 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh) {
         }
         const unsigned long long fb = __ballot(first);
         const unsigned long long bad = __ballot(in && !ok);
-        const int uidx = __popcll(fb & ((1ull << tid) - 1ull));
-        if (first) {
+        const int uidx = __popcll(fb & ((1ull << lane) - 1ull));
+        if (w0 && first) {
             sh.uexp[uidx] = e;
             sh.upairs[uidx] = pairs;
             sh.utok[uidx] = toks;
         }
-        if (tid == 0) {
+        if (threadIdx.x == 0) {
             sh.nu = __popcll(fb);
             sh.invalid = bad;
         }
@@ -462,11 +475,12 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     __shared__ StageRed red;
 
     constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
+    constexpr int kBS = gemv_threads(M, MODE);  // the launch's block size (run_plan)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the wave index is wave-uniform; say so, so that all task bookkeeping
     // stays in scalar registers and the loops are scalar branches
-    const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (tid >> 6));
+    const int gwave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kBS >> 6) + (tid >> 6));
     const int kq = xrow_chunks(p.upr);  // LDS float4 chunks per token row
     const int k64 = p.upr;
     float4* xl = smem;
@@ -475,9 +489,16 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // ---- the wave's task range ----
     int ntasks = p.ntasks;
     int tpe = 1;  // tasks per expert (expert call)
+    // Activation loads go out first (the expert call: right after its ids,
+    // so that their latency overlaps the dedupe; the barrier after the
+    // dedupe waits for LDS only)
+    constexpr int NX = xreg_chunks(MODE);
+    XStage<NX> xst;
     if constexpr (mode_moe(MODE)) {
-        moe_dedupe<M>(p, moe);
-        __syncthreads();
+        const int eid = moe_load_id<M>(p);
+        if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst, kBS);
+        moe_dedupe<M>(p, moe, eid);
+        sync_lds();
         tpe = p.nrg / p.rgw;
         ntasks = moe.nu * tpe;
     }
@@ -591,20 +612,18 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     Cursor ca = first_cursor();
     // Activation loads first, then the first weight loads, then the staging
     // arithmetic: the HBM latency of the first step overlaps the staging.
-    constexpr int NX = xreg_chunks(MODE);
-    XStage<NX> xst;
     int xe[M];  // per-token scale exponents of the staged activations
 #pragma unroll
     for (int m = 0; m < M; ++m) xe[m] = 0;
     // register-resident single token without RMSNorm: the scale is applied
     // when the lane copies its activations into registers (no extra barrier)
     constexpr bool kDefer = XR && !mode_norm(MODE);
-    if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst);
+    if constexpr (!PURE && !mode_moe(MODE)) stage_x_issue<MODE, NX>(p, M, xst, kBS);
     load(ca, bufA);  // a wave without tasks reads in-bounds rows it never uses
     if constexpr (!PURE)
-        stage_x_finish<FMT, M, MODE, TAIL, NX, kDefer>(p, xst, xl, xsum, red, xe);
+        stage_x_finish<FMT, M, MODE, TAIL, NX, kDefer>(p, xst, xl, xsum, red, xe, kBS);
     sync_lds();
-    if constexpr (kDefer && !PURE) xe[0] = stage_x_exponent(red, (int)(blockDim.x >> 6));
+    if constexpr (kDefer && !PURE) xe[0] = stage_x_exponent(red, kBS >> 6);
     // output scale of token m: 2^(24 - e_m) for Q4_K (whose sums carry the
     // 6-bit scales as sc * 2^-24), 2^-e_m for Q4_0
     int osh[M];
@@ -618,8 +637,8 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         if (moe.invalid) {
             const int P = M * p.top_k;
             const long long total = (long long)P * p.N;
-            const long long stride = (long long)gridDim.x * blockDim.x;
-            for (long long i = (long long)blockIdx.x * blockDim.x + tid; i < total; i += stride) {
+            const long long stride = (long long)gridDim.x * kBS;
+            for (long long i = (long long)blockIdx.x * kBS + tid; i < total; i += stride) {
                 const int pr = (int)(i / p.N);
                 if ((moe.invalid >> pr) & 1ull) {
                     if constexpr (PURE) {

@@ -849,7 +849,7 @@ __global__ __launch_bounds__(kMBlock) void mfma_gemv_kernel(const GemvParams p) 
     __shared__ std::conditional_t<kMoe, MfmaMoe, MfmaNoMoe> moe;
     int nu = 1;  // matrices of NMAT: 1, or the unique selected experts
     if constexpr (kMoe) {
-        moe_dedupe<M>(p, moe.d);
+        moe_dedupe<M>(p, moe.d, moe_load_id<M>(p));
         __syncthreads();
         // outputs of pairs with an invalid id: NaN (or all-ones checksums)
         if (moe.d.invalid) {

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kDownBlock) void moe_down_kernel(const GemvParams p
     float4* xl = smem;
     float* xsum = (float*)(smem + M * kq);
 
-    moe_dedupe<M>(p, moe);
+    moe_dedupe<M>(p, moe, moe_load_id<M>(p));
     __syncthreads();
     const int nu = __builtin_amdgcn_readfirstlane(moe.nu);
     // rows of pairs with an invalid id: NaN (or an all-ones checksum)

@@ -66,8 +66,8 @@ static __global__ __launch_bounds__(kRouterBlock) void router_kernel(int32_t* __
     p.upr = K / kUnitElems;
     XStage<> st;
     int xe[1];  // the row's scale exponent: the staged row is x * 2^xe
-    stage_x_issue<kModeDense>(p, 1, st);
-    stage_x_finish<kFmtQ4_0, 1, kModeDense, true>(p, st, xl, xsum, red, xe);
+    stage_x_issue<kModeDense>(p, 1, st, kRouterBlock);
+    stage_x_finish<kFmtQ4_0, 1, kModeDense, true>(p, st, xl, xsum, red, xe, kRouterBlock);
     __syncthreads();
 
     // ---- logits ----
