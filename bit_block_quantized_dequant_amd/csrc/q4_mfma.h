@@ -135,6 +135,30 @@ __device__ __forceinline__ int fslot(int K, int i, int p) { return i * ((K >> 3)
 // ---------------------------------------------------------------------------
 // Staging of the activations into A fragments.
 // ---------------------------------------------------------------------------
+// The A fragments of one piece of 8 elements v (token scale 2^e): slot t
+// holds element slot_byte(t) scaled by 2^e, 2^(e-4) for a piece met as high
+// nibbles; hi = its nearest f16, lo = the f16 of the remainder, which one
+// mixed fused multiply-add gives exactly in fp32.  part = the piece's sum
+// scaled by 2^e, added in element order (slot_byte is its own inverse); a
+// high piece's sum is formed 2^-4 lower and multiplied back by 16, exact
+// above the subnormal range.
+__device__ __forceinline__ void piece_frag(const float (&v)[8], int e, bool high, h8& hi, h8& lo,
+                                           float& part) {
+    const int ef = high ? e - 4 : e;
+    float xs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xs[t] = __builtin_ldexpf(v[slot_byte(t)], ef);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const _Float16 h = (_Float16)xs[t];
+        hi[t] = h;
+        lo[t] = (_Float16)__builtin_fmaf((float)h, -1.0f, xs[t]);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += xs[slot_byte(j)];
+    part = high ? sum * 16.0f : sum;
+}
 template <int FMT>
 __device__ __forceinline__ bool piece_is_high(int pp) {
     return FMT == kFmtQ4K ? ((pp >> 2) & 1) : ((pp >> 1) & 1);
@@ -303,18 +327,9 @@ __device__ __forceinline__ void mstage(const GemvParams& p, char* lds, const MLa
         const int pc = min(tid + k * kMBlock, np - 1);
         const int m = um[k];
         const int pp = pc - m * ppt;
-        const int e = ex[m];
-        const int ef = piece_is_high<FMT>(pp) ? e - 4 : e;
         h8 hi, lo;
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float xs = __builtin_ldexpf(v[k][slot_byte(t)], ef);
-            const _Float16 h = (_Float16)xs;
-            hi[t] = h;
-            lo[t] = (_Float16)(xs - (float)h);
-            part += __builtin_ldexpf(v[k][t], e);
-        }
+        float part;
+        piece_frag(v[k], ex[m], piece_is_high<FMT>(pp), hi, lo, part);
         // the 4 pieces of one 32-element group are 4 consecutive threads
         part = dpp_add(part, 0);
         part = dpp_add(part, 1);
@@ -521,18 +536,9 @@ __device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, con
                 for (int e = 0; e < 8; ++e) v[e] = (v[e] * r) * g[e];
             }
         }
-        const int e = ex[m];
-        const int ef = piece_is_high<FMT>(pin) ? e - 4 : e;
         h8 hi, lo;
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float xs = __builtin_ldexpf(v[slot_byte(t)], ef);
-            const _Float16 h = (_Float16)xs;
-            hi[t] = h;
-            lo[t] = (_Float16)(xs - (float)h);
-            part += __builtin_ldexpf(v[t], e);
-        }
+        float part;
+        piece_frag(v, ex[m], piece_is_high<FMT>(pin), hi, lo, part);
         part = dpp_add(part, 0);
         part = dpp_add(part, 1);
         if (staged) {
@@ -667,18 +673,9 @@ __device__ __forceinline__ void mstage_part_finish(const GemvParams& p, char* ld
         const int pc = min(tid + k * kMBlock, np - 1);
         const int m = um[k];
         const int pp = pc - m * ppt;
-        const int e = ex[m];
-        const int ef = piece_is_high<FMT>(pp) ? e - 4 : e;
         h8 hi, lo;
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float xs = __builtin_ldexpf(v[k][slot_byte(t)], ef);
-            const _Float16 h = (_Float16)xs;
-            hi[t] = h;
-            lo[t] = (_Float16)(xs - (float)h);
-            part += __builtin_ldexpf(v[k][t], e);
-        }
+        float part;
+        piece_frag(v[k], ex[m], piece_is_high<FMT>(pp), hi, lo, part);
         // the 4 pieces of one 32-element group are 4 consecutive threads
         // (ppt is a multiple of 32)
         part = dpp_add(part, 0);
