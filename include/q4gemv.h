@@ -98,6 +98,11 @@
  *   Q4GEMV_BLOCKS_PER_CU=n workgroups per CU in the VALU kernel's grid
  *   Q4GEMV_MFMA_KS=n       waves splitting a matrix-core tile's K range
  *                          (1, 2, 4 or 8)
+ *   Q4GEMV_SPLITK_KP=n     K parts of the split-K calls (their workspace
+ *                          size follows)
+ *   Q4GEMV_DOWN_RR=n       rows per lane of the expert down-projection (1 or 2)
+ *   Q4GEMV_DOWN_WG_PER_CU=n  resident workgroups per CU of the expert
+ *                          down-projection
  */
 #ifndef Q4GEMV_H
 #define Q4GEMV_H
