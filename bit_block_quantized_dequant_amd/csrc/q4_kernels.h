@@ -835,25 +835,35 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
             ca = cc;
         }
     } else {
+        // (cursors are selected field by field: a select of whole structs
+        // was compiled as a select of their stack addresses and a load)
+        auto pick = [](bool c, const Cursor& a, const Cursor& b) {
+            Cursor r;
+            r.t = c ? a.t : b.t;
+            r.ui = c ? a.ui : b.ui;
+            r.ue = c ? a.ue : b.ue;
+            r.rgt = c ? a.rgt : b.rgt;
+            return r;
+        };
         uint32_t bufC[NR][kUnitWords];
         Cursor cb = next_cursor(ca);
-        Cursor lastv = cb.t < t1 ? cb : ca;
+        Cursor lastv = pick(cb.t < t1, cb, ca);
         load(lastv, bufB);
         for (;;) {
             const Cursor cc = next_cursor(cb);
-            lastv = cc.t < t1 ? cc : lastv;
+            lastv = pick(cc.t < t1, cc, lastv);
             load(lastv, bufC);
             __builtin_amdgcn_sched_barrier(0);
             compute(ca, bufA);
             if (!(cb.t < t1)) break;
             const Cursor cd = next_cursor(cc);
-            lastv = cd.t < t1 ? cd : lastv;
+            lastv = pick(cd.t < t1, cd, lastv);
             load(lastv, bufA);
             __builtin_amdgcn_sched_barrier(0);
             compute(cb, bufB);
             if (!(cc.t < t1)) break;
             const Cursor ce = next_cursor(cd);
-            lastv = ce.t < t1 ? ce : lastv;
+            lastv = pick(ce.t < t1, ce, lastv);
             load(lastv, bufB);
             __builtin_amdgcn_sched_barrier(0);
             compute(cc, bufC);
