@@ -24,7 +24,8 @@ __all__ = [
     "fused_gate_up_silu_q4k_gemv", "fused_rmsnorm_gate_up_silu_q4k_gemv",
     "moe_q4_gemv", "moe_q4_gemv_silu", "moe_q4_gemv_down", "moe_router_q4_0", "dequant_q4k",
     "q4_0_gemv_soa", "q4_0_repack_soa", "q4_0_gemv_splitk", "q4k_gemv_splitk",
-    "splitk_workspace_bytes", "Q4_FORMAT_Q4_0", "Q4_FORMAT_Q4K",
+    "splitk_workspace_bytes", "q4_0_gemv_splitk_noalloc", "noalloc_scratch_bytes",
+    "Q4_FORMAT_Q4_0", "Q4_FORMAT_Q4K",
     "dequant_q4_0", "q4_pure_read", "Q4_READ_Q4_0_GEMV", "Q4_READ_Q4K_GEMV",
     "Q4_READ_GATE_UP", "Q4_READ_MOE", "Q4_READ_STREAM", "Q4_READ_MOE_DOWN", "LIB_PATH", "q4_0_row_bytes",
     "q4k_row_bytes",
@@ -356,9 +357,27 @@ def _splitk(name, fmt, y, w, x, M, N, K, workspace, stream):
 
 
 def q4_0_gemv_splitk(y, w, x, M, N, K, workspace, stream=None):
-    """q4_0_gemv with K split over workgroups (workspace: zero-filled device
-    bytes of at least splitk_workspace_bytes(Q4_FORMAT_Q4_0, M, N, K))."""
+    """q4_0_gemv with K split over workgroups (workspace: device bytes of at
+    least splitk_workspace_bytes(Q4_FORMAT_Q4_0, M, N, K), any content; the
+    call writes it before reading it and leaves nothing in it that a later
+    call needs)."""
     _splitk("q4_0_gemv_splitk", Q4_FORMAT_Q4_0, y, w, x, M, N, K, workspace, stream)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the library's own split-K workspace (per GPU)."""
+    return int(lib().q4_noalloc_scratch_bytes())
+
+
+def q4_0_gemv_splitk_noalloc(y, w, x, M, N, K, stream=None):
+    """q4_0_gemv_splitk with the library's own workspace: allocates nothing
+    (for graph capture and serving loops).  Calls that overlap on one GPU race
+    on that workspace and must not be made."""
+    rb = q4_0_row_bytes(K)
+    (py, pw, px), dev = _ptrs((y, "y", _sz(M * N, 4), F32), (w, "w", _sz(N, rb), U8),
+                              (x, "x", _sz(M * K, 4), F32))
+    _ok(lib().q4_0_gemv_splitk_noalloc(py, pw, px, M, N, K, _stream(stream, dev)),
+        "q4_0_gemv_splitk_noalloc")
 
 
 def q4k_gemv_splitk(y, w, x, M, N, K, workspace, stream=None):

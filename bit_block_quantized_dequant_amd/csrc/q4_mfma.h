@@ -789,8 +789,7 @@ __host__ __device__ inline void splitk_role(int b, int T, int kp, int& g, int& q
 }
 
 // Staging of the batched kernel: whole rows, K slices, or (split-K) one K
-// part per workgroup with partial sums merged by the last workgroup to
-// finish its tile group.
+// part per workgroup, whose partial sums splitk_reduce_kernel merges.
 constexpr int kStgWhole = 0;
 constexpr int kStgSliced = 1;
 constexpr int kStgSplitK = 2;

@@ -324,3 +324,27 @@ def test_splitk_validation(q4lib):
     assert f(A, A, A, 17, 16, 256, A, 1 << 20, None) == BATCH
     assert f(A, MIS, A, 8, 16, 256, A, 1 << 20, None) == ALIGN
     assert L().q4k_gemv_splitk(A, A, A, 8, 16, 48, A, 1 << 20, None) == SHAPE
+
+
+def test_splitk_noalloc_validation(q4lib):
+    """The allocation-free split-K call refuses bad arguments on the host,
+    before it takes its workspace's address."""
+    f = L().q4_0_gemv_splitk_noalloc
+    assert f(None, A, A, 8, 16, 256, None) == NULL
+    assert f(A, None, A, 8, 16, 256, None) == NULL
+    assert f(A, A, A, 0, 16, 256, None) == BATCH
+    assert f(A, A, A, 17, 16, 256, None) == BATCH
+    assert f(A, A, A, 8, 16, 96, None) == SHAPE          # Q4_0: K % 64
+    assert f(A, A, A, 8, 0, 256, None) == SHAPE
+    assert f(A, MIS, A, 8, 16, 256, None) == ALIGN
+    assert f(A, A, A + 4, 8, 16, 256, None) == ALIGN     # x: 16 bytes
+    assert L().q4_noalloc_scratch_bytes() == 8 << 20
+
+
+def test_binding_noalloc_refuses_host_tensors():
+    import torch
+    y = torch.zeros(8 * 16)
+    w = torch.zeros(16 * 144, dtype=torch.uint8)
+    x = torch.zeros(8 * 256)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q4.q4_0_gemv_splitk_noalloc(y, w, x, 8, 16, 256)
