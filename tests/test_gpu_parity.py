@@ -535,6 +535,22 @@ def test_graph_replay_matches_eager(dev):
     outs["ids"] = empty((4, top_k), dev, dtype=torch.int32)
     outs["wts"] = empty((4, top_k), dev)
     outs["hm"] = empty((4, top_k, NE), dev)
+    # split-K (two kernels and a caller workspace), its allocation-free form,
+    # split-array Q4_0, and the expert down-projection on the router's ids
+    wsb = max(q4.splitk_workspace_bytes(q4.Q4_FORMAT_Q4_0, 8, N, K),
+              q4.splitk_workspace_bytes(q4.Q4_FORMAT_Q4K, 4, N, K))
+    assert wsb > 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for k, m in (("sk8", 8), ("skk4", 4), ("na6", 6), ("soa3", 3)):
+        outs[k] = empty((m, N), dev)
+    nb = N * (K // 32)
+    sc = torch.empty(2 * nb, dtype=torch.uint8, device=dev)
+    qs = torch.empty(16 * nb, dtype=torch.uint8, device=dev)
+    q4.q4_0_repack_soa(sc, qs, w0d, N, K)
+    KD, ND = 128, 64
+    wdn = T(synth.q4_0_matrix(rng, E * ND, KD), dev)
+    hd = T(synth.activations(rng, 4 * top_k, KD), dev)
+    outs["dn"] = empty((4, top_k, ND), dev)
 
     def calls(stream):
         q4.fused_gate_up_q4k_gemv(outs["g1"], outs["u1"], wgd, wud, xd, 1, N, K, stream=stream)
@@ -545,6 +561,12 @@ def test_graph_replay_matches_eager(dev):
         q4.fused_gate_up_silu_q4k_gemv(outs["h5"], wgd, wud, xd, 5, N, K, stream=stream)
         q4.moe_router_q4_0(outs["ids"], outs["wts"], wr, xd, 4, E, K, top_k, 1, stream=stream)
         q4.moe_q4_gemv_silu(outs["hm"], mg, mu, xd, outs["ids"], 4, top_k, E, NE, K,
+                            stream=stream)
+        q4.q4_0_gemv_splitk(outs["sk8"], w0d, xd, 8, N, K, ws, stream=stream)
+        q4.q4k_gemv_splitk(outs["skk4"], wgd, xd, 4, N, K, ws, stream=stream)
+        q4.q4_0_gemv_splitk_noalloc(outs["na6"], w0d, xd, 6, N, K, stream=stream)
+        q4.q4_0_gemv_soa(outs["soa3"], sc, qs, xd, 3, N, K, stream=stream)
+        q4.moe_q4_gemv_down(outs["dn"], wdn, hd, outs["ids"], 4, top_k, E, ND, KD,
                             stream=stream)
 
     s = torch.cuda.Stream()
