@@ -62,6 +62,9 @@ def case(dev, orc, fmt, M, N, K, seed, x=None, ws=None):
     (Q4_0, 3, 4096, 4096), (Q4_0, 4, 4096, 4096), (Q4_0, 8, 4096, 4096),
     (Q4_0, 16, 4096, 4096), (Q4K, 4, 4096, 14336), (Q4K, 16, 2048, 4096),
     (Q4_0, 5, 777, 1408), (Q4K, 6, 513, 2080), (Q4K, 8, 33, 32768), (Q4_0, 12, 16, 4096),
+    # rows of more than 256 steps with many tile groups: parts of 6-7 steps,
+    # staged in two passes from global memory
+    (Q4_0, 3, 1024, 131072), (Q4K, 12, 512, 98304),
 ])
 def test_splitk_parity(dev, orc, fmt, M, N, K):
     assert ws_bytes(fmt, M, N, K) > 0
