@@ -313,12 +313,13 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
  *     workspace must not overlap.  A smaller workspace: Q4_ERR_SHAPE; NULL
  *     where one is needed: Q4_ERR_NULL.  Other limits and alignment as
  *     q4_0_gemv / q4k_gemv.
- * It pays where staging dominates: 16 tokens, or long K (on MI355X, 4 x
- * 14336 against 4096 rows: 19 against 30 us; 16 x 4096 against 4096 rows:
- * 19 against 31 us); at 4 or 8 tokens of K = 4096 the ordinary call is
- * faster.  (The pages' kernels stage x once per workgroup; splitting K over
- * workgroups is this library's answer to the staging cost of batches on a
- * 256-CU part.)
+ * It pays where staging dominates, i.e. for few output rows (on MI355X,
+ * 4096 x 4096 at 4 / 8 / 16 tokens: 9.2 / 9.9 / 11.9 against 10.0 / 11.5 /
+ * 30.7 us; the 4096 x 14336 down-projection at 4 tokens: 15.7 against
+ * 29.1 us); with many output rows the ordinary call already shares its
+ * staging among 128 rows per workgroup.  (The pages' kernels stage x once
+ * per workgroup; splitting K over workgroups is this library's answer to
+ * the staging cost of batches on a 256-CU part.)
  */
 enum { Q4_FORMAT_Q4_0 = 0, Q4_FORMAT_Q4K = 1 };
 int q4_splitk_workspace(int format, int64_t M, int64_t N, int64_t K, int64_t* bytes);
