@@ -28,6 +28,9 @@ totalling at least 1 GiB.
 
   --all REPORT   additionally time every named workload and its ceiling and
                  write REPORT.json and REPORT.md
+  --ceilings     only time the read ceilings of this part: the reference
+                 stream and a device copy at the headline's 66 MB and at 8
+                 times that
   --copy-calibration MIB
                  only run a plain device-to-device copy of MIB MiB 20 times:
                  the known-size reference that scales the FETCH_SIZE and
@@ -67,6 +70,9 @@ def parse_args():
                     help="only time dispatch chains (the smallest call back to back, a dense "
                          "FFN decode step, an expert decode step; eager and as HIP graph "
                          "replays) and the submit+wait / submit+spin turnaround")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only time the reference stream and a device copy at the headline's "
+                         "66 MB and at 8 times that (the read ceilings of this part)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 20 times (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -709,6 +715,49 @@ def measure_copy(torch, dev, nbytes, reps=50):
     return dict(bytes=n * 4, us_mean=us, read_write_gbs=2 * n * 4 / (us * 1e-6) / 1e9)
 
 
+CEILING_BYTES = (66060288, 8 * 66060288)  # the headline's weight bytes, and 8 times that
+
+
+def measure_ceilings(torch, dev, warmup=10, steps=100):
+    """The read ceilings of this part at the headline's size and at 8 times it:
+    the reference stream (Q4_READ_STREAM: 16-byte loads per lane, 4 KiB per
+    wave step, the next block's loads ahead, non-temporal) over a rotation of
+    at least 1 GiB, timed like every workload (HIP graphs of 100 launches,
+    events), and a device-to-device copy of the same bytes beside it."""
+    import numpy as np
+
+    import bit_block_quantized_dequant_amd as q4
+    from bit_block_quantized_dequant_amd import synth
+    L = q4.lib()
+    out = []
+    for nbytes in CEILING_BYTES:
+        rng = np.random.default_rng(7000 + nbytes % 997)
+        rot = Rotation(torch, dev, rng.integers(0, 256, nbytes, dtype=np.uint8))
+        srb = synth.q4k_row_bytes(256)
+        srows = nbytes // srb
+        cks = torch.empty((srows * srb + 4095) // 4096, dtype=torch.int32, device=dev)
+
+        def launch(i, stream):
+            check(L.q4_pure_read(cks.data_ptr(), q4.Q4_READ_STREAM, rot.ptr(i), None, None, 1,
+                                 0, 0, srows, 256, stream), "q4_pure_read")
+        wall, durs, cnts = time_launches(torch, launch, warmup, steps, [cks])
+        st = stats(durs, cnts)
+        cp = measure_copy(torch, dev, nbytes)
+        gbs = nbytes / (st["mean_ms"] * 1e-3) / 1e9
+        out.append(dict(bytes=nbytes, copies=rot.ncopies, stream_us_mean=st["mean_ms"] * 1e3,
+                        stream_us_median=st["median_ms"] * 1e3, stream_gbs=gbs,
+                        stream_frac_of_peak=gbs / HBM_PEAK_GBS,
+                        copy_us_mean=cp["us_mean"], copy_read_write_gbs=cp["read_write_gbs"]))
+        print("read ceiling %d bytes: stream %.2f us (%.0f GB/s, %.1f%% of 8 TB/s); device copy "
+              "%.2f us (%.0f GB/s read+write)" % (nbytes, st["mean_ms"] * 1e3, gbs,
+                                                  100 * gbs / HBM_PEAK_GBS, cp["us_mean"],
+                                                  cp["read_write_gbs"]),
+              file=sys.stderr, flush=True)
+        del rot, cks
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch, dev, mib):
     """A plain device-to-device copy of known size, run 20 times."""
     n = mib * (1 << 20) // 4
@@ -781,6 +830,9 @@ def main():
         return
     if args.chain:
         print(json.dumps({"chain": measure_chain(torch, dev)}), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps({"ceilings": measure_ceilings(torch, dev)}), flush=True)
         return
 
     head = measure(torch, dev, 4, 1, args.warmup, args.steps)
