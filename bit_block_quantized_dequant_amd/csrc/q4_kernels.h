@@ -419,48 +419,59 @@ __device__ __forceinline__ int moe_load_id(const GemvParams& p) {
     return p.ids[min((int)threadIdx.x & (kWave - 1), M * p.top_k - 1)];
 }
 
-// In-kernel dedupe of the expert ids (wave 0, from moe_load_id); everyone
-// reads it after the barrier that follows.
+// In-kernel dedupe of the expert ids (from moe_load_id); wave 0 writes the
+// result, and everyone reads it after the barrier that follows.
+//   uexp[u]   the u-th unique valid id, in order of first appearance
+//   upairs[u] the (token, slot) pairs that chose it (bit m * top_k + s)
+//   utok[u]   the tokens that chose it (bit m)
+//   nu, invalid: the count of unique valid ids; the pairs with an id outside [0, E)
+// One pass per unique expert, not per pair: the lowest pair not yet grouped
+// names the next expert (so the experts come in order of first appearance), a
+// ballot gives every pair with the same id, and lane u keeps expert u's id and
+// pair mask in registers.  The loop is wave-uniform and branch-free inside
+// (a first version looped over the pairs with a divergent branch per pair;
+// at 12 waves per CU that loop took about 4 us before any weight load).
 template <int M>
 __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh, int e_loaded) {
     // every wave computes it (its own copy of the ids, so that their load is
-    // used unconditionally and stays where it was issued); wave 0 writes it
+    // used unconditionally and stays where it was issued)
     const int lane = threadIdx.x & (kWave - 1);
-    const bool w0 = threadIdx.x < kWave;
-    {
-        const int P = M * p.top_k;
-        const bool in = lane < P;
-        const int e = in ? e_loaded : -1;
-        const bool ok = in && e >= 0 && e < p.E;
-        // (pair t's id and validity are read with v_readlane into scalar
-        // registers: t is uniform, so no LDS permute round trip per pair)
-        const int eo = ok ? e : -1;  // -1: an invalid pair matches nothing
-        // first appearance of e among the valid pairs; the pairs and tokens
-        // that chose it
-        bool first = ok;
-        unsigned long long pairs = 0;
-        unsigned int toks = 0;
-        for (int t = 0; t < P; ++t) {
-            const int et = __builtin_amdgcn_readlane(eo, t);
-            const bool same = ok && et == e;
-            if (t < lane && same) first = false;
-            if (same) {
-                pairs |= 1ull << t;
-                toks |= 1u << (t / p.top_k);
-            }
-        }
-        const unsigned long long fb = __ballot(first);
-        const unsigned long long bad = __ballot(in && !ok);
-        const int uidx = __popcll(fb & ((1ull << lane) - 1ull));
-        if (w0 && first) {
-            sh.uexp[uidx] = e;
-            sh.upairs[uidx] = pairs;
-            sh.utok[uidx] = toks;
-        }
-        if (threadIdx.x == 0) {
-            sh.nu = __popcll(fb);
-            sh.invalid = bad;
-        }
+    const int P = M * p.top_k;
+    const bool in = lane < P;
+    const bool ok = in && e_loaded >= 0 && e_loaded < p.E;
+    const int ev = ok ? e_loaded : -1;  // -1 (invalid, or no pair) matches no expert
+    unsigned long long todo = __ballot(ok);  // valid pairs not yet grouped
+    const unsigned long long bad = __ballot(in && !ok);
+    int uid = -1;
+    uint32_t plo = 0u, phi = 0u;
+    int nu = 0;
+    while (todo != 0ull) {
+        const int t = __builtin_ctzll(todo);
+        const int et = __builtin_amdgcn_readlane(ev, t);
+        const unsigned long long same = __ballot(ev == et);
+        todo &= ~same;
+        const bool mine = lane == nu;
+        uid = mine ? et : uid;
+        plo = mine ? (uint32_t)same : plo;
+        phi = mine ? (uint32_t)(same >> 32) : phi;
+        ++nu;
+    }
+    // lane u < nu: the tokens among expert u's pairs (m * top_k < 64 for m < M,
+    // as M * top_k <= 64)
+    const unsigned long long pm = ((unsigned long long)phi << 32) | plo;
+    const unsigned long long tkmask = p.top_k >= 64 ? ~0ull : ((1ull << p.top_k) - 1ull);
+    unsigned int toks = 0u;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        if ((pm >> (m * p.top_k)) & tkmask) toks |= 1u << m;
+    if (threadIdx.x < kWave && lane < nu) {
+        sh.uexp[lane] = uid;
+        sh.upairs[lane] = pm;
+        sh.utok[lane] = toks;
+    }
+    if (threadIdx.x == 0) {
+        sh.nu = nu;
+        sh.invalid = bad;
     }
 }
 
@@ -499,7 +510,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
         if constexpr (!PURE) stage_x_issue<MODE, NX>(p, M, xst, kBS);
         moe_dedupe<M>(p, moe, eid);
         sync_lds();
-        tpe = p.nrg / p.rgw;
+        tpe = p.nrg >> __builtin_ctz(p.rgw);  // (rgw: a power of two dividing nrg)
         ntasks = moe.nu * tpe;
     }
 #if Q4_TASK_ORDER == 1
@@ -514,8 +525,9 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     const int t1 = (int)(((long long)(gwave + 1) * ntasks) / p.nwaves);
     const int tstride = 1;
 #endif
-    const int gi = lane / p.lg;       // row group of this lane within a pass
-    const int li = lane - gi * p.lg;  // lane within its row group
+    // (lg: a power of two from 4 to 64)
+    const int gi = lane >> __builtin_ctz(p.lg);  // row group of this lane within a pass
+    const int li = lane & (p.lg - 1);            // lane within its row group
     const uint32_t sel = q4k_sel(li & 3);
 
     // ---- cursor over (task, unit) steps; advanced without divisions ----

@@ -182,6 +182,44 @@ def test_moe_invalid_ids_give_nan(dev, orc):
     assert np.all(np.abs(u[ok] - ru[ok]) <= 1e-4 * au[ok])
 
 
+def test_moe_dedupe_extremes(dev, orc):
+    """The in-kernel dedupe at its ends, for the gate/up, SiLU-gated and
+    down-projection expert calls: all 64 pairs on one expert (one unique
+    expert, every slot written), and every pair invalid (no expert to read,
+    every row NaN)."""
+    import bit_block_quantized_dequant_amd as q4
+    M, top_k, E, N, K = 8, 8, 9, 40, 512  # (top_k <= E)
+    rng = synth.make_rng(5077)
+    wg, wu = synth.q4_0_matrix(rng, E * N, K), synth.q4_0_matrix(rng, E * N, K)
+    wd = synth.q4_0_matrix(rng, E * N, K)
+    x = synth.activations(rng, M, K)
+    h = synth.activations(rng, M * top_k, K).reshape(M, top_k, K)
+    for ids, what in ((np.full((M, top_k), 3, np.int32), "one expert for all 64 pairs"),
+                      (np.full((M, top_k), E, np.int32), "every id invalid")):
+        g, u = empty((M, top_k, N), dev), empty((M, top_k, N), dev)
+        hs, yd = empty((M, top_k, N), dev), empty((M, top_k, N), dev)
+        q4.moe_q4_gemv(g, u, T(wg, dev), T(wu, dev), T(x, dev), T(ids, dev), M, top_k, E, N, K)
+        q4.moe_q4_gemv_silu(hs, T(wg, dev), T(wu, dev), T(x, dev), T(ids, dev), M, top_k, E, N,
+                            K)
+        q4.moe_q4_gemv_down(yd, T(wd, dev), T(h, dev), T(ids, dev), M, top_k, E, N, K)
+        g, u, hs, yd = host(g), host(u), host(hs), host(yd)
+        if ids[0, 0] >= E:
+            for a, nm in ((g, "gate"), (u, "up"), (hs, "silu"), (yd, "down")):
+                assert np.all(np.isnan(a)), "%s: %s rows must be NaN" % (what, nm)
+            continue
+        rg, ru, ag, au = orc.moe_q4_0_gemv(wg, wu, x, ids, E, N, K, NT)
+        assert_bound(g, rg, ag, what + " gate")
+        assert_bound(u, ru, au, what + " up")
+        rd, ad = orc.moe_q4_0_down(wd, h, ids, E, N, K, NT)
+        assert_bound(yd, rd, ad, what + " down")
+        ref = orc.silu_mul(rg, ru)
+        dg, du = 1e-4 * ag, 1e-4 * au
+        sg = np.abs(orc.silu_mul(rg, np.ones_like(rg)))
+        uu = np.abs(ru) + du
+        bound = 1.1 * dg * uu + sg * du + 2.0 ** -20 * (sg + 1.1 * dg) * uu + 1e-30
+        assert np.all(np.abs(hs - ref) <= bound), what + " silu"
+
+
 # ---------------------------------------------------------------------------
 # shape sweep: ragged N, every lane-group width, every M
 # ---------------------------------------------------------------------------
