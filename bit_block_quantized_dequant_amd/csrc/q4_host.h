@@ -144,11 +144,15 @@ inline int wg_per_cu(size_t lds, int mx = 2) {
 }
 
 // Raise a kernel's dynamic-LDS limit once per device: to 160 KB less
-// `reserve` bytes kept for its static shared variables.
+// `reserve` bytes kept for its static shared variables (at least what the
+// kernel declares).
 inline int allow_big_lds(const void* kern, std::atomic<int>* done, int reserve = 2048) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
     if (done[dev].load(std::memory_order_acquire)) return Q4_OK;
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, kern) != hipSuccess) return Q4_ERR_HIP;
+    if ((long long)fa.sharedSizeBytes > reserve) reserve = (int)fa.sharedSizeBytes;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        160 * 1024 - reserve);
     if (e != hipSuccess) return Q4_ERR_HIP;
@@ -261,10 +265,10 @@ inline bool xr_enabled() {
 template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
 inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     constexpr int RR = mode_moe(MODE) ? Q4_RR_MOE : (NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR);
-    // Workgroup shape (measured): single-token and expert calls run 256-thread
-    // groups; dense single-token calls at most two per CU (four were 4 %
-    // slower), expert calls up to four (their 136 VGPRs allow three: 12
-    // waves per CU instead of 8 with 512-thread groups, 9-14 % faster).
+    // Workgroup shape (measured): dense single-token calls run 256-thread
+    // groups, at most two per CU (four were 4 % slower); expert calls 256- or
+    // 768-thread groups (gemv_threads), as many as their 134-147 VGPRs allow:
+    // 12 waves per CU, which beat 8 waves of 512-thread groups by 9-14 %.
     // Dense batched calls on this kernel run two 512-thread groups.
     constexpr int BS = gemv_threads(M, MODE);
     constexpr int WGMAX = mode_moe(MODE) ? 4 : 2;
@@ -296,7 +300,7 @@ inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         if (upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
-    if ((long long)M * p.K > (long long)xreg_chunks(MODE) * 4 * gemv_threads(M, MODE))
+    if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }

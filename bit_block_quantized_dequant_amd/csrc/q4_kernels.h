@@ -29,10 +29,21 @@
 
 namespace q4 {
 
-// Threads per workgroup of the VALU GEMV kernel: 256 for single-token and
-// expert calls, 512 for dense batched calls.
+// Threads per workgroup of the VALU GEMV kernel: 256 for single-token calls,
+// 512 for dense batched calls; the expert calls 256 at M = 2 .. 4 and 768
+// otherwise.  An expert call stages all M token rows in every workgroup: one
+// 768-thread workgroup per CU stages them once per CU instead of three
+// times, at the same 12 waves per CU.  Measured (E = 64, top-6, K = 2048,
+// one box, 768 against 256 threads): M = 1 -5 %, M = 6 and 8 -10 to -12 %,
+// but M = 2 .. 4 +3 to +7 %.
 constexpr int kBlock = 512;
 constexpr int kBlock1 = 256;
+#ifndef Q4_MOE_BLOCK
+#define Q4_MOE_BLOCK 0  // 0: by M as above; else every expert call (for measurements)
+#endif
+constexpr int moe_block(int M) {
+    return Q4_MOE_BLOCK > 0 ? Q4_MOE_BLOCK : ((M >= 2 && M <= 4) ? 256 : 768);
+}
 constexpr int kModeDense = 0;
 constexpr int kModeNorm = 1;
 constexpr int kModeMoe = 2;
@@ -48,7 +59,7 @@ constexpr bool mode_silu(int mode) {
 }
 constexpr bool mode_norm(int mode) { return mode == kModeNorm || mode == kModeNormSilu; }
 constexpr int gemv_threads(int M, int mode) {
-    return (M == 1 || mode_moe(mode)) ? kBlock1 : kBlock;
+    return mode_moe(mode) ? moe_block(M) : (M == 1 ? kBlock1 : kBlock);
 }
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)), in fp32.  With
@@ -109,11 +120,11 @@ struct GemvParams {
 
 // Shared state of the expert call after the in-kernel dedupe.
 struct MoeShared {
-    int nu;                    // unique valid experts
-    int uexp[kMaxPairs];       // their ids, in order of first appearance
+    alignas(16) int uexp[kMaxPairs];       // unique valid ids, in order of first appearance
     unsigned long long upairs[kMaxPairs];  // (token, slot) pairs that chose each
     unsigned long long invalid;            // pairs with an id outside [0, E)
-    unsigned int utok[kMaxPairs];           // tokens that chose each (bit m)
+    unsigned int utok[kMaxPairs];          // tokens that chose each (bit m)
+    int nu;                                // unique valid experts
 };
 
 // Stage the M activation rows into LDS.  Chunk layout and pre-scaling as in
@@ -133,10 +144,13 @@ struct MoeShared {
 // global loads of the first NX chunks per thread go out first (the load
 // counter is in order, so waiting for them later does not wait for the
 // weights); chunks beyond that load in the second half, behind the weights.
-// NX is kXReg, or 8 for the expert call, whose 4 tokens of K = 2048 make 8
-// chunks per thread of its 256-thread workgroups.
+// NX is kXReg, or for the expert call the chunks per thread of M tokens of
+// K = 2048 (512 chunks each) in its workgroups (longer rows take the tail
+// loop).
 constexpr int kXReg = 4;
-constexpr int xreg_chunks(int mode) { return mode_moe(mode) ? 2 * kXReg : kXReg; }
+constexpr int xreg_chunks(int M, int mode) {
+    return mode_moe(mode) ? (M * 512 + moe_block(M) - 1) / moe_block(M) : kXReg;
+}
 constexpr int kXTarget = 60;
 
 template <int NX = kXReg>
@@ -146,14 +160,14 @@ struct XStage {
 };
 
 // Per-workgroup scratch of the staging reductions: per token and wave, the
-// sum of squares and the largest magnitude (workgroups of at most 8 waves).
+// sum of squares and the largest magnitude (W waves, 8 unless stated).
 constexpr int kMaxStageWaves = 8;
 static_assert(kBlock / kWave <= kMaxStageWaves && kBlock1 / kWave <= kMaxStageWaves,
               "staging scratch holds 8 waves");
-template <int MT>
+template <int MT, int W = kMaxStageWaves>
 struct StageRedT {
-    double ss[MT][kMaxStageWaves];
-    float am[MT][kMaxStageWaves];
+    double ss[MT][W];
+    float am[MT][W];
     float r[MT];  // per token: the RMSNorm factor
     int e[MT];    // per token: the scale exponent
 };
@@ -196,22 +210,48 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // (bs: the kernel's block size, a compile-time constant of every caller, so
 // that no load of the dispatch's block size precedes these loads)
+// The (token m, chunk c) position of chunk index i = i0 + k * step in rows of
+// kq chunks, advanced one step at a time with two divisions up front instead
+// of one per step.
+struct ChunkWalk {
+    int m, c, dm, dc, kq;
+    __device__ __forceinline__ ChunkWalk(int i0, int step, int kq_) : kq(kq_) {
+        m = i0 / kq;
+        c = i0 - m * kq;
+        dm = step / kq;
+        dc = step - dm * kq;
+    }
+    __device__ __forceinline__ void next() {
+        c += dc;
+        m += dm;
+        if (c >= kq) {
+            c -= kq;
+            ++m;
+        }
+    }
+};
+
 template <int MODE, int NX = kXReg>
 __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage<NX>& st, int bs) {
     const int kq = p.K >> 2;
     const int total = M * kq;
     const float4* x4 = (const float4*)p.x;
     const float4* g4 = (const float4*)p.gamma;
+    // (the gamma chunk, i mod K/4, is walked without a division per chunk)
+    ChunkWalk w((int)threadIdx.x, bs, mode_norm(MODE) ? kq : 1 << 30);
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
         // unconditional (clamped) loads keep the load-counter waits exact
-        const int i = min((int)threadIdx.x + k * bs, total - 1);
-        st.x[k] = x4[i];
-        if constexpr (mode_norm(MODE)) st.g[k] = g4[i % kq];
+        const int i = (int)threadIdx.x + k * bs;
+        st.x[k] = x4[min(i, total - 1)];
+        if constexpr (mode_norm(MODE)) {
+            st.g[k] = g4[i < total ? w.c : kq - 1];
+            w.next();
+        }
     }
 }
 
-// One float4 chunk i of the activations (of token m = i / (K/4), scaled by
+// One float4 chunk of the activations (chunk c of token m, scaled by
 // 2^e): its 32-element run sum (over the 8 lanes that hold the run) and its
 // pre-scaled, swizzled LDS copy.  Called by every lane; only lanes with
 // `store` write (the others hold a clamped duplicate chunk and only take
@@ -220,11 +260,8 @@ __device__ __forceinline__ void stage_x_issue(const GemvParams& p, int M, XStage
 // the register-resident kernel applies both when it copies its lane's
 // activations into registers.
 template <int FMT, int M, bool DEFER = false>
-__device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int i, bool store,
-                                            float4* xl, float* xsum, int e) {
-    const int kq = p.K >> 2;
-    const int m = i / kq;
-    const int c = i - m * kq;
+__device__ __forceinline__ void stage_chunk(const GemvParams& p, float4 v, int m, int c,
+                                            bool store, float4* xl, float* xsum, int e) {
     if constexpr (!DEFER) {
         v.x = __builtin_ldexpf(v.x, e);
         v.y = __builtin_ldexpf(v.y, e);
@@ -268,9 +305,9 @@ __device__ __forceinline__ void stage_pad(const GemvParams& p, float4* xl, float
 // DEFER (single token, no RMSNorm): no reduction barrier here; the chunks
 // are stored unscaled and each wave's partial maximum is left in red.am[0],
 // to be combined after the caller's barrier (stage_x_exponent).
-template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg, bool DEFER = false>
+template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg, bool DEFER = false, class RED>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
-                                               float4* xl, float* xsum, StageRed& red,
+                                               float4* xl, float* xsum, RED& red,
                                                int (&xe)[M], int bs) {
     static_assert(!DEFER || (M == 1 && !mode_norm(MODE)), "deferred scaling: one token, no norm");
     const int tid = threadIdx.x;
@@ -288,9 +325,8 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         am[m] = 0.f;
     }
     // sum of squares (RMSNorm) and the largest |x| (|x * gamma| for RMSNorm,
-    // whose rows are scaled by r afterwards) of chunk i
-    auto acc = [&](float4 v, float4 g, int i, bool valid) {
-        const int m = i / kq;
+    // whose rows are scaled by r afterwards) of a chunk of token m
+    auto acc = [&](float4 v, float4 g, int m, bool valid) {
         double t = 0.0;
         float a;
         if constexpr (mode_norm(MODE)) {
@@ -304,24 +340,37 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
         t = valid ? t : 0.0;
         a = valid ? a : 0.f;
+        // selects, not branches (a per-lane branch per token and chunk was
+        // compiled as divergent control flow); t, a >= 0, so adding 0 or
+        // taking the maximum with 0 leaves the other tokens unchanged
 #pragma unroll
-        for (int mm = 0; mm < M; ++mm)
-            if (m == mm) {
-                ss[mm] += t;
-                am[mm] = fmaxf(am[mm], a);
-            }
+        for (int mm = 0; mm < M; ++mm) {
+            const bool mine = m == mm;
+            if constexpr (mode_norm(MODE)) ss[mm] += mine ? t : 0.0;
+            am[mm] = fmaxf(am[mm], mine ? a : 0.f);
+        }
     };
+    // chunk positions: (mk[k], ck[k]) for the k-th register chunk (the
+    // clamped duplicate's for lanes past the end), then the tail's walk
+    int mk[NX], ck[NX];
+    ChunkWalk wk(tid, bs, kq);
 #pragma unroll
     for (int k = 0; k < NX; ++k) {
-        const int i = tid + k * bs;
-        acc(st.x[k], st.g[k], min(i, total - 1), i < total);
+        const bool valid = tid + k * bs < total;
+        mk[k] = valid ? wk.m : M - 1;
+        ck[k] = valid ? wk.c : kq - 1;
+        wk.next();
     }
-    if constexpr (TAIL)
-        for (int i = tid + NX * bs; i < total; i += bs) {
+#pragma unroll
+    for (int k = 0; k < NX; ++k) acc(st.x[k], st.g[k], mk[k], tid + k * bs < total);
+    if constexpr (TAIL) {
+        ChunkWalk wt = wk;
+        for (int i = tid + NX * bs; i < total; i += bs, wt.next()) {
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (mode_norm(MODE)) g = g4[i % kq];
-            acc(x4[i], g, i, true);
+            if constexpr (mode_norm(MODE)) g = g4[wt.c];
+            acc(x4[i], g, wt.m, true);
         }
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const float a = wave_max_nonneg(am[m]);  // exact in lane 63
@@ -335,14 +384,14 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
     if constexpr (DEFER) {
         (void)nw;
 #pragma unroll
-        for (int k = 0; k < NX; ++k) {
-            const int i = tid + k * bs;
-            const int ic = min(i, total - 1);
-            stage_chunk<FMT, M, true>(p, st.x[k], ic, i < total, xl, xsum, 0);
+        for (int k = 0; k < NX; ++k)
+            stage_chunk<FMT, M, true>(p, st.x[k], mk[k], ck[k], tid + k * bs < total, xl, xsum,
+                                      0);
+        if constexpr (TAIL) {
+            ChunkWalk wt = wk;
+            for (int i = tid + NX * bs; i < total; i += bs, wt.next())
+                stage_chunk<FMT, M, true>(p, x4[i], wt.m, wt.c, true, xl, xsum, 0);
         }
-        if constexpr (TAIL)
-            for (int i = tid + NX * bs; i < total; i += bs)
-                stage_chunk<FMT, M, true>(p, x4[i], i, true, xl, xsum, 0);
         return;
     }
     sync_lds();
@@ -376,9 +425,9 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
     }
     // (one token: the factor and exponent stay in registers)
-    auto norm = [&](float4 v, float4 g, int i) {
+    auto norm = [&](float4 v, float4 g, int m) {
         if constexpr (mode_norm(MODE)) {
-            const float r = M == 1 ? r1 : red.r[i / kq];
+            const float r = M == 1 ? r1 : red.r[m];
             v.x = (v.x * r) * g.x;
             v.y = (v.y * r) * g.y;
             v.z = (v.z * r) * g.z;
@@ -386,25 +435,25 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         }
         return v;
     };
-    auto tok_e = [&](int i) { return M == 1 ? xe[0] : red.e[i / kq]; };
+    auto tok_e = [&](int m) { return M == 1 ? xe[0] : red.e[m]; };
 #pragma unroll
-    for (int k = 0; k < NX; ++k) {
-        const int i = tid + k * bs;
-        const int ic = min(i, total - 1);
-        stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], ic), ic, i < total, xl, xsum, tok_e(ic));
-    }
+    for (int k = 0; k < NX; ++k)
+        stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], mk[k]), mk[k], ck[k], tid + k * bs < total,
+                            xl, xsum, tok_e(mk[k]));
     if constexpr (TAIL) {
-        for (int i = tid + NX * bs; i < total; i += bs) {
+        ChunkWalk wt = wk;
+        for (int i = tid + NX * bs; i < total; i += bs, wt.next()) {
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (mode_norm(MODE)) g = g4[i % kq];
-            stage_chunk<FMT, M>(p, norm(x4[i], g, i), i, true, xl, xsum, tok_e(i));
+            if constexpr (mode_norm(MODE)) g = g4[wt.c];
+            stage_chunk<FMT, M>(p, norm(x4[i], g, wt.m), wt.m, wt.c, true, xl, xsum, tok_e(wt.m));
         }
     }
 }
 
 // The scale exponent of a single token staged with DEFER, from the waves'
 // partial maxima (call after the barrier that follows the staging).
-__device__ __forceinline__ int stage_x_exponent(const StageRed& red, int nwaves) {
+template <class RED>
+__device__ __forceinline__ int stage_x_exponent(const RED& red, int nwaves) {
     float a = 0.f;
     for (int i = 0; i < nwaves; ++i) a = fmaxf(a, red.am[0][i]);
     return __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
@@ -419,58 +468,67 @@ __device__ __forceinline__ int moe_load_id(const GemvParams& p) {
     return p.ids[min((int)threadIdx.x & (kWave - 1), M * p.top_k - 1)];
 }
 
-// In-kernel dedupe of the expert ids (from moe_load_id); wave 0 writes the
-// result, and everyone reads it after the barrier that follows.
+// In-kernel dedupe of the expert ids (from moe_load_id); wave 0 computes and
+// writes the result, and everyone reads it after the barrier that follows.
 //   uexp[u]   the u-th unique valid id, in order of first appearance
 //   upairs[u] the (token, slot) pairs that chose it (bit m * top_k + s)
 //   utok[u]   the tokens that chose it (bit m)
 //   nu, invalid: the count of unique valid ids; the pairs with an id outside [0, E)
-// One pass per unique expert, not per pair: the lowest pair not yet grouped
-// names the next expert (so the experts come in order of first appearance), a
-// ballot gives every pair with the same id, and lane u keeps expert u's id and
-// pair mask in registers.  The loop is wave-uniform and branch-free inside
-// (a first version looped over the pairs with a divergent branch per pair;
-// at 12 waves per CU that loop took about 4 us before any weight load).
+// Lane t holds pair t's id.  The ids go through LDS (uexp doubles as the
+// buffer) and come back as broadcast reads, four at a time, so that every
+// lane compares its id with every pair's in plain vector arithmetic: the
+// pairs with the same id, and whether an earlier pair has it (then the lane
+// is not the expert's first appearance).  Its index among the first
+// appearances is a bit count over one ballot.  No lane mask is combined on
+// the scalar unit inside the loop: a version that did (one ballot and a
+// scalar update per unique expert) spent about 60 ns per expert waiting for
+// vector results on the scalar side, and one with a branch per pair about
+// 4 us in all before the first weight load.
 template <int M>
 __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh, int e_loaded) {
-    // every wave computes it (its own copy of the ids, so that their load is
-    // used unconditionally and stays where it was issued)
-    const int lane = threadIdx.x & (kWave - 1);
+    // every wave waits for its id load here, where it was issued (a load
+    // used only under the branch below could be moved into it, behind the
+    // activation loads)
+    asm volatile("" ::"v"(e_loaded));
+    if (threadIdx.x >= kWave) return;  // wave-uniform
+    const int lane = threadIdx.x;
     const int P = M * p.top_k;
     const bool in = lane < P;
     const bool ok = in && e_loaded >= 0 && e_loaded < p.E;
-    const int ev = ok ? e_loaded : -1;  // -1 (invalid, or no pair) matches no expert
-    unsigned long long todo = __ballot(ok);  // valid pairs not yet grouped
+    const int ev = ok ? e_loaded : -1;  // -1 (invalid, or no pair) matches no valid id
     const unsigned long long bad = __ballot(in && !ok);
-    int uid = -1;
-    uint32_t plo = 0u, phi = 0u;
-    int nu = 0;
-    while (todo != 0ull) {
-        const int t = __builtin_ctzll(todo);
-        const int et = __builtin_amdgcn_readlane(ev, t);
-        const unsigned long long same = __ballot(ev == et);
-        todo &= ~same;
-        const bool mine = lane == nu;
-        uid = mine ? et : uid;
-        plo = mine ? (uint32_t)same : plo;
-        phi = mine ? (uint32_t)(same >> 32) : phi;
-        ++nu;
+    // (wave 0's LDS operations complete in order: the reads see this write)
+    sh.uexp[lane] = ev;
+    unsigned long long mine = 0ull;  // the pairs whose id equals this lane's
+    uint32_t dup = 0u;               // 1: an earlier pair has this lane's id
+    for (int t0 = 0; t0 < P; t0 += 4) {
+        const int4 q = *(const int4*)&sh.uexp[t0];  // entries past P hold -1
+        const int et[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + j;
+            const uint32_t same = 1u - min((uint32_t)(ev ^ et[j]), 1u);
+            mine |= (unsigned long long)same << t;
+            dup |= same & ((uint32_t)(t - lane) >> 31);  // t < lane
+        }
     }
-    // lane u < nu: the tokens among expert u's pairs (m * top_k < 64 for m < M,
-    // as M * top_k <= 64)
-    const unsigned long long pm = ((unsigned long long)phi << 32) | plo;
+    const bool first = ok && dup == 0u;
+    const unsigned long long fb = __ballot(first);
+    const int u = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(fb >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)fb, 0u));
+    // the tokens among the pairs (m * top_k < 64 for m < M, as M * top_k <= 64)
     const unsigned long long tkmask = p.top_k >= 64 ? ~0ull : ((1ull << p.top_k) - 1ull);
     unsigned int toks = 0u;
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        if ((pm >> (m * p.top_k)) & tkmask) toks |= 1u << m;
-    if (threadIdx.x < kWave && lane < nu) {
-        sh.uexp[lane] = uid;
-        sh.upairs[lane] = pm;
-        sh.utok[lane] = toks;
+        if ((mine >> (m * p.top_k)) & tkmask) toks |= 1u << m;
+    if (first) {
+        sh.uexp[u] = e_loaded;
+        sh.upairs[u] = mine;
+        sh.utok[u] = toks;
     }
-    if (threadIdx.x == 0) {
-        sh.nu = nu;
+    if (lane == 0) {
+        sh.nu = __popcll(fb);
         sh.invalid = bad;
     }
 }
@@ -483,10 +541,9 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     static_assert(!XR || (M == 1 && !mode_moe(MODE)), "register-resident x: M = 1 only");
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
-    __shared__ StageRed red;
-
     constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
     constexpr int kBS = gemv_threads(M, MODE);  // the launch's block size (run_plan)
+    __shared__ StageRedT<8, (kBS / kWave > kMaxStageWaves ? kBS / kWave : kMaxStageWaves)> red;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the wave index is wave-uniform; say so, so that all task bookkeeping
@@ -503,7 +560,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     // Activation loads go out first (the expert call: right after its ids,
     // so that their latency overlaps the dedupe; the barrier after the
     // dedupe waits for LDS only)
-    constexpr int NX = xreg_chunks(MODE);
+    constexpr int NX = xreg_chunks(M, MODE);
     XStage<NX> xst;
     if constexpr (mode_moe(MODE)) {
         const int eid = moe_load_id<M>(p);

@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kDownBlock) void moe_down_kernel(const GemvParams p
             float am[M];
 #pragma unroll
             for (int j = 0; j < M; ++j) am[j] = 0.f;
-            for (int i = tid; i < total; i += kDownBlock) {
-                const int j = i / kq4, c = i - j * kq4;
+            ChunkWalk w(tid, kDownBlock, kq4);
+            for (int i = tid; i < total; i += kDownBlock, w.next()) {
+                const int j = w.m, c = w.c;
                 const float4 v = h4[(long long)sh_pr[j] * kq4 + c];
                 const float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
                                       fmaxf(fabsf(v.z), fabsf(v.w)));
@@ -169,9 +170,10 @@ __global__ __launch_bounds__(kDownBlock) void moe_down_kernel(const GemvParams p
                 sh_e[tid] = xscale_exp(a, kXTarget);
             }
             sync_lds();
-            for (int i = tid; i < total; i += kDownBlock) {
-                const int j = i / kq4, c = i - j * kq4;
-                stage_chunk<FMT, M>(p, h4[(long long)sh_pr[j] * kq4 + c], i, true, xl, xsum,
+            ChunkWalk w2(tid, kDownBlock, kq4);
+            for (int i = tid; i < total; i += kDownBlock, w2.next()) {
+                const int j = w2.m, c = w2.c;
+                stage_chunk<FMT, M>(p, h4[(long long)sh_pr[j] * kq4 + c], j, c, true, xl, xsum,
                                     sh_e[j]);
             }
             sync_lds();
