@@ -270,7 +270,7 @@ inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     // 768-thread groups (gemv_threads), as many as their 134-147 VGPRs allow:
     // 12 waves per CU, which beat 8 waves of 512-thread groups by 9-14 %.
     // Dense batched calls on this kernel run two 512-thread groups.
-    constexpr int BS = gemv_threads(M, MODE);
+    constexpr int BS = gemv_threads(M, MODE, XR);
     constexpr int WGMAX = mode_moe(MODE) ? 4 : 2;
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
@@ -300,7 +300,7 @@ inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         if (upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
-    if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE))
+    if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE, false))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     return run_plan<FMT, NMAT, MODE, PURE, M, false, false>(p, cus, npairs_max, stream);
 }

@@ -58,8 +58,13 @@ constexpr bool mode_silu(int mode) {
     return mode == kModeSilu || mode == kModeMoeSilu || mode == kModeNormSilu;
 }
 constexpr bool mode_norm(int mode) { return mode == kModeNorm || mode == kModeNormSilu; }
-constexpr int gemv_threads(int M, int mode) {
-    return mode_moe(mode) ? moe_block(M) : (M == 1 ? kBlock1 : kBlock);
+#ifndef Q4_LONGK1_BLOCK
+#define Q4_LONGK1_BLOCK 512
+#endif
+// xr: the single-token kernel with register-resident activations (K <= 4096);
+// a single token with longer rows stages them in LDS, in the larger groups.
+constexpr int gemv_threads(int M, int mode, bool xr = true) {
+    return mode_moe(mode) ? moe_block(M) : (M == 1 ? (xr ? kBlock1 : Q4_LONGK1_BLOCK) : kBlock);
 }
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)), in fp32.  With
@@ -148,6 +153,10 @@ struct MoeShared {
 // K = 2048 (512 chunks each) in its workgroups (longer rows take the tail
 // loop).
 constexpr int kXReg = 4;
+#ifndef Q4_TAIL_BATCH
+#define Q4_TAIL_BATCH 4
+#endif
+constexpr int kTailBatch = Q4_TAIL_BATCH;  // tail chunks per batch of loads (stage_x_finish)
 constexpr int xreg_chunks(int M, int mode) {
     return mode_moe(mode) ? (M * 512 + moe_block(M) - 1) / moe_block(M) : kXReg;
 }
@@ -363,12 +372,34 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
     }
 #pragma unroll
     for (int k = 0; k < NX; ++k) acc(st.x[k], st.g[k], mk[k], tid + k * bs < total);
+    // The tail: chunks beyond the NX in registers, loaded kTailBatch at a
+    // time (one wait per batch; a wait for a load issued after the weight
+    // loads also waits for those) and kept in their LDS slots unscaled, so
+    // that the second pass reads them back from LDS instead of loading them
+    // again.  Chunks past the end (whole 32-element runs, as K/4 is a multiple
+    // of 8) take part as clamped duplicates and are neither counted nor stored.
+    const int kqr = xrow_chunks(p.upr);
+    auto slot = [&](int m, int c) { return m * kqr + xchunk(c >> 4, c & 15); };
     if constexpr (TAIL) {
         ChunkWalk wt = wk;
-        for (int i = tid + NX * bs; i < total; i += bs, wt.next()) {
-            float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (mode_norm(MODE)) g = g4[wt.c];
-            acc(x4[i], g, wt.m, true);
+        for (int i0 = tid + NX * bs; i0 < total; i0 += kTailBatch * bs) {
+            float4 t[kTailBatch], tg[kTailBatch];
+            ChunkWalk wl = wt;
+#pragma unroll
+            for (int j = 0; j < kTailBatch; ++j) {
+                const int i = i0 + j * bs;
+                t[j] = x4[min(i, total - 1)];
+                tg[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+                if constexpr (mode_norm(MODE)) tg[j] = g4[i < total ? wl.c : kq - 1];
+                wl.next();
+            }
+#pragma unroll
+            for (int j = 0; j < kTailBatch; ++j) {
+                const bool valid = i0 + j * bs < total;
+                acc(t[j], tg[j], valid ? wt.m : M - 1, valid);
+                if (valid) xl[slot(wt.m, wt.c)] = t[j];
+                wt.next();
+            }
         }
     }
 #pragma unroll
@@ -387,11 +418,7 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         for (int k = 0; k < NX; ++k)
             stage_chunk<FMT, M, true>(p, st.x[k], mk[k], ck[k], tid + k * bs < total, xl, xsum,
                                       0);
-        if constexpr (TAIL) {
-            ChunkWalk wt = wk;
-            for (int i = tid + NX * bs; i < total; i += bs, wt.next())
-                stage_chunk<FMT, M, true>(p, x4[i], wt.m, wt.c, true, xl, xsum, 0);
-        }
+        static_assert(!TAIL, "deferred scaling: whole rows in registers");
         return;
     }
     sync_lds();
@@ -441,11 +468,26 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
         stage_chunk<FMT, M>(p, norm(st.x[k], st.g[k], mk[k]), mk[k], ck[k], tid + k * bs < total,
                             xl, xsum, tok_e(mk[k]));
     if constexpr (TAIL) {
+        // (each chunk's slot was written by this thread in the first pass)
         ChunkWalk wt = wk;
-        for (int i = tid + NX * bs; i < total; i += bs, wt.next()) {
-            float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (mode_norm(MODE)) g = g4[wt.c];
-            stage_chunk<FMT, M>(p, norm(x4[i], g, wt.m), wt.m, wt.c, true, xl, xsum, tok_e(wt.m));
+        for (int i0 = tid + NX * bs; i0 < total; i0 += kTailBatch * bs) {
+            float4 t[kTailBatch], tg[kTailBatch];
+            ChunkWalk wl = wt;
+#pragma unroll
+            for (int j = 0; j < kTailBatch; ++j) {
+                const bool valid = i0 + j * bs < total;
+                t[j] = xl[valid ? slot(wl.m, wl.c) : slot(M - 1, kq - 1)];
+                tg[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+                if constexpr (mode_norm(MODE)) tg[j] = g4[valid ? wl.c : kq - 1];
+                wl.next();
+            }
+#pragma unroll
+            for (int j = 0; j < kTailBatch; ++j) {
+                const bool valid = i0 + j * bs < total;
+                const int m = valid ? wt.m : M - 1, c = valid ? wt.c : kq - 1;
+                stage_chunk<FMT, M>(p, norm(t[j], tg[j], m), m, c, valid, xl, xsum, tok_e(m));
+                wt.next();
+            }
         }
     }
 }
@@ -542,7 +584,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
     constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
-    constexpr int kBS = gemv_threads(M, MODE);  // the launch's block size (run_plan)
+    constexpr int kBS = gemv_threads(M, MODE, XR);  // the launch's block size (run_plan)
     __shared__ StageRedT<8, (kBS / kWave > kMaxStageWaves ? kBS / kWave : kMaxStageWaves)> red;
     const int tid = threadIdx.x;
     const int lane = tid & 63;

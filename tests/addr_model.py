@@ -29,12 +29,13 @@ def pow2ceil(v):
 
 
 def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
-    # single-token calls run 256-thread workgroups (4 waves), dense batched
-    # calls 512-thread ones (8 waves), up to 2 per CU; expert calls 256-thread
-    # ones at M = 2..4 (3 per CU) and 768-thread ones otherwise (1 per CU)
+    # single-token calls with rows of at most 64 units run 256-thread
+    # workgroups (4 waves), longer single-token rows and dense batched calls
+    # 512-thread ones (8 waves), up to 2 per CU; expert calls 256-thread ones
+    # at M = 2..4 (3 per CU) and 768-thread ones otherwise (1 per CU)
     moe4 = moe and 2 <= M <= 4
     if wpb is None:
-        wpb = (4 if moe4 else 12) if moe else (4 if M == 1 else 8)
+        wpb = (4 if moe4 else 12) if moe else (4 if M == 1 and (K + 63) // 64 <= 64 else 8)
     if bpc is None:
         bpc = (3 if moe4 else 1) if moe else 2
     upr = (K + 63) // 64
