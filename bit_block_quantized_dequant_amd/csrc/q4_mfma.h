@@ -418,6 +418,47 @@ __host__ __device__ inline int mslice_regions(int KS, int npg) { return (KS + np
 // Per-token factors from whole rows read from global memory: the RMSNorm
 // factor r_m (fp64 sum of squares) and the exponent e_m with
 // max_k |x_hat[m,k]| 2^e_m in [2^14, 2^15), into the exps region.
+// A batch of kMBatch activation pieces (8 floats each) per thread: pieces
+// i0 + j * kMBlock of the M token rows of x, columns c0 + 8 * (piece within
+// the row), loaded together so that the thread waits once per batch, not once
+// per piece (a wait for a load issued after the weight loads also waits for
+// those).  Pieces past np load the last piece and have ok = false.  w walks
+// the (token, piece) positions (rows of ppr pieces) without divisions.
+constexpr int kMBatch = 4;
+struct MPieces {
+    float v[kMBatch][8];
+    int m[kMBatch];  // token (the last for pieces past np)
+    int c[kMBatch];  // piece within the token's row
+    bool ok[kMBatch];
+};
+template <int M>
+__device__ __forceinline__ void mpiece_batch(const GemvParams& p, int i0, int np, int ppr, int c0,
+                                             ChunkWalk& w, MPieces& b) {
+#pragma unroll
+    for (int j = 0; j < kMBatch; ++j) {
+        b.ok[j] = i0 + j * kMBlock < np;
+        b.m[j] = b.ok[j] ? w.m : M - 1;
+        b.c[j] = b.ok[j] ? w.c : ppr - 1;
+        const float4* src =
+            (const float4*)(p.x + (long long)b.m[j] * p.K + c0 + 8 * b.c[j]);
+        const float4 x0 = src[0], x1 = src[1];
+        b.v[j][0] = x0.x; b.v[j][1] = x0.y; b.v[j][2] = x0.z; b.v[j][3] = x0.w;
+        b.v[j][4] = x1.x; b.v[j][5] = x1.y; b.v[j][6] = x1.z; b.v[j][7] = x1.w;
+        w.next();
+    }
+}
+// gamma for the pieces of a batch
+__device__ __forceinline__ void mpiece_gamma(const GemvParams& p, const MPieces& b, int c0,
+                                             float (&g)[kMBatch][8]) {
+#pragma unroll
+    for (int j = 0; j < kMBatch; ++j) {
+        const float4* gs = (const float4*)(p.gamma + c0 + 8 * b.c[j]);
+        const float4 ga = gs[0], gb = gs[1];
+        g[j][0] = ga.x; g[j][1] = ga.y; g[j][2] = ga.z; g[j][3] = ga.w;
+        g[j][4] = gb.x; g[j][5] = gb.y; g[j][6] = gb.z; g[j][7] = gb.w;
+    }
+}
+
 template <int M, int MODE, typename Red>
 __device__ __forceinline__ void mstage_factors(const GemvParams& p, char* lds, const MLayout& ly,
                                                Red& red) {
@@ -426,26 +467,23 @@ __device__ __forceinline__ void mstage_factors(const GemvParams& p, char* lds, c
     const int np = M * ppt;
     int* ex = (int*)(lds + ly.exps);
     float* rn = (float*)(lds + ly.exps) + 16;
-    auto piece = [&](int i, float (&v)[8]) {
-        const int m = i / ppt;
-        const float4* src = (const float4*)(p.x + (long long)m * p.K + 8 * (i - m * ppt));
-        const float4 a = src[0], b = src[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        return m;
-    };
     if constexpr (MODE == kModeNorm) {
         double ss[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) ss[m] = 0.0;
-        for (int i = tid; i < np; i += kMBlock) {
-            float v[8];
-            const int m = piece(i, v);
-            double t = 0.0;
+        ChunkWalk w(tid, kMBlock, ppt);
+        for (int i0 = tid; i0 < np; i0 += kMBatch * kMBlock) {
+            MPieces b;
+            mpiece_batch<M>(p, i0, np, ppt, 0, w, b);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) t += (double)v[e] * (double)v[e];
+            for (int j = 0; j < kMBatch; ++j) {
+                double t = 0.0;
 #pragma unroll
-            for (int mm = 0; mm < M; ++mm) ss[mm] += m == mm ? t : 0.0;
+                for (int e = 0; e < 8; ++e) t += (double)b.v[j][e] * (double)b.v[j][e];
+                t = b.ok[j] ? t : 0.0;
+#pragma unroll
+                for (int mm = 0; mm < M; ++mm) ss[mm] += b.m[j] == mm ? t : 0.0;
+            }
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -464,23 +502,27 @@ __device__ __forceinline__ void mstage_factors(const GemvParams& p, char* lds, c
     float am[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) am[m] = 0.f;
-    for (int i = tid; i < np; i += kMBlock) {
-        float v[8];
-        const int m = piece(i, v);
-        float t = 0.f;
-        if constexpr (MODE == kModeNorm) {
-            const float r = rn[m];
-            const float4* gs = (const float4*)(p.gamma + 8 * (i - m * ppt));
-            const float4 ga = gs[0], gb = gs[1];
-            const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+    ChunkWalk w(tid, kMBlock, ppt);
+    for (int i0 = tid; i0 < np; i0 += kMBatch * kMBlock) {
+        MPieces b;
+        mpiece_batch<M>(p, i0, np, ppt, 0, w, b);
+        float g[kMBatch][8];
+        if constexpr (MODE == kModeNorm) mpiece_gamma(p, b, 0, g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf((v[e] * r) * g[e]));
-        } else {
+        for (int j = 0; j < kMBatch; ++j) {
+            float t = 0.f;
+            if constexpr (MODE == kModeNorm) {
+                const float r = rn[b.m[j]];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(v[e]));
+                for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf((b.v[j][e] * r) * g[j][e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(b.v[j][e]));
+            }
+            t = b.ok[j] ? t : 0.f;
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], b.m[j] == mm ? t : 0.f);
         }
-#pragma unroll
-        for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], m == mm ? t : 0.f);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -508,55 +550,76 @@ __device__ __forceinline__ void mstage_slice(const GemvParams& p, char* lds, con
     const int* ex = (const int*)(lds + ly.exps);
     const float* rn = (const float*)(lds + ly.exps) + 16;
     // (a 32-element group's 4 pieces are 4 consecutive threads, all active
-    // together: ppl and the block size are multiples of 4)
-    for (int i = tid; i < np; i += kMBlock) {
-        const int m = i / ppl;
-        const int pl = i - m * ppl;
-        const int ls = pl >> 5, pin = pl & 31;
-        const int rg = ls / sc.msl, j = ls - rg * sc.msl;
-        const int sl = sc.position(rg, s);
-        int a = 0, b = 0, reg = 0;
-        if (sl >= 0) sc.range(sl, s, a, b, reg);
-        const bool staged = j < b - a;  // (a region's unused tail is never read)
-        const int col = (a + j) * 256 + pin * 8;
-        float v[8];
+    // together: ppl and the block size are multiples of 4).  Pieces are
+    // loaded kMBatch at a time, unconditionally (a piece that is not staged,
+    // or lies past K, loads the row's first piece and is staged as zeros).
+    ChunkWalk w(tid, kMBlock, ppl);
+    for (int i0 = tid; i0 < np; i0 += kMBatch * kMBlock) {
+        float v[kMBatch][8], g[kMBatch][8];
+        int mj[kMBatch], plj[kMBatch];
+        bool stj[kMBatch], ldj[kMBatch];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        if (staged && col < p.K) {
-            const float4* src = (const float4*)(p.x + (long long)m * p.K + col);
+        for (int j = 0; j < kMBatch; ++j) {
+            const bool ok = i0 + j * kMBlock < np;
+            const int m = ok ? w.m : M - 1;
+            const int pl = ok ? w.c : ppl - 1;
+            w.next();
+            const int ls = pl >> 5, pin = pl & 31;
+            const int rg = ls / sc.msl, jj = ls - rg * sc.msl;
+            const int sl = sc.position(rg, s);
+            int a = 0, b = 0, reg = 0;
+            if (sl >= 0) sc.range(sl, s, a, b, reg);
+            const bool staged = ok && jj < b - a;  // (a region's unused tail is never read)
+            const int col = (a + jj) * 256 + pin * 8;
+            const bool ld = staged && col < p.K;
+            const int colc = ld ? col : 0;
+            const float4* src = (const float4*)(p.x + (long long)m * p.K + colc);
             const float4 x0 = src[0], x1 = src[1];
-            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+            v[j][0] = x0.x; v[j][1] = x0.y; v[j][2] = x0.z; v[j][3] = x0.w;
+            v[j][4] = x1.x; v[j][5] = x1.y; v[j][6] = x1.z; v[j][7] = x1.w;
+            if constexpr (MODE == kModeNorm) {
+                const float4* gs = (const float4*)(p.gamma + colc);
+                const float4 ga = gs[0], gb = gs[1];
+                g[j][0] = ga.x; g[j][1] = ga.y; g[j][2] = ga.z; g[j][3] = ga.w;
+                g[j][4] = gb.x; g[j][5] = gb.y; g[j][6] = gb.z; g[j][7] = gb.w;
+            }
+            mj[j] = m;
+            plj[j] = pl;
+            stj[j] = staged;
+            ldj[j] = ld;
+        }
+#pragma unroll
+        for (int j = 0; j < kMBatch; ++j) {
+            const int m = mj[j], pl = plj[j], pin = pl & 31;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = ldj[j] ? v[j][e] : 0.f;
             if constexpr (MODE == kModeNorm) {
                 const float r = rn[m];
-                const float4* gs = (const float4*)(p.gamma + col);
-                const float4 ga = gs[0], gb = gs[1];
-                const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (v[e] * r) * g[e];
+                for (int e = 0; e < 8; ++e) v[j][e] = (v[j][e] * r) * g[j][e];
             }
-        }
-        h8 hi, lo;
-        float part;
-        piece_frag(v, ex[m], piece_is_high<FMT>(pin), hi, lo, part);
-        part = dpp_add(part, 0);
-        part = dpp_add(part, 1);
-        if (staged) {
-            *(h8*)(lds + ly.frag + fslot(kst, 2 * m, pl) * 16) = hi;
-            *(h8*)(lds + ly.frag + fslot(kst, 2 * m + 1, pl) * 16) = lo;
-            if ((pl & 3) == 0) {
-                const int g32 = pl >> 2;  // local block / sub-block index
-                if constexpr (FMT != kFmtQ4K) {
-                    ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
-                } else {
-                    const int sb = g32 >> 3, J = g32 & 7;
-                    const float xs = part * 0.03125f;
-                    const _Float16 h = (_Float16)xs;
-                    const _Float16 l = (_Float16)(xs - (float)h);
-                    _Float16* ap = (_Float16*)(lds + ly.aux);
-                    const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
-                    ap[base] = h;
-                    ap[base + 2] = l;
+            h8 hi, lo;
+            float part;
+            piece_frag(v[j], ex[m], piece_is_high<FMT>(pin), hi, lo, part);
+            part = dpp_add(part, 0);
+            part = dpp_add(part, 1);
+            if (stj[j]) {
+                *(h8*)(lds + ly.frag + fslot(kst, 2 * m, pl) * 16) = hi;
+                *(h8*)(lds + ly.frag + fslot(kst, 2 * m + 1, pl) * 16) = lo;
+                if ((pl & 3) == 0) {
+                    const int g32 = pl >> 2;  // local block / sub-block index
+                    if constexpr (FMT != kFmtQ4K) {
+                        ((float*)(lds + ly.aux))[g32 * sums_stride(M) + m] = part;
+                    } else {
+                        const int sb = g32 >> 3, J = g32 & 7;
+                        const float xs = part * 0.03125f;
+                        const _Float16 h = (_Float16)xs;
+                        const _Float16 l = (_Float16)(xs - (float)h);
+                        _Float16* ap = (_Float16*)(lds + ly.aux);
+                        const int base = ((sb * 4 + (J >> 1)) * 2 * M + 2 * m) * 2 + (J & 1);
+                        ap[base] = h;
+                        ap[base + 2] = l;
+                    }
                 }
             }
         }
@@ -577,14 +640,19 @@ __device__ __forceinline__ void mstage_part_factors(const GemvParams& p, char* l
     float am[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) am[m] = 0.f;
-    for (int i = tid; i < np; i += kMBlock) {
-        const int m = i / ppr;
-        const float4* src = (const float4*)(p.x + (long long)m * p.K + c0 + 8 * (i - m * ppr));
-        const float4 a = src[0], b = src[1];
-        const float t = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                              fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    ChunkWalk w(tid, kMBlock, ppr);
+    for (int i0 = tid; i0 < np; i0 += kMBatch * kMBlock) {
+        MPieces b;
+        mpiece_batch<M>(p, i0, np, ppr, c0, w, b);
 #pragma unroll
-        for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], m == mm ? t : 0.f);
+        for (int j = 0; j < kMBatch; ++j) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, fabsf(b.v[j][e]));
+            t = b.ok[j] ? t : 0.f;
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) am[mm] = fmaxf(am[mm], b.m[j] == mm ? t : 0.f);
+        }
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
