@@ -31,6 +31,10 @@
 namespace q4 {
 
 constexpr int kDownBlock = 256;
+#ifndef Q4_DOWN_BATCH
+#define Q4_DOWN_BATCH 2
+#endif
+constexpr int kDownBatch = Q4_DOWN_BATCH;  // staging chunks per thread per wait
 constexpr int kDownWaves = kDownBlock / kWave;
 static_assert(kDownWaves <= kMaxStageWaves, "staging scratch holds 8 waves");
 
@@ -148,15 +152,33 @@ __global__ __launch_bounds__(kDownBlock) void moe_down_kernel(const GemvParams p
             float am[M];
 #pragma unroll
             for (int j = 0; j < M; ++j) am[j] = 0.f;
+            // kDownBatch chunks per wait (a wait also waits for the weight
+            // loads issued before it), kept unscaled in their LDS slots for
+            // the second pass; chunks past the end are clamped duplicates
+            const int kqr = xrow_chunks(p.upr);
+            auto slot = [&](int j, int c) { return j * kqr + xchunk(c >> 4, c & 15); };
             ChunkWalk w(tid, kDownBlock, kq4);
-            for (int i = tid; i < total; i += kDownBlock, w.next()) {
-                const int j = w.m, c = w.c;
-                const float4 v = h4[(long long)sh_pr[j] * kq4 + c];
-                const float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
-                                      fmaxf(fabsf(v.z), fabsf(v.w)));
+            for (int i0 = tid; i0 < total; i0 += kDownBatch * kDownBlock) {
+                float4 t[kDownBatch];
+                int tj[kDownBatch], tc[kDownBatch];
+                bool ok[kDownBatch];
 #pragma unroll
-                for (int jj = 0; jj < M; ++jj)
-                    if (j == jj) am[jj] = fmaxf(am[jj], a);
+                for (int k = 0; k < kDownBatch; ++k) {
+                    ok[k] = i0 + k * kDownBlock < total;
+                    tj[k] = ok[k] ? w.m : nb - 1;
+                    tc[k] = ok[k] ? w.c : kq4 - 1;
+                    t[k] = h4[(long long)sh_pr[tj[k]] * kq4 + tc[k]];
+                    w.next();
+                }
+#pragma unroll
+                for (int k = 0; k < kDownBatch; ++k) {
+                    float a = fmaxf(fmaxf(fabsf(t[k].x), fabsf(t[k].y)),
+                                    fmaxf(fabsf(t[k].z), fabsf(t[k].w)));
+                    a = ok[k] ? a : 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < M; ++jj) am[jj] = fmaxf(am[jj], tj[k] == jj ? a : 0.f);
+                    if (ok[k]) xl[slot(tj[k], tc[k])] = t[k];
+                }
             }
 #pragma unroll
             for (int j = 0; j < M; ++j) {
@@ -170,11 +192,11 @@ __global__ __launch_bounds__(kDownBlock) void moe_down_kernel(const GemvParams p
                 sh_e[tid] = xscale_exp(a, kXTarget);
             }
             sync_lds();
+            // (each chunk's slot was written by this thread above)
             ChunkWalk w2(tid, kDownBlock, kq4);
             for (int i = tid; i < total; i += kDownBlock, w2.next()) {
                 const int j = w2.m, c = w2.c;
-                stage_chunk<FMT, M>(p, h4[(long long)sh_pr[j] * kq4 + c], j, c, true, xl, xsum,
-                                    sh_e[j]);
+                stage_chunk<FMT, M>(p, xl[slot(j, c)], j, c, true, xl, xsum, sh_e[j]);
             }
             sync_lds();
         }
