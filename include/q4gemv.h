@@ -314,9 +314,9 @@ int moe_router_q4_0(int32_t* ids, float* weights, const void* w_router, const fl
  *     where one is needed: Q4_ERR_NULL.  Other limits and alignment as
  *     q4_0_gemv / q4k_gemv.
  * It pays where staging dominates, i.e. for few output rows (on MI355X,
- * 4096 x 4096 at 4 / 8 / 16 tokens: 9.2 / 9.9 / 11.9 against 10.0 / 11.5 /
- * 30.7 us; the 4096 x 14336 down-projection at 4 tokens: 15.7 against
- * 29.1 us); with many output rows the ordinary call already shares its
+ * 4096 x 4096 at 4 / 8 / 16 tokens: 9.3 / 10.0 / 12.0 against 9.9 / 11.5 /
+ * 28.0 us; the 4096 x 14336 down-projection at 4 tokens: 15.3 against
+ * 25.9 us); with many output rows the ordinary call already shares its
  * staging among 128 rows per workgroup.  (The pages' kernels stage x once
  * per workgroup; splitting K over workgroups is this library's answer to
  * the staging cost of batches on a 256-CU part.)
