@@ -291,13 +291,19 @@ inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     return launch(kern(PURE), p, blocks, lds, stream, big_lds_done, BS);
 }
 
+constexpr int kXrTwoMaxRows = 8192;  // single-matrix calls at M = 2 with register-resident x
 template <int FMT, int NMAT, int MODE, bool PURE, int M>
 inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
-    if constexpr (M == 1 && !mode_moe(MODE)) {
+    if constexpr (M <= kXrMaxM && !mode_moe(MODE)) {
         // one 64-weight unit per lane per row: at most 64 units (and then
-        // the activations need no staging loop beyond the first kXReg chunks)
+        // the activations need no staging loop beyond the first kXReg chunks).
+        // Two tokens hold 128 activations per lane (about 240 VGPRs, one
+        // 512-thread workgroup per CU): worth it for short single-matrix calls,
+        // whose waves have one or two steps (Q4_0 4096 x 4096: 7.0 -> 6.5 us),
+        // not for the gate+up pair of 2 x 14336 rows (19.5 -> 19.7 us).
         const int upr = (int)k_units(p.K);
-        if (upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
+        const bool two_ok = M == 1 || (NMAT == 1 && p.N <= kXrTwoMaxRows);
+        if (two_ok && upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
     }
     if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE, false))

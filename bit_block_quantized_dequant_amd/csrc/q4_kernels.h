@@ -38,6 +38,10 @@ namespace q4 {
 // but M = 2 .. 4 +3 to +7 %.
 constexpr int kBlock = 512;
 constexpr int kBlock1 = 256;
+#ifndef Q4_XR_MAX_M
+#define Q4_XR_MAX_M 2
+#endif
+constexpr int kXrMaxM = Q4_XR_MAX_M;  // largest batch with register-resident activations
 #ifndef Q4_MOE_BLOCK
 #define Q4_MOE_BLOCK 0  // 0: by M as above; else every expert call (for measurements)
 #endif
@@ -311,14 +315,16 @@ __device__ __forceinline__ void stage_pad(const GemvParams& p, float4* xl, float
 // blockDim); kernels that cannot are compiled without the extra loops,
 // whose load waits would otherwise also cover the weight loads in flight.
 // xe[m] receives token m's scale exponent e_m (the same in every thread).
-// DEFER (single token, no RMSNorm): no reduction barrier here; the chunks
-// are stored unscaled and each wave's partial maximum is left in red.am[0],
-// to be combined after the caller's barrier (stage_x_exponent).
+// DEFER (register-resident activations, no RMSNorm): no reduction barrier
+// here; the chunks are stored unscaled and each wave's partial maxima are
+// left in red.am[m], to be combined after the caller's barrier
+// (stage_x_exponent).
 template <int FMT, int M, int MODE, bool TAIL, int NX = kXReg, bool DEFER = false, class RED>
 __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage<NX>& st,
                                                float4* xl, float* xsum, RED& red,
                                                int (&xe)[M], int bs) {
-    static_assert(!DEFER || (M == 1 && !mode_norm(MODE)), "deferred scaling: one token, no norm");
+    static_assert(!DEFER || (M <= kXrMaxM && !mode_norm(MODE)),
+                  "deferred scaling: register-resident tokens, no norm");
     const int tid = threadIdx.x;
         const int kq = p.K >> 2;
     const int total = M * kq;
@@ -492,12 +498,12 @@ __device__ __forceinline__ void stage_x_finish(const GemvParams& p, const XStage
     }
 }
 
-// The scale exponent of a single token staged with DEFER, from the waves'
-// partial maxima (call after the barrier that follows the staging).
+// The scale exponent of token m staged with DEFER, from the waves' partial
+// maxima (call after the barrier that follows the staging).
 template <class RED>
-__device__ __forceinline__ int stage_x_exponent(const RED& red, int nwaves) {
+__device__ __forceinline__ int stage_x_exponent(const RED& red, int nwaves, int m) {
     float a = 0.f;
-    for (int i = 0; i < nwaves; ++i) a = fmaxf(a, red.am[0][i]);
+    for (int i = 0; i < nwaves; ++i) a = fmaxf(a, red.am[m][i]);
     return __builtin_amdgcn_readfirstlane(xscale_exp(a, kXTarget));
 }
 
@@ -575,12 +581,12 @@ __device__ __forceinline__ void moe_dedupe(const GemvParams& p, MoeShared& sh, i
     }
 }
 
-// XR: every lane works on one fixed unit of each row (M = 1, K <= 64 units of
-// 64 weights): its 64 activations and two run sums are copied from LDS into
-// registers once, and the main loop reads no LDS at all.
+// XR: every lane works on one fixed unit of each row (M <= kXrMaxM tokens,
+// K <= 64 units of 64 weights): its 64 activations and two run sums per token
+// are copied from LDS into registers once, and the main loop reads no LDS.
 template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, bool XR, bool TAIL>
 __device__ __forceinline__ void gemv_body(const GemvParams& p) {
-    static_assert(!XR || (M == 1 && !mode_moe(MODE)), "register-resident x: M = 1 only");
+    static_assert(!XR || (M <= kXrMaxM && !mode_moe(MODE)), "register-resident x: M <= 2");
     extern __shared__ float4 smem[];
     __shared__ MoeShared moe;
     constexpr int NR = NMAT * RR;  // rows of one step, matrix-major: q = mt * RR + r
@@ -734,7 +740,10 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     if constexpr (!PURE)
         stage_x_finish<FMT, M, MODE, TAIL, NX, kDefer>(p, xst, xl, xsum, red, xe, kBS);
     sync_lds();
-    if constexpr (kDefer && !PURE) xe[0] = stage_x_exponent(red, kBS >> 6);
+    if constexpr (kDefer && !PURE) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) xe[m] = stage_x_exponent(red, kBS >> 6, m);
+    }
     // output scale of token m: 2^(24 - e_m) for Q4_K (whose sums carry the
     // 6-bit scales as sc * 2^-24), 2^-e_m for Q4_0
     int osh[M];
@@ -765,28 +774,34 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
     }
     if (t0 >= t1) return;
 
-    // register-resident activations of this lane's unit (XR)
-    float4 xr[XR ? kUnitChunks - 1 : 1];
-    float2 xsr[1];
+    // register-resident activations of this lane's unit (XR): token m's
+    // 16 chunks at xr[16 m ..], its two run sums at xsr[m]
+    constexpr int kXrChunks = kUnitChunks - 1;
+    float4 xr[XR ? M * kXrChunks : 1];
+    float2 xsr[XR ? M : 1];
     if constexpr (XR) {
         const int uc = min(li, p.upr - 1);
 #pragma unroll
-        for (int c = 0; c < kUnitChunks - 1; ++c) xr[c] = xl[xchunk(uc, c)];
-        xsr[0] = ((const float2*)xsum)[uc];
-        if constexpr (kDefer) {
-            // 2^e and the 2^24 (2^20 for elements met as high nibbles)
-            // pre-scale of the staging, applied here
-            const int e = xe[0];
+        for (int m = 0; m < M; ++m) {
 #pragma unroll
-            for (int c = 0; c < kUnitChunks - 1; ++c) {
-                const int sh = e + (elem_is_high<FMT>(4 * c) ? 20 : 24);
-                xr[c].x = __builtin_ldexpf(xr[c].x, sh);
-                xr[c].y = __builtin_ldexpf(xr[c].y, sh);
-                xr[c].z = __builtin_ldexpf(xr[c].z, sh);
-                xr[c].w = __builtin_ldexpf(xr[c].w, sh);
+            for (int c = 0; c < kXrChunks; ++c) xr[m * kXrChunks + c] = xl[m * kq + xchunk(uc, c)];
+            xsr[m] = ((const float2*)xsum)[m * k64 + uc];
+            if constexpr (kDefer) {
+                // 2^e and the 2^24 (2^20 for elements met as high nibbles)
+                // pre-scale of the staging, applied here
+                const int e = xe[m];
+#pragma unroll
+                for (int c = 0; c < kXrChunks; ++c) {
+                    const int sh = e + (elem_is_high<FMT>(4 * c) ? 20 : 24);
+                    float4& v = xr[m * kXrChunks + c];
+                    v.x = __builtin_ldexpf(v.x, sh);
+                    v.y = __builtin_ldexpf(v.y, sh);
+                    v.z = __builtin_ldexpf(v.z, sh);
+                    v.w = __builtin_ldexpf(v.w, sh);
+                }
+                xsr[m].x = __builtin_ldexpf(xsr[m].x, e);
+                xsr[m].y = __builtin_ldexpf(xsr[m].y, e);
             }
-            xsr[0].x = __builtin_ldexpf(xsr[0].x, e);
-            xsr[0].y = __builtin_ldexpf(xsr[0].y, e);
         }
     }
 
@@ -829,7 +844,7 @@ __device__ __forceinline__ void gemv_body(const GemvParams& p) {
                 if constexpr (M > 1) __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (XR) {
-            rows_dot<FMT, M, NR>(w, 0, sel, xr, 0, xsr, 0, acc, act);
+            rows_dot<FMT, M, NR>(w, 0, sel, xr, kXrChunks, xsr, 1, acc, act);
         } else {
             rows_dot<FMT, M, NR>(w, uc, sel, xl, kq, (const float2*)xsum, k64, acc, act);
         }
