@@ -266,7 +266,8 @@ template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
 inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     constexpr int RR = mode_moe(MODE) ? Q4_RR_MOE : (NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR);
     // Workgroup shape (measured): dense single-token calls run 256-thread
-    // groups, at most two per CU (four were 4 % slower); expert calls 256- or
+    // groups, at most two per CU (four were 4 % slower), 512-thread ones for
+    // rows over 64 units (the staging then halves per CU); expert calls 256- or
     // 768-thread groups (gemv_threads), as many as their 134-147 VGPRs allow:
     // 12 waves per CU, which beat 8 waves of 512-thread groups by 9-14 %.
     // Dense batched calls on this kernel run two 512-thread groups.

@@ -29,7 +29,8 @@
 
 namespace q4 {
 
-// Threads per workgroup of the VALU GEMV kernel: 256 for single-token calls,
+// Threads per workgroup of the VALU GEMV kernel: 256 for single-token calls
+// with register-resident activations (512 for longer rows, staged in LDS),
 // 512 for dense batched calls; the expert calls 256 at M = 2 .. 4 and 768
 // otherwise.  An expert call stages all M token rows in every workgroup: one
 // 768-thread workgroup per CU stages them once per CU instead of three
@@ -1005,8 +1006,9 @@ __global__ __launch_bounds__(BS) void gemv_kernel(const GemvParams p) {
     gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, false, TAIL>(p);
 }
 
-// The register-resident variant runs two 256-thread workgroups per CU (two
-// waves per SIMD), so it may use up to 256 VGPRs.
+// The register-resident variant runs two 256-thread workgroups per CU (one
+// 512-thread group for two tokens), two waves per SIMD, so it may use up to
+// 256 VGPRs.
 template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, int BS>
 __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(2)))
 void gemv_kernel_xr(const GemvParams p) {
