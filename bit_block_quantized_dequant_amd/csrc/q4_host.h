@@ -262,9 +262,11 @@ inline bool xr_enabled() {
     return on;
 }
 
-template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL>
+// RRX > 0 overrides the rows per lane and step (RR).
+template <int FMT, int NMAT, int MODE, bool PURE, int M, bool XR, bool TAIL, int RRX = 0>
 inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
-    constexpr int RR = mode_moe(MODE) ? Q4_RR_MOE : (NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR);
+    constexpr int RR = RRX > 0 ? RRX
+                               : (mode_moe(MODE) ? Q4_RR_MOE : (NMAT == 1 ? Q4_RR_SINGLE : Q4_RR_PAIR));
     // Workgroup shape (measured): dense single-token calls run 256-thread
     // groups, at most two per CU (four were 4 % slower), 512-thread ones for
     // rows over 64 units (the staging then halves per CU); expert calls 256- or
@@ -304,8 +306,21 @@ inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         // not for the gate+up pair of 2 x 14336 rows (19.5 -> 19.7 us).
         const int upr = (int)k_units(p.K);
         const bool two_ok = M == 1 || (NMAT == 1 && p.N <= kXrTwoMaxRows);
-        if (two_ok && upr <= kWave && choose_lg(upr) >= upr && xr_enabled())
+        if (two_ok && upr <= kWave && choose_lg(upr) >= upr && xr_enabled()) {
+            // A single-matrix call too small to give every CU a task at two
+            // rows per lane takes one row per lane: twice the waves for a call
+            // that is all latency (Q4_0 K=512 N=256: 3.36 -> 2.88 us; at
+            // 4096 x 4096 and up two rows per lane stay faster, 4.9 against
+            // 5.2 us).
+            if constexpr (M == 1 && NMAT == 1 && Q4_RR_SINGLE != 1) {
+                const long long rgw = kWave / choose_lg(upr);
+                const long long tasks2 = ((p.N + Q4_RR_SINGLE - 1) / Q4_RR_SINGLE + rgw - 1) / rgw;
+                if (tasks2 < cus)
+                    return run_plan<FMT, NMAT, MODE, PURE, M, true, false, 1>(p, cus, npairs_max,
+                                                                             stream);
+            }
             return run_plan<FMT, NMAT, MODE, PURE, M, true, false>(p, cus, npairs_max, stream);
+        }
     }
     if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE, false))
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);

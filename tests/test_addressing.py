@@ -18,6 +18,15 @@ def test_single_matrix_loads_in_bounds(fmt, M, N, K):
     assert A.check(fmt, M, N, K, RR=2, nmat=1, cus=8) > 0
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q4_0"])
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 512), (256, 512), (1000, 2048), (77, 4096)])
+def test_single_token_one_row_per_lane_loads_in_bounds(fmt, N, K):
+    # single-matrix calls too small for one task per CU at two rows per lane
+    # run one row per lane (run_m)
+    assert A.check(fmt, 1, N, K, RR=1, nmat=1, cus=8) > 0
+    assert A.check(fmt, 1, N, K, RR=1, nmat=1, cus=256) > 0
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 41, 512), (8, 130, 4096), (2, 9, 8192),
                                    (1, 14336, 4096)])
 def test_two_matrix_loads_in_bounds(M, N, K):
