@@ -195,17 +195,24 @@ inline int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* 
 // on one row when the row has at least 64 units, else the power of two that
 // covers the row, at least 4 (the group reduction sums whole quads).  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
 // measurements; the kernel takes any such width.
-inline int choose_lg(int upr) {
+// The expert call of two or more tokens takes half that width (two units per
+// lane and row) where that leaves at least 16 lanes per row: E = 64, top-6,
+// K = 2048, M = 4, three runs on one box: 18.4 against 19.3 us (seeded ids),
+// 18.4 against 19.4 (SiLU-gated), 20.3 against 20.2 (all ids distinct).  A
+// single token keeps the dense call's width, so that each of its outputs
+// equals q4_0_gemv on that expert bit for bit.
+inline int choose_lg(int upr, bool moe = false) {
     static const int forced = env_int("Q4GEMV_LG", 0);
     if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
-    return upr >= kWave ? kWave : (upr <= 4 ? 4 : pow2ceil(upr));
+    const int lg = upr >= kWave ? kWave : (upr <= 4 ? 4 : pow2ceil(upr));
+    return moe && lg >= 32 ? lg / 2 : lg;
 }
 
 inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npairs_max, bool pure,
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = (int)k_units(K);
-    p.lg = choose_lg(p.upr);
+    p.lg = choose_lg(p.upr, moe && M >= 2);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
     const int nrg = (rows + RR - 1) / RR;
@@ -274,7 +281,10 @@ inline int run_plan(GemvParams& p, int cus, int npairs_max, void* stream) {
     // 12 waves per CU, which beat 8 waves of 512-thread groups by 9-14 %.
     // Dense batched calls on this kernel run two 512-thread groups.
     constexpr int BS = gemv_threads(M, MODE, XR);
-    constexpr int WGMAX = mode_moe(MODE) ? 4 : 2;
+    // (three register-resident single-token groups per CU: headline 15.06
+    // against 15.17 us, its SiLU form 15.29 against 15.61, the fused RMSNorm
+    // call 11.72 against 11.92; three runs on one box)
+    constexpr int WGMAX = mode_moe(MODE) ? 4 : (XR && M == 1 ? 3 : 2);
     static std::atomic<int> big_lds_done[kMaxDevices];
     static std::atomic<int> resident[kMaxDevices];
     // a pure-read pass takes the launch shape of the call it mirrors

@@ -36,11 +36,15 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
     moe4 = moe and 2 <= M <= 4
     if wpb is None:
         wpb = (4 if moe4 else 12) if moe else (4 if M == 1 and (K + 63) // 64 <= 64 else 8)
-    if bpc is None:
-        bpc = (3 if moe4 else 1) if moe else 2
     upr = (K + 63) // 64
+    xr = not moe and M == 1 and upr <= 64
+    if bpc is None:
+        # (register-resident single-token calls: up to 3 per CU)
+        bpc = (3 if moe4 else 1) if moe else (3 if xr else 2)
     if lg is None:
         lg = 64 if upr >= 64 else max(4, pow2ceil(upr))
+        if moe and M >= 2 and lg >= 32:
+            lg //= 2  # expert calls of 2+ tokens: two units per lane and row
     upl = (upr + lg - 1) // lg
     rgw = 64 // lg
     nrg = (rows + RR - 1) // RR

@@ -36,10 +36,11 @@ def test_two_matrix_loads_in_bounds(M, N, K):
 @pytest.mark.parametrize("fmt,N,K,nmat", [("q4_0", 4096, 4096, 1), ("q4_0", 256, 512, 1),
                                           ("q4k", 18944, 3584, 1), ("q4k", 3, 4096, 2)])
 def test_single_token_plans_at_full_chip(fmt, N, K, nmat):
-    # 256 CUs: the grid is cut to two steps per wave (one workgroup per CU)
+    # 256 CUs: up to three workgroups per CU, the grid cut to two steps per
+    # wave (down to one workgroup per CU)
     RR = 2 if nmat == 1 else 1
     pl = A.plan(1, K, N, RR, False, 1, cus=256)
-    assert pl["nwaves"] <= 2 * 4 * 256 and pl["nwaves"] * 4 >= min(pl["ntasks"], 4 * 256)
+    assert pl["nwaves"] <= 3 * 4 * 256 and pl["nwaves"] * 4 >= min(pl["ntasks"], 4 * 256)
     assert A.check(fmt, 1, N, K, RR=RR, nmat=nmat, cus=256) > 0
 
 
