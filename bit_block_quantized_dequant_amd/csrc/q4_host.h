@@ -195,12 +195,14 @@ inline int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* 
 // on one row when the row has at least 64 units, else the power of two that
 // covers the row, at least 4 (the group reduction sums whole quads).  Q4GEMV_LG (a power of two from 4 to 64) overrides it for
 // measurements; the kernel takes any such width.
-// The expert call of two or more tokens takes half that width (two units per
-// lane and row) where that leaves at least 16 lanes per row: E = 64, top-6,
-// K = 2048, M = 4, three runs on one box: 18.4 against 19.3 us (seeded ids),
-// 18.4 against 19.4 (SiLU-gated), 20.3 against 20.2 (all ids distinct).  A
-// single token keeps the dense call's width, so that each of its outputs
-// equals q4_0_gemv on that expert bit for bit.
+// The expert call of 2 to 4 tokens (256-thread workgroups) takes half that
+// width (two units per lane and row) where that leaves at least 16 lanes per
+// row: E = 64, top-6, K = 2048, M = 4, on one box: 18.4 against 19.3 us
+// (seeded ids), 18.4 against 19.4 (SiLU-gated), 20.3 against 20.2 (all ids
+// distinct).  With 768-thread groups it was slower (M = 6: 31.7 against
+// 28.2 us, M = 8: 37.1 against 36.1).  A single token keeps the dense call's
+// width, so that each of its outputs equals q4_0_gemv on that expert bit for
+// bit.
 inline int choose_lg(int upr, bool moe = false) {
     static const int forced = env_int("Q4GEMV_LG", 0);
     if (forced >= 4 && forced <= kWave && (forced & (forced - 1)) == 0) return forced;
@@ -212,7 +214,7 @@ inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npa
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = (int)k_units(K);
-    p.lg = choose_lg(p.upr, moe && M >= 2);
+    p.lg = choose_lg(p.upr, moe && M >= 2 && M <= 4);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
     const int nrg = (rows + RR - 1) / RR;
