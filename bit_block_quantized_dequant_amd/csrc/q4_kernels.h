@@ -1006,9 +1006,11 @@ __global__ __launch_bounds__(BS) void gemv_kernel(const GemvParams p) {
     gemv_body<FMT, M, NMAT, RR, MODE, PURE, PF, false, TAIL>(p);
 }
 
-// The register-resident variant runs two 256-thread workgroups per CU (one
-// 512-thread group for two tokens), two waves per SIMD, so it may use up to
-// 256 VGPRs.
+// The register-resident variant runs up to three 256-thread workgroups per CU
+// for one token (as many as its register count lets the occupancy calculator
+// place) and one 512-thread group for two tokens.  It is built for at least
+// two waves per SIMD, so it may use up to 256 VGPRs where it needs them (two
+// tokens' activations take about 245).
 template <int FMT, int M, int NMAT, int RR, int MODE, bool PURE, int PF, int BS>
 __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(2)))
 void gemv_kernel_xr(const GemvParams p) {
