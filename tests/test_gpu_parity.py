@@ -477,7 +477,9 @@ def test_gate_up_equals_two_single_calls(dev):
 
 def test_moe_single_token_equals_single_calls(dev):
     """At M = 1 the expert call runs on the VALU kernel: each (slot) output
-    equals the single-matrix q4_0_gemv on that expert, bit for bit."""
+    equals the single-matrix q4_0_gemv on that expert, bit for bit, for rows
+    of at most 64 units (K <= 4096; longer dense rows take narrower lane
+    groups than the expert call)."""
     import bit_block_quantized_dequant_amd as q4
     d = synth.workload_inputs(5)
     N, K, E, top_k = d["N"], d["K"], d["E"], d["top_k"]
