@@ -203,13 +203,14 @@ inline int launch(Kern kern, const GemvParams& p, int blocks, size_t lds, void* 
 // 28.2 us, M = 8: 37.1 against 36.1).  A single token keeps the dense call's
 // width, so that each of its outputs equals q4_0_gemv on that expert bit for
 // bit.
-// A single token's dense rows of more than 64 units (activations in LDS)
+// Dense rows of more than 64 units at one or two tokens (activations in LDS)
 // take 32 lanes per row: fewer idle lanes in a row's last step (224 units: 7
 // steps of 32 lanes against 4 of 64 with the last half idle).  With one row
 // per lane (run_m) the 4096 x 14336 Q4_K down-projection measured 10.57
-// against 11.66 us (two runs on one box; 16 lanes: 14.2 us); eager timings at
-// K = 14336, N = 4096: gate+up 16.7 against 18.1 us, fused RMSNorm 11.2
-// against 11.8-12.4.  The single-token expert call keeps 64 lanes (E = 16,
+// against 11.66 us at M = 1 and 16.1 against 17.8 at M = 2 (two runs each on
+// one box; 16 lanes at M = 1: 14.2 us); eager timings at K = 14336,
+// N = 4096, M = 1: gate+up 16.7 against 18.1 us, fused RMSNorm 11.2 against
+// 11.8-12.4.  The single-token expert call keeps 64 lanes (E = 16,
 // top-4, N = 2048, K = 8192: 32 lanes were 7 % slower, its tasks splitting
 // unevenly over the waves), so it equals q4_0_gemv bit for bit only for rows
 // of at most 64 units.
@@ -225,7 +226,7 @@ inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npa
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = (int)k_units(K);
-    p.lg = choose_lg(p.upr, moe && M >= 2 && M <= 4, M == 1 && !moe);
+    p.lg = choose_lg(p.upr, moe && M >= 2 && M <= 4, M <= 2 && !moe);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
     const int nrg = (rows + RR - 1) / RR;
@@ -346,10 +347,10 @@ inline int run_m(GemvParams& p, int cus, int npairs_max, void* stream) {
         }
     }
     if ((long long)M * p.K > (long long)xreg_chunks(M, MODE) * 4 * gemv_threads(M, MODE, false)) {
-        // a single token's long rows: one row per lane and step (with the
-        // 32-lane groups of choose_lg, 10.57 against 11.66 us on the
-        // 4096 x 14336 down-projection; two rows per lane: 13.56 us)
-        if constexpr (M == 1 && NMAT == 1 && !mode_moe(MODE))
+        // long rows at one or two tokens: one row per lane and step (with
+        // the 32-lane groups of choose_lg, 10.57 against 11.66 us on the
+        // 4096 x 14336 down-projection at M = 1; two rows per lane: 13.56 us)
+        if constexpr (M <= 2 && NMAT == 1 && !mode_moe(MODE))
             return run_plan<FMT, NMAT, MODE, PURE, M, false, true, 1>(p, cus, npairs_max, stream);
         return run_plan<FMT, NMAT, MODE, PURE, M, false, true>(p, cus, npairs_max, stream);
     }

@@ -43,8 +43,8 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
         bpc = (3 if moe4 else 1) if moe else (3 if xr else 2)
     if lg is None:
         lg = 64 if upr >= 64 else max(4, pow2ceil(upr))
-        if M == 1 and upr > 64 and not moe:
-            lg = 32  # a single token's long dense rows
+        if M <= 2 and upr > 64 and not moe:
+            lg = 32  # long dense rows at one or two tokens
         if moe and 2 <= M <= 4 and lg >= 32:
             lg //= 2  # expert calls of 2-4 tokens: two units per lane and row
     upl = (upr + lg - 1) // lg

@@ -170,7 +170,7 @@ Q4_0_TAIL_K = [64, 192, 1408]
 @pytest.mark.parametrize("M", [1, 2])
 def test_tail_loads_in_bounds_q4k(M, K):
     assert A.check("q4k", M, 301, K, RR=2, nmat=1, cus=8) > 0
-    assert A.check("q4k", M, 301, K, RR=1, nmat=1, cus=8) > 0  # one row per lane at M = 1
+    assert A.check("q4k", M, 301, K, RR=1, nmat=1, cus=8) > 0  # one row per lane at M <= 2
     assert A.check("q4k", M, 203, K, RR=1, nmat=2, cus=8) > 0
 
 
