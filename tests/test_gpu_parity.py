@@ -475,6 +475,31 @@ def test_gate_up_equals_two_single_calls(dev):
     assert_bits(host(g), host(u), "gate == up for Wg == Wu")
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_long_rows_pair_equals_two_single_calls(dev, M):
+    """Rows over 64 units at one or two tokens (narrower lane groups, one row
+    per lane in the single-matrix call): the gate+up pair and its RMSNorm
+    form still equal two single-matrix calls bit for bit."""
+    import bit_block_quantized_dequant_amd as q4
+    rng = synth.make_rng(34 + M)
+    N, K = 300, 8224
+    wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
+    x = synth.activations(rng, M, K, sigma=2.0)
+    gam = synth.gamma(rng, K)
+    wgd, wud, xd, gd = T(wg, dev), T(wu, dev), T(x, dev), T(gam, dev)
+    g, u, g1, u1 = (empty((M, N), dev) for _ in range(4))
+    q4.fused_gate_up_q4k_gemv(g, u, wgd, wud, xd, M, N, K)
+    q4.q4k_gemv(g1, wgd, xd, M, N, K)
+    q4.q4k_gemv(u1, wud, xd, M, N, K)
+    assert_bits(host(g), host(g1), "gate vs q4k_gemv M=%d K=%d" % (M, K))
+    assert_bits(host(u), host(u1), "up vs q4k_gemv M=%d K=%d" % (M, K))
+    q4.fused_rmsnorm_gate_up_q4k_gemv(g, u, wgd, wud, xd, gd, 1e-5, M, N, K)
+    q4.fused_rmsnorm_q4k_gemv(g1, wgd, xd, gd, 1e-5, M, N, K)
+    q4.fused_rmsnorm_q4k_gemv(u1, wud, xd, gd, 1e-5, M, N, K)
+    assert_bits(host(g), host(g1), "norm gate M=%d K=%d" % (M, K))
+    assert_bits(host(u), host(u1), "norm up M=%d K=%d" % (M, K))
+
+
 def test_moe_single_token_equals_single_calls(dev):
     """At M = 1 the expert call runs on the VALU kernel: each (slot) output
     equals the single-matrix q4_0_gemv on that expert, bit for bit, for rows
