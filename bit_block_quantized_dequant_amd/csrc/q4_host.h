@@ -226,7 +226,18 @@ inline int plan(GemvParams& p, int M, int K, int rows, int RR, bool moe, int npa
          int cus, int resident, int threads, int wgmax) {
     p.K = K;
     p.upr = (int)k_units(K);
-    p.lg = choose_lg(p.upr, moe && M >= 2 && M <= 4, M <= 2 && !moe);
+    // The 32-lane groups of long dense rows only where their workgroups
+    // (two rows per wave, `threads`-thread groups) fill the CUs evenly: at
+    // N = 5120, K = 13824 the 320 groups left 64 CUs with two and were 4-6 %
+    // slower than 64 lanes (eager, M = 1 and 2).  The test depends on the
+    // shape only, so the gate+up pair decides as its single-matrix calls do.
+    bool long_rows = M <= 2 && !moe;
+    if (long_rows && p.upr > kWave) {
+        const long long need32 = ((rows + 2LL * RR - 1) / (2LL * RR) + threads / kWave - 1) /
+                                 (threads / kWave);
+        long_rows = need32 % cus == 0 || need32 >= 2LL * cus;
+    }
+    p.lg = choose_lg(p.upr, moe && M >= 2 && M <= 4, long_rows);
     p.upl = (p.upr + p.lg - 1) / p.lg;
     p.rgw = kWave / p.lg;
     const int nrg = (rows + RR - 1) / RR;

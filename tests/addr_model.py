@@ -44,7 +44,9 @@ def plan(M, K, rows, RR, moe, npairs_max, cus=256, bpc=None, wpb=None, lg=None):
     if lg is None:
         lg = 64 if upr >= 64 else max(4, pow2ceil(upr))
         if M <= 2 and upr > 64 and not moe:
-            lg = 32  # long dense rows at one or two tokens
+            need32 = ((rows + 2 * RR - 1) // (2 * RR) + wpb - 1) // wpb
+            if need32 % cus == 0 or need32 >= 2 * cus:
+                lg = 32  # long dense rows at one or two tokens, filling the CUs evenly
         if moe and 2 <= M <= 4 and lg >= 32:
             lg //= 2  # expert calls of 2-4 tokens: two units per lane and row
     upl = (upr + lg - 1) // lg

@@ -271,3 +271,15 @@ def test_soa_batched_loads_in_bounds(M, K):
 def test_splitk_plans(fmt, M, N, K):
     pl = A.splitk_check(fmt, M, N, K)
     assert pl["kp"] >= 1
+
+
+def test_long_row_lane_groups_fill_the_chip_evenly():
+    # dense rows over 64 units at M <= 2 take 32-lane groups only where their
+    # 512-thread workgroups fill the CUs evenly (plan() in q4_host.h)
+    assert A.plan(1, 14336, 4096, 1, False, 1, cus=256)["lg"] == 32   # 256 groups
+    assert A.plan(2, 28672, 8192, 1, False, 1, cus=256)["lg"] == 32   # 512 groups
+    assert A.plan(1, 13824, 5120, 1, False, 1, cus=256)["lg"] == 64   # 320 groups
+    assert A.plan(1, 14336, 1024, 1, False, 1, cus=256)["lg"] == 64   # 64 groups
+    assert A.plan(1, 4096, 5120, 2, False, 1, cus=256)["lg"] == 64    # rows of 64 units
+    assert A.check("q4k", 1, 640, 13824, RR=1, nmat=1, cus=32) > 0   # 40 groups on 32 CUs
+    assert A.check("q4k", 2, 512, 13824, RR=1, nmat=2, cus=32) > 0   # 32 groups on 32 CUs
