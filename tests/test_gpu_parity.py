@@ -475,14 +475,16 @@ def test_gate_up_equals_two_single_calls(dev):
     assert_bits(host(g), host(u), "gate == up for Wg == Wu")
 
 
+@pytest.mark.parametrize("N", [300, 4096])
 @pytest.mark.parametrize("M", [1, 2])
-def test_long_rows_pair_equals_two_single_calls(dev, M):
-    """Rows over 64 units at one or two tokens (narrower lane groups, one row
-    per lane in the single-matrix call): the gate+up pair and its RMSNorm
-    form still equal two single-matrix calls bit for bit."""
+def test_long_rows_pair_equals_two_single_calls(dev, M, N):
+    """Rows over 64 units at one or two tokens (one row per lane in the
+    single-matrix call; 32-lane groups where their workgroups fill the CUs
+    evenly, as at N = 4096 on 256 CUs, else 64): the gate+up pair and its
+    RMSNorm form still equal two single-matrix calls bit for bit."""
     import bit_block_quantized_dequant_amd as q4
-    rng = synth.make_rng(34 + M)
-    N, K = 300, 8224
+    rng = synth.make_rng(34 + M + N)
+    K = 8224
     wg, wu = synth.q4k_matrix(rng, N, K), synth.q4k_matrix(rng, N, K)
     x = synth.activations(rng, M, K, sigma=2.0)
     gam = synth.gamma(rng, K)
